@@ -1,0 +1,134 @@
+// Host-side launchers of the gfx950 kernels (internal to the library).
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace moe {
+
+enum class Act { F32 = 0, BF16 = 1 };
+enum class WFmt { F32 = 0, BF16 = 1, U8 = 2 };
+
+// ------------------------------------------------------------------ routing
+struct TopkArgs {
+  const float* logits;      // [P][T][E] fp32 partial logits (summed over P)
+  int64_t part_stride;      // elements between partials (T * E)
+  int P;
+  int T, E, k, G, g;
+  int score_sigmoid, norm, use_ebias;
+  float rsf;
+  const float* router_bias;  // [E] or null
+  const float* expert_bias;  // [E] or null
+  int32_t* idx;              // [T, k]
+  float* w;                  // [T, k]
+};
+hipError_t launch_topk(const TopkArgs& a, hipStream_t s);
+
+struct PermuteArgs {
+  const int32_t* idx;   // [nslots]
+  int nslots, E, BM;    // BM > 0: also build the M-tile map for tile GEMMs of BM rows
+  int32_t* counts;      // [E]
+  int32_t* offsets;     // [E + 1]
+  int32_t* perm;        // [nslots]  slot ids grouped by expert, -1 tail
+  int32_t* slot_pos;    // [nslots]  position of each slot in perm, -1 if dropped
+  int32_t* active;      // [E]       experts with at least one slot, ascending
+  int32_t* tiles;       // [max_tiles * 2] (expert, start position)
+  int32_t* meta;        // [4]: D, number of M-tiles, valid slots
+  int32_t* counts_copy; // optional extra copy of counts (caller output) or null
+};
+hipError_t launch_permute(const PermuteArgs& a, hipStream_t s);
+
+// -------------------------------------------------- weight-streaming (decode) path
+// C[m][n] = sum_k A[m][k] W[n][k] with the weight rows streamed from HBM once per
+// group of <= 64 tokens.
+struct SkinnyRouterArgs {
+  const void* x;        // [T, H]
+  const void* W;        // [E, H]
+  float* out;           // [P][T][E]
+  int T, H, E, P;
+};
+hipError_t launch_skinny_router(const SkinnyRouterArgs& a, Act act, int ncu, hipStream_t s);
+
+struct SkinnyUpArgs {
+  const void* x;           // [T, H]
+  const void* gate;        // [E, I, H]
+  const void* up;          // [E, I, H]
+  const uint16_t *gate_s, *gate_z, *up_s, *up_z;  // u8 only: [E, I, H/64]
+  const void* sgate;       // [Is, H] or null
+  const void* sup;
+  void* hm;                // [T*k, I] act, rows in permuted (position) order
+  void* hs;                // [T, Is] act
+  const int32_t* counts;
+  const int32_t* offsets;
+  const int32_t* perm;
+  const int32_t* active;
+  const int32_t* meta;
+  int T, H, I, Is, k, E;
+};
+hipError_t launch_skinny_up(const SkinnyUpArgs& a, Act act, WFmt wf, int ncu, hipStream_t s);
+
+struct SkinnyDownArgs {
+  const void* hm;          // [T*k, I] position order
+  const void* hs;          // [T, Is]
+  const void* down;        // [E, H, I]
+  const uint16_t *down_s, *down_z;  // u8 only: [E, H, I/64]
+  const void* sdown;       // [H, Is] or null
+  const float* topk_w;     // [T*k]
+  float* r;                // [T*k, H] fp32, slot order, scaled by the routing weight
+  float* rs;               // [T, H] fp32 shared expert output
+  const int32_t* counts;
+  const int32_t* offsets;
+  const int32_t* perm;
+  const int32_t* active;
+  const int32_t* meta;
+  int T, H, I, Is, k, E;
+};
+hipError_t launch_skinny_down(const SkinnyDownArgs& a, Act act, WFmt wf, int ncu, hipStream_t s);
+
+struct CombineArgs {
+  const void* r;            // [T*k, H] slot order (fp32 or bf16)
+  const float* rs;          // [T, H] fp32 or null
+  const int32_t* idx;       // [T*k] routing (entries outside [0,E) skipped)
+  void* y;                  // [T, H] act
+  int T, H, k, E;
+  int r_bf16;
+};
+hipError_t launch_combine(const CombineArgs& a, Act act, hipStream_t s);
+
+// ------------------------------------------------------------- tiled MFMA path
+enum class AMode { DENSE = 0, GATHER = 1 };
+enum class Epi { F32 = 0, SWIGLU = 1, SCALED_SLOT = 2, COMBINE = 3 };
+
+struct TileArgs {
+  // A operand rows (bf16, K contiguous)
+  const uint16_t* A;      // DENSE: row r at A + r*K; GATHER: row = token perm[pos]/k
+  int K;
+  // B operand (weights, K contiguous): B0 (and B1 for SwiGLU) [experts][N][K]
+  const void* B0;
+  const void* B1;
+  const uint16_t *B0s, *B0z, *B1s, *B1z;  // u8 scale / zero [experts][N][K/64]
+  int64_t b_expert_stride;  // elements (codes) between experts
+  int N;                    // weight rows per expert (output columns)
+  // M tiling
+  int routed;               // 1: tiles from the permutation's tile map
+  int M;                    // dense: number of rows
+  const int32_t* tiles;     // routed: (expert, start position) per M-tile
+  const int32_t* meta;      // routed: meta[1] = number of M-tiles
+  const int32_t* offsets;   // routed: expert position ranges
+  const int32_t* perm;      // routed: slot of each position
+  int k;                    // top_k (slot -> token)
+  // epilogue
+  void* out;                // F32: float [M][N]; SWIGLU: bf16 [pos|row][N]; SCALED_SLOT: bf16 [slot][N];
+                            // COMBINE: bf16 y [T][N]
+  int ldo;                  // output row stride (elements)
+  const float* topk_w;      // SCALED_SLOT
+  const uint16_t* r;        // COMBINE: routed terms bf16 [T*k][N]
+  const int32_t* idx;       // COMBINE: routing
+  int E;                    // COMBINE: expert count (validity of idx)
+  int mtiles_bound;         // grid bound on M-tiles
+};
+hipError_t launch_tile_gemm(const TileArgs& a, AMode am, WFmt wf, Epi epi, hipStream_t s);
+
+constexpr int kTileM = 128;
+
+}  // namespace moe

@@ -1,0 +1,675 @@
+// Host side of the C ABI declared in include/moe.h: configuration checks, workspace
+// layout, and the launch sequence of the layer's kernels on the caller's stream.
+//
+// Checks follow the pages' defensive rules [mlxcel #838 "Defensive requirements"]:
+// magnitude ceilings on every architecture scalar before it is used, zero checks
+// before divisibility checks, routing bounds (1 <= top_k <= experts; with groups,
+// experts divisible by n_group and 1 <= topk_group <= n_group), sizes taken from
+// the caller's real arguments, and no exception or abort ever crossing the ABI.
+#include <cmath>
+#include <cstdarg>
+#include <cstdio>
+#include <cstring>
+
+#include "../../include/moe.h"
+#include "kernels.h"
+
+using namespace moe;
+
+namespace {
+
+thread_local char g_err[512];
+
+moe_status fail(moe_status s, const char* fmt, ...) {
+  va_list ap;
+  va_start(ap, fmt);
+  vsnprintf(g_err, sizeof g_err, fmt, ap);
+  va_end(ap);
+  return s;
+}
+
+moe_status ok() {
+  g_err[0] = 0;
+  return MOE_OK;
+}
+
+constexpr int64_t kMaxH = 16384, kMaxE = 1024, kMaxI = 32768, kMaxT = int64_t(1) << 20, kMaxK = 16;
+constexpr int64_t kMaxGroupsGpu = 64;
+constexpr int kDecodeMaxT = 64;
+
+bool is_flag(int32_t v) { return v == 0 || v == 1; }
+
+moe_status check_config(const moe_config* c) {
+  if (!c) return fail(MOE_EINVAL_ARG, "cfg is null");
+  // magnitudes first
+  if (c->hidden < 1 || c->hidden > kMaxH) return fail(MOE_EINVAL_CONFIG, "hidden=%lld outside [1, %lld]", (long long)c->hidden, (long long)kMaxH);
+  if (c->num_experts < 1 || c->num_experts > kMaxE)
+    return fail(MOE_EINVAL_CONFIG, "num_experts=%lld outside [1, %lld]", (long long)c->num_experts, (long long)kMaxE);
+  if (c->moe_intermediate < 1 || c->moe_intermediate > kMaxI)
+    return fail(MOE_EINVAL_CONFIG, "moe_intermediate=%lld outside [1, %lld]", (long long)c->moe_intermediate, (long long)kMaxI);
+  if (c->shared_intermediate < 0 || c->shared_intermediate > kMaxI)
+    return fail(MOE_EINVAL_CONFIG, "shared_intermediate=%lld outside [0, %lld]", (long long)c->shared_intermediate, (long long)kMaxI);
+  if (c->top_k < 1 || c->top_k > kMaxK || c->top_k > c->num_experts)
+    return fail(MOE_EINVAL_CONFIG, "top_k=%lld outside [1, min(num_experts, %lld)]", (long long)c->top_k, (long long)kMaxK);
+  // grouping: zero checks before divisibility
+  if (c->n_group < 1 || c->n_group > c->num_experts)
+    return fail(MOE_EINVAL_CONFIG, "n_group=%lld outside [1, num_experts]", (long long)c->n_group);
+  if (c->topk_group < 1 || c->topk_group > c->n_group)
+    return fail(MOE_EINVAL_CONFIG, "topk_group=%lld outside [1, n_group=%lld]", (long long)c->topk_group, (long long)c->n_group);
+  if (c->n_group > 1) {
+    if (c->num_experts % c->n_group != 0)
+      return fail(MOE_EINVAL_CONFIG, "num_experts=%lld not divisible by n_group=%lld", (long long)c->num_experts, (long long)c->n_group);
+    const int64_t gs = c->num_experts / c->n_group;
+    if (gs < 2) return fail(MOE_EINVAL_CONFIG, "n_group=%lld leaves groups of %lld expert(s); a group score needs two", (long long)c->n_group, (long long)gs);
+    if (c->top_k > c->topk_group * gs)
+      return fail(MOE_EINVAL_CONFIG, "top_k=%lld exceeds the %lld experts of the kept groups", (long long)c->top_k, (long long)(c->topk_group * gs));
+  }
+  if (c->score_function != MOE_SCORE_SOFTMAX && c->score_function != MOE_SCORE_SIGMOID)
+    return fail(MOE_EINVAL_CONFIG, "score_function=%d is neither softmax (0) nor sigmoid (1)", c->score_function);
+  if (!std::isfinite(c->routed_scaling_factor) || !(c->routed_scaling_factor > 0.f))
+    return fail(MOE_EINVAL_CONFIG, "routed_scaling_factor must be finite and > 0");
+  if (!is_flag(c->norm_topk_prob)) return fail(MOE_EINVAL_CONFIG, "norm_topk_prob must be 0 or 1");
+  if (!is_flag(c->use_expert_bias)) return fail(MOE_EINVAL_CONFIG, "use_expert_bias must be 0 or 1");
+  if (c->act_dtype != MOE_DT_F32 && c->act_dtype != MOE_DT_BF16)
+    return fail(MOE_EINVAL_CONFIG, "act_dtype=%d must be F32 or BF16", c->act_dtype);
+  if (c->router_dtype != c->act_dtype) return fail(MOE_EINVAL_CONFIG, "router_dtype must equal act_dtype");
+  if (c->shared_dtype != c->act_dtype) return fail(MOE_EINVAL_CONFIG, "shared_dtype must equal act_dtype");
+  if (c->expert_dtype != c->act_dtype && !(c->expert_dtype == MOE_DT_U8_AFFINE && c->act_dtype == MOE_DT_BF16))
+    return fail(MOE_EINVAL_CONFIG, "expert_dtype=%d must equal act_dtype or be U8_AFFINE with BF16 activations", c->expert_dtype);
+  if (c->expert_dtype == MOE_DT_U8_AFFINE && c->quant_group != 64)
+    return fail(MOE_EINVAL_CONFIG, "quant_group=%lld must be 64 for U8_AFFINE experts", (long long)c->quant_group);
+  if (c->path < MOE_PATH_AUTO || c->path > MOE_PATH_PREFILL) return fail(MOE_EINVAL_CONFIG, "path=%d unknown", c->path);
+  // valid, but outside what the gfx950 kernels implement
+  if (c->hidden % 64 || c->moe_intermediate % 64 || c->shared_intermediate % 64)
+    return fail(MOE_EUNSUPPORTED, "hidden, moe_intermediate and shared_intermediate must be multiples of 64");
+  if (c->n_group > kMaxGroupsGpu) return fail(MOE_EUNSUPPORTED, "n_group=%lld > %lld", (long long)c->n_group, (long long)kMaxGroupsGpu);
+  if (c->path == MOE_PATH_PREFILL && c->act_dtype == MOE_DT_F32)
+    return fail(MOE_EUNSUPPORTED, "the tiled MFMA path needs BF16 activations");
+  return MOE_OK;
+}
+
+size_t align256(size_t v) { return (v + 255) & ~size_t(255); }
+
+struct Plan {
+  bool decode;
+  int P;
+  int mtiles_bound;
+  size_t o_logits, o_idx, o_w, o_counts, o_offsets, o_perm, o_slotpos, o_active, o_meta, o_tiles, o_hm,
+      o_hs, o_r, o_rs, total;
+};
+
+int router_parts(const moe_config& c) {
+  const int rc = static_cast<int>((c.num_experts + 15) / 16);
+  int p = 256 / rc;
+  const int cap = static_cast<int>(c.hidden / 256) < 16 ? static_cast<int>(c.hidden / 256) : 16;
+  if (p > cap) p = cap;
+  if (p < 1) p = 1;
+  return p;
+}
+
+void make_plan(const moe_config& c, int64_t T, Plan& p) {
+  p.decode = c.path == MOE_PATH_DECODE ||
+             (c.path == MOE_PATH_AUTO && (T <= kDecodeMaxT || c.act_dtype == MOE_DT_F32));
+  const int64_t H = c.hidden, E = c.num_experts, k = c.top_k, I = c.moe_intermediate, Is = c.shared_intermediate;
+  const size_t ab = c.act_dtype == MOE_DT_F32 ? 4 : 2;
+  const int64_t slots = T * k;
+  p.P = p.decode ? router_parts(c) : 1;
+  const int64_t dmax = slots < E ? slots : E;
+  p.mtiles_bound = p.decode ? 0 : static_cast<int>((slots + dmax * (kTileM - 1)) / kTileM);
+  size_t o = 0;
+  auto take = [&](size_t bytes) {
+    const size_t at = o;
+    o += align256(bytes);
+    return at;
+  };
+  p.o_logits = take(size_t(p.P) * T * E * 4);
+  p.o_idx = take(slots * 4);
+  p.o_w = take(slots * 4);
+  p.o_counts = take(E * 4);
+  p.o_offsets = take((E + 1) * 4);
+  p.o_perm = take(slots * 4);
+  p.o_slotpos = take(slots * 4);
+  p.o_active = take(E * 4);
+  p.o_meta = take(64);
+  p.o_tiles = take(size_t(p.mtiles_bound) * 8);
+  p.o_hm = take(slots * I * ab);
+  p.o_hs = take(T * Is * ab);
+  p.o_r = take(slots * H * (p.decode ? 4 : 2));
+  p.o_rs = take(p.decode && Is > 0 ? T * H * 4 : 0);
+  p.total = o;
+}
+
+bool aligned(const void* p, size_t a) { return (reinterpret_cast<uintptr_t>(p) % a) == 0; }
+
+int device_cus() {
+  static int cache[64] = {0};
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) return 256;
+  if (!cache[dev]) {
+    int n = 0;
+    if (hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || n <= 0) n = 256;
+    cache[dev] = n;
+  }
+  return cache[dev];
+}
+
+template <class T>
+T* at(void* ws, size_t off) {
+  return reinterpret_cast<T*>(static_cast<char*>(ws) + off);
+}
+
+moe_status hip_fail(hipError_t e, const char* what) {
+  return fail(MOE_EHIP, "%s: %s", what, hipGetErrorString(e));
+}
+
+// ---------------------------------------------------------------- kernel timing
+struct ProfPair {
+  hipEvent_t start, stop;
+  int32_t stage;
+};
+struct Profiler {
+  int32_t mask = 0;
+  int32_t capacity = 0;
+  int32_t used = 0;
+  ProfPair* pool = nullptr;
+};
+Profiler g_prof;
+
+struct ProfScope {
+  ProfPair* pair = nullptr;
+  hipStream_t stream;
+  ProfScope(int32_t stage, hipStream_t s) : stream(s) {
+    if ((g_prof.mask & stage) && g_prof.used < g_prof.capacity) {
+      pair = &g_prof.pool[g_prof.used++];
+      pair->stage = stage;
+      if (hipEventRecord(pair->start, s) != hipSuccess) pair = nullptr;
+    }
+  }
+  ~ProfScope() {
+    if (pair) (void)hipEventRecord(pair->stop, stream);
+  }
+};
+
+#define MOE_LAUNCH_STAGE(stage, expr, what)            \
+  do {                                                 \
+    hipError_t e_;                                     \
+    {                                                  \
+      ProfScope ps_((stage), s);                       \
+      e_ = (expr);                                     \
+    }                                                  \
+    if (e_ != hipSuccess) return hip_fail(e_, what);   \
+  } while (0)
+
+moe_status check_T(int64_t T) {
+  if (T < 0 || T > kMaxT) return fail(MOE_EINVAL_ARG, "T=%lld outside [0, %lld]", (long long)T, (long long)kMaxT);
+  return MOE_OK;
+}
+
+moe_status check_ws(const moe_config& c, int64_t T, void* ws, size_t ws_bytes, Plan& p) {
+  make_plan(c, T, p);
+  if (ws_bytes < p.total) return fail(MOE_EWORKSPACE, "workspace of %zu bytes < %zu required", ws_bytes, p.total);
+  if (p.total > 0 && (!ws || !aligned(ws, 256))) return fail(MOE_EWORKSPACE, "workspace must be non-null and 256-byte aligned");
+  return MOE_OK;
+}
+
+#define REQUIRE_PTR(ptr, align, name)                                                           \
+  do {                                                                                          \
+    if (!(ptr)) return fail(MOE_EINVAL_ARG, "%s is null", name);                                \
+    if (!aligned((ptr), (align))) return fail(MOE_EINVAL_ARG, "%s is not %d-byte aligned", name, (int)(align)); \
+  } while (0)
+
+// router: logits + top-k into (idx, w)
+moe_status run_route(const moe_config& c, const Plan& p, int64_t T, const void* x, const void* router_w,
+                     const float* router_bias, const float* expert_bias, int32_t* idx, float* w, void* ws,
+                     hipStream_t s) {
+  const Act act = c.act_dtype == MOE_DT_F32 ? Act::F32 : Act::BF16;
+  float* logits = at<float>(ws, p.o_logits);
+  if (p.decode) {
+    SkinnyRouterArgs r{x, router_w, logits, static_cast<int>(T), static_cast<int>(c.hidden),
+                       static_cast<int>(c.num_experts), p.P};
+    MOE_LAUNCH_STAGE(MOE_STAGE_ROUTER, launch_skinny_router(r, act, device_cus(), s), "router logits");
+  } else {
+    TileArgs g{};
+    g.A = static_cast<const uint16_t*>(x);
+    g.K = static_cast<int>(c.hidden);
+    g.B0 = router_w;
+    g.b_expert_stride = 0;
+    g.N = static_cast<int>(c.num_experts);
+    g.routed = 0;
+    g.M = static_cast<int>(T);
+    g.out = logits;
+    g.ldo = static_cast<int>(c.num_experts);
+    g.mtiles_bound = static_cast<int>((T + kTileM - 1) / kTileM);
+    MOE_LAUNCH_STAGE(MOE_STAGE_ROUTER, launch_tile_gemm(g, AMode::DENSE, WFmt::BF16, Epi::F32, s), "router logits (tiled)");
+  }
+  TopkArgs t{};
+  t.logits = logits;
+  t.part_stride = T * c.num_experts;
+  t.P = p.P;
+  t.T = static_cast<int>(T);
+  t.E = static_cast<int>(c.num_experts);
+  t.k = static_cast<int>(c.top_k);
+  t.G = static_cast<int>(c.n_group);
+  t.g = static_cast<int>(c.topk_group);
+  t.score_sigmoid = c.score_function == MOE_SCORE_SIGMOID;
+  t.norm = c.norm_topk_prob;
+  t.use_ebias = c.use_expert_bias;
+  t.rsf = c.routed_scaling_factor;
+  t.router_bias = router_bias;
+  t.expert_bias = expert_bias;
+  t.idx = idx;
+  t.w = w;
+  MOE_LAUNCH_STAGE(MOE_STAGE_TOPK, launch_topk(t, s), "top-k");
+  return MOE_OK;
+}
+
+moe_status run_permute(const moe_config& c, const Plan& p, int64_t T, const int32_t* idx, int32_t* counts,
+                       int32_t* offsets, int32_t* perm, int32_t* counts_copy, void* ws, hipStream_t s) {
+  PermuteArgs a{};
+  a.idx = idx;
+  a.nslots = static_cast<int>(T * c.top_k);
+  a.E = static_cast<int>(c.num_experts);
+  a.BM = p.decode ? 0 : kTileM;
+  a.counts = counts;
+  a.offsets = offsets;
+  a.perm = perm;
+  a.slot_pos = at<int32_t>(ws, p.o_slotpos);
+  a.active = at<int32_t>(ws, p.o_active);
+  a.tiles = at<int32_t>(ws, p.o_tiles);
+  a.meta = at<int32_t>(ws, p.o_meta);
+  a.counts_copy = counts_copy;
+  MOE_LAUNCH_STAGE(MOE_STAGE_PERMUTE, launch_permute(a, s), "permutation");
+  return MOE_OK;
+}
+
+moe_status run_experts(const moe_config& c, const Plan& p, int64_t T, const void* x, const moe_weights* w,
+                       const int32_t* idx, const float* topk_w, void* y, void* ws, hipStream_t s) {
+  const Act act = c.act_dtype == MOE_DT_F32 ? Act::F32 : Act::BF16;
+  const WFmt wf = c.expert_dtype == MOE_DT_U8_AFFINE ? WFmt::U8 : (act == Act::F32 ? WFmt::F32 : WFmt::BF16);
+  const int Ti = static_cast<int>(T), H = static_cast<int>(c.hidden), I = static_cast<int>(c.moe_intermediate),
+            Is = static_cast<int>(c.shared_intermediate), k = static_cast<int>(c.top_k), E = static_cast<int>(c.num_experts);
+  int32_t* counts = at<int32_t>(ws, p.o_counts);
+  int32_t* offsets = at<int32_t>(ws, p.o_offsets);
+  int32_t* perm = at<int32_t>(ws, p.o_perm);
+  const int32_t* active = at<int32_t>(ws, p.o_active);
+  const int32_t* meta = at<int32_t>(ws, p.o_meta);
+  void* hm = at<void>(ws, p.o_hm);
+  void* hs = at<void>(ws, p.o_hs);
+  void* r = at<void>(ws, p.o_r);
+  float* rs = at<float>(ws, p.o_rs);
+  moe_status st = run_permute(c, p, T, idx, counts, offsets, perm, nullptr, ws, s);
+  if (st != MOE_OK) return st;
+  const int ncu = device_cus();
+  if (p.decode) {
+    SkinnyUpArgs u{};
+    u.x = x;
+    u.gate = w->gate;
+    u.up = w->up;
+    u.gate_s = w->gate_scale;
+    u.gate_z = w->gate_zero;
+    u.up_s = w->up_scale;
+    u.up_z = w->up_zero;
+    u.sgate = w->shared_gate;
+    u.sup = w->shared_up;
+    u.hm = hm;
+    u.hs = hs;
+    u.counts = counts;
+    u.offsets = offsets;
+    u.perm = perm;
+    u.active = active;
+    u.meta = meta;
+    u.T = Ti;
+    u.H = H;
+    u.I = I;
+    u.Is = Is;
+    u.k = k;
+    u.E = E;
+    MOE_LAUNCH_STAGE(MOE_STAGE_UP, launch_skinny_up(u, act, wf, ncu, s), "expert gate/up (streaming)");
+    SkinnyDownArgs d{};
+    d.hm = hm;
+    d.hs = hs;
+    d.down = w->down;
+    d.down_s = w->down_scale;
+    d.down_z = w->down_zero;
+    d.sdown = w->shared_down;
+    d.topk_w = topk_w;
+    d.r = static_cast<float*>(r);
+    d.rs = rs;
+    d.counts = counts;
+    d.offsets = offsets;
+    d.perm = perm;
+    d.active = active;
+    d.meta = meta;
+    d.T = Ti;
+    d.H = H;
+    d.I = I;
+    d.Is = Is;
+    d.k = k;
+    d.E = E;
+    MOE_LAUNCH_STAGE(MOE_STAGE_DOWN, launch_skinny_down(d, act, wf, ncu, s), "expert down (streaming)");
+    CombineArgs cb{r, Is > 0 ? rs : nullptr, idx, y, Ti, H, k, E, 0};
+    MOE_LAUNCH_STAGE(MOE_STAGE_COMBINE, launch_combine(cb, act, s), "combine");
+    return MOE_OK;
+  }
+  // tiled MFMA path (bf16 activations)
+  const int64_t slots = T * c.top_k;
+  const int64_t dmax = slots < E ? slots : E;
+  TileArgs g{};
+  g.A = static_cast<const uint16_t*>(x);
+  g.K = H;
+  g.B0 = w->gate;
+  g.B1 = w->up;
+  g.B0s = w->gate_scale;
+  g.B0z = w->gate_zero;
+  g.B1s = w->up_scale;
+  g.B1z = w->up_zero;
+  g.b_expert_stride = static_cast<int64_t>(I) * H;
+  g.N = I;
+  g.routed = 1;
+  g.tiles = at<int32_t>(ws, p.o_tiles);
+  g.meta = meta;
+  g.offsets = offsets;
+  g.perm = perm;
+  g.k = k;
+  g.out = hm;
+  g.ldo = I;
+  g.mtiles_bound = p.mtiles_bound;
+  MOE_LAUNCH_STAGE(MOE_STAGE_UP, launch_tile_gemm(g, AMode::GATHER, wf, Epi::SWIGLU, s), "expert gate/up (tiled)");
+  TileArgs d{};
+  d.A = static_cast<const uint16_t*>(hm);
+  d.K = I;
+  d.B0 = w->down;
+  d.B0s = w->down_scale;
+  d.B0z = w->down_zero;
+  d.b_expert_stride = static_cast<int64_t>(H) * I;
+  d.N = H;
+  d.routed = 1;
+  d.tiles = g.tiles;
+  d.meta = meta;
+  d.offsets = offsets;
+  d.perm = perm;
+  d.k = k;
+  d.out = r;
+  d.ldo = H;
+  d.topk_w = topk_w;
+  d.mtiles_bound = p.mtiles_bound;
+  MOE_LAUNCH_STAGE(MOE_STAGE_DOWN, launch_tile_gemm(d, AMode::DENSE, wf, Epi::SCALED_SLOT, s), "expert down (tiled)");
+  (void)dmax;
+  if (Is > 0) {
+    TileArgs su{};
+    su.A = static_cast<const uint16_t*>(x);
+    su.K = H;
+    su.B0 = w->shared_gate;
+    su.B1 = w->shared_up;
+    su.N = Is;
+    su.routed = 0;
+    su.M = Ti;
+    su.out = hs;
+    su.ldo = Is;
+    su.mtiles_bound = static_cast<int>((T + kTileM - 1) / kTileM);
+    MOE_LAUNCH_STAGE(MOE_STAGE_SHARED_UP, launch_tile_gemm(su, AMode::DENSE, WFmt::BF16, Epi::SWIGLU, s), "shared gate/up (tiled)");
+    TileArgs sd{};
+    sd.A = static_cast<const uint16_t*>(hs);
+    sd.K = Is;
+    sd.B0 = w->shared_down;
+    sd.N = H;
+    sd.routed = 0;
+    sd.M = Ti;
+    sd.out = y;
+    sd.ldo = H;
+    sd.r = static_cast<const uint16_t*>(r);
+    sd.idx = idx;
+    sd.k = k;
+    sd.E = E;
+    sd.mtiles_bound = su.mtiles_bound;
+    MOE_LAUNCH_STAGE(MOE_STAGE_SHARED_DOWN, launch_tile_gemm(sd, AMode::DENSE, WFmt::BF16, Epi::COMBINE, s), "shared down + combine (tiled)");
+  } else {
+    CombineArgs cb{r, nullptr, idx, y, Ti, H, k, E, 1};
+    MOE_LAUNCH_STAGE(MOE_STAGE_COMBINE, launch_combine(cb, act, s), "combine");
+  }
+  return MOE_OK;
+}
+
+moe_status check_weights(const moe_config& c, const moe_weights* w, bool need_router) {
+  if (!w) return fail(MOE_EINVAL_ARG, "weights is null");
+  if (need_router) REQUIRE_PTR(w->router, 16, "weights.router");
+  if (w->router_bias && !aligned(w->router_bias, 4)) return fail(MOE_EINVAL_ARG, "weights.router_bias is not 4-byte aligned");
+  if (need_router && c.use_expert_bias) REQUIRE_PTR(w->expert_bias, 4, "weights.expert_bias");
+  REQUIRE_PTR(w->gate, 16, "weights.gate");
+  REQUIRE_PTR(w->up, 16, "weights.up");
+  REQUIRE_PTR(w->down, 16, "weights.down");
+  if (c.expert_dtype == MOE_DT_U8_AFFINE) {
+    REQUIRE_PTR(w->gate_scale, 2, "weights.gate_scale");
+    REQUIRE_PTR(w->gate_zero, 2, "weights.gate_zero");
+    REQUIRE_PTR(w->up_scale, 2, "weights.up_scale");
+    REQUIRE_PTR(w->up_zero, 2, "weights.up_zero");
+    REQUIRE_PTR(w->down_scale, 2, "weights.down_scale");
+    REQUIRE_PTR(w->down_zero, 2, "weights.down_zero");
+  }
+  if (c.shared_intermediate > 0) {
+    REQUIRE_PTR(w->shared_gate, 16, "weights.shared_gate");
+    REQUIRE_PTR(w->shared_up, 16, "weights.shared_up");
+    REQUIRE_PTR(w->shared_down, 16, "weights.shared_down");
+  }
+  return MOE_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+moe_status moe_config_default(moe_config* cfg) {
+  if (!cfg) return fail(MOE_EINVAL_ARG, "cfg is null");
+  std::memset(cfg, 0, sizeof *cfg);
+  cfg->n_group = 1;
+  cfg->topk_group = 1;
+  cfg->score_function = MOE_SCORE_SOFTMAX;
+  cfg->norm_topk_prob = 1;
+  cfg->use_expert_bias = 0;
+  cfg->routed_scaling_factor = 1.0f;
+  cfg->act_dtype = cfg->router_dtype = cfg->expert_dtype = cfg->shared_dtype = MOE_DT_BF16;
+  cfg->quant_group = 64;
+  cfg->path = MOE_PATH_AUTO;
+  return ok();
+}
+
+moe_status moe_validate_config(const moe_config* cfg) {
+  try {
+    const moe_status s = check_config(cfg);
+    return s == MOE_OK ? ok() : s;
+  } catch (...) {
+    return fail(MOE_EINVAL_ARG, "internal error while validating");
+  }
+}
+
+moe_status moe_workspace_size(const moe_config* cfg, int64_t T, size_t* bytes) {
+  try {
+    moe_status s = check_config(cfg);
+    if (s != MOE_OK) return s;
+    if ((s = check_T(T)) != MOE_OK) return s;
+    if (!bytes) return fail(MOE_EINVAL_ARG, "bytes is null");
+    Plan p;
+    make_plan(*cfg, T, p);
+    *bytes = p.total;
+    return ok();
+  } catch (...) {
+    return fail(MOE_EINVAL_ARG, "internal error while sizing");
+  }
+}
+
+moe_status moe_route(const moe_config* cfg, int64_t T, const void* x, const void* router_w, const float* router_bias,
+                     const float* expert_bias, int32_t* topk_idx, float* topk_w, void* ws, size_t ws_bytes,
+                     moe_stream_t stream) {
+  try {
+    moe_status s = check_config(cfg);
+    if (s != MOE_OK) return s;
+    if ((s = check_T(T)) != MOE_OK) return s;
+    if (T == 0) return ok();
+    REQUIRE_PTR(x, 16, "x");
+    REQUIRE_PTR(router_w, 16, "router_w");
+    if (router_bias && !aligned(router_bias, 4)) return fail(MOE_EINVAL_ARG, "router_bias is not 4-byte aligned");
+    if (cfg->use_expert_bias) REQUIRE_PTR(expert_bias, 4, "expert_bias");
+    REQUIRE_PTR(topk_idx, 4, "topk_idx");
+    REQUIRE_PTR(topk_w, 4, "topk_w");
+    Plan p;
+    if ((s = check_ws(*cfg, T, ws, ws_bytes, p)) != MOE_OK) return s;
+    s = run_route(*cfg, p, T, x, router_w, router_bias, cfg->use_expert_bias ? expert_bias : nullptr, topk_idx,
+                  topk_w, ws, static_cast<hipStream_t>(stream));
+    return s == MOE_OK ? ok() : s;
+  } catch (...) {
+    return fail(MOE_EINVAL_ARG, "internal error in moe_route");
+  }
+}
+
+moe_status moe_permute(const moe_config* cfg, int64_t T, const int32_t* topk_idx, int32_t* counts, int32_t* offsets,
+                       int32_t* perm, void* ws, size_t ws_bytes, moe_stream_t stream) {
+  try {
+    moe_status s = check_config(cfg);
+    if (s != MOE_OK) return s;
+    if ((s = check_T(T)) != MOE_OK) return s;
+    if (T == 0) return ok();
+    REQUIRE_PTR(topk_idx, 4, "topk_idx");
+    REQUIRE_PTR(counts, 4, "counts");
+    REQUIRE_PTR(offsets, 4, "offsets");
+    REQUIRE_PTR(perm, 4, "perm");
+    Plan p;
+    if ((s = check_ws(*cfg, T, ws, ws_bytes, p)) != MOE_OK) return s;
+    s = run_permute(*cfg, p, T, topk_idx, counts, offsets, perm, nullptr, ws, static_cast<hipStream_t>(stream));
+    return s == MOE_OK ? ok() : s;
+  } catch (...) {
+    return fail(MOE_EINVAL_ARG, "internal error in moe_permute");
+  }
+}
+
+moe_status moe_experts(const moe_config* cfg, int64_t T, const void* x, const moe_weights* w, const int32_t* topk_idx,
+                       const float* topk_w, void* y, void* ws, size_t ws_bytes, moe_stream_t stream) {
+  try {
+    moe_status s = check_config(cfg);
+    if (s != MOE_OK) return s;
+    if ((s = check_T(T)) != MOE_OK) return s;
+    if (T == 0) return ok();
+    REQUIRE_PTR(x, 16, "x");
+    REQUIRE_PTR(y, 16, "y");
+    REQUIRE_PTR(topk_idx, 4, "topk_idx");
+    REQUIRE_PTR(topk_w, 4, "topk_w");
+    if ((s = check_weights(*cfg, w, false)) != MOE_OK) return s;
+    Plan p;
+    if ((s = check_ws(*cfg, T, ws, ws_bytes, p)) != MOE_OK) return s;
+    s = run_experts(*cfg, p, T, x, w, topk_idx, topk_w, y, ws, static_cast<hipStream_t>(stream));
+    return s == MOE_OK ? ok() : s;
+  } catch (...) {
+    return fail(MOE_EINVAL_ARG, "internal error in moe_experts");
+  }
+}
+
+moe_status moe_forward(const moe_config* cfg, int64_t T, const void* x, const moe_weights* w, void* y,
+                       int32_t* topk_idx_out, float* topk_w_out, int32_t* expert_counts_out, void* ws,
+                       size_t ws_bytes, moe_stream_t stream) {
+  try {
+    moe_status s = check_config(cfg);
+    if (s != MOE_OK) return s;
+    if ((s = check_T(T)) != MOE_OK) return s;
+    if (T == 0) return ok();
+    REQUIRE_PTR(x, 16, "x");
+    REQUIRE_PTR(y, 16, "y");
+    if (topk_idx_out && !aligned(topk_idx_out, 4)) return fail(MOE_EINVAL_ARG, "topk_idx_out is not 4-byte aligned");
+    if (topk_w_out && !aligned(topk_w_out, 4)) return fail(MOE_EINVAL_ARG, "topk_w_out is not 4-byte aligned");
+    if (expert_counts_out && !aligned(expert_counts_out, 4)) return fail(MOE_EINVAL_ARG, "expert_counts_out is not 4-byte aligned");
+    if ((s = check_weights(*cfg, w, true)) != MOE_OK) return s;
+    Plan p;
+    if ((s = check_ws(*cfg, T, ws, ws_bytes, p)) != MOE_OK) return s;
+    const hipStream_t st = static_cast<hipStream_t>(stream);
+    int32_t* idx = topk_idx_out ? topk_idx_out : at<int32_t>(ws, p.o_idx);
+    float* wt = topk_w_out ? topk_w_out : at<float>(ws, p.o_w);
+    s = run_route(*cfg, p, T, x, w->router, w->router_bias, cfg->use_expert_bias ? w->expert_bias : nullptr, idx, wt,
+                  ws, st);
+    if (s != MOE_OK) return s;
+    s = run_experts(*cfg, p, T, x, w, idx, wt, y, ws, st);
+    if (s != MOE_OK) return s;
+    if (expert_counts_out) {
+      const hipError_t e = hipMemcpyAsync(expert_counts_out, at<int32_t>(ws, p.o_counts),
+                                          sizeof(int32_t) * cfg->num_experts, hipMemcpyDeviceToDevice, st);
+      if (e != hipSuccess) return hip_fail(e, "expert counts copy");
+    }
+    return ok();
+  } catch (...) {
+    return fail(MOE_EINVAL_ARG, "internal error in moe_forward");
+  }
+}
+
+moe_status moe_profile_enable(int32_t stage_mask, int32_t capacity) {
+  try {
+    if (capacity < 1 || capacity > (1 << 20)) return fail(MOE_EINVAL_ARG, "capacity must be in [1, 2^20]");
+    moe_profile_disable();
+    g_prof.pool = new ProfPair[capacity];
+    for (int32_t i = 0; i < capacity; ++i) {
+      hipError_t e = hipEventCreate(&g_prof.pool[i].start);
+      if (e == hipSuccess) e = hipEventCreate(&g_prof.pool[i].stop);
+      if (e != hipSuccess) {
+        g_prof.capacity = i;
+        moe_profile_disable();
+        return hip_fail(e, "hipEventCreate");
+      }
+    }
+    g_prof.capacity = capacity;
+    g_prof.used = 0;
+    g_prof.mask = stage_mask;
+    return ok();
+  } catch (...) {
+    return fail(MOE_EINVAL_ARG, "internal error in moe_profile_enable");
+  }
+}
+
+moe_status moe_profile_collect(int32_t stage, float* total_ms, int32_t* launches) {
+  if (!total_ms || !launches) return fail(MOE_EINVAL_ARG, "null output");
+  float sum = 0.f;
+  int32_t n = 0;
+  for (int32_t i = 0; i < g_prof.used; ++i) {
+    ProfPair& p = g_prof.pool[i];
+    if (p.stage != stage) continue;
+    hipError_t e = hipEventSynchronize(p.stop);
+    float ms = 0.f;
+    if (e == hipSuccess) e = hipEventElapsedTime(&ms, p.start, p.stop);
+    if (e != hipSuccess) return hip_fail(e, "event timing");
+    sum += ms;
+    ++n;
+  }
+  *total_ms = sum;
+  *launches = n;
+  return ok();
+}
+
+moe_status moe_profile_disable(void) {
+  if (g_prof.pool) {
+    for (int32_t i = 0; i < g_prof.capacity; ++i) {
+      (void)hipEventDestroy(g_prof.pool[i].start);
+      (void)hipEventDestroy(g_prof.pool[i].stop);
+    }
+    delete[] g_prof.pool;
+  }
+  g_prof = Profiler{};
+  return ok();
+}
+
+moe_status moe_profile_reset(void) {
+  g_prof.used = 0;
+  return ok();
+}
+
+const char* moe_status_str(moe_status s) {
+  switch (s) {
+    case MOE_OK: return "ok";
+    case MOE_EINVAL_CONFIG: return "invalid configuration";
+    case MOE_EINVAL_ARG: return "invalid argument";
+    case MOE_EWORKSPACE: return "workspace missing or too small";
+    case MOE_EUNSUPPORTED: return "valid layer not supported by the gfx950 kernels";
+    case MOE_EHIP: return "HIP runtime error";
+  }
+  return "unknown status";
+}
+
+const char* moe_last_error(void) { return g_err; }
+
+int32_t moe_abi_version(void) { return 1; }
+
+}  // extern "C"

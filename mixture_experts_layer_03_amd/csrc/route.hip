@@ -1,0 +1,299 @@
+// Router top-k (one wavefront per token) and token permutation by expert (one
+// workgroup: LDS histogram, exclusive scan, scatter) for gfx950.
+//
+// Routing semantics follow the model pages: scores are softmax over all experts or
+// an elementwise sigmoid of the logits; the correction bias is added to a copy of
+// the scores used for selection only; with grouping, each contiguous group is scored
+// by the sum of its two largest biased scores, the topk_group best groups are kept
+// and the other experts' selection scores are set to zero; the top_k experts by
+// selection score are taken, their weights gathered from the unbiased scores,
+// renormalised by (sum + 1e-20) when top_k > 1 and norm_topk_prob, and multiplied by
+// routed_scaling_factor [mlxcel #838 "Router: selection uses biased scores, weights
+// come from unbiased scores", "Architecture notes", "moe_router_enable_routed_scaling
+// is dead code upstream"; Ling-2.6-flash-JANGTQ card, MoE routing paragraph].
+#include "common.h"
+#include "kernels.h"
+
+namespace moe {
+
+namespace {
+
+constexpr float kNegInf = -__builtin_huge_valf();
+
+// Expert e lives in lane e / EPL, register e % EPL: each lane owns EPL consecutive
+// experts, so a row of logits is read with contiguous per-lane runs.
+template <int EPL>
+__global__ __launch_bounds__(256) void k_topk(TopkArgs a) {
+  const int lane = lane_id();
+  const int t = blockIdx.x * 4 + (threadIdx.x >> 6);
+  if (t >= a.T) return;  // whole wavefront leaves; no block barrier below
+  const int E = a.E;
+
+  float s[EPL], sel[EPL];
+  bool valid[EPL];
+#pragma unroll
+  for (int i = 0; i < EPL; ++i) {
+    const int e = lane * EPL + i;
+    valid[i] = e < E;
+    float v = 0.f;
+    if (valid[i]) {
+      const float* p = a.logits + static_cast<int64_t>(t) * E + e;
+      for (int q = 0; q < a.P; ++q) v += p[q * a.part_stride];
+      if (a.router_bias) v += a.router_bias[e];
+    }
+    s[i] = v;
+  }
+
+  // scores
+  if (a.score_sigmoid) {
+#pragma unroll
+    for (int i = 0; i < EPL; ++i) s[i] = valid[i] ? 1.0f / (1.0f + expf(-s[i])) : 0.f;
+  } else {
+    float m = kNegInf;
+#pragma unroll
+    for (int i = 0; i < EPL; ++i)
+      if (valid[i]) m = fmaxf(m, s[i]);
+    m = wave_max(m);
+    float sum = 0.f;
+#pragma unroll
+    for (int i = 0; i < EPL; ++i) {
+      s[i] = valid[i] ? expf(s[i] - m) : 0.f;
+      sum += s[i];
+    }
+    sum = wave_sum(sum);
+#pragma unroll
+    for (int i = 0; i < EPL; ++i) s[i] = s[i] / sum;
+  }
+
+  // selection copy (correction bias for selection only)
+#pragma unroll
+  for (int i = 0; i < EPL; ++i) {
+    const int e = lane * EPL + i;
+    float b = (valid[i] && a.use_ebias) ? a.expert_bias[e] : 0.f;
+    sel[i] = valid[i] ? s[i] + b : kNegInf;
+  }
+
+  // grouped mask: keep the g groups with the largest top-2 sums, zero the rest
+  if (a.G > 1 && a.g < a.G) {
+    const int gs = E / a.G;
+    int grp[EPL];
+#pragma unroll
+    for (int i = 0; i < EPL; ++i) grp[i] = valid[i] ? (lane * EPL + i) / gs : -1;
+    float sig_mine = kNegInf;
+    for (int gr = 0; gr < a.G; ++gr) {
+      float t1 = kNegInf, t2 = kNegInf;
+#pragma unroll
+      for (int i = 0; i < EPL; ++i) {
+        if (grp[i] == gr) {
+          const float x = sel[i];
+          if (x > t1) {
+            t2 = t1;
+            t1 = x;
+          } else if (x > t2) {
+            t2 = x;
+          }
+        }
+      }
+#pragma unroll
+      for (int o = 32; o > 0; o >>= 1) {
+        const float o1 = __shfl_xor(t1, o, kWave), o2 = __shfl_xor(t2, o, kWave);
+        const float hi = fmaxf(t1, o1);
+        const float lo = fmaxf(fminf(t1, o1), fmaxf(t2, o2));
+        t1 = hi;
+        t2 = lo;
+      }
+      if (lane == gr) sig_mine = t1 + t2;
+    }
+    int rank = 0;
+    for (int gr = 0; gr < a.G; ++gr) {
+      const float o = __shfl(sig_mine, gr, kWave);
+      rank += (o > sig_mine || (o == sig_mine && gr < lane)) ? 1 : 0;
+    }
+    const unsigned long long kept = __ballot(lane < a.G && rank < a.g);
+#pragma unroll
+    for (int i = 0; i < EPL; ++i)
+      if (grp[i] >= 0 && !((kept >> grp[i]) & 1ull)) sel[i] = 0.0f;
+  }
+
+  // top-k: k rounds of wave arg-max, larger score first, equal scores -> lower index
+  uint32_t taken = 0;
+  int my_idx = 0x7fffffff;
+  float my_w = 0.f;
+  for (int j = 0; j < a.k; ++j) {
+    float bv = kNegInf, bo = 0.f;
+    int bi = 0x7fffffff;
+#pragma unroll
+    for (int i = 0; i < EPL; ++i) {
+      if (valid[i] && !((taken >> i) & 1u) && sel[i] > bv) {
+        bv = sel[i];
+        bi = lane * EPL + i;
+        bo = s[i];
+      }
+    }
+#pragma unroll
+    for (int o = 32; o > 0; o >>= 1) {
+      const float ov = __shfl_xor(bv, o, kWave), oo = __shfl_xor(bo, o, kWave);
+      const int oi = __shfl_xor(bi, o, kWave);
+      if (ov > bv || (ov == bv && oi < bi)) {
+        bv = ov;
+        bi = oi;
+        bo = oo;
+      }
+    }
+    if (bi != 0x7fffffff && bi / EPL == lane) taken |= 1u << (bi - lane * EPL);
+    if (lane == j) {
+      my_idx = bi;
+      my_w = bo;
+    }
+  }
+
+  const float tot = wave_sum(lane < a.k ? my_w : 0.f);
+  if (a.k > 1 && a.norm) my_w = my_w / (tot + 1e-20f);
+  my_w *= a.rsf;
+  if (lane < a.k) {
+    a.idx[static_cast<int64_t>(t) * a.k + lane] = my_idx;
+    a.w[static_cast<int64_t>(t) * a.k + lane] = my_w;
+  }
+}
+
+constexpr int kPermThreads = 1024;
+constexpr int kPermUnroll = 4;
+
+__global__ __launch_bounds__(kPermThreads) void k_permute(PermuteArgs a) {
+  __shared__ int cnt[1024];
+  __shared__ int off[1024];
+  __shared__ int wtot[3][16];
+  __shared__ int total_s;
+  const int tid = threadIdx.x;
+  const int lane = tid & 63;
+  const int wv = tid >> 6;
+  const int E = a.E;
+  const int n = a.nslots;
+  if (tid < E) cnt[tid] = 0;
+  __syncthreads();
+
+  // pass 1: rank of each slot inside its expert (LDS atomics)
+  for (int base = 0; base < n; base += kPermThreads * kPermUnroll) {
+    int e[kPermUnroll];
+#pragma unroll
+    for (int u = 0; u < kPermUnroll; ++u) {
+      const int s = base + u * kPermThreads + tid;
+      e[u] = s < n ? a.idx[s] : -1;
+    }
+#pragma unroll
+    for (int u = 0; u < kPermUnroll; ++u) {
+      const int s = base + u * kPermThreads + tid;
+      if (s < n) {
+        int p = -1;
+        if (e[u] >= 0 && e[u] < E) p = atomicAdd(&cnt[e[u]], 1);
+        a.slot_pos[s] = p;
+      }
+    }
+  }
+  __syncthreads();
+
+  // exclusive scans of: counts, active flags, M-tiles per expert
+  const int c = tid < E ? cnt[tid] : 0;
+  const int f = c > 0 ? 1 : 0;
+  const int nt = (a.BM > 0) ? (c + a.BM - 1) / a.BM : 0;
+  int ci = c, fi = f, ti = nt;
+#pragma unroll
+  for (int o = 1; o < 64; o <<= 1) {
+    const int x = __shfl_up(ci, o, kWave), y = __shfl_up(fi, o, kWave), z = __shfl_up(ti, o, kWave);
+    if (lane >= o) {
+      ci += x;
+      fi += y;
+      ti += z;
+    }
+  }
+  if (lane == 63) {
+    wtot[0][wv] = ci;
+    wtot[1][wv] = fi;
+    wtot[2][wv] = ti;
+  }
+  __syncthreads();
+  if (wv == 0) {
+#pragma unroll
+    for (int q = 0; q < 3; ++q) {
+      const int v = lane < 16 ? wtot[q][lane] : 0;
+      int inc = v;
+#pragma unroll
+      for (int o = 1; o < 16; o <<= 1) {
+        const int x = __shfl_up(inc, o, kWave);
+        if (lane >= o) inc += x;
+      }
+      if (lane < 16) wtot[q][lane] = inc - v;
+    }
+  }
+  __syncthreads();
+  const int ce = ci - c + wtot[0][wv];
+  const int fe = fi - f + wtot[1][wv];
+  const int te = ti - nt + wtot[2][wv];
+  if (tid < E) {
+    off[tid] = ce;
+    a.counts[tid] = c;
+    a.offsets[tid] = ce;
+    if (a.counts_copy) a.counts_copy[tid] = c;
+    if (f) a.active[fe] = tid;
+    for (int q = 0; q < nt; ++q) {
+      a.tiles[2 * (te + q)] = tid;
+      a.tiles[2 * (te + q) + 1] = ce + q * a.BM;
+    }
+  }
+  if (tid == E - 1) {
+    a.offsets[E] = ce + c;
+    a.meta[0] = fe + f;
+    a.meta[1] = te + nt;
+    a.meta[2] = ce + c;
+    total_s = ce + c;
+  }
+  __syncthreads();
+
+  // pass 2: scatter slot ids to their positions
+  for (int base = 0; base < n; base += kPermThreads * kPermUnroll) {
+    int p[kPermUnroll], e[kPermUnroll];
+#pragma unroll
+    for (int u = 0; u < kPermUnroll; ++u) {
+      const int s = base + u * kPermThreads + tid;
+      p[u] = s < n ? a.slot_pos[s] : -1;
+      e[u] = s < n ? a.idx[s] : -1;
+    }
+#pragma unroll
+    for (int u = 0; u < kPermUnroll; ++u) {
+      const int s = base + u * kPermThreads + tid;
+      if (p[u] >= 0) {
+        const int pos = off[e[u]] + p[u];
+        a.perm[pos] = s;
+        a.slot_pos[s] = pos;
+      }
+    }
+  }
+  const int total = total_s;
+  for (int q = total + tid; q < n; q += kPermThreads) a.perm[q] = -1;
+}
+
+}  // namespace
+
+hipError_t launch_topk(const TopkArgs& a, hipStream_t s) {
+  if (a.T <= 0) return hipSuccess;
+  const dim3 grid((a.T + 3) / 4), block(256);
+  const int epl = (a.E + 63) / 64;
+  if (epl <= 1)
+    hipLaunchKernelGGL(k_topk<1>, grid, block, 0, s, a);
+  else if (epl <= 2)
+    hipLaunchKernelGGL(k_topk<2>, grid, block, 0, s, a);
+  else if (epl <= 4)
+    hipLaunchKernelGGL(k_topk<4>, grid, block, 0, s, a);
+  else if (epl <= 8)
+    hipLaunchKernelGGL(k_topk<8>, grid, block, 0, s, a);
+  else
+    hipLaunchKernelGGL(k_topk<16>, grid, block, 0, s, a);
+  return hipGetLastError();
+}
+
+hipError_t launch_permute(const PermuteArgs& a, hipStream_t s) {
+  hipLaunchKernelGGL(k_permute, dim3(1), dim3(kPermThreads), 0, s, a);
+  return hipGetLastError();
+}
+
+}  // namespace moe

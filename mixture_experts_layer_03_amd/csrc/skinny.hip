@@ -1,0 +1,677 @@
+// Weight-streaming kernels for small token batches (decode).
+//
+// Decode is bound by reading weights: only the selected experts' weights are read
+// [Ling-3.0-flash-GGUF card, "Measured performance": decode is memory-bandwidth
+// bound and only the selected experts are read].  Each wavefront owns 16 weight
+// rows (one MFMA N-tile) and a range of the reduction axis, streams those rows once
+// with 16-byte loads, and multiplies them against up to 64 tokens held as four
+// 16-row MFMA M-tiles (tokens padded to 16; padded rows are computed and dropped).
+//
+// K ordering: per 64-element step, lane l covers the 16 consecutive elements
+// [16 * (l / 16), +16) of the step for its row l % 16 and feeds them to the MFMA
+// K-group l / 16.  The same ordering is applied to the token operand, so each
+// product pairs equal k; every row is read in 128-byte runs (4 lanes x 32 bytes).
+#include "common.h"
+#include "kernels.h"
+
+namespace moe {
+
+namespace {
+
+template <Act A>
+struct ActType;
+template <>
+struct ActType<Act::BF16> {
+  using T = uint16_t;
+};
+template <>
+struct ActType<Act::F32> {
+  using T = float;
+};
+
+template <WFmt F>
+struct WType;
+template <>
+struct WType<WFmt::BF16> {
+  using T = uint16_t;
+};
+template <>
+struct WType<WFmt::F32> {
+  using T = float;
+};
+template <>
+struct WType<WFmt::U8> {
+  using T = uint8_t;
+};
+
+// Per-lane operand pointers of one wavefront task.
+template <Act ACT, WFmt WF, int NMAT, int MT>
+struct Task {
+  using AT = typename ActType<ACT>::T;
+  using WT = typename WType<WF>::T;
+  const AT* arow[MT];          // token row of lane (l % 16) in each M-tile (clamped valid)
+  const WT* wrow[NMAT];        // weight row of lane (l % 16) (clamped valid)
+  const uint16_t* srow[NMAT];  // u8: scale row (one per 64 elements)
+  const uint16_t* zrow[NMAT];  // u8: zero-point row
+  int mt_live;                 // M-tiles holding at least one real token
+};
+
+__device__ __forceinline__ uint4 ld16(const void* p) { return *reinterpret_cast<const uint4*>(p); }
+
+// 16 u8 codes -> 16 bf16 values (q - z), exact (integers in [-255, 255]).
+__device__ __forceinline__ void dequant16(const uint4& q, float z, uint4& lo, uint4& hi) {
+  const uint32_t w[4] = {q.x, q.y, q.z, q.w};
+  uint32_t o[8];
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    const float f0 = static_cast<float>(w[i] & 0xffu) - z;
+    const float f1 = static_cast<float>((w[i] >> 8) & 0xffu) - z;
+    const float f2 = static_cast<float>((w[i] >> 16) & 0xffu) - z;
+    const float f3 = static_cast<float>(w[i] >> 24) - z;
+    o[2 * i] = pack_bf16x2(f0, f1);
+    o[2 * i + 1] = pack_bf16x2(f2, f3);
+  }
+  lo = make_uint4(o[0], o[1], o[2], o[3]);
+  hi = make_uint4(o[4], o[5], o[6], o[7]);
+}
+
+// acc[mat][mt] += A(tokens) x W(rows)^T over elements [k0, k1) (multiples of 64).
+template <Act ACT, WFmt WF, int NMAT, int MT>
+__device__ __forceinline__ void stream_rows(const Task<ACT, WF, NMAT, MT>& t, int k0, int k1,
+                                            f32x4 (&acc)[NMAT][MT]) {
+  const int q = lane_id() >> 4;
+  if constexpr (ACT == Act::BF16 && WF == WFmt::BF16) {
+    constexpr int U = 4;
+    int k = k0;
+    for (; k + 64 * U <= k1; k += 64 * U) {
+      uint4 w0[U][NMAT], w1[U][NMAT];
+#pragma unroll
+      for (int u = 0; u < U; ++u)
+#pragma unroll
+        for (int m = 0; m < NMAT; ++m) {
+          const uint16_t* p = t.wrow[m] + k + 64 * u + 16 * q;
+          w0[u][m] = ld_stream(reinterpret_cast<const uint4*>(p));
+          w1[u][m] = ld_stream(reinterpret_cast<const uint4*>(p + 8));
+        }
+#pragma unroll
+      for (int mt = 0; mt < MT; ++mt) {
+        if (mt < t.mt_live) {
+          uint4 a0[U], a1[U];
+#pragma unroll
+          for (int u = 0; u < U; ++u) {
+            const uint16_t* p = t.arow[mt] + k + 64 * u + 16 * q;
+            a0[u] = ld16(p);
+            a1[u] = ld16(p + 8);
+          }
+#pragma unroll
+          for (int u = 0; u < U; ++u)
+#pragma unroll
+            for (int m = 0; m < NMAT; ++m) {
+              acc[m][mt] = mfma16_bf16(a0[u], w0[u][m], acc[m][mt]);
+              acc[m][mt] = mfma16_bf16(a1[u], w1[u][m], acc[m][mt]);
+            }
+        }
+      }
+    }
+    for (; k < k1; k += 64) {
+      uint4 w0[NMAT], w1[NMAT];
+#pragma unroll
+      for (int m = 0; m < NMAT; ++m) {
+        const uint16_t* p = t.wrow[m] + k + 16 * q;
+        w0[m] = ld_stream(reinterpret_cast<const uint4*>(p));
+        w1[m] = ld_stream(reinterpret_cast<const uint4*>(p + 8));
+      }
+#pragma unroll
+      for (int mt = 0; mt < MT; ++mt) {
+        if (mt < t.mt_live) {
+          const uint16_t* p = t.arow[mt] + k + 16 * q;
+          const uint4 a0 = ld16(p), a1 = ld16(p + 8);
+#pragma unroll
+          for (int m = 0; m < NMAT; ++m) {
+            acc[m][mt] = mfma16_bf16(a0, w0[m], acc[m][mt]);
+            acc[m][mt] = mfma16_bf16(a1, w1[m], acc[m][mt]);
+          }
+        }
+      }
+    }
+  } else if constexpr (ACT == Act::BF16 && WF == WFmt::U8) {
+    // one 64-element step = one quantisation group: exact (q - z) products per
+    // group, then one fp32 scale per row and group
+    constexpr int U = 2;
+    int k = k0;
+    for (; k + 64 * U <= k1; k += 64 * U) {
+      uint4 wq[U][NMAT];
+      float sc[U][NMAT], zp[U][NMAT];
+#pragma unroll
+      for (int u = 0; u < U; ++u)
+#pragma unroll
+        for (int m = 0; m < NMAT; ++m) {
+          wq[u][m] = ld_stream(reinterpret_cast<const uint4*>(t.wrow[m] + k + 64 * u + 16 * q));
+          const int gi = (k >> 6) + u;
+          sc[u][m] = f16_to_f32(t.srow[m][gi]);
+          zp[u][m] = f16_to_f32(t.zrow[m][gi]);
+        }
+      uint4 wl[U][NMAT], wh[U][NMAT];
+#pragma unroll
+      for (int u = 0; u < U; ++u)
+#pragma unroll
+        for (int m = 0; m < NMAT; ++m) dequant16(wq[u][m], zp[u][m], wl[u][m], wh[u][m]);
+#pragma unroll
+      for (int mt = 0; mt < MT; ++mt) {
+        if (mt < t.mt_live) {
+#pragma unroll
+          for (int u = 0; u < U; ++u) {
+            const uint16_t* p = t.arow[mt] + k + 64 * u + 16 * q;
+            const uint4 a0 = ld16(p), a1 = ld16(p + 8);
+#pragma unroll
+            for (int m = 0; m < NMAT; ++m) {
+              f32x4 g = {0.f, 0.f, 0.f, 0.f};
+              g = mfma16_bf16(a0, wl[u][m], g);
+              g = mfma16_bf16(a1, wh[u][m], g);
+              acc[m][mt] += sc[u][m] * g;
+            }
+          }
+        }
+      }
+    }
+    for (; k < k1; k += 64) {
+#pragma unroll
+      for (int m = 0; m < NMAT; ++m) {
+        const uint4 wq = ld_stream(reinterpret_cast<const uint4*>(t.wrow[m] + k + 16 * q));
+        const float sc = f16_to_f32(t.srow[m][k >> 6]);
+        const float zp = f16_to_f32(t.zrow[m][k >> 6]);
+        uint4 wl, wh;
+        dequant16(wq, zp, wl, wh);
+#pragma unroll
+        for (int mt = 0; mt < MT; ++mt) {
+          if (mt < t.mt_live) {
+            const uint16_t* p = t.arow[mt] + k + 16 * q;
+            f32x4 g = {0.f, 0.f, 0.f, 0.f};
+            g = mfma16_bf16(ld16(p), wl, g);
+            g = mfma16_bf16(ld16(p + 8), wh, g);
+            acc[m][mt] += sc * g;
+          }
+        }
+      }
+    }
+  } else {
+    // fp32 activations and weights: 16 MFMA 16x16x4 per 64-element step
+    for (int k = k0; k < k1; k += 64) {
+      float4 w[NMAT][4];
+#pragma unroll
+      for (int m = 0; m < NMAT; ++m)
+#pragma unroll
+        for (int c = 0; c < 4; ++c)
+          w[m][c] = *reinterpret_cast<const float4*>(t.wrow[m] + k + 16 * q + 4 * c);
+#pragma unroll
+      for (int mt = 0; mt < MT; ++mt) {
+        if (mt < t.mt_live) {
+          float4 av[4];
+#pragma unroll
+          for (int c = 0; c < 4; ++c)
+            av[c] = *reinterpret_cast<const float4*>(t.arow[mt] + k + 16 * q + 4 * c);
+#pragma unroll
+          for (int m = 0; m < NMAT; ++m)
+#pragma unroll
+            for (int c = 0; c < 4; ++c) {
+              acc[m][mt] = mfma16_f32(av[c].x, w[m][c].x, acc[m][mt]);
+              acc[m][mt] = mfma16_f32(av[c].y, w[m][c].y, acc[m][mt]);
+              acc[m][mt] = mfma16_f32(av[c].z, w[m][c].z, acc[m][mt]);
+              acc[m][mt] = mfma16_f32(av[c].w, w[m][c].w, acc[m][mt]);
+            }
+        }
+      }
+    }
+  }
+}
+
+// Split the 64-element units of [0, K) into `parts` near-equal ranges.
+__device__ __forceinline__ void unit_range(int K, int part, int parts, int& k0, int& k1) {
+  const int U = K >> 6;
+  k0 = (part * U / parts) << 6;
+  k1 = ((part + 1) * U / parts) << 6;
+}
+
+template <int NMAT, int MT>
+__device__ __forceinline__ void zero_acc(f32x4 (&acc)[NMAT][MT]) {
+#pragma unroll
+  for (int m = 0; m < NMAT; ++m)
+#pragma unroll
+    for (int mt = 0; mt < MT; ++mt) acc[m][mt] = f32x4{0.f, 0.f, 0.f, 0.f};
+}
+
+// K-split reduction across the 4 wavefronts of a block: afterwards wavefront w holds
+// the full sums of M-tile w in acc[.][0].  Must be reached by the whole block.
+template <int NMAT, int MT>
+__device__ __forceinline__ void block_reduce(float* red, f32x4 (&acc)[NMAT][MT]) {
+  const int lane = lane_id(), w = threadIdx.x >> 6;
+#pragma unroll
+  for (int m = 0; m < NMAT; ++m)
+#pragma unroll
+    for (int mt = 0; mt < MT; ++mt)
+      *reinterpret_cast<f32x4*>(red + (((w * NMAT + m) * MT + mt) * 64 + lane) * 4) = acc[m][mt];
+  __syncthreads();
+  if (w < MT) {
+#pragma unroll
+    for (int m = 0; m < NMAT; ++m) {
+      f32x4 s = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+      for (int p = 0; p < 4; ++p) s += *reinterpret_cast<const f32x4*>(red + (((p * NMAT + m) * MT + w) * 64 + lane) * 4);
+      acc[m][0] = s;
+    }
+  }
+  __syncthreads();
+}
+
+template <Act ACT>
+__device__ __forceinline__ void store_act(typename ActType<ACT>::T* p, float v) {
+  if constexpr (ACT == Act::BF16)
+    *p = f32_to_bf16(v);
+  else
+    *p = v;
+}
+
+// ------------------------------------------------------------------ router
+template <Act ACT, int MT, int NWK>
+__global__ __launch_bounds__(256) void k_skinny_router(SkinnyRouterArgs a) {
+  using AT = typename ActType<ACT>::T;
+  constexpr WFmt WF = ACT == Act::BF16 ? WFmt::BF16 : WFmt::F32;
+  using WT = typename WType<WF>::T;
+  constexpr int IPB = 4 / NWK;
+  __shared__ float red[NWK > 1 ? 4 * MT * 256 : 1];
+  const int lane = lane_id(), w = threadIdx.x >> 6;
+  const int n = lane & 15;
+  const int RC = (a.E + 15) / 16;
+  const int nitems = RC * a.P;
+  const AT* x = static_cast<const AT*>(a.x);
+  const WT* W = static_cast<const WT*>(a.W);
+  for (int base = blockIdx.x * IPB; base < nitems; base += gridDim.x * IPB) {
+    const int item = base + w / NWK;
+    const bool live = item < nitems;
+    const int it = live ? item : 0;
+    const int rc = it % RC, part = it / RC;
+    const int row = min(rc * 16 + n, a.E - 1);
+    int k0, k1;
+    unit_range(a.H, part, a.P, k0, k1);
+    if (NWK > 1) {
+      const int kk0 = k0, span = k1 - k0;
+      const int U = span >> 6, kp = w % NWK;
+      k0 = kk0 + ((kp * U / NWK) << 6);
+      k1 = kk0 + (((kp + 1) * U / NWK) << 6);
+    }
+    for (int t0 = 0; t0 < a.T; t0 += 64) {
+      const int ntok = min(64, a.T - t0);
+      Task<ACT, WF, 1, MT> tk;
+      tk.wrow[0] = W + static_cast<int64_t>(row) * a.H;
+      tk.mt_live = (ntok + 15) / 16;
+#pragma unroll
+      for (int mt = 0; mt < MT; ++mt) {
+        const int m = min(mt * 16 + n, ntok - 1);
+        tk.arow[mt] = x + static_cast<int64_t>(t0 + m) * a.H;
+      }
+      f32x4 acc[1][MT];
+      zero_acc(acc);
+      if (live) stream_rows(tk, k0, k1, acc);
+      int mt_lo = 0, mt_hi = MT;
+      if constexpr (NWK > 1) {
+        block_reduce<1, MT>(red, acc);
+        mt_lo = w;
+        mt_hi = w + 1;
+      }
+      if (live && (NWK == 1 || w < MT)) {
+        const int col = rc * 16 + n;
+#pragma unroll
+        for (int mt = 0; mt < MT; ++mt) {
+          if (mt < mt_lo || mt >= mt_hi) continue;
+          const int ai = NWK > 1 ? 0 : mt;
+#pragma unroll
+          for (int v = 0; v < 4; ++v) {
+            const int m = mt * 16 + 4 * (lane >> 4) + v;
+            if (m < ntok && col < a.E)
+              a.out[(static_cast<int64_t>(part) * a.T + t0 + m) * a.E + col] = acc[0][ai][v];
+          }
+        }
+      }
+    }
+  }
+}
+
+// ------------------------------------------------- routed + shared gate/up, SwiGLU
+template <Act ACT, WFmt WF, int MT, int NWK>
+__global__ __launch_bounds__(256) void k_skinny_up(SkinnyUpArgs a) {
+  using AT = typename ActType<ACT>::T;
+  using WT = typename WType<WF>::T;
+  using ST = typename WType<ACT == Act::BF16 ? WFmt::BF16 : WFmt::F32>::T;  // shared weights
+  constexpr int IPB = 4 / NWK;
+  __shared__ float red[NWK > 1 ? 4 * 2 * MT * 256 : 1];
+  const int lane = lane_id(), w = threadIdx.x >> 6;
+  const int n = lane & 15;
+  const int D = a.meta[0];
+  const int CH = a.I / 16, CHs = a.Is / 16;
+  const int TC = (a.T + 63) / 64;
+  const int n_routed = D * CH;
+  const int nitems = n_routed + CHs * TC;
+  const AT* x = static_cast<const AT*>(a.x);
+  for (int base = blockIdx.x * IPB; base < nitems; base += gridDim.x * IPB) {
+    const int item = base + w / NWK;
+    const bool live = item < nitems;
+    const int it = live ? item : 0;
+    const bool shared = it >= n_routed;
+    int k0 = 0, k1 = a.H;
+    if (NWK > 1) unit_range(a.H, w % NWK, NWK, k0, k1);
+    // item geometry
+    int e = 0, off = 0, ntot, row0, tc_begin, tc_end;
+    if (!shared) {
+      e = a.active[it / CH];
+      row0 = (it % CH) * 16;
+      off = a.offsets[e];
+      ntot = a.counts[e];
+      tc_begin = 0;
+      tc_end = (ntot + 63) / 64;
+    } else {
+      const int si = it - n_routed;
+      row0 = (si % CHs) * 16;
+      tc_begin = si / CHs;
+      tc_end = tc_begin + 1;
+      ntot = a.T;
+    }
+    for (int tc = tc_begin; tc < tc_end; ++tc) {
+      const int ntok = min(64, ntot - tc * 64);
+      Task<ACT, WF, 2, MT> tk;
+      tk.mt_live = (ntok + 15) / 16;
+#pragma unroll
+      for (int mt = 0; mt < MT; ++mt) {
+        const int m = tc * 64 + min(mt * 16 + n, ntok - 1);
+        const int tok = shared ? m : a.perm[off + m] / a.k;
+        tk.arow[mt] = x + static_cast<int64_t>(tok) * a.H;
+      }
+      if (!shared) {
+        const int64_t ro = static_cast<int64_t>(e) * a.I + row0 + n;
+        tk.wrow[0] = static_cast<const WT*>(a.gate) + ro * a.H;
+        tk.wrow[1] = static_cast<const WT*>(a.up) + ro * a.H;
+        if constexpr (WF == WFmt::U8) {
+          tk.srow[0] = a.gate_s + ro * (a.H / 64);
+          tk.zrow[0] = a.gate_z + ro * (a.H / 64);
+          tk.srow[1] = a.up_s + ro * (a.H / 64);
+          tk.zrow[1] = a.up_z + ro * (a.H / 64);
+        }
+      }
+      f32x4 acc[2][MT];
+      zero_acc(acc);
+      if (live) {
+        if (!shared) {
+          stream_rows(tk, k0, k1, acc);
+        } else {
+          // the shared expert keeps the activation dtype
+          constexpr WFmt SF = ACT == Act::BF16 ? WFmt::BF16 : WFmt::F32;
+          Task<ACT, SF, 2, MT> ts;
+          ts.mt_live = tk.mt_live;
+#pragma unroll
+          for (int mt = 0; mt < MT; ++mt) ts.arow[mt] = tk.arow[mt];
+          const int64_t ro = row0 + n;
+          ts.wrow[0] = static_cast<const ST*>(a.sgate) + ro * a.H;
+          ts.wrow[1] = static_cast<const ST*>(a.sup) + ro * a.H;
+          stream_rows(ts, k0, k1, acc);
+        }
+      }
+      int mt_lo = 0, mt_hi = MT;
+      if constexpr (NWK > 1) {
+        block_reduce<2, MT>(red, acc);
+        mt_lo = w;
+        mt_hi = w + 1;
+      }
+      if (live && (NWK == 1 || w < MT)) {
+        AT* out = static_cast<AT*>(shared ? a.hs : a.hm);
+        const int ld = shared ? a.Is : a.I;
+        const int64_t rbase = shared ? 0 : off;
+#pragma unroll
+        for (int mt = 0; mt < MT; ++mt) {
+          if (mt < mt_lo || mt >= mt_hi) continue;
+          const int ai = NWK > 1 ? 0 : mt;
+#pragma unroll
+          for (int v = 0; v < 4; ++v) {
+            const int m = mt * 16 + 4 * (lane >> 4) + v;
+            if (m < ntok) {
+              const float h = silu(acc[0][ai][v]) * acc[1][ai][v];
+              store_act<ACT>(out + (rbase + tc * 64 + m) * ld + row0 + n, h);
+            }
+          }
+        }
+      }
+    }
+  }
+}
+
+// ------------------------------------------------------ routed + shared down
+template <Act ACT, WFmt WF, int MT, int NWK>
+__global__ __launch_bounds__(256) void k_skinny_down(SkinnyDownArgs a) {
+  using AT = typename ActType<ACT>::T;
+  using WT = typename WType<WF>::T;
+  using ST = typename WType<ACT == Act::BF16 ? WFmt::BF16 : WFmt::F32>::T;
+  constexpr int IPB = 4 / NWK;
+  __shared__ float red[NWK > 1 ? 4 * MT * 256 : 1];
+  const int lane = lane_id(), w = threadIdx.x >> 6;
+  const int n = lane & 15;
+  const int D = a.meta[0];
+  const int CH = a.H / 16;
+  const int TC = (a.T + 63) / 64;
+  const int n_routed = D * CH;
+  const int nitems = n_routed + (a.Is > 0 ? CH * TC : 0);
+  const AT* hm = static_cast<const AT*>(a.hm);
+  const AT* hs = static_cast<const AT*>(a.hs);
+  for (int base = blockIdx.x * IPB; base < nitems; base += gridDim.x * IPB) {
+    const int item = base + w / NWK;
+    const bool live = item < nitems;
+    const int it = live ? item : 0;
+    const bool shared = it >= n_routed;
+    const int K = shared ? a.Is : a.I;
+    int k0 = 0, k1 = K;
+    if (NWK > 1) unit_range(K, w % NWK, NWK, k0, k1);
+    int e = 0, off = 0, ntot, row0, tc_begin, tc_end;
+    if (!shared) {
+      e = a.active[it / CH];
+      row0 = (it % CH) * 16;
+      off = a.offsets[e];
+      ntot = a.counts[e];
+      tc_begin = 0;
+      tc_end = (ntot + 63) / 64;
+    } else {
+      const int si = it - n_routed;
+      row0 = (si % CH) * 16;
+      tc_begin = si / CH;
+      tc_end = tc_begin + 1;
+      ntot = a.T;
+    }
+    for (int tc = tc_begin; tc < tc_end; ++tc) {
+      const int ntok = min(64, ntot - tc * 64);
+      f32x4 acc[1][MT];
+      zero_acc(acc);
+      const int mt_live = (ntok + 15) / 16;
+      if (live) {
+        if (!shared) {
+          Task<ACT, WF, 1, MT> tk;
+          tk.mt_live = mt_live;
+#pragma unroll
+          for (int mt = 0; mt < MT; ++mt)
+            tk.arow[mt] = hm + static_cast<int64_t>(off + tc * 64 + min(mt * 16 + n, ntok - 1)) * a.I;
+          const int64_t ro = static_cast<int64_t>(e) * a.H + row0 + n;
+          tk.wrow[0] = static_cast<const WT*>(a.down) + ro * a.I;
+          if constexpr (WF == WFmt::U8) {
+            tk.srow[0] = a.down_s + ro * (a.I / 64);
+            tk.zrow[0] = a.down_z + ro * (a.I / 64);
+          }
+          stream_rows(tk, k0, k1, acc);
+        } else {
+          constexpr WFmt SF = ACT == Act::BF16 ? WFmt::BF16 : WFmt::F32;
+          Task<ACT, SF, 1, MT> ts;
+          ts.mt_live = mt_live;
+#pragma unroll
+          for (int mt = 0; mt < MT; ++mt)
+            ts.arow[mt] = hs + static_cast<int64_t>(tc * 64 + min(mt * 16 + n, ntok - 1)) * a.Is;
+          ts.wrow[0] = static_cast<const ST*>(a.sdown) + static_cast<int64_t>(row0 + n) * a.Is;
+          stream_rows(ts, k0, k1, acc);
+        }
+      }
+      int mt_lo = 0, mt_hi = MT;
+      if constexpr (NWK > 1) {
+        block_reduce<1, MT>(red, acc);
+        mt_lo = w;
+        mt_hi = w + 1;
+      }
+      if (live && (NWK == 1 || w < MT)) {
+#pragma unroll
+        for (int mt = 0; mt < MT; ++mt) {
+          if (mt < mt_lo || mt >= mt_hi) continue;
+          const int ai = NWK > 1 ? 0 : mt;
+#pragma unroll
+          for (int v = 0; v < 4; ++v) {
+            const int m = mt * 16 + 4 * (lane >> 4) + v;
+            if (m < ntok) {
+              if (!shared) {
+                const int slot = a.perm[off + tc * 64 + m];
+                a.r[static_cast<int64_t>(slot) * a.H + row0 + n] = a.topk_w[slot] * acc[0][ai][v];
+              } else {
+                a.rs[static_cast<int64_t>(tc * 64 + m) * a.H + row0 + n] = acc[0][ai][v];
+              }
+            }
+          }
+        }
+      }
+    }
+  }
+}
+
+// y[t] = sum_j r[t*k + j] (valid experts only, fixed j order) + rs[t]
+template <Act ACT>
+__global__ __launch_bounds__(256) void k_combine(CombineArgs a) {
+  using AT = typename ActType<ACT>::T;
+  const int64_t nvec = static_cast<int64_t>(a.T) * (a.H / 4);
+  for (int64_t i = blockIdx.x * 256ll + threadIdx.x; i < nvec; i += static_cast<int64_t>(gridDim.x) * 256) {
+    const int t = static_cast<int>(i / (a.H / 4));
+    const int h = static_cast<int>(i % (a.H / 4)) * 4;
+    float4 s = make_float4(0.f, 0.f, 0.f, 0.f);
+    for (int j = 0; j < a.k; ++j) {
+      const int64_t slot = static_cast<int64_t>(t) * a.k + j;
+      const int e = a.idx[slot];
+      if (e < 0 || e >= a.E) continue;
+      if (a.r_bf16) {
+        const uint2 v = *reinterpret_cast<const uint2*>(static_cast<const uint16_t*>(a.r) + slot * a.H + h);
+        s.x += __uint_as_float(v.x << 16);
+        s.y += __uint_as_float(v.x & 0xffff0000u);
+        s.z += __uint_as_float(v.y << 16);
+        s.w += __uint_as_float(v.y & 0xffff0000u);
+      } else {
+        const float4 v = *reinterpret_cast<const float4*>(static_cast<const float*>(a.r) + slot * a.H + h);
+        s.x += v.x;
+        s.y += v.y;
+        s.z += v.z;
+        s.w += v.w;
+      }
+    }
+    if (a.rs) {
+      const float4 v = *reinterpret_cast<const float4*>(a.rs + static_cast<int64_t>(t) * a.H + h);
+      s.x += v.x;
+      s.y += v.y;
+      s.z += v.z;
+      s.w += v.w;
+    }
+    AT* y = static_cast<AT*>(a.y) + static_cast<int64_t>(t) * a.H + h;
+    if constexpr (ACT == Act::BF16) {
+      *reinterpret_cast<uint2*>(y) = make_uint2(pack_bf16x2(s.x, s.y), pack_bf16x2(s.z, s.w));
+    } else {
+      *reinterpret_cast<float4*>(y) = s;
+    }
+  }
+}
+
+int pick_mt(int T) {
+  const int t = T < 64 ? T : 64;
+  return t <= 16 ? 1 : (t <= 32 ? 2 : 4);
+}
+
+int grid_for(int64_t items, int ipb, int ncu) {
+  int64_t blocks = (items + ipb - 1) / ipb;
+  const int64_t cap = static_cast<int64_t>(ncu) * 8;
+  if (blocks > cap) blocks = cap;
+  if (blocks < 1) blocks = 1;
+  return static_cast<int>(blocks);
+}
+
+}  // namespace
+
+#define MOE_DISPATCH_MT_NWK(KERNEL, ARGS, ITEMS, T_, NWK_SMALL_ITEMS, ...)                     \
+  do {                                                                                          \
+    const int mt_ = pick_mt(T_);                                                                \
+    const bool k4_ = (ITEMS) < (NWK_SMALL_ITEMS);                                               \
+    const int grid_ = grid_for((ITEMS), k4_ ? 1 : 4, ncu);                                      \
+    if (k4_) {                                                                                  \
+      if (mt_ == 1)                                                                             \
+        hipLaunchKernelGGL((KERNEL<__VA_ARGS__, 1, 4>), dim3(grid_), dim3(256), 0, s, ARGS);    \
+      else if (mt_ == 2)                                                                        \
+        hipLaunchKernelGGL((KERNEL<__VA_ARGS__, 2, 4>), dim3(grid_), dim3(256), 0, s, ARGS);    \
+      else                                                                                      \
+        hipLaunchKernelGGL((KERNEL<__VA_ARGS__, 4, 4>), dim3(grid_), dim3(256), 0, s, ARGS);    \
+    } else {                                                                                    \
+      if (mt_ == 1)                                                                             \
+        hipLaunchKernelGGL((KERNEL<__VA_ARGS__, 1, 1>), dim3(grid_), dim3(256), 0, s, ARGS);    \
+      else if (mt_ == 2)                                                                        \
+        hipLaunchKernelGGL((KERNEL<__VA_ARGS__, 2, 1>), dim3(grid_), dim3(256), 0, s, ARGS);    \
+      else                                                                                      \
+        hipLaunchKernelGGL((KERNEL<__VA_ARGS__, 4, 1>), dim3(grid_), dim3(256), 0, s, ARGS);    \
+    }                                                                                           \
+  } while (0)
+
+hipError_t launch_skinny_router(const SkinnyRouterArgs& a, Act act, int ncu, hipStream_t s) {
+  if (a.T <= 0) return hipSuccess;
+  const int64_t items = static_cast<int64_t>((a.E + 15) / 16) * a.P;
+  const int64_t small = 4ll * ncu;
+  if (act == Act::BF16)
+    MOE_DISPATCH_MT_NWK(k_skinny_router, a, items, a.T, small, Act::BF16);
+  else
+    MOE_DISPATCH_MT_NWK(k_skinny_router, a, items, a.T, small, Act::F32);
+  return hipGetLastError();
+}
+
+hipError_t launch_skinny_up(const SkinnyUpArgs& a, Act act, WFmt wf, int ncu, hipStream_t s) {
+  if (a.T <= 0) return hipSuccess;
+  const int64_t slots = static_cast<int64_t>(a.T) * a.k;
+  const int64_t dmax = slots < a.E ? slots : a.E;
+  const int64_t items = dmax * (a.I / 16) + static_cast<int64_t>(a.Is / 16) * ((a.T + 63) / 64);
+  const int64_t small = 4ll * ncu;
+  if (act == Act::F32)
+    MOE_DISPATCH_MT_NWK(k_skinny_up, a, items, a.T, small, Act::F32, WFmt::F32);
+  else if (wf == WFmt::U8)
+    MOE_DISPATCH_MT_NWK(k_skinny_up, a, items, a.T, small, Act::BF16, WFmt::U8);
+  else
+    MOE_DISPATCH_MT_NWK(k_skinny_up, a, items, a.T, small, Act::BF16, WFmt::BF16);
+  return hipGetLastError();
+}
+
+hipError_t launch_skinny_down(const SkinnyDownArgs& a, Act act, WFmt wf, int ncu, hipStream_t s) {
+  if (a.T <= 0) return hipSuccess;
+  const int64_t slots = static_cast<int64_t>(a.T) * a.k;
+  const int64_t dmax = slots < a.E ? slots : a.E;
+  const int64_t items = dmax * (a.H / 16) + (a.Is > 0 ? static_cast<int64_t>(a.H / 16) * ((a.T + 63) / 64) : 0);
+  const int64_t small = 4ll * ncu;
+  if (act == Act::F32)
+    MOE_DISPATCH_MT_NWK(k_skinny_down, a, items, a.T, small, Act::F32, WFmt::F32);
+  else if (wf == WFmt::U8)
+    MOE_DISPATCH_MT_NWK(k_skinny_down, a, items, a.T, small, Act::BF16, WFmt::U8);
+  else
+    MOE_DISPATCH_MT_NWK(k_skinny_down, a, items, a.T, small, Act::BF16, WFmt::BF16);
+  return hipGetLastError();
+}
+
+hipError_t launch_combine(const CombineArgs& a, Act act, hipStream_t s) {
+  if (a.T <= 0) return hipSuccess;
+  const int64_t nvec = static_cast<int64_t>(a.T) * (a.H / 4);
+  int64_t blocks = (nvec + 255) / 256;
+  if (blocks > 4096) blocks = 4096;
+  if (act == Act::BF16)
+    hipLaunchKernelGGL(k_combine<Act::BF16>, dim3(blocks), dim3(256), 0, s, a);
+  else
+    hipLaunchKernelGGL(k_combine<Act::F32>, dim3(blocks), dim3(256), 0, s, a);
+  return hipGetLastError();
+}
+
+}  // namespace moe
