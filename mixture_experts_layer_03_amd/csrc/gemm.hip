@@ -7,13 +7,18 @@
 // Expert weights are [out, in] per expert [mlxcel #838 "Validation checkpoint"], so
 // the weight operand rows are the output features and K runs along memory.
 //
-// Tile 128 (tokens) x 128 (weight rows) x 64, 256 threads as 2 x 2 wavefronts of
-// 64 x 64, each a 4 x 4 grid of v_mfma_f32_16x16x32_bf16.  Operands are staged
-// global -> registers -> LDS (double buffered, 16-byte chunks XOR-swizzled by row so
-// fragment reads do not collide on banks).  u8 weights are dequantised to bf16
-// (s * (q - z), rounded to nearest even) while being written to LDS.
-// Blocks are numbered so that consecutive tiles share an XCD (its L2 holds the
-// shared A rows and weight panels).
+// Block tile 128 (tokens) x BN (weight rows: 128 or 256) x 64 with BN/32 wavefronts,
+// each owning a 64 x 64 sub-tile (a 4 x 4 grid of v_mfma_f32_16x16x32_bf16).  Two
+// wavefronts share each SIMD, so one computes while the other waits on memory.  The
+// wide tile halves the L2 -> LDS bytes per flop against a square 128 x 128 tile,
+// which is what bounds a 128 x 128 tile on this chip.  Operands are staged global ->
+// registers -> LDS (double buffered; 16-byte chunks XOR-swizzled by row so fragment
+// reads do not collide on banks); the next K-step's global loads are issued before the
+// current step's MFMAs.  u8 weights are dequantised to bf16 (s * (q - z), rounded to
+// nearest even) on their way to LDS, eight codes per thread and chunk.  The epilogue
+// stages 64-row halves of the tile through LDS as fp32 and writes 16-byte chunks, so
+// every output, gather and scatter is coalesced.  Blocks are numbered so that
+// consecutive tiles share an XCD (its L2 holds the shared A rows and weight panels).
 #include "common.h"
 #include "kernels.h"
 
@@ -21,21 +26,29 @@ namespace moe {
 
 namespace {
 
-constexpr int BM = kTileM, BN = 128, BK = 64;
-
-__device__ __forceinline__ int swz(int row, int chunk) { return row * BK + ((chunk ^ (row & 7)) << 3); }
+constexpr int BM = kTileM, BK = 64;
 
 __device__ __forceinline__ uint4 ldg16(const void* p) { return *reinterpret_cast<const uint4*>(p); }
 
-template <WFmt WF, bool DUAL, AMode AM, Epi EPI>
-__global__ __launch_bounds__(256, 2) void k_tile(TileArgs a) {
-  __shared__ __attribute__((aligned(16))) uint16_t As[2][BM * BK];
-  __shared__ __attribute__((aligned(16))) uint16_t Bs[2][BN * BK];
+template <int BN, WFmt WF, bool DUAL, AMode AM, Epi EPI>
+__global__ __launch_bounds__(BN * 2) void k_tile(TileArgs a) {
+  constexpr int NTHR = BN * 2;                  // BN/32 wavefronts
+  constexpr int RSTEP = NTHR / 8;               // tile rows between one thread's chunks
+  constexpr int AR = BM * 8 / NTHR;             // A chunks per thread
+  constexpr int BR = BN * 8 / NTHR;             // B chunks per thread (= 4)
+  constexpr int WN = BN / 64;                   // wavefronts along N
+  constexpr int STAGE_ELEMS = (BM + BN) * BK;   // bf16 elements per LDS stage
+  constexpr int NCOL = DUAL ? BN / 2 : BN;      // output columns per tile
+  constexpr int EPI_LD = NCOL + 4;              // fp32 epilogue row stride (bank spread)
+  static_assert(64 * EPI_LD * 4 <= 2 * STAGE_ELEMS * 2, "epilogue staging must fit the LDS stages");
+  __shared__ __attribute__((aligned(16))) uint16_t smem[2 * STAGE_ELEMS];
 
   const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
-  const int NT = DUAL ? a.N / 64 : (a.N + BN - 1) / BN;
+  const int NT = (a.N + NCOL - 1) / NCOL;
   const int per = gridDim.x / 8;
-  const int L = (blockIdx.x % 8) * per + blockIdx.x / 8;
+  const int KS = a.ksplit > 1 ? a.ksplit : 1;
+  const int Lx = (blockIdx.x % 8) * per + blockIdx.x / 8;
+  const int kp = Lx % KS, L = Lx / KS;
   const int mt = L / NT, nt = L % NT;
 
   int e = 0, m_begin, m_rows;
@@ -50,103 +63,93 @@ __global__ __launch_bounds__(256, 2) void k_tile(TileArgs a) {
     m_rows = min(BM, a.M - m_begin);
   }
   const int K = a.K;
+  const int kt0 = kp * (K / BK) / KS, kt1 = (kp + 1) * (K / BK) / KS;  // this block's K-steps
 
-  // staging assignment: A rows r = tid/8 + 32 i, 16-byte chunk tid % 8
-  const int sc = tid & 7;
-  const uint16_t* arow[4];
+  // ---- staging: thread rows tid/8 + RSTEP*i (congruent mod 8, so one swizzled LDS
+  // base plus immediate offsets), 16-byte chunk tid % 8 (8 elements: bf16, or 8 u8
+  // codes for quantised weights).  A rows use 32-bit element offsets (the host keeps
+  // rows * K below 2^32); rows past the tile's end are clamped (computed, never stored).
+  const int sc = tid & 7, r0 = tid >> 3;
+  uint32_t a_off[AR];
 #pragma unroll
-  for (int i = 0; i < 4; ++i) {
-    const int r = min((tid >> 3) + 32 * i, m_rows - 1);
-    int64_t row;
+  for (int i = 0; i < AR; ++i) {
+    const int r = min(r0 + RSTEP * i, m_rows - 1);
+    int row;
     if constexpr (AM == AMode::GATHER)
       row = a.perm[m_begin + r] / a.k;
     else
       row = m_begin + r;
-    arow[i] = a.A + row * K + sc * 8;
+    a_off[i] = static_cast<uint32_t>(row) * K + sc * 8;
   }
-
-  // weight rows
-  constexpr int BR = WF == WFmt::U8 ? 2 : 4;  // rows staged per thread
-  const uint8_t* brow[BR];
-  const uint16_t* bsrow[BR];
-  const uint16_t* bzrow[BR];
-  int brow_lds[BR];
-  const int bchunk = WF == WFmt::U8 ? (tid & 3) : sc;
-  const int esz = WF == WFmt::U8 ? 1 : 2;
+  constexpr int esz = WF == WFmt::U8 ? 1 : 2;
+  const uint8_t* bp[BR];
+  const uint16_t* bsp[BR];
+  const uint16_t* bzp[BR];
 #pragma unroll
   for (int i = 0; i < BR; ++i) {
-    const int rb = WF == WFmt::U8 ? (tid >> 2) + 64 * i : (tid >> 3) + 32 * i;
-    brow_lds[i] = rb;
+    const int r = r0 + RSTEP * i;  // B tile row
     int n;
-    const void* base;
-    const uint16_t *bs, *bz;
+    bool second;
     if (DUAL) {
-      const int blk = rb >> 5;
-      n = nt * 64 + (blk >> 1) * 32 + (rb & 31);
-      base = (blk & 1) ? a.B1 : a.B0;
-      bs = (blk & 1) ? a.B1s : a.B0s;
-      bz = (blk & 1) ? a.B1z : a.B0z;
+      // B tile rows in blocks of 32: gate, up, gate, up, ... so each wavefront's 64
+      // rows are the gate and up rows of the same 32 output columns
+      const int blk = r >> 5;
+      second = blk & 1;
+      n = nt * NCOL + (blk >> 1) * 32 + (r & 31);
     } else {
-      n = min(nt * BN + rb, a.N - 1);
-      base = a.B0;
-      bs = a.B0s;
-      bz = a.B0z;
+      second = false;
+      n = min(nt * BN + r, a.N - 1);
     }
-    const int64_t ro = static_cast<int64_t>(e) * a.N + n;
-    brow[i] = static_cast<const uint8_t*>(base) +
-              (static_cast<int64_t>(e) * a.b_expert_stride + static_cast<int64_t>(n) * K) * esz +
-              bchunk * 16;
+    const void* base = second ? a.B1 : a.B0;
+    bp[i] = static_cast<const uint8_t*>(base) +
+            (static_cast<int64_t>(e) * a.b_expert_stride + static_cast<int64_t>(n) * K + sc * 8) * esz;
     if constexpr (WF == WFmt::U8) {
-      bsrow[i] = bs + ro * (K / 64);
-      bzrow[i] = bz + ro * (K / 64);
+      const int64_t ro = (static_cast<int64_t>(e) * a.N + n) * (K / 64);
+      bsp[i] = (second ? a.B1s : a.B0s) + ro;
+      bzp[i] = (second ? a.B1z : a.B0z) + ro;
     } else {
-      bsrow[i] = nullptr;
-      bzrow[i] = nullptr;
+      bsp[i] = bzp[i] = nullptr;
     }
   }
 
-  uint4 ra[4], rbv[4];
-  float rsc[BR], rzp[BR];
+  uint4 ra[AR], rb[BR];
+  uint2 rq[WF == WFmt::U8 ? BR : 1];
+  float rs[WF == WFmt::U8 ? BR : 1], rz[WF == WFmt::U8 ? BR : 1];
   auto gload = [&](int kt) {
     const int k0 = kt * BK;
 #pragma unroll
-    for (int i = 0; i < 4; ++i) ra[i] = ldg16(arow[i] + k0);
-    if constexpr (WF == WFmt::U8) {
+    for (int i = 0; i < AR; ++i) ra[i] = ldg16(a.A + a_off[i] + k0);
 #pragma unroll
-      for (int i = 0; i < BR; ++i) {
-        rbv[i] = ldg16(brow[i] + k0);
-        rsc[i] = f16_to_f32(bsrow[i][kt]);
-        rzp[i] = f16_to_f32(bzrow[i][kt]);
+    for (int i = 0; i < BR; ++i) {
+      if constexpr (WF == WFmt::U8) {
+        rq[i] = *reinterpret_cast<const uint2*>(bp[i] + k0);
+        rs[i] = f16_to_f32(bsp[i][kt]);
+        rz[i] = f16_to_f32(bzp[i][kt]);
+      } else {
+        rb[i] = ldg16(bp[i] + 2 * k0);
       }
-    } else {
-#pragma unroll
-      for (int i = 0; i < BR; ++i) rbv[i] = ldg16(brow[i] + 2 * k0);
     }
   };
+  const int wr = r0 * BK + ((sc ^ (r0 & 7)) << 3);  // LDS write base (elements)
   auto sstore = [&](int buf) {
+    uint16_t* As = smem + buf * STAGE_ELEMS;
+    uint16_t* Bs = As + BM * BK;
 #pragma unroll
-    for (int i = 0; i < 4; ++i)
-      *reinterpret_cast<uint4*>(&As[buf][swz((tid >> 3) + 32 * i, sc)]) = ra[i];
-    if constexpr (WF == WFmt::U8) {
+    for (int i = 0; i < AR; ++i) *reinterpret_cast<uint4*>(&As[wr + RSTEP * i * BK]) = ra[i];
 #pragma unroll
-      for (int i = 0; i < BR; ++i) {
-        const uint32_t q[4] = {rbv[i].x, rbv[i].y, rbv[i].z, rbv[i].w};
-        uint32_t o[8];
-#pragma unroll
-        for (int c = 0; c < 4; ++c) {
-          const float s = rsc[i], z = rzp[i];
-          o[2 * c] = pack_bf16x2(s * (static_cast<float>(q[c] & 0xffu) - z),
-                                 s * (static_cast<float>((q[c] >> 8) & 0xffu) - z));
-          o[2 * c + 1] = pack_bf16x2(s * (static_cast<float>((q[c] >> 16) & 0xffu) - z),
-                                     s * (static_cast<float>(q[c] >> 24) - z));
-        }
-        const int r = brow_lds[i];
-        *reinterpret_cast<uint4*>(&Bs[buf][swz(r, 2 * bchunk)]) = make_uint4(o[0], o[1], o[2], o[3]);
-        *reinterpret_cast<uint4*>(&Bs[buf][swz(r, 2 * bchunk + 1)]) = make_uint4(o[4], o[5], o[6], o[7]);
+    for (int i = 0; i < BR; ++i) {
+      uint4 v;
+      if constexpr (WF == WFmt::U8) {
+        const float s = rs[i], z = rz[i];
+        const uint32_t lo = rq[i].x, hi = rq[i].y;
+        v.x = pack_bf16x2(s * (static_cast<float>(lo & 0xffu) - z), s * (static_cast<float>((lo >> 8) & 0xffu) - z));
+        v.y = pack_bf16x2(s * (static_cast<float>((lo >> 16) & 0xffu) - z), s * (static_cast<float>(lo >> 24) - z));
+        v.z = pack_bf16x2(s * (static_cast<float>(hi & 0xffu) - z), s * (static_cast<float>((hi >> 8) & 0xffu) - z));
+        v.w = pack_bf16x2(s * (static_cast<float>((hi >> 16) & 0xffu) - z), s * (static_cast<float>(hi >> 24) - z));
+      } else {
+        v = rb[i];
       }
-    } else {
-#pragma unroll
-      for (int i = 0; i < BR; ++i) *reinterpret_cast<uint4*>(&Bs[buf][swz(brow_lds[i], sc)]) = rbv[i];
+      *reinterpret_cast<uint4*>(&Bs[wr + RSTEP * i * BK]) = v;
     }
   };
 
@@ -156,95 +159,134 @@ __global__ __launch_bounds__(256, 2) void k_tile(TileArgs a) {
 #pragma unroll
     for (int j = 0; j < 4; ++j) acc[i][j] = f32x4{0.f, 0.f, 0.f, 0.f};
 
-  const int wm = w >> 1, wn = w & 1;
+  const int wm = w / WN, wn = w % WN;
   const int fr = lane & 15, fq = lane >> 4;
-  const int nk = K / BK;
-  gload(0);
-  sstore(0);
-  __syncthreads();
-  for (int kt = 0; kt < nk; ++kt) {
-    const int buf = kt & 1;
-    if (kt + 1 < nk) gload(kt + 1);
+  // fragment read bases: (row + 16 i) & 7 == fr & 7 for every sub-tile, and the second
+  // K-half's chunk (4 + fq) swizzles to the first's with bit 2 flipped
+  const int c0 = (fq ^ (fr & 7)) << 3;
+  const int a_rd = (wm * 64 + fr) * BK, b_rd = (wn * 64 + fr) * BK;
+  auto compute = [&](int buf) {
+    const uint16_t* As = smem + buf * STAGE_ELEMS;
+    const uint16_t* Bs = As + BM * BK;
 #pragma unroll
     for (int ks = 0; ks < 2; ++ks) {
+      const int cc = ks ? (c0 ^ 32) : c0;
       uint4 af[4], bf[4];
 #pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        const int row = wm * 64 + i * 16 + fr;
-        af[i] = *reinterpret_cast<const uint4*>(&As[buf][swz(row, ks * 4 + fq)]);
-      }
+      for (int i = 0; i < 4; ++i) af[i] = *reinterpret_cast<const uint4*>(&As[a_rd + cc + i * 16 * BK]);
 #pragma unroll
-      for (int j = 0; j < 4; ++j) {
-        const int row = wn * 64 + j * 16 + fr;
-        bf[j] = *reinterpret_cast<const uint4*>(&Bs[buf][swz(row, ks * 4 + fq)]);
-      }
+      for (int j = 0; j < 4; ++j) bf[j] = *reinterpret_cast<const uint4*>(&Bs[b_rd + cc + j * 16 * BK]);
 #pragma unroll
       for (int i = 0; i < 4; ++i)
 #pragma unroll
         for (int j = 0; j < 4; ++j) acc[i][j] = mfma16_bf16(af[i], bf[j], acc[i][j]);
     }
-    if (kt + 1 < nk) sstore(buf ^ 1);
+  };
+
+  if (kt0 < kt1) {
+    gload(kt0);
+    sstore(0);
+  }
+  __syncthreads();
+  for (int kt = kt0; kt < kt1; ++kt) {
+    const int buf = (kt - kt0) & 1;
+    if (kt + 1 < kt1) gload(kt + 1);
+    compute(buf);
+    if (kt + 1 < kt1) sstore(buf ^ 1);
     __syncthreads();
   }
 
-  // epilogue: lane holds C[m][n], m = wm*64 + i*16 + 4*fq + v, n = wn*64 + j*16 + fr
+  // ---- epilogue: two 64-row halves staged through LDS as fp32
+  float* ep = reinterpret_cast<float*>(smem);
+  constexpr int CPR = NCOL / 8;  // 8-column chunks per row
+#pragma unroll 1
+  for (int h = 0; h < 2; ++h) {
+    if (wm == h) {
 #pragma unroll
-  for (int i = 0; i < 4; ++i) {
+      for (int i = 0; i < 4; ++i)
 #pragma unroll
-    for (int v = 0; v < 4; ++v) {
-      const int m = wm * 64 + i * 16 + 4 * fq + v;
-      if (m >= m_rows) continue;
-      const int64_t orow = m_begin + m;
-      if constexpr (EPI == Epi::SWIGLU) {
-        uint16_t* out = static_cast<uint16_t*>(a.out);
+        for (int v = 0; v < 4; ++v) {
+          const int r = i * 16 + 4 * fq + v;
+          if constexpr (DUAL) {
 #pragma unroll
-        for (int j = 0; j < 2; ++j) {
-          const int col = nt * 64 + wn * 32 + j * 16 + fr;
-          out[orow * a.ldo + col] = f32_to_bf16(silu(acc[i][j][v]) * acc[i][j + 2][v]);
-        }
-      } else if constexpr (EPI == Epi::F32) {
-        float* out = static_cast<float*>(a.out);
+            for (int j = 0; j < 2; ++j)
+              ep[r * EPI_LD + wn * 32 + j * 16 + fr] = silu(acc[i][j][v]) * acc[i][j + 2][v];
+          } else {
 #pragma unroll
-        for (int j = 0; j < 4; ++j) {
-          const int col = nt * BN + wn * 64 + j * 16 + fr;
-          if (col < a.N) out[orow * a.ldo + col] = acc[i][j][v];
-        }
-      } else if constexpr (EPI == Epi::SCALED_SLOT) {
-        uint16_t* out = static_cast<uint16_t*>(a.out);
-        const int slot = a.perm[orow];
-        const float ws = a.topk_w[slot];
-#pragma unroll
-        for (int j = 0; j < 4; ++j) {
-          const int col = nt * BN + wn * 64 + j * 16 + fr;
-          if (col < a.N) out[static_cast<int64_t>(slot) * a.ldo + col] = f32_to_bf16(ws * acc[i][j][v]);
-        }
-      } else {  // COMBINE: y[t] = shared + sum_j r[t*k + j]
-        uint16_t* out = static_cast<uint16_t*>(a.out);
-#pragma unroll
-        for (int j = 0; j < 4; ++j) {
-          const int col = nt * BN + wn * 64 + j * 16 + fr;
-          if (col >= a.N) continue;
-          float s = acc[i][j][v];
-          for (int jj = 0; jj < a.k; ++jj) {
-            const int64_t slot = orow * a.k + jj;
-            const int ex = a.idx[slot];
-            if (ex >= 0 && ex < a.E) s += bf16_to_f32(a.r[slot * a.N + col]);
+            for (int j = 0; j < 4; ++j) ep[r * EPI_LD + wn * 64 + j * 16 + fr] = acc[i][j][v];
           }
-          out[orow * a.ldo + col] = f32_to_bf16(s);
+        }
+    }
+    __syncthreads();
+#pragma unroll 1
+    for (int c = tid; c < 64 * CPR; c += NTHR) {
+      const int r = c / CPR, c8 = (c % CPR) * 8;
+      const int m = h * 64 + r;
+      const int col = nt * NCOL + c8;
+      if (m < m_rows && col < a.N) {
+        const float4 v0 = *reinterpret_cast<const float4*>(&ep[r * EPI_LD + c8]);
+        const float4 v1 = *reinterpret_cast<const float4*>(&ep[r * EPI_LD + c8 + 4]);
+        float f[8] = {v0.x, v0.y, v0.z, v0.w, v1.x, v1.y, v1.z, v1.w};
+        const int64_t orow = m_begin + m;
+        if constexpr (EPI == Epi::F32) {
+          float* out = static_cast<float*>(a.out) + kp * a.part_stride + orow * a.ldo + col;
+          if (col + 8 <= a.N && (a.ldo & 3) == 0) {
+            *reinterpret_cast<float4*>(out) = v0;
+            *reinterpret_cast<float4*>(out + 4) = v1;
+          } else {
+            for (int q = 0; q < 8 && col + q < a.N; ++q) out[q] = f[q];
+          }
+        } else {
+          int64_t drow = orow;
+          if constexpr (EPI == Epi::SCALED_SLOT) {
+            const int slot = a.perm[orow];
+            const float ws = a.topk_w[slot];
+#pragma unroll
+            for (int q = 0; q < 8; ++q) f[q] *= ws;
+            drow = slot;
+          } else if constexpr (EPI == Epi::COMBINE) {
+            for (int jj = 0; jj < a.k; ++jj) {
+              const int64_t slot = orow * a.k + jj;
+              const int ex = a.idx[slot];
+              if (ex < 0 || ex >= a.E) continue;
+              const uint4 rv = ldg16(a.r + slot * a.N + col);
+              const uint32_t u[4] = {rv.x, rv.y, rv.z, rv.w};
+#pragma unroll
+              for (int q = 0; q < 4; ++q) {
+                f[2 * q] += __uint_as_float(u[q] << 16);
+                f[2 * q + 1] += __uint_as_float(u[q] & 0xffff0000u);
+              }
+            }
+          }
+          uint16_t* out = static_cast<uint16_t*>(a.out) + drow * a.ldo + col;
+          *reinterpret_cast<uint4*>(out) = make_uint4(pack_bf16x2(f[0], f[1]), pack_bf16x2(f[2], f[3]),
+                                                      pack_bf16x2(f[4], f[5]), pack_bf16x2(f[6], f[7]));
         }
       }
     }
+    __syncthreads();
   }
 }
 
-template <WFmt WF, bool DUAL, AMode AM, Epi EPI>
+template <int BN, WFmt WF, bool DUAL, AMode AM, Epi EPI>
 hipError_t launch_one(const TileArgs& a, hipStream_t s) {
-  const int NT = DUAL ? a.N / 64 : (a.N + BN - 1) / BN;
-  int64_t blocks = static_cast<int64_t>(a.mtiles_bound) * NT;
+  constexpr int NCOL = DUAL ? BN / 2 : BN;
+  const int NT = (a.N + NCOL - 1) / NCOL;
+  int64_t blocks = static_cast<int64_t>(a.mtiles_bound) * NT * (a.ksplit > 1 ? a.ksplit : 1);
   blocks = (blocks + 7) / 8 * 8;
   if (blocks <= 0) return hipSuccess;
-  hipLaunchKernelGGL((k_tile<WF, DUAL, AM, EPI>), dim3(static_cast<unsigned>(blocks)), dim3(256), 0, s, a);
+  hipLaunchKernelGGL((k_tile<BN, WF, DUAL, AM, EPI>), dim3(static_cast<unsigned>(blocks)), dim3(BN * 2), 0, s, a);
   return hipGetLastError();
+}
+
+template <WFmt WF, bool DUAL, AMode AM, Epi EPI>
+hipError_t launch_bn(const TileArgs& a, hipStream_t s) {
+  // Single-matrix products take the wide 8-wavefront tile (half the L2 -> LDS bytes
+  // per flop).  The gate/up product keeps the 4-wavefront 128 x 128 tile: measured
+  // faster on the workloads' shapes (two blocks per CU instead of one).
+  const bool wide = !DUAL && a.N >= 256;
+  if (wide) return launch_one<256, WF, DUAL, AM, EPI>(a, s);
+  return launch_one<128, WF, DUAL, AM, EPI>(a, s);
 }
 
 }  // namespace
@@ -252,19 +294,19 @@ hipError_t launch_one(const TileArgs& a, hipStream_t s) {
 hipError_t launch_tile_gemm(const TileArgs& a, AMode am, WFmt wf, Epi epi, hipStream_t s) {
   // the combinations the layer uses
   if (epi == Epi::F32 && am == AMode::DENSE && wf == WFmt::BF16)
-    return launch_one<WFmt::BF16, false, AMode::DENSE, Epi::F32>(a, s);
+    return launch_one<128, WFmt::BF16, false, AMode::DENSE, Epi::F32>(a, s);
   if (epi == Epi::SWIGLU && am == AMode::GATHER && wf == WFmt::BF16)
-    return launch_one<WFmt::BF16, true, AMode::GATHER, Epi::SWIGLU>(a, s);
+    return launch_bn<WFmt::BF16, true, AMode::GATHER, Epi::SWIGLU>(a, s);
   if (epi == Epi::SWIGLU && am == AMode::GATHER && wf == WFmt::U8)
-    return launch_one<WFmt::U8, true, AMode::GATHER, Epi::SWIGLU>(a, s);
+    return launch_bn<WFmt::U8, true, AMode::GATHER, Epi::SWIGLU>(a, s);
   if (epi == Epi::SWIGLU && am == AMode::DENSE && wf == WFmt::BF16)
-    return launch_one<WFmt::BF16, true, AMode::DENSE, Epi::SWIGLU>(a, s);
+    return launch_bn<WFmt::BF16, true, AMode::DENSE, Epi::SWIGLU>(a, s);
   if (epi == Epi::SCALED_SLOT && am == AMode::DENSE && wf == WFmt::BF16)
-    return launch_one<WFmt::BF16, false, AMode::DENSE, Epi::SCALED_SLOT>(a, s);
+    return launch_bn<WFmt::BF16, false, AMode::DENSE, Epi::SCALED_SLOT>(a, s);
   if (epi == Epi::SCALED_SLOT && am == AMode::DENSE && wf == WFmt::U8)
-    return launch_one<WFmt::U8, false, AMode::DENSE, Epi::SCALED_SLOT>(a, s);
+    return launch_bn<WFmt::U8, false, AMode::DENSE, Epi::SCALED_SLOT>(a, s);
   if (epi == Epi::COMBINE && am == AMode::DENSE && wf == WFmt::BF16)
-    return launch_one<WFmt::BF16, false, AMode::DENSE, Epi::COMBINE>(a, s);
+    return launch_bn<WFmt::BF16, false, AMode::DENSE, Epi::COMBINE>(a, s);
   return hipErrorInvalidValue;
 }
 

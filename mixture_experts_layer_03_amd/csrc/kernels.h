@@ -35,7 +35,10 @@ struct PermuteArgs {
   int32_t* tiles;       // [max_tiles * 2] (expert, start position)
   int32_t* meta;        // [4]: D, number of M-tiles, valid slots
   int32_t* counts_copy; // optional extra copy of counts (caller output) or null
+  int32_t* hist;        // [ceil(nslots / kPermChunk)][E] per-block histograms (multi-block form)
 };
+constexpr int kPermChunk = 2048;   // slots per workgroup in the multi-block permutation
+constexpr int kPermSingleMax = 4096;  // up to this many slots one workgroup does everything
 hipError_t launch_permute(const PermuteArgs& a, hipStream_t s);
 
 // -------------------------------------------------- weight-streaming (decode) path
@@ -126,6 +129,8 @@ struct TileArgs {
   const int32_t* idx;       // COMBINE: routing
   int E;                    // COMBINE: expert count (validity of idx)
   int mtiles_bound;         // grid bound on M-tiles
+  int ksplit;               // F32 epilogue only: K split into this many partial outputs
+  int64_t part_stride;      // elements between partial outputs
 };
 hipError_t launch_tile_gemm(const TileArgs& a, AMode am, WFmt wf, Epi epi, hipStream_t s);
 

@@ -11,7 +11,7 @@
 #include <cstdio>
 #include <cstring>
 
-#include "../../include/moe.h"
+#include "moe.h"
 #include "kernels.h"
 
 using namespace moe;
@@ -94,8 +94,8 @@ struct Plan {
   bool decode;
   int P;
   int mtiles_bound;
-  size_t o_logits, o_idx, o_w, o_counts, o_offsets, o_perm, o_slotpos, o_active, o_meta, o_tiles, o_hm,
-      o_hs, o_r, o_rs, total;
+  size_t o_logits, o_idx, o_w, o_counts, o_offsets, o_perm, o_slotpos, o_active, o_meta, o_tiles, o_hist,
+      o_hm, o_hs, o_r, o_rs, total;
 };
 
 int router_parts(const moe_config& c) {
@@ -107,13 +107,24 @@ int router_parts(const moe_config& c) {
   return p;
 }
 
+// K-split of the tiled router GEMM: enough blocks to fill the chip when E is small.
+int router_ksplit(const moe_config& c, int64_t T) {
+  const int64_t mtiles = (T + kTileM - 1) / kTileM;
+  const int64_t ntiles = (c.num_experts + 127) / 128;
+  int64_t ks = (512 + mtiles * ntiles - 1) / (mtiles * ntiles);
+  const int64_t cap = c.hidden / 256 < 8 ? c.hidden / 256 : 8;
+  if (ks > cap) ks = cap;
+  if (ks < 1) ks = 1;
+  return static_cast<int>(ks);
+}
+
 void make_plan(const moe_config& c, int64_t T, Plan& p) {
   p.decode = c.path == MOE_PATH_DECODE ||
              (c.path == MOE_PATH_AUTO && (T <= kDecodeMaxT || c.act_dtype == MOE_DT_F32));
   const int64_t H = c.hidden, E = c.num_experts, k = c.top_k, I = c.moe_intermediate, Is = c.shared_intermediate;
   const size_t ab = c.act_dtype == MOE_DT_F32 ? 4 : 2;
   const int64_t slots = T * k;
-  p.P = p.decode ? router_parts(c) : 1;
+  p.P = p.decode ? router_parts(c) : router_ksplit(c, T);
   const int64_t dmax = slots < E ? slots : E;
   p.mtiles_bound = p.decode ? 0 : static_cast<int>((slots + dmax * (kTileM - 1)) / kTileM);
   size_t o = 0;
@@ -132,6 +143,7 @@ void make_plan(const moe_config& c, int64_t T, Plan& p) {
   p.o_active = take(E * 4);
   p.o_meta = take(64);
   p.o_tiles = take(size_t(p.mtiles_bound) * 8);
+  p.o_hist = take(slots > kPermSingleMax ? size_t((slots + kPermChunk - 1) / kPermChunk) * E * 4 : 0);
   p.o_hm = take(slots * I * ab);
   p.o_hs = take(T * Is * ab);
   p.o_r = take(slots * H * (p.decode ? 4 : 2));
@@ -207,6 +219,13 @@ moe_status check_T(int64_t T) {
 
 moe_status check_ws(const moe_config& c, int64_t T, void* ws, size_t ws_bytes, Plan& p) {
   make_plan(c, T, p);
+  if (!p.decode) {
+    // the tiled kernels address activation rows with 32-bit element offsets
+    int64_t kmax = c.hidden > c.moe_intermediate ? c.hidden : c.moe_intermediate;
+    if (c.shared_intermediate > kmax) kmax = c.shared_intermediate;
+    if (T * c.top_k * kmax >= (int64_t(1) << 32))
+      return fail(MOE_EUNSUPPORTED, "T * top_k * max(hidden, intermediate) >= 2^32 on the tiled path; split the batch");
+  }
   if (ws_bytes < p.total) return fail(MOE_EWORKSPACE, "workspace of %zu bytes < %zu required", ws_bytes, p.total);
   if (p.total > 0 && (!ws || !aligned(ws, 256))) return fail(MOE_EWORKSPACE, "workspace must be non-null and 256-byte aligned");
   return MOE_OK;
@@ -240,6 +259,8 @@ moe_status run_route(const moe_config& c, const Plan& p, int64_t T, const void* 
     g.out = logits;
     g.ldo = static_cast<int>(c.num_experts);
     g.mtiles_bound = static_cast<int>((T + kTileM - 1) / kTileM);
+    g.ksplit = p.P;
+    g.part_stride = T * c.num_experts;
     MOE_LAUNCH_STAGE(MOE_STAGE_ROUTER, launch_tile_gemm(g, AMode::DENSE, WFmt::BF16, Epi::F32, s), "router logits (tiled)");
   }
   TopkArgs t{};
@@ -278,6 +299,7 @@ moe_status run_permute(const moe_config& c, const Plan& p, int64_t T, const int3
   a.tiles = at<int32_t>(ws, p.o_tiles);
   a.meta = at<int32_t>(ws, p.o_meta);
   a.counts_copy = counts_copy;
+  a.hist = p.o_hist && T * c.top_k > kPermSingleMax ? at<int32_t>(ws, p.o_hist) : nullptr;
   MOE_LAUNCH_STAGE(MOE_STAGE_PERMUTE, launch_permute(a, s), "permutation");
   return MOE_OK;
 }

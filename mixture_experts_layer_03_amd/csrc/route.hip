@@ -1,5 +1,6 @@
-// Router top-k (one wavefront per token) and token permutation by expert (one
-// workgroup: LDS histogram, exclusive scan, scatter) for gfx950.
+// Router top-k (one wavefront per token) and token permutation by expert (LDS
+// histograms, exclusive scans, scatter; one workgroup for small batches, a
+// histogram pass and a scan-and-scatter pass over 2048-slot chunks otherwise).
 //
 // Routing semantics follow the model pages: scores are softmax over all experts or
 // an elementwise sigmoid of the logits; the correction bias is added to a copy of
@@ -159,41 +160,13 @@ __global__ __launch_bounds__(256) void k_topk(TopkArgs a) {
 constexpr int kPermThreads = 1024;
 constexpr int kPermUnroll = 4;
 
-__global__ __launch_bounds__(kPermThreads) void k_permute(PermuteArgs a) {
-  __shared__ int cnt[1024];
-  __shared__ int off[1024];
-  __shared__ int wtot[3][16];
-  __shared__ int total_s;
-  const int tid = threadIdx.x;
-  const int lane = tid & 63;
-  const int wv = tid >> 6;
+// Exclusive scans over the experts of: counts c[e], active flags and M-tiles per
+// expert.  Fills off[e] (LDS) with each expert's first position; when `write` is
+// set, also stores counts, offsets, the active-expert list, the M-tile map and meta.
+// Called by all kPermThreads threads with c = this thread's expert count (0 past E).
+__device__ void scan_experts(const PermuteArgs& a, int c, bool write, int* off, int (*wtot)[16], int* total_s) {
+  const int tid = threadIdx.x, lane = tid & 63, wv = tid >> 6;
   const int E = a.E;
-  const int n = a.nslots;
-  if (tid < E) cnt[tid] = 0;
-  __syncthreads();
-
-  // pass 1: rank of each slot inside its expert (LDS atomics)
-  for (int base = 0; base < n; base += kPermThreads * kPermUnroll) {
-    int e[kPermUnroll];
-#pragma unroll
-    for (int u = 0; u < kPermUnroll; ++u) {
-      const int s = base + u * kPermThreads + tid;
-      e[u] = s < n ? a.idx[s] : -1;
-    }
-#pragma unroll
-    for (int u = 0; u < kPermUnroll; ++u) {
-      const int s = base + u * kPermThreads + tid;
-      if (s < n) {
-        int p = -1;
-        if (e[u] >= 0 && e[u] < E) p = atomicAdd(&cnt[e[u]], 1);
-        a.slot_pos[s] = p;
-      }
-    }
-  }
-  __syncthreads();
-
-  // exclusive scans of: counts, active flags, M-tiles per expert
-  const int c = tid < E ? cnt[tid] : 0;
   const int f = c > 0 ? 1 : 0;
   const int nt = (a.BM > 0) ? (c + a.BM - 1) / a.BM : 0;
   int ci = c, fi = f, ti = nt;
@@ -231,45 +204,125 @@ __global__ __launch_bounds__(kPermThreads) void k_permute(PermuteArgs a) {
   const int te = ti - nt + wtot[2][wv];
   if (tid < E) {
     off[tid] = ce;
-    a.counts[tid] = c;
-    a.offsets[tid] = ce;
-    if (a.counts_copy) a.counts_copy[tid] = c;
-    if (f) a.active[fe] = tid;
-    for (int q = 0; q < nt; ++q) {
-      a.tiles[2 * (te + q)] = tid;
-      a.tiles[2 * (te + q) + 1] = ce + q * a.BM;
+    if (write) {
+      a.counts[tid] = c;
+      a.offsets[tid] = ce;
+      if (a.counts_copy) a.counts_copy[tid] = c;
+      if (f) a.active[fe] = tid;
+      for (int q = 0; q < nt; ++q) {
+        a.tiles[2 * (te + q)] = tid;
+        a.tiles[2 * (te + q) + 1] = ce + q * a.BM;
+      }
     }
   }
   if (tid == E - 1) {
-    a.offsets[E] = ce + c;
-    a.meta[0] = fe + f;
-    a.meta[1] = te + nt;
-    a.meta[2] = ce + c;
-    total_s = ce + c;
+    if (write) {
+      a.offsets[E] = ce + c;
+      a.meta[0] = fe + f;
+      a.meta[1] = te + nt;
+      a.meta[2] = ce + c;
+    }
+    *total_s = ce + c;
   }
   __syncthreads();
+}
 
-  // pass 2: scatter slot ids to their positions
-  for (int base = 0; base < n; base += kPermThreads * kPermUnroll) {
-    int p[kPermUnroll], e[kPermUnroll];
+// Rank of each slot of [s0, s1) among the slots of its expert in that range (LDS
+// atomics; the order inside an expert is not fixed), counts into cnt.
+__device__ void rank_slots(const PermuteArgs& a, int s0, int s1, int* cnt) {
+  const int tid = threadIdx.x;
+  for (int base = s0; base < s1; base += kPermThreads * kPermUnroll) {
+    int e[kPermUnroll];
 #pragma unroll
     for (int u = 0; u < kPermUnroll; ++u) {
       const int s = base + u * kPermThreads + tid;
-      p[u] = s < n ? a.slot_pos[s] : -1;
-      e[u] = s < n ? a.idx[s] : -1;
+      e[u] = s < s1 ? a.idx[s] : -1;
     }
 #pragma unroll
     for (int u = 0; u < kPermUnroll; ++u) {
       const int s = base + u * kPermThreads + tid;
+      if (s < s1) {
+        int p = -1;
+        if (e[u] >= 0 && e[u] < a.E) p = atomicAdd(&cnt[e[u]], 1);
+        a.slot_pos[s] = p;
+      }
+    }
+  }
+}
+
+// Scatter slot ids of [s0, s1) to position base[e] + rank.
+__device__ void scatter_slots(const PermuteArgs& a, int s0, int s1, const int* base) {
+  const int tid = threadIdx.x;
+  for (int b = s0; b < s1; b += kPermThreads * kPermUnroll) {
+    int p[kPermUnroll], e[kPermUnroll];
+#pragma unroll
+    for (int u = 0; u < kPermUnroll; ++u) {
+      const int s = b + u * kPermThreads + tid;
+      p[u] = s < s1 ? a.slot_pos[s] : -1;
+      e[u] = s < s1 ? a.idx[s] : -1;
+    }
+#pragma unroll
+    for (int u = 0; u < kPermUnroll; ++u) {
+      const int s = b + u * kPermThreads + tid;
       if (p[u] >= 0) {
-        const int pos = off[e[u]] + p[u];
+        const int pos = base[e[u]] + p[u];
         a.perm[pos] = s;
         a.slot_pos[s] = pos;
       }
     }
   }
-  const int total = total_s;
-  for (int q = total + tid; q < n; q += kPermThreads) a.perm[q] = -1;
+}
+
+// One workgroup: histogram, scans, scatter (small slot counts).
+__global__ __launch_bounds__(kPermThreads) void k_permute(PermuteArgs a) {
+  __shared__ int cnt[1024];
+  __shared__ int off[1024];
+  __shared__ int wtot[3][16];
+  __shared__ int total_s;
+  const int tid = threadIdx.x;
+  if (tid < a.E) cnt[tid] = 0;
+  __syncthreads();
+  rank_slots(a, 0, a.nslots, cnt);
+  __syncthreads();
+  scan_experts(a, tid < a.E ? cnt[tid] : 0, true, off, wtot, &total_s);
+  scatter_slots(a, 0, a.nslots, off);
+  for (int q = total_s + tid; q < a.nslots; q += kPermThreads) a.perm[q] = -1;
+}
+
+// Multi-block form, pass 1: per-chunk histogram and in-chunk ranks.
+__global__ __launch_bounds__(kPermThreads) void k_perm_count(PermuteArgs a) {
+  __shared__ int cnt[1024];
+  const int tid = threadIdx.x;
+  if (tid < a.E) cnt[tid] = 0;
+  __syncthreads();
+  const int s0 = blockIdx.x * kPermChunk, s1 = min(a.nslots, s0 + kPermChunk);
+  rank_slots(a, s0, s1, cnt);
+  __syncthreads();
+  if (tid < a.E) a.hist[static_cast<int64_t>(blockIdx.x) * a.E + tid] = cnt[tid];
+}
+
+// Pass 2: every block recomputes the expert totals and scans (block 0 publishes
+// them), adds the counts of earlier chunks, and scatters its own chunk.
+__global__ __launch_bounds__(kPermThreads) void k_perm_scatter(PermuteArgs a) {
+  __shared__ int off[1024];
+  __shared__ int wtot[3][16];
+  __shared__ int total_s;
+  const int tid = threadIdx.x;
+  const int nb = gridDim.x, b = blockIdx.x;
+  int tot = 0, pre = 0;
+  if (tid < a.E) {
+    for (int q = 0; q < nb; ++q) {
+      const int h = a.hist[static_cast<int64_t>(q) * a.E + tid];
+      tot += h;
+      pre += q < b ? h : 0;
+    }
+  }
+  scan_experts(a, tot, b == 0, off, wtot, &total_s);
+  if (tid < a.E) off[tid] += pre;
+  __syncthreads();
+  const int s0 = b * kPermChunk, s1 = min(a.nslots, s0 + kPermChunk);
+  scatter_slots(a, s0, s1, off);
+  for (int q = max(s0, total_s) + tid; q < s1; q += kPermThreads) a.perm[q] = -1;
 }
 
 }  // namespace
@@ -292,7 +345,15 @@ hipError_t launch_topk(const TopkArgs& a, hipStream_t s) {
 }
 
 hipError_t launch_permute(const PermuteArgs& a, hipStream_t s) {
-  hipLaunchKernelGGL(k_permute, dim3(1), dim3(kPermThreads), 0, s, a);
+  if (a.nslots <= kPermSingleMax || a.hist == nullptr) {
+    hipLaunchKernelGGL(k_permute, dim3(1), dim3(kPermThreads), 0, s, a);
+    return hipGetLastError();
+  }
+  const int nb = (a.nslots + kPermChunk - 1) / kPermChunk;
+  hipLaunchKernelGGL(k_perm_count, dim3(nb), dim3(kPermThreads), 0, s, a);
+  const hipError_t e = hipGetLastError();
+  if (e != hipSuccess) return e;
+  hipLaunchKernelGGL(k_perm_scatter, dim3(nb), dim3(kPermThreads), 0, s, a);
   return hipGetLastError();
 }
 

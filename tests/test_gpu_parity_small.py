@@ -64,6 +64,30 @@ def test_permute(cid, T):
         assert np.array_equal(got, slots), f"expert {e}"
 
 
+@pytest.mark.parametrize("T,E,k", [(1000, 40, 8), (2049, 512, 8), (600, 7, 7)])
+def test_permute_multi_block(T, E, k):
+    """Slot counts above one workgroup's share (2048-slot chunks, ragged last chunk),
+    with some dropped slots."""
+    import mixture_experts_layer_03_amd as moe
+    cfg = moe.MoEConfig(hidden=64, num_experts=E, top_k=k, moe_intermediate=64)
+    rng = np.random.default_rng(T + E)
+    idx_h = rng.integers(0, E, size=(T, k)).astype(np.int32)
+    idx_h[rng.random((T, k)) < 0.01] = -7
+    log(f"permute multi-block T={T} E={E} k={k}")
+    counts, offsets, perm = moe.permute(torch.from_numpy(idx_h).cuda(), cfg)
+    torch.cuda.synchronize()
+    valid = (idx_h >= 0) & (idx_h < E)
+    c_o = np.bincount(idx_h[valid], minlength=E)
+    assert np.array_equal(counts.cpu().numpy(), c_o)
+    off_o = np.concatenate([[0], np.cumsum(c_o)])
+    assert np.array_equal(offsets.cpu().numpy(), off_o)
+    p = perm.cpu().numpy()
+    flat = np.where(valid, idx_h, -1).reshape(-1)
+    for e in range(E):
+        assert np.array_equal(np.sort(p[off_o[e]:off_o[e + 1]]), np.nonzero(flat == e)[0]), f"expert {e}"
+    assert (p[off_o[-1]:] == -1).all()
+
+
 def test_permute_drops_out_of_range_indices():
     import mixture_experts_layer_03_amd as moe
     spec = SMALL[2]
