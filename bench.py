@@ -6,14 +6,17 @@ SwiGLU experts, shared expert, combine) on one batch of seeded synthetic tokens,
 inputs and weights already resident in HBM.  The headline workload is the
 Ling-lite-shaped layer (hidden 2048, 64 experts top-6, moe_intermediate 1408,
 shared width 2816, bf16) at T=4096 tokens; decode batches T=1 and T=64 of the
-same layer are reported alongside.  Layer copies are rotated between steps so
-that weight reads come from HBM, not from the 256 MB Infinity Cache.
+same layer are reported alongside (eager calls and HIP-graph replays).  Layer
+copies are rotated between steps so that weight reads come from HBM, not from
+the 256 MB Infinity Cache.
 
-Prints one JSON line (see the repository's design notes for every field).
+Prints one JSON line (field meanings are in the repository's design notes).
 """
 from __future__ import annotations
 
 import argparse
+import ctypes as C
+import hashlib
 import json
 import os
 import sys
@@ -21,9 +24,11 @@ import time
 
 import numpy as np
 
+ROOT = os.path.dirname(os.path.abspath(__file__))
 HBM_PEAK_GBPS = 8000.0          # MI355X HBM3E, published
 BF16_PEAK_TFLOPS = 2500.0       # MI355X dense bf16 MFMA, published
 METRIC = "MoE-layer tokens/s at T=1/64/4096; achieved HBM GB/s & MFMA % of peak"
+TRAFFIC_FILE = os.path.join(ROOT, "profiles", "traffic_counters.json")
 
 
 def parse():
@@ -38,8 +43,21 @@ def parse():
                     help="rotate layer copies until this many weight bytes separate reuses")
     ap.add_argument("--max-copies", type=int, default=8)
     ap.add_argument("--no-cpu-baseline", action="store_true")
-    ap.add_argument("--cpu-sample-tokens", type=int, default=256)
+    ap.add_argument("--cpu-sample-tokens", type=int, default=4096)
+    ap.add_argument("--no-graph", action="store_true", help="skip the HIP-graph replay timing")
+    ap.add_argument("--calib-copy", action="store_true",
+                    help="also run a 1 GiB device copy (reference kernel for counter scaling)")
     return ap.parse_args()
+
+
+def source_digest() -> str:
+    """Hash of the kernel sources (counter results are valid only for this exact code)."""
+    h = hashlib.sha256()
+    d = os.path.join(ROOT, "mixture_experts_layer_03_amd", "csrc")
+    for f in sorted(os.listdir(d)):
+        with open(os.path.join(d, f), "rb") as fh:
+            h.update(f.encode() + fh.read())
+    return h.hexdigest()[:16]
 
 
 def gpu_copy(spec, c, ref, device):
@@ -73,15 +91,32 @@ def algorithmic(spec, T, counts):
     byt = D * lb["expert"] + lb["shared"] + lb["router"] + T * H * 2 * lb["act"]
     byt += 4 * E if spec.use_expert_bias else 0
     flops = 2.0 * T * E * H + 6.0 * T * k * H * I + 6.0 * T * H * Is
-    per_expert_up_bytes = lb["expert"] * 2 / 3
-    up_bytes = D * per_expert_up_bytes + (2 * Is * H * lb["act"]) + T * H * lb["act"] + T * k * I * lb["act"]
+    # dominant kernel (routed + shared gate/up): weights of the D experts (and, on the
+    # streaming path, the shared gate/up), token rows in, SwiGLU rows out
+    up_bytes = D * lb["expert"] * 2 / 3 + T * H * lb["act"] + T * k * I * lb["act"]
+    up_bytes_decode = up_bytes + 2 * Is * H * lb["act"] + T * Is * lb["act"]
     up_flops = 4.0 * T * k * H * I
-    return dict(bytes=byt, flops=flops, D=D, up_bytes=up_bytes, up_flops=up_flops)
+    return dict(bytes=byt, flops=flops, D=D, up_bytes=up_bytes, up_bytes_decode=up_bytes_decode,
+                up_flops=up_flops)
 
 
-def run_case(moe, spec, cfg, copies, x, steps, warmup, stage_mask):
-    """Time `steps` layer calls over rotating copies; returns (seconds, stage timings)."""
+def stage_times(moe, stage_mask):
+    from mixture_experts_layer_03_amd import _lib
+    lib = moe.lib()
+    out = {}
+    for name, bit in _lib.STAGES.items():
+        if stage_mask & bit:
+            ms, n = C.c_float(0), C.c_int32(0)
+            _lib.check(lib.moe_profile_collect(bit, C.byref(ms), C.byref(n)))
+            if n.value:
+                out[name] = ms.value / n.value
+    return out
+
+
+def run_eager(moe, cfg, copies, x, steps, warmup, stage_mask):
+    """Time `steps` layer calls over rotating copies with per-stage HIP events."""
     import torch
+    from mixture_experts_layer_03_amd import _lib
     y = torch.empty_like(x)
     T = x.shape[0]
     ws = torch.empty(cfg.workspace_size(T), dtype=torch.uint8, device=x.device)
@@ -89,25 +124,50 @@ def run_case(moe, spec, cfg, copies, x, steps, warmup, stage_mask):
     for i in range(warmup):
         moe.forward(x, copies[i % L], cfg, ws=ws, out=y)
     torch.cuda.synchronize()
-    lib = moe.lib()
-    from mixture_experts_layer_03_amd import _lib
-    _lib.check(lib.moe_profile_enable(stage_mask, max(8, 8 * steps)))
+    _lib.check(moe.lib().moe_profile_enable(stage_mask, max(8, 16 * steps)))
     torch.cuda.synchronize()
     t0 = time.perf_counter()
     for i in range(steps):
         moe.forward(x, copies[i % L], cfg, ws=ws, out=y)
     torch.cuda.synchronize()
     t1 = time.perf_counter()
-    import ctypes as C
-    stages = {}
-    for name, bit in _lib.STAGES.items():
-        if stage_mask & bit:
-            ms, n = C.c_float(0), C.c_int32(0)
-            _lib.check(lib.moe_profile_collect(bit, C.byref(ms), C.byref(n)))
-            if n.value:
-                stages[name] = ms.value / n.value
-    _lib.check(lib.moe_profile_disable())
-    return t1 - t0, stages, y
+    st = stage_times(moe, stage_mask)
+    _lib.check(moe.lib().moe_profile_disable())
+    return t1 - t0, st
+
+
+def run_graph(moe, cfg, copies, x, steps, warmup):
+    """Capture one layer call per copy in a HIP graph and time replays."""
+    import torch
+    T = x.shape[0]
+    L = len(copies)
+    ys = [torch.empty_like(x) for _ in range(L)]
+    wss = [torch.empty(cfg.workspace_size(T), dtype=torch.uint8, device=x.device) for _ in range(L)]
+    for i in range(L):                      # eager reference outputs (and warm caches)
+        moe.forward(x, copies[i], cfg, ws=wss[i], out=ys[i])
+    torch.cuda.synchronize()
+    ref = [y.clone() for y in ys]
+    graphs = []
+    s = torch.cuda.Stream()
+    s.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(s):
+        for i in range(L):
+            g = torch.cuda.CUDAGraph()
+            with torch.cuda.graph(g, stream=s):
+                moe.forward(x, copies[i], cfg, ws=wss[i], out=ys[i])
+            graphs.append(g)
+    torch.cuda.current_stream().wait_stream(s)
+    torch.cuda.synchronize()
+    for i in range(max(warmup, L)):
+        graphs[i % L].replay()
+    torch.cuda.synchronize()
+    ok = all(torch.equal(ys[i], ref[i]) for i in range(L))
+    t0 = time.perf_counter()
+    for i in range(steps):
+        graphs[i % L].replay()
+    torch.cuda.synchronize()
+    t1 = time.perf_counter()
+    return t1 - t0, ok
 
 
 def cpu_baseline(spec, L_host, x_host, n_tok):
@@ -119,13 +179,34 @@ def cpu_baseline(spec, L_host, x_host, n_tok):
     except Exception:
         cores = os.cpu_count() or 1
     tok = np.arange(min(n_tok, x_host.shape[0]))
-    t0 = time.perf_counter()
     ocfg = om.OracleConfig(**{f.name: getattr(spec, f.name) for f in fields(om.OracleConfig)})
-    om.forward(x_host, L_host, ocfg, tokens=tok)
-    dt = time.perf_counter() - t0
-    return dict(value=len(tok) / dt, unit="tokens/s", cores=int(cores), kind="oracle",
-                sample=f"fp64 oracle, {len(tok)} tokens of the T={x_host.shape[0]} batch, "
-                       f"same layer, {dt:.1f} s")
+    # repeat the token sample until about min_seconds of oracle work (bounded by max_passes)
+    min_seconds, max_passes = 10.0, 20
+    passes, t0 = 0, time.perf_counter()
+    while True:
+        om.forward(x_host, L_host, ocfg, tokens=tok)
+        passes += 1
+        dt = time.perf_counter() - t0
+        if dt >= min_seconds or passes >= max_passes:
+            break
+    return dict(value=passes * len(tok) / dt, unit="tokens/s", cores=int(cores), kind="oracle",
+                sample=f"fp64 oracle (NumPy/BLAS) on {len(tok)} tokens of the T={x_host.shape[0]} batch "
+                       f"(same layer and routing), {passes} passes, {dt:.1f} s on {cores} threads")
+
+
+def recorded_traffic(kernel_key, digest, launch_div=1.0):
+    """Counter-measured HBM bytes per launch, if recorded for exactly this source."""
+    try:
+        with open(TRAFFIC_FILE) as f:
+            rec = json.load(f)
+    except (OSError, ValueError):
+        return None
+    if rec.get("source_digest") != digest:
+        return None
+    k = rec.get("kernels", {}).get(kernel_key)
+    if not k:
+        return None
+    return k.get("hbm_bytes_per_launch")
 
 
 def main():
@@ -135,10 +216,11 @@ def main():
         print("bench.py runs on exactly one GPU: this layer build has no multi-GPU path "
               "(expert-parallel sharding is a design note only); use --gpus 1.", file=sys.stderr)
         sys.exit(2)
-    sys.path.insert(0, os.path.dirname(os.path.abspath(__file__)))
+    sys.path.insert(0, ROOT)
     import torch
     import synth
     import mixture_experts_layer_03_amd as moe
+    from mixture_experts_layer_03_amd import _lib
 
     spec = synth.SPECS[args.config]
     dev = torch.device("cuda:0")
@@ -148,10 +230,7 @@ def main():
     gen_s = time.perf_counter() - t_gen
     lb = synth.layer_bytes(spec)
     layer_bytes = spec.num_experts * lb["expert"] + lb["shared"] + lb["router"]
-
-    def copies_for(touched):
-        n = int(np.ceil(args.min_rotation_bytes / max(touched, 1.0)))
-        return max(1, min(args.max_copies, n))
+    digest = source_digest()
 
     all_copies = [W0]
 
@@ -163,52 +242,73 @@ def main():
     cfg = moe.MoEConfig.from_object(spec)
     results = {}
     Ts = [args.tokens] + [int(t) for t in args.decode_tokens.split(",") if t.strip()]
+    head_x_host = None
     for T in Ts:
         x_host = synth.make_x(spec, T)
         x = moe.host_tensor_to_device(x_host, dev)
         _, (idx, wt, counts) = moe.forward(x, W0, cfg, return_routing=True)
         torch.cuda.synchronize()
         alg = algorithmic(spec, T, counts.cpu().numpy())
-        ncp = copies_for(alg["bytes"])
+        ncp = max(1, min(args.max_copies, int(np.ceil(args.min_rotation_bytes / max(alg["bytes"], 1.0)))))
         cps = get_copies(ncp)
-        mask = moe._lib.STAGES["up"] | moe._lib.STAGES["down"]
-        steps = args.steps if T == args.tokens else max(args.steps, 50)
-        secs, stages, _ = run_case(moe, spec, cfg, cps, x, steps, args.warmup, mask)
+        mask = _lib.STAGES["up"] | _lib.STAGES["down"]
+        steps = args.steps if T == args.tokens else max(args.steps, 100)
+        secs, stages = run_eager(moe, cfg, cps, x, steps, args.warmup, mask)
         t_step = secs / steps
-        results[T] = dict(T=T, copies=ncp, ms_per_step=t_step * 1e3, tokens_per_s=T / t_step,
-                          hbm_gbps=alg["bytes"] / t_step / 1e9, mfma_tflops=alg["flops"] / t_step / 1e12,
-                          distinct_experts=alg["D"], stage_ms=stages, alg=alg)
-        results[T]["hbm_frac"] = results[T]["hbm_gbps"] / HBM_PEAK_GBPS
-        results[T]["mfma_frac"] = results[T]["mfma_tflops"] / BF16_PEAK_TFLOPS
-        results[T]["roofline_frac"] = max(alg["bytes"] / (HBM_PEAK_GBPS * 1e9),
-                                          alg["flops"] / (BF16_PEAK_TFLOPS * 1e12)) / t_step
+        r = dict(T=T, copies=ncp, ms_per_step=t_step * 1e3, tokens_per_s=T / t_step,
+                 hbm_gbps=alg["bytes"] / t_step / 1e9, mfma_tflops=alg["flops"] / t_step / 1e12,
+                 distinct_experts=alg["D"], stage_ms=stages, alg=alg,
+                 path="decode" if T <= 64 else "prefill")
+        r["hbm_frac"] = r["hbm_gbps"] / HBM_PEAK_GBPS
+        r["mfma_frac"] = r["mfma_tflops"] / BF16_PEAK_TFLOPS
+        r["roofline_frac"] = max(alg["bytes"] / (HBM_PEAK_GBPS * 1e9),
+                                 alg["flops"] / (BF16_PEAK_TFLOPS * 1e12)) / t_step
+        if not args.no_graph:
+            gsecs, ok = run_graph(moe, cfg, cps, x, steps, args.warmup)
+            gt = gsecs / steps
+            r.update(graph_ms_per_step=gt * 1e3, graph_tokens_per_s=T / gt,
+                     graph_hbm_gbps=alg["bytes"] / gt / 1e9,
+                     graph_hbm_frac=alg["bytes"] / gt / 1e9 / HBM_PEAK_GBPS,
+                     graph_roofline_frac=max(alg["bytes"] / (HBM_PEAK_GBPS * 1e9),
+                                             alg["flops"] / (BF16_PEAK_TFLOPS * 1e12)) / gt,
+                     graph_matches_eager=ok)
+        results[T] = r
         if T == args.tokens:
             head_x_host = x_host
+
+    if args.calib_copy:
+        a = torch.empty(1 << 30, dtype=torch.uint8, device=dev)
+        b = torch.empty_like(a)
+        b.copy_(a)
+        torch.cuda.synchronize()
 
     head = results[args.tokens]
     alg = head["alg"]
     up_ms = head["stage_ms"].get("up")
-    prefill = args.tokens > 64 and spec.act_dtype == "bf16"
+    prefill = head["path"] == "prefill"
+    roof = None
     if up_ms:
         if prefill:
             ach = alg["up_flops"] / (up_ms * 1e-3) / 1e12
+            key = f"up_tiled_cfg{args.config}_T{args.tokens}"
             roof = dict(bound="mfma", achieved=ach, peak=BF16_PEAK_TFLOPS, unit="TFLOP/s",
-                        frac=ach / BF16_PEAK_TFLOPS, traffic=None,
-                        kernel="routed gate/up grouped GEMM + SwiGLU", avg_ms=up_ms)
+                        frac=ach / BF16_PEAK_TFLOPS, traffic=recorded_traffic(key, digest),
+                        kernel="routed gate/up grouped GEMM + SwiGLU (k_tile, gather, dual)",
+                        avg_ms=up_ms, algorithmic_flops=alg["up_flops"])
         else:
-            ach = alg["up_bytes"] / (up_ms * 1e-3) / 1e9
+            ach = alg["up_bytes_decode"] / (up_ms * 1e-3) / 1e9
+            key = f"up_stream_cfg{args.config}_T{args.tokens}"
             roof = dict(bound="hbm", achieved=ach, peak=HBM_PEAK_GBPS, unit="GB/s",
-                        frac=ach / HBM_PEAK_GBPS, traffic=None,
-                        kernel="routed+shared gate/up weight streaming + SwiGLU", avg_ms=up_ms)
-    else:
-        roof = None
+                        frac=ach / HBM_PEAK_GBPS, traffic=recorded_traffic(key, digest),
+                        kernel="routed+shared gate/up weight streaming + SwiGLU (k_skinny_up)",
+                        avg_ms=up_ms, algorithmic_bytes=alg["up_bytes_decode"])
 
     cpu = None
     if not args.no_cpu_baseline:
         cpu = cpu_baseline(spec, L_host, head_x_host, args.cpu_sample_tokens)
 
     def brief(r):
-        return {k: (round(v, 4) if isinstance(v, float) else v) for k, v in r.items() if k != "alg"}
+        return {k: (round(v, 5) if isinstance(v, float) else v) for k, v in r.items() if k != "alg"}
 
     line = {
         "metric": METRIC,
@@ -227,14 +327,15 @@ def main():
                                f"top-{spec.top_k}, moe_intermediate {spec.moe_intermediate}, shared "
                                f"{spec.shared_intermediate}, {spec.score_function}, n_group {spec.n_group}, "
                                f"experts {spec.expert_dtype}; T={args.tokens}",
-                   "tokens": args.tokens, "layer_gb": layer_bytes / 1e9},
+                   "tokens": args.tokens, "layer_gb": round(layer_bytes / 1e9, 4)},
         "roofline": roof,
         "cpu_baseline": cpu,
         "hbm_gbps": head["hbm_gbps"],
         "mfma_frac": head["mfma_frac"],
         "roofline_frac": head["roofline_frac"],
         "per_T": [brief(results[T]) for T in Ts],
-        "gen_seconds": gen_s,
+        "source_digest": digest,
+        "gen_seconds": round(gen_s, 2),
     }
     print(json.dumps(line), flush=True)
 

@@ -47,9 +47,15 @@ __global__ __launch_bounds__(BN * 2) void k_tile(TileArgs a) {
   const int NT = (a.N + NCOL - 1) / NCOL;
   const int per = gridDim.x / 8;
   const int KS = a.ksplit > 1 ? a.ksplit : 1;
+  // logical tile order: consecutive blocks land on one XCD (hardware deals blocks
+  // round-robin over the 8 XCDs); within a group of G consecutive M-tiles the N-tile
+  // index varies slowest, so the G blocks that read the same weight panel run
+  // together and share it through L2, and the group's G activation panels stay hot
   const int Lx = (blockIdx.x % 8) * per + blockIdx.x / 8;
   const int kp = Lx % KS, L = Lx / KS;
-  const int mt = L / NT, nt = L % NT;
+  const int G = a.group_m > 1 ? a.group_m : 1;
+  const int grp = L / (G * NT), rem = L % (G * NT);
+  const int mt = grp * G + rem % G, nt = rem / G;
 
   int e = 0, m_begin, m_rows;
   if (a.routed) {
@@ -112,42 +118,44 @@ __global__ __launch_bounds__(BN * 2) void k_tile(TileArgs a) {
     }
   }
 
-  uint4 ra[AR], rb[BR];
-  uint2 rq[WF == WFmt::U8 ? BR : 1];
-  float rs[WF == WFmt::U8 ? BR : 1], rz[WF == WFmt::U8 ? BR : 1];
-  auto gload = [&](int kt) {
+  struct Regs {
+    uint4 a[AR], b[WF == WFmt::U8 ? 1 : BR];
+    uint2 q[WF == WFmt::U8 ? BR : 1];
+    float s[WF == WFmt::U8 ? BR : 1], z[WF == WFmt::U8 ? BR : 1];
+  };
+  auto gload = [&](Regs& R, int kt) {
     const int k0 = kt * BK;
 #pragma unroll
-    for (int i = 0; i < AR; ++i) ra[i] = ldg16(a.A + a_off[i] + k0);
+    for (int i = 0; i < AR; ++i) R.a[i] = ldg16(a.A + a_off[i] + k0);
 #pragma unroll
     for (int i = 0; i < BR; ++i) {
       if constexpr (WF == WFmt::U8) {
-        rq[i] = *reinterpret_cast<const uint2*>(bp[i] + k0);
-        rs[i] = f16_to_f32(bsp[i][kt]);
-        rz[i] = f16_to_f32(bzp[i][kt]);
+        R.q[i] = *reinterpret_cast<const uint2*>(bp[i] + k0);
+        R.s[i] = f16_to_f32(bsp[i][kt]);
+        R.z[i] = f16_to_f32(bzp[i][kt]);
       } else {
-        rb[i] = ldg16(bp[i] + 2 * k0);
+        R.b[i] = ldg16(bp[i] + 2 * k0);
       }
     }
   };
   const int wr = r0 * BK + ((sc ^ (r0 & 7)) << 3);  // LDS write base (elements)
-  auto sstore = [&](int buf) {
+  auto sstore = [&](const Regs& R, int buf) {
     uint16_t* As = smem + buf * STAGE_ELEMS;
     uint16_t* Bs = As + BM * BK;
 #pragma unroll
-    for (int i = 0; i < AR; ++i) *reinterpret_cast<uint4*>(&As[wr + RSTEP * i * BK]) = ra[i];
+    for (int i = 0; i < AR; ++i) *reinterpret_cast<uint4*>(&As[wr + RSTEP * i * BK]) = R.a[i];
 #pragma unroll
     for (int i = 0; i < BR; ++i) {
       uint4 v;
       if constexpr (WF == WFmt::U8) {
-        const float s = rs[i], z = rz[i];
-        const uint32_t lo = rq[i].x, hi = rq[i].y;
+        const float s = R.s[i], z = R.z[i];
+        const uint32_t lo = R.q[i].x, hi = R.q[i].y;
         v.x = pack_bf16x2(s * (static_cast<float>(lo & 0xffu) - z), s * (static_cast<float>((lo >> 8) & 0xffu) - z));
         v.y = pack_bf16x2(s * (static_cast<float>((lo >> 16) & 0xffu) - z), s * (static_cast<float>(lo >> 24) - z));
         v.z = pack_bf16x2(s * (static_cast<float>(hi & 0xffu) - z), s * (static_cast<float>((hi >> 8) & 0xffu) - z));
         v.w = pack_bf16x2(s * (static_cast<float>((hi >> 16) & 0xffu) - z), s * (static_cast<float>(hi >> 24) - z));
       } else {
-        v = rb[i];
+        v = R.b[i];
       }
       *reinterpret_cast<uint4*>(&Bs[wr + RSTEP * i * BK]) = v;
     }
@@ -183,16 +191,20 @@ __global__ __launch_bounds__(BN * 2) void k_tile(TileArgs a) {
     }
   };
 
+  // one register stage: the next K-step's loads are issued before this step's MFMAs.
+  // (A second register stage to double the load lead time measured 1.6-1.9x slower on
+  // the workloads: it either spills or halves the wavefronts per SIMD.)
+  Regs R;
   if (kt0 < kt1) {
-    gload(kt0);
-    sstore(0);
+    gload(R, kt0);
+    sstore(R, 0);
   }
   __syncthreads();
   for (int kt = kt0; kt < kt1; ++kt) {
     const int buf = (kt - kt0) & 1;
-    if (kt + 1 < kt1) gload(kt + 1);
+    if (kt + 1 < kt1) gload(R, kt + 1);
     compute(buf);
-    if (kt + 1 < kt1) sstore(buf ^ 1);
+    if (kt + 1 < kt1) sstore(R, buf ^ 1);
     __syncthreads();
   }
 
@@ -272,7 +284,9 @@ template <int BN, WFmt WF, bool DUAL, AMode AM, Epi EPI>
 hipError_t launch_one(const TileArgs& a, hipStream_t s) {
   constexpr int NCOL = DUAL ? BN / 2 : BN;
   const int NT = (a.N + NCOL - 1) / NCOL;
-  int64_t blocks = static_cast<int64_t>(a.mtiles_bound) * NT * (a.ksplit > 1 ? a.ksplit : 1);
+  const int G = a.group_m > 1 ? a.group_m : 1;
+  const int64_t mt_pad = (a.mtiles_bound + G - 1) / G * G;  // whole groups (extra tiles exit)
+  int64_t blocks = mt_pad * NT * (a.ksplit > 1 ? a.ksplit : 1);
   blocks = (blocks + 7) / 8 * 8;
   if (blocks <= 0) return hipSuccess;
   hipLaunchKernelGGL((k_tile<BN, WF, DUAL, AM, EPI>), dim3(static_cast<unsigned>(blocks)), dim3(BN * 2), 0, s, a);

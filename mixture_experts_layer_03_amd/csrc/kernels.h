@@ -40,6 +40,8 @@ struct PermuteArgs {
 constexpr int kPermChunk = 2048;   // slots per workgroup in the multi-block permutation
 constexpr int kPermSingleMax = 4096;  // up to this many slots one workgroup does everything
 hipError_t launch_permute(const PermuteArgs& a, hipStream_t s);
+// top-k of every token and the permutation in one workgroup (a.nslots <= kPermSingleMax)
+hipError_t launch_route_permute(const TopkArgs& t, const PermuteArgs& a, hipStream_t s);
 
 // -------------------------------------------------- weight-streaming (decode) path
 // C[m][n] = sum_k A[m][k] W[n][k] with the weight rows streamed from HBM once per
@@ -131,6 +133,7 @@ struct TileArgs {
   int mtiles_bound;         // grid bound on M-tiles
   int ksplit;               // F32 epilogue only: K split into this many partial outputs
   int64_t part_stride;      // elements between partial outputs
+  int group_m;              // M-tiles per block-order group (weight-panel reuse in L2)
 };
 hipError_t launch_tile_gemm(const TileArgs& a, AMode am, WFmt wf, Epi epi, hipStream_t s);
 

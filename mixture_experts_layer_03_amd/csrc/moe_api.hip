@@ -36,6 +36,8 @@ moe_status ok() {
 constexpr int64_t kMaxH = 16384, kMaxE = 1024, kMaxI = 32768, kMaxT = int64_t(1) << 20, kMaxK = 16;
 constexpr int64_t kMaxGroupsGpu = 64;
 constexpr int kDecodeMaxT = 64;
+constexpr int kFusedRouteMaxT = 16;  // one workgroup routes and permutes up to this many tokens
+constexpr int kGroupM = 4;           // M-tiles per block-order group of the tiled GEMMs
 
 bool is_flag(int32_t v) { return v == 0 || v == 1; }
 
@@ -202,11 +204,11 @@ struct ProfScope {
   }
 };
 
-#define MOE_LAUNCH_STAGE(stage, expr, what)            \
+#define MOE_LAUNCH_STAGE(stage, stream, expr, what)    \
   do {                                                 \
     hipError_t e_;                                     \
     {                                                  \
-      ProfScope ps_((stage), s);                       \
+      ProfScope ps_((stage), (stream));                \
       e_ = (expr);                                     \
     }                                                  \
     if (e_ != hipSuccess) return hip_fail(e_, what);   \
@@ -237,16 +239,18 @@ moe_status check_ws(const moe_config& c, int64_t T, void* ws, size_t ws_bytes, P
     if (!aligned((ptr), (align))) return fail(MOE_EINVAL_ARG, "%s is not %d-byte aligned", name, (int)(align)); \
   } while (0)
 
-// router: logits + top-k into (idx, w)
-moe_status run_route(const moe_config& c, const Plan& p, int64_t T, const void* x, const void* router_w,
-                     const float* router_bias, const float* expert_bias, int32_t* idx, float* w, void* ws,
-                     hipStream_t s) {
+TopkArgs topk_args(const moe_config& c, const Plan& p, int64_t T, void* ws, const float* router_bias,
+                   const float* expert_bias, int32_t* idx, float* w);
+
+// router logits (partials) into the workspace
+moe_status run_logits(const moe_config& c, const Plan& p, int64_t T, const void* x, const void* router_w,
+                      void* ws, hipStream_t s) {
   const Act act = c.act_dtype == MOE_DT_F32 ? Act::F32 : Act::BF16;
   float* logits = at<float>(ws, p.o_logits);
   if (p.decode) {
     SkinnyRouterArgs r{x, router_w, logits, static_cast<int>(T), static_cast<int>(c.hidden),
                        static_cast<int>(c.num_experts), p.P};
-    MOE_LAUNCH_STAGE(MOE_STAGE_ROUTER, launch_skinny_router(r, act, device_cus(), s), "router logits");
+    MOE_LAUNCH_STAGE(MOE_STAGE_ROUTER, s, launch_skinny_router(r, act, device_cus(), s), "router logits");
   } else {
     TileArgs g{};
     g.A = static_cast<const uint16_t*>(x);
@@ -259,10 +263,28 @@ moe_status run_route(const moe_config& c, const Plan& p, int64_t T, const void* 
     g.out = logits;
     g.ldo = static_cast<int>(c.num_experts);
     g.mtiles_bound = static_cast<int>((T + kTileM - 1) / kTileM);
+  g.group_m = kGroupM;
     g.ksplit = p.P;
     g.part_stride = T * c.num_experts;
-    MOE_LAUNCH_STAGE(MOE_STAGE_ROUTER, launch_tile_gemm(g, AMode::DENSE, WFmt::BF16, Epi::F32, s), "router logits (tiled)");
+    MOE_LAUNCH_STAGE(MOE_STAGE_ROUTER, s, launch_tile_gemm(g, AMode::DENSE, WFmt::BF16, Epi::F32, s), "router logits (tiled)");
   }
+  return MOE_OK;
+}
+
+// router: logits + top-k into (idx, w)
+moe_status run_route(const moe_config& c, const Plan& p, int64_t T, const void* x, const void* router_w,
+                     const float* router_bias, const float* expert_bias, int32_t* idx, float* w, void* ws,
+                     hipStream_t s) {
+  const moe_status st = run_logits(c, p, T, x, router_w, ws, s);
+  if (st != MOE_OK) return st;
+  TopkArgs t = topk_args(c, p, T, ws, router_bias, expert_bias, idx, w);
+  MOE_LAUNCH_STAGE(MOE_STAGE_TOPK, s, launch_topk(t, s), "top-k");
+  return MOE_OK;
+}
+
+TopkArgs topk_args(const moe_config& c, const Plan& p, int64_t T, void* ws, const float* router_bias,
+                   const float* expert_bias, int32_t* idx, float* w) {
+  float* logits = at<float>(ws, p.o_logits);
   TopkArgs t{};
   t.logits = logits;
   t.part_stride = T * c.num_experts;
@@ -280,12 +302,11 @@ moe_status run_route(const moe_config& c, const Plan& p, int64_t T, const void* 
   t.expert_bias = expert_bias;
   t.idx = idx;
   t.w = w;
-  MOE_LAUNCH_STAGE(MOE_STAGE_TOPK, launch_topk(t, s), "top-k");
-  return MOE_OK;
+  return t;
 }
 
-moe_status run_permute(const moe_config& c, const Plan& p, int64_t T, const int32_t* idx, int32_t* counts,
-                       int32_t* offsets, int32_t* perm, int32_t* counts_copy, void* ws, hipStream_t s) {
+PermuteArgs permute_args(const moe_config& c, const Plan& p, int64_t T, const int32_t* idx, int32_t* counts,
+                         int32_t* offsets, int32_t* perm, int32_t* counts_copy, void* ws) {
   PermuteArgs a{};
   a.idx = idx;
   a.nslots = static_cast<int>(T * c.top_k);
@@ -300,12 +321,19 @@ moe_status run_permute(const moe_config& c, const Plan& p, int64_t T, const int3
   a.meta = at<int32_t>(ws, p.o_meta);
   a.counts_copy = counts_copy;
   a.hist = p.o_hist && T * c.top_k > kPermSingleMax ? at<int32_t>(ws, p.o_hist) : nullptr;
-  MOE_LAUNCH_STAGE(MOE_STAGE_PERMUTE, launch_permute(a, s), "permutation");
+  return a;
+}
+
+moe_status run_permute(const moe_config& c, const Plan& p, int64_t T, const int32_t* idx, int32_t* counts,
+                       int32_t* offsets, int32_t* perm, int32_t* counts_copy, void* ws, hipStream_t s) {
+  const PermuteArgs a = permute_args(c, p, T, idx, counts, offsets, perm, counts_copy, ws);
+  MOE_LAUNCH_STAGE(MOE_STAGE_PERMUTE, s, launch_permute(a, s), "permutation");
   return MOE_OK;
 }
 
 moe_status run_experts(const moe_config& c, const Plan& p, int64_t T, const void* x, const moe_weights* w,
-                       const int32_t* idx, const float* topk_w, void* y, void* ws, hipStream_t s) {
+                       const int32_t* idx, const float* topk_w, void* y, void* ws, hipStream_t s,
+                       bool permuted = false) {
   const Act act = c.act_dtype == MOE_DT_F32 ? Act::F32 : Act::BF16;
   const WFmt wf = c.expert_dtype == MOE_DT_U8_AFFINE ? WFmt::U8 : (act == Act::F32 ? WFmt::F32 : WFmt::BF16);
   const int Ti = static_cast<int>(T), H = static_cast<int>(c.hidden), I = static_cast<int>(c.moe_intermediate),
@@ -319,8 +347,10 @@ moe_status run_experts(const moe_config& c, const Plan& p, int64_t T, const void
   void* hs = at<void>(ws, p.o_hs);
   void* r = at<void>(ws, p.o_r);
   float* rs = at<float>(ws, p.o_rs);
-  moe_status st = run_permute(c, p, T, idx, counts, offsets, perm, nullptr, ws, s);
-  if (st != MOE_OK) return st;
+  if (!permuted) {
+    const moe_status st = run_permute(c, p, T, idx, counts, offsets, perm, nullptr, ws, s);
+    if (st != MOE_OK) return st;
+  }
   const int ncu = device_cus();
   if (p.decode) {
     SkinnyUpArgs u{};
@@ -346,7 +376,7 @@ moe_status run_experts(const moe_config& c, const Plan& p, int64_t T, const void
     u.Is = Is;
     u.k = k;
     u.E = E;
-    MOE_LAUNCH_STAGE(MOE_STAGE_UP, launch_skinny_up(u, act, wf, ncu, s), "expert gate/up (streaming)");
+    MOE_LAUNCH_STAGE(MOE_STAGE_UP, s, launch_skinny_up(u, act, wf, ncu, s), "expert gate/up (streaming)");
     SkinnyDownArgs d{};
     d.hm = hm;
     d.hs = hs;
@@ -368,9 +398,9 @@ moe_status run_experts(const moe_config& c, const Plan& p, int64_t T, const void
     d.Is = Is;
     d.k = k;
     d.E = E;
-    MOE_LAUNCH_STAGE(MOE_STAGE_DOWN, launch_skinny_down(d, act, wf, ncu, s), "expert down (streaming)");
+    MOE_LAUNCH_STAGE(MOE_STAGE_DOWN, s, launch_skinny_down(d, act, wf, ncu, s), "expert down (streaming)");
     CombineArgs cb{r, Is > 0 ? rs : nullptr, idx, y, Ti, H, k, E, 0};
-    MOE_LAUNCH_STAGE(MOE_STAGE_COMBINE, launch_combine(cb, act, s), "combine");
+    MOE_LAUNCH_STAGE(MOE_STAGE_COMBINE, s, launch_combine(cb, act, s), "combine");
     return MOE_OK;
   }
   // tiled MFMA path (bf16 activations)
@@ -396,7 +426,8 @@ moe_status run_experts(const moe_config& c, const Plan& p, int64_t T, const void
   g.out = hm;
   g.ldo = I;
   g.mtiles_bound = p.mtiles_bound;
-  MOE_LAUNCH_STAGE(MOE_STAGE_UP, launch_tile_gemm(g, AMode::GATHER, wf, Epi::SWIGLU, s), "expert gate/up (tiled)");
+  g.group_m = kGroupM;
+  MOE_LAUNCH_STAGE(MOE_STAGE_UP, s, launch_tile_gemm(g, AMode::GATHER, wf, Epi::SWIGLU, s), "expert gate/up (tiled)");
   TileArgs d{};
   d.A = static_cast<const uint16_t*>(hm);
   d.K = I;
@@ -415,7 +446,8 @@ moe_status run_experts(const moe_config& c, const Plan& p, int64_t T, const void
   d.ldo = H;
   d.topk_w = topk_w;
   d.mtiles_bound = p.mtiles_bound;
-  MOE_LAUNCH_STAGE(MOE_STAGE_DOWN, launch_tile_gemm(d, AMode::DENSE, wf, Epi::SCALED_SLOT, s), "expert down (tiled)");
+  d.group_m = kGroupM;
+  MOE_LAUNCH_STAGE(MOE_STAGE_DOWN, s, launch_tile_gemm(d, AMode::DENSE, wf, Epi::SCALED_SLOT, s), "expert down (tiled)");
   (void)dmax;
   if (Is > 0) {
     TileArgs su{};
@@ -429,7 +461,8 @@ moe_status run_experts(const moe_config& c, const Plan& p, int64_t T, const void
     su.out = hs;
     su.ldo = Is;
     su.mtiles_bound = static_cast<int>((T + kTileM - 1) / kTileM);
-    MOE_LAUNCH_STAGE(MOE_STAGE_SHARED_UP, launch_tile_gemm(su, AMode::DENSE, WFmt::BF16, Epi::SWIGLU, s), "shared gate/up (tiled)");
+  su.group_m = kGroupM;
+    MOE_LAUNCH_STAGE(MOE_STAGE_SHARED_UP, s, launch_tile_gemm(su, AMode::DENSE, WFmt::BF16, Epi::SWIGLU, s), "shared gate/up (tiled)");
     TileArgs sd{};
     sd.A = static_cast<const uint16_t*>(hs);
     sd.K = Is;
@@ -444,10 +477,11 @@ moe_status run_experts(const moe_config& c, const Plan& p, int64_t T, const void
     sd.k = k;
     sd.E = E;
     sd.mtiles_bound = su.mtiles_bound;
-    MOE_LAUNCH_STAGE(MOE_STAGE_SHARED_DOWN, launch_tile_gemm(sd, AMode::DENSE, WFmt::BF16, Epi::COMBINE, s), "shared down + combine (tiled)");
+  sd.group_m = kGroupM;
+    MOE_LAUNCH_STAGE(MOE_STAGE_SHARED_DOWN, s, launch_tile_gemm(sd, AMode::DENSE, WFmt::BF16, Epi::COMBINE, s), "shared down + combine (tiled)");
   } else {
     CombineArgs cb{r, nullptr, idx, y, Ti, H, k, E, 1};
-    MOE_LAUNCH_STAGE(MOE_STAGE_COMBINE, launch_combine(cb, act, s), "combine");
+    MOE_LAUNCH_STAGE(MOE_STAGE_COMBINE, s, launch_combine(cb, act, s), "combine");
   }
   return MOE_OK;
 }
@@ -603,10 +637,20 @@ moe_status moe_forward(const moe_config* cfg, int64_t T, const void* x, const mo
     const hipStream_t st = static_cast<hipStream_t>(stream);
     int32_t* idx = topk_idx_out ? topk_idx_out : at<int32_t>(ws, p.o_idx);
     float* wt = topk_w_out ? topk_w_out : at<float>(ws, p.o_w);
-    s = run_route(*cfg, p, T, x, w->router, w->router_bias, cfg->use_expert_bias ? w->expert_bias : nullptr, idx, wt,
-                  ws, st);
-    if (s != MOE_OK) return s;
-    s = run_experts(*cfg, p, T, x, w, idx, wt, y, ws, st);
+    const float* ebias = cfg->use_expert_bias ? w->expert_bias : nullptr;
+    if (p.decode && T <= kFusedRouteMaxT && T * cfg->top_k <= kPermSingleMax) {
+      // small batch: route and permute in one workgroup
+      if ((s = run_logits(*cfg, p, T, x, w->router, ws, st)) != MOE_OK) return s;
+      const TopkArgs ta = topk_args(*cfg, p, T, ws, w->router_bias, ebias, idx, wt);
+      const PermuteArgs pa = permute_args(*cfg, p, T, idx, at<int32_t>(ws, p.o_counts), at<int32_t>(ws, p.o_offsets),
+                                          at<int32_t>(ws, p.o_perm), nullptr, ws);
+      MOE_LAUNCH_STAGE(MOE_STAGE_TOPK, st, launch_route_permute(ta, pa, st), "top-k + permutation");
+      s = run_experts(*cfg, p, T, x, w, idx, wt, y, ws, st, true);
+    } else {
+      s = run_route(*cfg, p, T, x, w->router, w->router_bias, ebias, idx, wt, ws, st);
+      if (s != MOE_OK) return s;
+      s = run_experts(*cfg, p, T, x, w, idx, wt, y, ws, st);
+    }
     if (s != MOE_OK) return s;
     if (expert_counts_out) {
       const hipError_t e = hipMemcpyAsync(expert_counts_out, at<int32_t>(ws, p.o_counts),

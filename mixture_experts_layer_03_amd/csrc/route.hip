@@ -23,26 +23,53 @@ constexpr float kNegInf = -__builtin_huge_valf();
 
 // Expert e lives in lane e / EPL, register e % EPL: each lane owns EPL consecutive
 // experts, so a row of logits is read with contiguous per-lane runs.
+// Routes token t with one wavefront (all 64 lanes active).
 template <int EPL>
-__global__ __launch_bounds__(256) void k_topk(TopkArgs a) {
+__device__ void route_token(const TopkArgs& a, int t) {
   const int lane = lane_id();
-  const int t = blockIdx.x * 4 + (threadIdx.x >> 6);
-  if (t >= a.T) return;  // whole wavefront leaves; no block barrier below
   const int E = a.E;
 
   float s[EPL], sel[EPL];
   bool valid[EPL];
 #pragma unroll
   for (int i = 0; i < EPL; ++i) {
-    const int e = lane * EPL + i;
-    valid[i] = e < E;
-    float v = 0.f;
-    if (valid[i]) {
-      const float* p = a.logits + static_cast<int64_t>(t) * E + e;
-      for (int q = 0; q < a.P; ++q) v += p[q * a.part_stride];
-      if (a.router_bias) v += a.router_bias[e];
+    valid[i] = lane * EPL + i < E;
+    s[i] = 0.f;
+  }
+  // sum the P partial logits; every load of a partial is issued before any is used
+  const float* row = a.logits + static_cast<int64_t>(t) * E + lane * EPL;
+  if (EPL % 4 == 0 && (E % 4) == 0 && lane * EPL + EPL <= E) {
+    for (int q0 = 0; q0 < a.P; q0 += 4) {
+      float4 v[4][EPL / 4 > 0 ? EPL / 4 : 1];
+#pragma unroll
+      for (int u = 0; u < 4; ++u)
+#pragma unroll
+        for (int c = 0; c < EPL / 4; ++c)
+          v[u][c] = q0 + u < a.P ? *reinterpret_cast<const float4*>(row + (q0 + u) * a.part_stride + 4 * c)
+                                 : make_float4(0.f, 0.f, 0.f, 0.f);
+#pragma unroll
+      for (int u = 0; u < 4; ++u)
+#pragma unroll
+        for (int c = 0; c < EPL / 4; ++c) {
+          s[4 * c] += v[u][c].x;
+          s[4 * c + 1] += v[u][c].y;
+          s[4 * c + 2] += v[u][c].z;
+          s[4 * c + 3] += v[u][c].w;
+        }
     }
-    s[i] = v;
+  } else {
+    for (int q = 0; q < a.P; ++q) {
+      float v[EPL];
+#pragma unroll
+      for (int i = 0; i < EPL; ++i) v[i] = valid[i] ? row[q * a.part_stride + i] : 0.f;
+#pragma unroll
+      for (int i = 0; i < EPL; ++i) s[i] += v[i];
+    }
+  }
+  if (a.router_bias) {
+#pragma unroll
+    for (int i = 0; i < EPL; ++i)
+      if (valid[i]) s[i] += a.router_bias[lane * EPL + i];
   }
 
   // scores
@@ -155,6 +182,13 @@ __global__ __launch_bounds__(256) void k_topk(TopkArgs a) {
     a.idx[static_cast<int64_t>(t) * a.k + lane] = my_idx;
     a.w[static_cast<int64_t>(t) * a.k + lane] = my_w;
   }
+}
+
+template <int EPL>
+__global__ __launch_bounds__(256) void k_topk(TopkArgs a) {
+  const int t = blockIdx.x * 4 + (threadIdx.x >> 6);
+  if (t >= a.T) return;  // whole wavefront leaves; no block barrier here
+  route_token<EPL>(a, t);
 }
 
 constexpr int kPermThreads = 1024;
@@ -289,6 +323,25 @@ __global__ __launch_bounds__(kPermThreads) void k_permute(PermuteArgs a) {
   for (int q = total_s + tid; q < a.nslots; q += kPermThreads) a.perm[q] = -1;
 }
 
+// Small batches: 16 wavefronts route the tokens, then the same workgroup permutes
+// them (one launch instead of two on the decode critical path).
+template <int EPL>
+__global__ __launch_bounds__(kPermThreads) void k_route_permute(TopkArgs ta, PermuteArgs a) {
+  __shared__ int cnt[1024];
+  __shared__ int off[1024];
+  __shared__ int wtot[3][16];
+  __shared__ int total_s;
+  const int tid = threadIdx.x;
+  for (int t = tid >> 6; t < ta.T; t += kPermThreads / 64) route_token<EPL>(ta, t);
+  if (tid < a.E) cnt[tid] = 0;
+  __syncthreads();  // routing written by this workgroup is visible to it after the barrier
+  rank_slots(a, 0, a.nslots, cnt);
+  __syncthreads();
+  scan_experts(a, tid < a.E ? cnt[tid] : 0, true, off, wtot, &total_s);
+  scatter_slots(a, 0, a.nslots, off);
+  for (int q = total_s + tid; q < a.nslots; q += kPermThreads) a.perm[q] = -1;
+}
+
 // Multi-block form, pass 1: per-chunk histogram and in-chunk ranks.
 __global__ __launch_bounds__(kPermThreads) void k_perm_count(PermuteArgs a) {
   __shared__ int cnt[1024];
@@ -341,6 +394,22 @@ hipError_t launch_topk(const TopkArgs& a, hipStream_t s) {
     hipLaunchKernelGGL(k_topk<8>, grid, block, 0, s, a);
   else
     hipLaunchKernelGGL(k_topk<16>, grid, block, 0, s, a);
+  return hipGetLastError();
+}
+
+hipError_t launch_route_permute(const TopkArgs& t, const PermuteArgs& a, hipStream_t s) {
+  const int epl = (t.E + 63) / 64;
+  const dim3 g(1), b(kPermThreads);
+  if (epl <= 1)
+    hipLaunchKernelGGL(k_route_permute<1>, g, b, 0, s, t, a);
+  else if (epl <= 2)
+    hipLaunchKernelGGL(k_route_permute<2>, g, b, 0, s, t, a);
+  else if (epl <= 4)
+    hipLaunchKernelGGL(k_route_permute<4>, g, b, 0, s, t, a);
+  else if (epl <= 8)
+    hipLaunchKernelGGL(k_route_permute<8>, g, b, 0, s, t, a);
+  else
+    hipLaunchKernelGGL(k_route_permute<16>, g, b, 0, s, t, a);
   return hipGetLastError();
 }
 

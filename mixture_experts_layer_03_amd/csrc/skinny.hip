@@ -7,10 +7,11 @@
 // with 16-byte loads, and multiplies them against up to 64 tokens held as four
 // 16-row MFMA M-tiles (tokens padded to 16; padded rows are computed and dropped).
 //
-// K ordering: per 64-element step, lane l covers the 16 consecutive elements
-// [16 * (l / 16), +16) of the step for its row l % 16 and feeds them to the MFMA
-// K-group l / 16.  The same ordering is applied to the token operand, so each
-// product pairs equal k; every row is read in 128-byte runs (4 lanes x 32 bytes).
+// K ordering: the MFMA pairs A and B values by K-group (lane / 16) and position, so
+// any permutation of k applied identically to both operands leaves the products
+// unchanged.  Each 64-element step is mapped so that one load instruction covers 64
+// contiguous bytes of every one of its 16 rows (bf16: two instructions per step,
+// u8: one), i.e. whole cache-line halves.
 #include "common.h"
 #include "kernels.h"
 
@@ -76,12 +77,18 @@ __device__ __forceinline__ void dequant16(const uint4& q, float z, uint4& lo, ui
 }
 
 // acc[mat][mt] += A(tokens) x W(rows)^T over elements [k0, k1) (multiples of 64).
+// The weight loads of U steps are all issued before the first is used (they stream
+// from HBM).
 template <Act ACT, WFmt WF, int NMAT, int MT>
 __device__ __forceinline__ void stream_rows(const Task<ACT, WF, NMAT, MT>& t, int k0, int k1,
                                             f32x4 (&acc)[NMAT][MT]) {
   const int q = lane_id() >> 4;
   if constexpr (ACT == Act::BF16 && WF == WFmt::BF16) {
-    constexpr int U = 4;
+    // K-group q of MFMA 0 takes elements [8q, 8q+8) of the 64-element step and of
+    // MFMA 1 [32+8q, 40+8q): each load instruction reads 64 contiguous bytes per row.
+    // U steps of weights are in flight per wavefront (4 with two matrices, 8 with one:
+    // measured best), and the token rows of those U steps are loaded as one batch.
+    constexpr int U = NMAT == 2 ? 4 : 8;
     int k = k0;
     for (; k + 64 * U <= k1; k += 64 * U) {
       uint4 w0[U][NMAT], w1[U][NMAT];
@@ -89,9 +96,9 @@ __device__ __forceinline__ void stream_rows(const Task<ACT, WF, NMAT, MT>& t, in
       for (int u = 0; u < U; ++u)
 #pragma unroll
         for (int m = 0; m < NMAT; ++m) {
-          const uint16_t* p = t.wrow[m] + k + 64 * u + 16 * q;
-          w0[u][m] = ld_stream(reinterpret_cast<const uint4*>(p));
-          w1[u][m] = ld_stream(reinterpret_cast<const uint4*>(p + 8));
+          const uint16_t* p = t.wrow[m] + k + 64 * u + 8 * q;
+          w0[u][m] = ld_stream(p);
+          w1[u][m] = ld_stream(p + 32);
         }
 #pragma unroll
       for (int mt = 0; mt < MT; ++mt) {
@@ -99,9 +106,9 @@ __device__ __forceinline__ void stream_rows(const Task<ACT, WF, NMAT, MT>& t, in
           uint4 a0[U], a1[U];
 #pragma unroll
           for (int u = 0; u < U; ++u) {
-            const uint16_t* p = t.arow[mt] + k + 64 * u + 16 * q;
+            const uint16_t* p = t.arow[mt] + k + 64 * u + 8 * q;
             a0[u] = ld16(p);
-            a1[u] = ld16(p + 8);
+            a1[u] = ld16(p + 32);
           }
 #pragma unroll
           for (int u = 0; u < U; ++u)
@@ -117,15 +124,15 @@ __device__ __forceinline__ void stream_rows(const Task<ACT, WF, NMAT, MT>& t, in
       uint4 w0[NMAT], w1[NMAT];
 #pragma unroll
       for (int m = 0; m < NMAT; ++m) {
-        const uint16_t* p = t.wrow[m] + k + 16 * q;
-        w0[m] = ld_stream(reinterpret_cast<const uint4*>(p));
-        w1[m] = ld_stream(reinterpret_cast<const uint4*>(p + 8));
+        const uint16_t* p = t.wrow[m] + k + 8 * q;
+        w0[m] = ld_stream(p);
+        w1[m] = ld_stream(p + 32);
       }
 #pragma unroll
       for (int mt = 0; mt < MT; ++mt) {
         if (mt < t.mt_live) {
-          const uint16_t* p = t.arow[mt] + k + 16 * q;
-          const uint4 a0 = ld16(p), a1 = ld16(p + 8);
+          const uint16_t* p = t.arow[mt] + k + 8 * q;
+          const uint4 a0 = ld16(p), a1 = ld16(p + 32);
 #pragma unroll
           for (int m = 0; m < NMAT; ++m) {
             acc[m][mt] = mfma16_bf16(a0, w0[m], acc[m][mt]);
@@ -136,39 +143,36 @@ __device__ __forceinline__ void stream_rows(const Task<ACT, WF, NMAT, MT>& t, in
     }
   } else if constexpr (ACT == Act::BF16 && WF == WFmt::U8) {
     // one 64-element step = one quantisation group: exact (q - z) products per
-    // group, then one fp32 scale per row and group
-    constexpr int U = 2;
+    // group, then one fp32 scale per row and group.  Lane q holds codes
+    // [16q, 16q+16) of the step (16 contiguous bytes; 64 per row per instruction).
+    constexpr int U = 8;
     int k = k0;
     for (; k + 64 * U <= k1; k += 64 * U) {
       uint4 wq[U][NMAT];
-      float sc[U][NMAT], zp[U][NMAT];
+      uint16_t sh[U][NMAT], zh[U][NMAT];
 #pragma unroll
       for (int u = 0; u < U; ++u)
 #pragma unroll
         for (int m = 0; m < NMAT; ++m) {
-          wq[u][m] = ld_stream(reinterpret_cast<const uint4*>(t.wrow[m] + k + 64 * u + 16 * q));
-          const int gi = (k >> 6) + u;
-          sc[u][m] = f16_to_f32(t.srow[m][gi]);
-          zp[u][m] = f16_to_f32(t.zrow[m][gi]);
+          wq[u][m] = ld_stream(t.wrow[m] + k + 64 * u + 16 * q);
+          sh[u][m] = t.srow[m][(k >> 6) + u];
+          zh[u][m] = t.zrow[m][(k >> 6) + u];
         }
-      uint4 wl[U][NMAT], wh[U][NMAT];
 #pragma unroll
-      for (int u = 0; u < U; ++u)
+      for (int u = 0; u < U; ++u) {
 #pragma unroll
-        for (int m = 0; m < NMAT; ++m) dequant16(wq[u][m], zp[u][m], wl[u][m], wh[u][m]);
+        for (int m = 0; m < NMAT; ++m) {
+          uint4 wl, wh;
+          dequant16(wq[u][m], f16_to_f32(zh[u][m]), wl, wh);
+          const float sc = f16_to_f32(sh[u][m]);
 #pragma unroll
-      for (int mt = 0; mt < MT; ++mt) {
-        if (mt < t.mt_live) {
-#pragma unroll
-          for (int u = 0; u < U; ++u) {
-            const uint16_t* p = t.arow[mt] + k + 64 * u + 16 * q;
-            const uint4 a0 = ld16(p), a1 = ld16(p + 8);
-#pragma unroll
-            for (int m = 0; m < NMAT; ++m) {
+          for (int mt = 0; mt < MT; ++mt) {
+            if (mt < t.mt_live) {
+              const uint16_t* p = t.arow[mt] + k + 64 * u + 16 * q;
               f32x4 g = {0.f, 0.f, 0.f, 0.f};
-              g = mfma16_bf16(a0, wl[u][m], g);
-              g = mfma16_bf16(a1, wh[u][m], g);
-              acc[m][mt] += sc[u][m] * g;
+              g = mfma16_bf16(ld16(p), wl, g);
+              g = mfma16_bf16(ld16(p + 8), wh, g);
+              acc[m][mt] += sc * g;
             }
           }
         }
@@ -177,7 +181,7 @@ __device__ __forceinline__ void stream_rows(const Task<ACT, WF, NMAT, MT>& t, in
     for (; k < k1; k += 64) {
 #pragma unroll
       for (int m = 0; m < NMAT; ++m) {
-        const uint4 wq = ld_stream(reinterpret_cast<const uint4*>(t.wrow[m] + k + 16 * q));
+        const uint4 wq = ld_stream(t.wrow[m] + k + 16 * q);
         const float sc = f16_to_f32(t.srow[m][k >> 6]);
         const float zp = f16_to_f32(t.zrow[m][k >> 6]);
         uint4 wl, wh;
