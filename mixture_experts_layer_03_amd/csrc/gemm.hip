@@ -26,22 +26,32 @@ namespace moe {
 
 namespace {
 
-constexpr int BM = kTileM, BK = 64;
+constexpr int BM = kTileM;
+
+// Swizzled 16-byte chunk of (row, logical chunk) in an LDS tile of BK-element rows.
+// 128-byte rows (BK = 64): XOR with row % 8.  64-byte rows (BK = 32): rows r and r + 4
+// share banks, so XOR with (row / 4) % 4.  Either way every thread's staging rows and
+// every fragment's rows keep the same XOR term, so one base address serves them all.
+template <int BK>
+__device__ __forceinline__ int phys_chunk(int row, int c) {
+  return BK == 64 ? (c ^ (row & 7)) : (c ^ ((row >> 2) & 3));
+}
 
 __device__ __forceinline__ uint4 ldg16(const void* p) { return *reinterpret_cast<const uint4*>(p); }
 
-template <int BN, WFmt WF, bool DUAL, AMode AM, Epi EPI>
+template <int BN, int BK, WFmt WF, bool DUAL, AMode AM, Epi EPI>
 __global__ __launch_bounds__(BN * 2) void k_tile(TileArgs a) {
   constexpr int NTHR = BN * 2;                  // BN/32 wavefronts
-  constexpr int RSTEP = NTHR / 8;               // tile rows between one thread's chunks
-  constexpr int AR = BM * 8 / NTHR;             // A chunks per thread
-  constexpr int BR = BN * 8 / NTHR;             // B chunks per thread (= 4)
+  constexpr int CPRK = BK / 8;                  // 16-byte chunks per LDS row
+  constexpr int RSTEP = NTHR / CPRK;            // tile rows between one thread's chunks
+  constexpr int AR = BM * CPRK / NTHR;          // A chunks per thread
+  constexpr int BR = BN * CPRK / NTHR;          // B chunks per thread
   constexpr int WN = BN / 64;                   // wavefronts along N
   constexpr int STAGE_ELEMS = (BM + BN) * BK;   // bf16 elements per LDS stage
   constexpr int NCOL = DUAL ? BN / 2 : BN;      // output columns per tile
   constexpr int EPI_LD = NCOL + 4;              // fp32 epilogue row stride (bank spread)
-  static_assert(64 * EPI_LD * 4 <= 2 * STAGE_ELEMS * 2, "epilogue staging must fit the LDS stages");
-  __shared__ __attribute__((aligned(16))) uint16_t smem[2 * STAGE_ELEMS];
+  constexpr int SMEM_ELEMS = (64 * EPI_LD * 2 > 2 * STAGE_ELEMS) ? 64 * EPI_LD * 2 : 2 * STAGE_ELEMS;
+  __shared__ __attribute__((aligned(16))) uint16_t smem[SMEM_ELEMS];
 
   const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
   const int NT = (a.N + NCOL - 1) / NCOL;
@@ -75,7 +85,7 @@ __global__ __launch_bounds__(BN * 2) void k_tile(TileArgs a) {
   // base plus immediate offsets), 16-byte chunk tid % 8 (8 elements: bf16, or 8 u8
   // codes for quantised weights).  A rows use 32-bit element offsets (the host keeps
   // rows * K below 2^32); rows past the tile's end are clamped (computed, never stored).
-  const int sc = tid & 7, r0 = tid >> 3;
+  const int sc = tid % CPRK, r0 = tid / CPRK;
   uint32_t a_off[AR];
 #pragma unroll
   for (int i = 0; i < AR; ++i) {
@@ -131,14 +141,14 @@ __global__ __launch_bounds__(BN * 2) void k_tile(TileArgs a) {
     for (int i = 0; i < BR; ++i) {
       if constexpr (WF == WFmt::U8) {
         R.q[i] = *reinterpret_cast<const uint2*>(bp[i] + k0);
-        R.s[i] = f16_to_f32(bsp[i][kt]);
-        R.z[i] = f16_to_f32(bzp[i][kt]);
+        R.s[i] = f16_to_f32(bsp[i][(kt * BK) >> 6]);
+        R.z[i] = f16_to_f32(bzp[i][(kt * BK) >> 6]);
       } else {
         R.b[i] = ldg16(bp[i] + 2 * k0);
       }
     }
   };
-  const int wr = r0 * BK + ((sc ^ (r0 & 7)) << 3);  // LDS write base (elements)
+  const int wr = r0 * BK + (phys_chunk<BK>(r0, sc) << 3);  // LDS write base (elements)
   auto sstore = [&](const Regs& R, int buf) {
     uint16_t* As = smem + buf * STAGE_ELEMS;
     uint16_t* Bs = As + BM * BK;
@@ -169,16 +179,14 @@ __global__ __launch_bounds__(BN * 2) void k_tile(TileArgs a) {
 
   const int wm = w / WN, wn = w % WN;
   const int fr = lane & 15, fq = lane >> 4;
-  // fragment read bases: (row + 16 i) & 7 == fr & 7 for every sub-tile, and the second
-  // K-half's chunk (4 + fq) swizzles to the first's with bit 2 flipped
-  const int c0 = (fq ^ (fr & 7)) << 3;
+  // fragment read bases (the XOR term is the same for every sub-tile of a lane)
   const int a_rd = (wm * 64 + fr) * BK, b_rd = (wn * 64 + fr) * BK;
   auto compute = [&](int buf) {
     const uint16_t* As = smem + buf * STAGE_ELEMS;
     const uint16_t* Bs = As + BM * BK;
 #pragma unroll
-    for (int ks = 0; ks < 2; ++ks) {
-      const int cc = ks ? (c0 ^ 32) : c0;
+    for (int ks = 0; ks < BK / 32; ++ks) {
+      const int cc = phys_chunk<BK>(fr, ks * 4 + fq) << 3;
       uint4 af[4], bf[4];
 #pragma unroll
       for (int i = 0; i < 4; ++i) af[i] = *reinterpret_cast<const uint4*>(&As[a_rd + cc + i * 16 * BK]);
@@ -280,7 +288,7 @@ __global__ __launch_bounds__(BN * 2) void k_tile(TileArgs a) {
   }
 }
 
-template <int BN, WFmt WF, bool DUAL, AMode AM, Epi EPI>
+template <int BN, int BK, WFmt WF, bool DUAL, AMode AM, Epi EPI>
 hipError_t launch_one(const TileArgs& a, hipStream_t s) {
   constexpr int NCOL = DUAL ? BN / 2 : BN;
   const int NT = (a.N + NCOL - 1) / NCOL;
@@ -289,7 +297,7 @@ hipError_t launch_one(const TileArgs& a, hipStream_t s) {
   int64_t blocks = mt_pad * NT * (a.ksplit > 1 ? a.ksplit : 1);
   blocks = (blocks + 7) / 8 * 8;
   if (blocks <= 0) return hipSuccess;
-  hipLaunchKernelGGL((k_tile<BN, WF, DUAL, AM, EPI>), dim3(static_cast<unsigned>(blocks)), dim3(BN * 2), 0, s, a);
+  hipLaunchKernelGGL((k_tile<BN, BK, WF, DUAL, AM, EPI>), dim3(static_cast<unsigned>(blocks)), dim3(BN * 2), 0, s, a);
   return hipGetLastError();
 }
 
@@ -299,8 +307,10 @@ hipError_t launch_bn(const TileArgs& a, hipStream_t s) {
   // per flop).  The gate/up product keeps the 4-wavefront 128 x 128 tile: measured
   // faster on the workloads' shapes (two blocks per CU instead of one).
   const bool wide = !DUAL && a.N >= 256;
-  if (wide) return launch_one<256, WF, DUAL, AM, EPI>(a, s);
-  return launch_one<128, WF, DUAL, AM, EPI>(a, s);
+  // K-step: 32 for the wide tile (48 KB of LDS, several blocks per CU), 64 for the
+  // narrow one (measured best for each)
+  if (wide) return launch_one<256, 32, WF, DUAL, AM, EPI>(a, s);
+  return launch_one<128, 64, WF, DUAL, AM, EPI>(a, s);
 }
 
 }  // namespace
@@ -308,7 +318,7 @@ hipError_t launch_bn(const TileArgs& a, hipStream_t s) {
 hipError_t launch_tile_gemm(const TileArgs& a, AMode am, WFmt wf, Epi epi, hipStream_t s) {
   // the combinations the layer uses
   if (epi == Epi::F32 && am == AMode::DENSE && wf == WFmt::BF16)
-    return launch_one<128, WFmt::BF16, false, AMode::DENSE, Epi::F32>(a, s);
+    return launch_one<128, 64, WFmt::BF16, false, AMode::DENSE, Epi::F32>(a, s);
   if (epi == Epi::SWIGLU && am == AMode::GATHER && wf == WFmt::BF16)
     return launch_bn<WFmt::BF16, true, AMode::GATHER, Epi::SWIGLU>(a, s);
   if (epi == Epi::SWIGLU && am == AMode::GATHER && wf == WFmt::U8)

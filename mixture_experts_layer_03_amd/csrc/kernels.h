@@ -27,11 +27,13 @@ hipError_t launch_topk(const TopkArgs& a, hipStream_t s);
 struct PermuteArgs {
   const int32_t* idx;   // [nslots]
   int nslots, E, BM;    // BM > 0: also build the M-tile map for tile GEMMs of BM rows
+  int small_max;        // experts with 1..small_max slots go to the active list (streaming
+                        // kernels); with BM > 0 only experts above it get M-tiles
   int32_t* counts;      // [E]
   int32_t* offsets;     // [E + 1]
   int32_t* perm;        // [nslots]  slot ids grouped by expert, -1 tail
   int32_t* slot_pos;    // [nslots]  position of each slot in perm, -1 if dropped
-  int32_t* active;      // [E]       experts with at least one slot, ascending
+  int32_t* active;      // [E]       experts with 1..small_max slots, ascending
   int32_t* tiles;       // [max_tiles * 2] (expert, start position)
   int32_t* meta;        // [4]: D, number of M-tiles, valid slots
   int32_t* counts_copy; // optional extra copy of counts (caller output) or null
@@ -79,8 +81,10 @@ struct SkinnyDownArgs {
   const uint16_t *down_s, *down_z;  // u8 only: [E, H, I/64]
   const void* sdown;       // [H, Is] or null
   const float* topk_w;     // [T*k]
-  float* r;                // [T*k, H] fp32, slot order, scaled by the routing weight
+  void* r;                 // [T*k, H] fp32 (or bf16 when r_bf16), slot order, scaled by
+                           // the routing weight
   float* rs;               // [T, H] fp32 shared expert output
+  int r_bf16;
   const int32_t* counts;
   const int32_t* offsets;
   const int32_t* perm;

@@ -312,6 +312,11 @@ PermuteArgs permute_args(const moe_config& c, const Plan& p, int64_t T, const in
   a.nslots = static_cast<int>(T * c.top_k);
   a.E = static_cast<int>(c.num_experts);
   a.BM = p.decode ? 0 : kTileM;
+  // decode: every active expert goes to the streaming kernels; tiled path: every
+  // active expert gets M-tiles.  (Sending experts with few tokens to the streaming
+  // kernels on the tiled path measured slower on the skewed workload: inside one tiled
+  // launch their memory-bound blocks overlap the large experts' MFMA-bound blocks.)
+  a.small_max = p.decode ? 0x7fffffff : 0;
   a.counts = counts;
   a.offsets = offsets;
   a.perm = perm;
@@ -385,8 +390,9 @@ moe_status run_experts(const moe_config& c, const Plan& p, int64_t T, const void
     d.down_z = w->down_zero;
     d.sdown = w->shared_down;
     d.topk_w = topk_w;
-    d.r = static_cast<float*>(r);
+    d.r = r;
     d.rs = rs;
+    d.r_bf16 = 0;
     d.counts = counts;
     d.offsets = offsets;
     d.perm = perm;

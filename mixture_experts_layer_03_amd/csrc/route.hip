@@ -194,15 +194,16 @@ __global__ __launch_bounds__(256) void k_topk(TopkArgs a) {
 constexpr int kPermThreads = 1024;
 constexpr int kPermUnroll = 4;
 
-// Exclusive scans over the experts of: counts c[e], active flags and M-tiles per
-// expert.  Fills off[e] (LDS) with each expert's first position; when `write` is
-// set, also stores counts, offsets, the active-expert list, the M-tile map and meta.
+// Exclusive scans over the experts of: counts c[e], small-expert flags (1..small_max
+// slots: handled by the streaming kernels) and M-tiles of the larger experts.  Fills
+// off[e] (LDS) with each expert's first position; when `write` is set, also stores
+// counts, offsets, the small-expert list, the M-tile map and meta.
 // Called by all kPermThreads threads with c = this thread's expert count (0 past E).
 __device__ void scan_experts(const PermuteArgs& a, int c, bool write, int* off, int (*wtot)[16], int* total_s) {
   const int tid = threadIdx.x, lane = tid & 63, wv = tid >> 6;
   const int E = a.E;
-  const int f = c > 0 ? 1 : 0;
-  const int nt = (a.BM > 0) ? (c + a.BM - 1) / a.BM : 0;
+  const int f = (c > 0 && c <= a.small_max) ? 1 : 0;
+  const int nt = (a.BM > 0 && c > a.small_max) ? (c + a.BM - 1) / a.BM : 0;
   int ci = c, fi = f, ti = nt;
 #pragma unroll
   for (int o = 1; o < 64; o <<= 1) {

@@ -533,7 +533,12 @@ __global__ __launch_bounds__(256) void k_skinny_down(SkinnyDownArgs a) {
             if (m < ntok) {
               if (!shared) {
                 const int slot = a.perm[off + tc * 64 + m];
-                a.r[static_cast<int64_t>(slot) * a.H + row0 + n] = a.topk_w[slot] * acc[0][ai][v];
+                const float val = a.topk_w[slot] * acc[0][ai][v];
+                const int64_t o = static_cast<int64_t>(slot) * a.H + row0 + n;
+                if (a.r_bf16)
+                  static_cast<uint16_t*>(a.r)[o] = f32_to_bf16(val);
+                else
+                  static_cast<float*>(a.r)[o] = val;
               } else {
                 a.rs[static_cast<int64_t>(tc * 64 + m) * a.H + row0 + n] = acc[0][ai][v];
               }
