@@ -7,18 +7,28 @@
 // Expert weights are [out, in] per expert [mlxcel #838 "Validation checkpoint"], so
 // the weight operand rows are the output features and K runs along memory.
 //
-// Block tile 128 (tokens) x BN (weight rows: 128 or 256) x 64 with BN/32 wavefronts,
-// each owning a 64 x 64 sub-tile (a 4 x 4 grid of v_mfma_f32_16x16x32_bf16).  Two
-// wavefronts share each SIMD, so one computes while the other waits on memory.  The
-// wide tile halves the L2 -> LDS bytes per flop against a square 128 x 128 tile,
-// which is what bounds a 128 x 128 tile on this chip.  Operands are staged global ->
-// registers -> LDS (double buffered; 16-byte chunks XOR-swizzled by row so fragment
-// reads do not collide on banks); the next K-step's global loads are issued before the
-// current step's MFMAs.  u8 weights are dequantised to bf16 (s * (q - z), rounded to
-// nearest even) on their way to LDS, eight codes per thread and chunk.  The epilogue
-// stages 64-row halves of the tile through LDS as fp32 and writes 16-byte chunks, so
-// every output, gather and scatter is coalesced.  Blocks are numbered so that
-// consecutive tiles share an XCD (its L2 holds the shared A rows and weight panels).
+// Block tile 128 (tokens) x BN (weight rows) x BK with BN/32 wavefronts, each owning a
+// 64 x 64 sub-tile (a 4 x 4 grid of v_mfma_f32_16x16x32_bf16).  LDS tiles hold 16-byte
+// chunks XOR-swizzled by row, so fragment reads do not collide on banks.
+//
+// bf16 weights (k_tile_dma): both operands go HBM/L2 -> LDS through the load unit's
+// direct copy (global_load_lds_dwordx4), S LDS stages deep, with explicit waits.  The
+// layer's products take 128 x 512 x 64 with two stages (160 KB of LDS, 16 wavefronts,
+// four per SIMD): measured on this chip, the load path is what bounds these GEMMs, and
+// per K-step it is paced by the number of wavefronts issuing copies and by the average
+// L2 latency, so the tile moving the fewest bytes per flop with the most wavefronts
+// wins.  Dense single-matrix products too small to fill the chip with such blocks take
+// 128 x 256 x 64 with three stages.  The router product (fp32 out, split over K) takes
+// 128 x 128 x 64.
+//
+// u8 weights (k_tile): operands are staged global -> registers -> LDS (double buffered),
+// the weight codes dequantised to bf16 (s * (q - z), rounded to nearest even) on the
+// way, eight codes per thread and chunk.
+//
+// Epilogues stage 64-row slices of the tile through LDS as fp32 and write 16-byte
+// chunks, so every output, gather and scatter is coalesced.  Blocks are numbered so that
+// consecutive tiles share an XCD (its L2 holds the shared activation rows and weight
+// panels); the routed products group, for each N-tile, all M-tiles of one expert.
 #include "common.h"
 #include "kernels.h"
 
@@ -28,16 +38,160 @@ namespace {
 
 constexpr int BM = kTileM;
 
-// Swizzled 16-byte chunk of (row, logical chunk) in an LDS tile of BK-element rows.
-// 128-byte rows (BK = 64): XOR with row % 8.  64-byte rows (BK = 32): rows r and r + 4
-// share banks, so XOR with (row / 4) % 4.  Either way every thread's staging rows and
-// every fragment's rows keep the same XOR term, so one base address serves them all.
+// Swizzle term of a tile row: a row's 16-byte chunk c sits at chunk c ^ swz(row).
+// 128-byte rows (BK = 64): row % 8, so the 8 rows a group of 8 lanes reads in one
+// 16-byte fragment load hit 8 different bank groups.  64-byte rows (BK = 32): two rows
+// share a 128-byte bank line, so rows r and r + 2 collide unless their terms differ:
+// (row / 2) % 4.  Every thread's staging rows and every fragment's rows differ by
+// multiples of 16, which keep the term, so one base address serves them all.
+template <int BK>
+__device__ __forceinline__ int swz(int row) {
+  return BK == 64 ? (row & 7) : ((row >> 1) & 3);
+}
 template <int BK>
 __device__ __forceinline__ int phys_chunk(int row, int c) {
-  return BK == 64 ? (c ^ (row & 7)) : (c ^ ((row >> 2) & 3));
+  return c ^ swz<BK>(row);
 }
 
 __device__ __forceinline__ uint4 ldg16(const void* p) { return *reinterpret_cast<const uint4*>(p); }
+
+// Position of this block's tile.  Logical tile order: consecutive blocks land on one
+// XCD (hardware deals blocks round-robin over the 8 XCDs); within a group of G
+// consecutive M-tiles the N-tile index varies slowest, so the G blocks that read the
+// same weight panel run together and share it through L2, and the group's G
+// activation panels stay hot.  Returns false for a block past the last M-tile.
+struct TilePos {
+  int nt, kp, e, m_begin, m_rows, kt0, kt1;
+};
+template <int NCOL, int BK, int TBM = BM>
+__device__ __forceinline__ bool tile_pos(const TileArgs& a, TilePos& p) {
+  const int NT = (a.N + NCOL - 1) / NCOL;
+  const int per = gridDim.x / 8;
+  const int KS = a.ksplit > 1 ? a.ksplit : 1;
+  const int Lx = (blockIdx.x % 8) * per + blockIdx.x / 8;
+  p.kp = Lx % KS;
+  const int L = Lx / KS;
+  int mt;
+  if (a.routed && a.group_m <= 0) {
+    // grouped by expert: for each N-tile, all M-tiles of one expert in a row, so the
+    // blocks reading an expert's weight panel run together.  Tiles are stored in expert
+    // order, so the logical range of expert e is [first_e * NT, (first_e + m_e) * NT)
+    // and contains L exactly when M-tile L / NT belongs to e.
+    const int q = L / NT;
+    if (q >= a.meta[1]) return false;
+    const int e = a.tiles[2 * q];
+    const int first = q - (a.tiles[2 * q + 1] - a.offsets[e]) / TBM;
+    const int me = (a.offsets[e + 1] - a.offsets[e] + TBM - 1) / TBM;
+    const int local = L - first * NT;
+    p.nt = local / me;
+    mt = first + local % me;
+  } else {
+    const int G = a.group_m > 1 ? a.group_m : 1;
+    const int grp = L / (G * NT), rem = L % (G * NT);
+    mt = grp * G + rem % G;
+    p.nt = rem / G;
+  }
+  p.e = 0;
+  if (a.routed) {
+    if (mt >= a.meta[1]) return false;
+    p.e = a.tiles[2 * mt];
+    p.m_begin = a.tiles[2 * mt + 1];
+    p.m_rows = min(TBM, a.offsets[p.e + 1] - p.m_begin);
+  } else {
+    p.m_begin = mt * TBM;
+    if (p.m_begin >= a.M) return false;
+    p.m_rows = min(TBM, a.M - p.m_begin);
+  }
+  const int nk = a.K / BK;  // K-steps of this block's split
+  p.kt0 = p.kp * nk / KS;
+  p.kt1 = (p.kp + 1) * nk / KS;
+  return true;
+}
+
+// Epilogue shared by the tile kernels: the TBM x NCOL result goes through LDS as fp32
+// in passes of RP rows (RP = 64, 32 or 16, whatever the LDS area holds), then every
+// thread writes 16-byte chunks of 8 columns.  Caller: all LDS reads of the main loop
+// are finished (a barrier) before the first pass.
+template <int NTHR, int BN, int RP, bool DUAL, Epi EPI, int TBM = BM>
+__device__ __forceinline__ void epilogue(const TileArgs& a, f32x4 (&acc)[4][4], float* ep, int tid, int wm, int wn,
+                                         int fr, int fq, int nt, int kp, int m_begin, int m_rows) {
+  constexpr int NCOL = DUAL ? BN / 2 : BN;
+  constexpr int EPI_LD = NCOL + 4;  // fp32 row stride (bank spread)
+  constexpr int CPR = NCOL / 8;     // 8-column chunks per row
+  static_assert(RP == 64 || RP == 32 || RP == 16, "rows per pass");
+#pragma unroll 1
+  for (int h = 0; h < TBM / RP && h * RP < m_rows; ++h) {
+    // pass h covers tile rows [h*RP, h*RP + RP): 16-row fragments i0 .. i0 + RP/16 of
+    // the wavefronts in 64-row band (h*RP)/64
+    const int i0 = ((h * RP) & 63) >> 4;
+    if (wm == (h * RP) >> 6) {
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        if (i < i0 || i >= i0 + RP / 16) continue;
+#pragma unroll
+        for (int v = 0; v < 4; ++v) {
+          const int r = (i - i0) * 16 + 4 * fq + v;
+          if constexpr (DUAL) {
+#pragma unroll
+            for (int j = 0; j < 2; ++j)
+              ep[r * EPI_LD + wn * 32 + j * 16 + fr] = silu(acc[i][j][v]) * acc[i][j + 2][v];
+          } else {
+#pragma unroll
+            for (int j = 0; j < 4; ++j) ep[r * EPI_LD + wn * 64 + j * 16 + fr] = acc[i][j][v];
+          }
+        }
+      }
+    }
+    __syncthreads();
+#pragma unroll 1
+    for (int c = tid; c < RP * CPR; c += NTHR) {
+      const int r = c / CPR, c8 = (c % CPR) * 8;
+      const int m = h * RP + r;
+      const int col = nt * NCOL + c8;
+      if (m < m_rows && col < a.N) {
+        const float4 v0 = *reinterpret_cast<const float4*>(&ep[r * EPI_LD + c8]);
+        const float4 v1 = *reinterpret_cast<const float4*>(&ep[r * EPI_LD + c8 + 4]);
+        float f[8] = {v0.x, v0.y, v0.z, v0.w, v1.x, v1.y, v1.z, v1.w};
+        const int64_t orow = m_begin + m;
+        if constexpr (EPI == Epi::F32) {
+          float* out = static_cast<float*>(a.out) + kp * a.part_stride + orow * a.ldo + col;
+          if (col + 8 <= a.N && (a.ldo & 3) == 0) {
+            *reinterpret_cast<float4*>(out) = v0;
+            *reinterpret_cast<float4*>(out + 4) = v1;
+          } else {
+            for (int q = 0; q < 8 && col + q < a.N; ++q) out[q] = f[q];
+          }
+        } else {
+          int64_t drow = orow;
+          if constexpr (EPI == Epi::SCALED_SLOT) {
+            const int slot = a.perm[orow];
+            const float ws = a.topk_w[slot];
+#pragma unroll
+            for (int q = 0; q < 8; ++q) f[q] *= ws;
+            drow = slot;
+          } else if constexpr (EPI == Epi::COMBINE) {
+            for (int jj = 0; jj < a.k; ++jj) {
+              const int64_t slot = orow * a.k + jj;
+              const int ex = a.idx[slot];
+              if (ex < 0 || ex >= a.E) continue;
+              const uint4 rv = ldg16(a.r + slot * a.N + col);
+              const uint32_t u[4] = {rv.x, rv.y, rv.z, rv.w};
+#pragma unroll
+              for (int q = 0; q < 4; ++q) {
+                f[2 * q] += __uint_as_float(u[q] << 16);
+                f[2 * q + 1] += __uint_as_float(u[q] & 0xffff0000u);
+              }
+            }
+          }
+          uint16_t* out = static_cast<uint16_t*>(a.out) + drow * a.ldo + col;
+          *reinterpret_cast<uint4*>(out) = make_uint4(pack_bf16x2(f[0], f[1]), pack_bf16x2(f[2], f[3]),
+                                                      pack_bf16x2(f[4], f[5]), pack_bf16x2(f[6], f[7]));
+        }
+      }
+    }
+    __syncthreads();
+  }
+}
 
 template <int BN, int BK, WFmt WF, bool DUAL, AMode AM, Epi EPI>
 __global__ __launch_bounds__(BN * 2) void k_tile(TileArgs a) {
@@ -54,32 +208,11 @@ __global__ __launch_bounds__(BN * 2) void k_tile(TileArgs a) {
   __shared__ __attribute__((aligned(16))) uint16_t smem[SMEM_ELEMS];
 
   const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
-  const int NT = (a.N + NCOL - 1) / NCOL;
-  const int per = gridDim.x / 8;
-  const int KS = a.ksplit > 1 ? a.ksplit : 1;
-  // logical tile order: consecutive blocks land on one XCD (hardware deals blocks
-  // round-robin over the 8 XCDs); within a group of G consecutive M-tiles the N-tile
-  // index varies slowest, so the G blocks that read the same weight panel run
-  // together and share it through L2, and the group's G activation panels stay hot
-  const int Lx = (blockIdx.x % 8) * per + blockIdx.x / 8;
-  const int kp = Lx % KS, L = Lx / KS;
-  const int G = a.group_m > 1 ? a.group_m : 1;
-  const int grp = L / (G * NT), rem = L % (G * NT);
-  const int mt = grp * G + rem % G, nt = rem / G;
-
-  int e = 0, m_begin, m_rows;
-  if (a.routed) {
-    if (mt >= a.meta[1]) return;
-    e = a.tiles[2 * mt];
-    m_begin = a.tiles[2 * mt + 1];
-    m_rows = min(BM, a.offsets[e + 1] - m_begin);
-  } else {
-    m_begin = mt * BM;
-    if (m_begin >= a.M) return;
-    m_rows = min(BM, a.M - m_begin);
-  }
+  TilePos tp;
+  if (!tile_pos<NCOL, BK>(a, tp)) return;
+  const int nt = tp.nt, kp = tp.kp, e = tp.e, m_begin = tp.m_begin, m_rows = tp.m_rows;
   const int K = a.K;
-  const int kt0 = kp * (K / BK) / KS, kt1 = (kp + 1) * (K / BK) / KS;  // this block's K-steps
+  const int kt0 = tp.kt0, kt1 = tp.kt1;
 
   // ---- staging: thread rows tid/8 + RSTEP*i (congruent mod 8, so one swizzled LDS
   // base plus immediate offsets), 16-byte chunk tid % 8 (8 elements: bf16, or 8 u8
@@ -111,7 +244,7 @@ __global__ __launch_bounds__(BN * 2) void k_tile(TileArgs a) {
       // rows are the gate and up rows of the same 32 output columns
       const int blk = r >> 5;
       second = blk & 1;
-      n = nt * NCOL + (blk >> 1) * 32 + (r & 31);
+      n = min(nt * NCOL + (blk >> 1) * 32 + (r & 31), a.N - 1);  // past N: computed, never stored
     } else {
       second = false;
       n = min(nt * BN + r, a.N - 1);
@@ -216,101 +349,252 @@ __global__ __launch_bounds__(BN * 2) void k_tile(TileArgs a) {
     __syncthreads();
   }
 
-  // ---- epilogue: two 64-row halves staged through LDS as fp32
-  float* ep = reinterpret_cast<float*>(smem);
-  constexpr int CPR = NCOL / 8;  // 8-column chunks per row
-#pragma unroll 1
-  for (int h = 0; h < 2; ++h) {
-    if (wm == h) {
+  epilogue<NTHR, BN, 64, DUAL, EPI>(a, acc, reinterpret_cast<float*>(smem), tid, wm, wn, fr, fq, nt, kp, m_begin,
+                                      m_rows);
+}
+
+// ---------------------------------------------------------------------------------
+// bf16 weights: the same tile, with both operands copied HBM/L2 -> LDS by the load
+// unit itself (global_load_lds_dwordx4: each lane names a 16-byte source, the wave's
+// 64 chunks land in 1 KB of consecutive LDS at M0), so no registers or VALU carry the
+// staging and S LDS stages can be in flight at once.  The copies are issued from
+// inline asm, which the compiler's wait insertion does not track (it would otherwise
+// drain every copy in flight once per loop trip); the kernel waits for them itself:
+// before the barrier of each K-step a wave lets at most the copies of the stages
+// after the current one stay outstanding.  The compiler's own loads are unaffected:
+// extra outstanding copies only make its vmcnt waits stricter.  A copy has no
+// destination register, so nothing it writes can be reused early.
+//
+// A copy instruction covers 64 / (BK/8) whole tile rows; lane l takes row l / (BK/8)
+// of them and logical chunk (l % (BK/8)) XOR the row's swizzle term, so the LDS image
+// is the same swizzled tile the register-staged kernel writes.
+// 16 bytes per lane from global memory to LDS at M0 + 16 * lane (M0 wave-uniform)
+__device__ __forceinline__ void copy_to_lds(const void* src, const uint16_t* lds_dst) {
+  const uint32_t m0 =
+      static_cast<uint32_t>(reinterpret_cast<uintptr_t>((const __attribute__((address_space(3))) void*)lds_dst));
+  asm volatile("global_load_lds_dwordx4 %0, off" ::"v"(src), "{m0}"(m0) : "memory");
+}
+// the same from a wave-uniform base plus a per-lane 32-bit byte offset
+__device__ __forceinline__ void copy_to_lds(const char* base, uint32_t off, const uint16_t* lds_dst) {
+  const uint32_t m0 =
+      static_cast<uint32_t>(reinterpret_cast<uintptr_t>((const __attribute__((address_space(3))) void*)lds_dst));
+  asm volatile("global_load_lds_dwordx4 %0, %1" ::"v"(off), "s"(base), "{m0}"(m0) : "memory");
+}
+// a pointer known to be the same in every lane, kept in scalar registers
+__device__ __forceinline__ const char* uniform_ptr(const void* p) {
+  const uint64_t v = reinterpret_cast<uint64_t>(p);
+  const uint32_t lo = __builtin_amdgcn_readfirstlane(static_cast<uint32_t>(v));
+  const uint32_t hi = __builtin_amdgcn_readfirstlane(static_cast<uint32_t>(v >> 32));
+  return reinterpret_cast<const char*>((static_cast<uint64_t>(hi) << 32) | lo);
+}
+
+// Wait until at most N of this wave's copies are outstanding and its LDS reads are
+// done.  Followed by lds_barrier(): afterwards every wave's copies older than its last
+// N have landed and no wave still reads a stage that is about to be refilled.
+template <int N>
+__device__ __forceinline__ void copy_wait() {
+  static_assert(N >= 0 && N < 64, "vmcnt range");
+  asm volatile("s_waitcnt vmcnt(%0) lgkmcnt(0)" ::"n"(N) : "memory");
+}
+__device__ __forceinline__ void lds_barrier() { asm volatile("s_barrier" ::: "memory"); }
+
+// copy_wait<min(ahead, A) * L>() for a runtime ahead >= 0
+template <int L, int A>
+__device__ __forceinline__ void copy_wait_ahead(int ahead) {
+  if constexpr (A == 0) {
+    copy_wait<0>();
+  } else {
+    if (ahead >= A)
+      copy_wait<A * L>();
+    else
+      copy_wait_ahead<L, A - 1>(ahead);
+  }
+}
+
+// The stage image is BM + BN rows of BK elements: Q = (BM + BN) / RPI copy
+// instructions of 1 KB (A rows first, then B rows), dealt round-robin to the NW
+// wavefronts, so wave w issues instructions w, w + NW, ... and waits on its own count.
+template <int BN, int BK, int S, bool DUAL, AMode AM, Epi EPI>
+__global__ __launch_bounds__(BN * 2) void k_tile_dma(TileArgs a) {
+  constexpr int NW = BN / 32;                   // wavefronts (each a 64 x 64 sub-tile)
+  constexpr int NTHR = NW * 64;
+  constexpr int CPRK = BK / 8;                  // 16-byte chunks per LDS row
+  constexpr int RPI = 64 / CPRK;                // tile rows per copy instruction
+  constexpr int QA = BM / RPI, Q = (BM + BN) / RPI;
+  constexpr int J = (Q + NW - 1) / NW;          // copy slots per wave
+  constexpr int NHI = Q % NW == 0 ? NW : Q % NW;  // waves with J copies (the rest J - 1)
+  constexpr int WN = BN / 64;
+  constexpr int NCOL = DUAL ? BN / 2 : BN;
+  constexpr int STAGE_ELEMS = (BM + BN) * BK;
+  constexpr int EPI_LD = NCOL + 4;
+  constexpr int EPI_ELEMS = 64 * EPI_LD * 2;   // 64 fp32 rows of the epilogue
+  constexpr int SMEM_ELEMS = S * STAGE_ELEMS > EPI_ELEMS ? S * STAGE_ELEMS : EPI_ELEMS;
+  static_assert(S >= 2 && BM % RPI == 0 && BN % RPI == 0, "pipeline shape");
+  static_assert(J * (S - 1) < 64, "vmcnt range");
+  __shared__ __attribute__((aligned(16))) uint16_t smem[SMEM_ELEMS];
+
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int w = __builtin_amdgcn_readfirstlane(tid >> 6);
+  TilePos tp;
+  if (!tile_pos<NCOL, BK>(a, tp)) return;
+  const int nt = tp.nt, e = tp.e, m_begin = tp.m_begin, m_rows = tp.m_rows;
+  const int K = a.K;
+
+  // Weight row r of the B tile: matrix (gate or up for the gate/up product) and row.
+  // Copy sources are 32-bit byte offsets from wave-uniform bases: the activation
+  // matrix (the host keeps its size below 4 GB) or this block's expert matrix.
+  auto weight_row = [&](int r, bool& second) {
+    if (DUAL) {
+      // rows in blocks of 32: gate, up, gate, up, ... (each wavefront's 64 rows are the
+      // gate and up rows of the same 32 output columns)
+      const int blk = r >> 5;
+      second = blk & 1;
+      return min(nt * NCOL + (blk >> 1) * 32 + (r & 31), a.N - 1);  // past N: computed, never stored
+    }
+    second = false;
+    return min(nt * BN + r, a.N - 1);
+  };
+  const char* a_base = uniform_ptr(a.A);
+  const char* b0_base = uniform_ptr(static_cast<const uint16_t*>(a.B0) + static_cast<int64_t>(e) * a.b_expert_stride);
+  const char* b1_base =
+      DUAL ? uniform_ptr(static_cast<const uint16_t*>(a.B1) + static_cast<int64_t>(e) * a.b_expert_stride) : b0_base;
+
+  // ---- per-lane copy offsets: instruction q fills stage rows [RPI*q, RPI*q + RPI)
+  const int lr = lane / CPRK;
+  const int lc = (lane % CPRK) ^ swz<BK>(lr);   // logical chunk (RPI*q is a multiple of 8 or 16)
+  uint32_t off[J];
+#pragma unroll
+  for (int j = 0; j < J; ++j) {
+    const int q = min(w + j * NW, Q - 1);       // slot past Q: never issued
+    if (q < QA) {
+      const int r = min(RPI * q + lr, m_rows - 1);  // clamped rows: computed, never stored
+      int row;
+      if constexpr (AM == AMode::GATHER)
+        row = a.perm[m_begin + r] / a.k;
+      else
+        row = m_begin + r;
+      off[j] = (static_cast<uint32_t>(row) * K + lc * 8) * 2;
+    } else {
+      bool second;
+      off[j] = (static_cast<uint32_t>(weight_row(RPI * (q - QA) + lr, second)) * K + lc * 8) * 2;
+    }
+  }
+  // the base of each of this wave's instructions (an instruction's RPI rows lie in one
+  // 32-row block, so one matrix), in scalar registers
+  const char* ibase[J];
+#pragma unroll
+  for (int j = 0; j < J; ++j) {
+    const int q = min(w + j * NW, Q - 1);
+    bool second = false;
+    if (q >= QA) weight_row(RPI * (q - QA), second);
+    ibase[j] = uniform_ptr(q < QA ? a_base : second ? b1_base : b0_base);
+  }
+  auto issue = [&](int stage, int kt) {
+    const uint16_t* st = smem + stage * STAGE_ELEMS;
+    const int kb = kt * BK * 2;
+#pragma unroll
+    for (int j = 0; j < J; ++j) {
+      const int q = w + j * NW;
+      if (j < J - 1 || w < NHI) copy_to_lds(ibase[j] + kb, off[j], st + q * 512);
+    }
+  };
+
+  f32x4 acc[4][4];
+#pragma unroll
+  for (int i = 0; i < 4; ++i)
+#pragma unroll
+    for (int j = 0; j < 4; ++j) acc[i][j] = f32x4{0.f, 0.f, 0.f, 0.f};
+
+  const int wm = w / WN, wn = w % WN;
+  const int fr = lane & 15, fq = lane >> 4;
+  const int a_rd = (wm * 64 + fr) * BK, b_rd = (wn * 64 + fr) * BK;
+  auto compute = [&](int stage) {
+    const uint16_t* As = smem + stage * STAGE_ELEMS;
+    const uint16_t* Bs = As + BM * BK;
+#pragma unroll
+    for (int ks = 0; ks < BK / 32; ++ks) {
+      const int cc = ((ks * 4 + fq) ^ swz<BK>(fr)) << 3;
+      uint4 af[4], bf[4];
+#pragma unroll
+      for (int i = 0; i < 4; ++i) af[i] = *reinterpret_cast<const uint4*>(&As[a_rd + cc + i * 16 * BK]);
+#pragma unroll
+      for (int j = 0; j < 4; ++j) bf[j] = *reinterpret_cast<const uint4*>(&Bs[b_rd + cc + j * 16 * BK]);
 #pragma unroll
       for (int i = 0; i < 4; ++i)
 #pragma unroll
-        for (int v = 0; v < 4; ++v) {
-          const int r = i * 16 + 4 * fq + v;
-          if constexpr (DUAL) {
-#pragma unroll
-            for (int j = 0; j < 2; ++j)
-              ep[r * EPI_LD + wn * 32 + j * 16 + fr] = silu(acc[i][j][v]) * acc[i][j + 2][v];
-          } else {
-#pragma unroll
-            for (int j = 0; j < 4; ++j) ep[r * EPI_LD + wn * 64 + j * 16 + fr] = acc[i][j][v];
-          }
-        }
+        for (int j = 0; j < 4; ++j) acc[i][j] = mfma16_bf16(af[i], bf[j], acc[i][j]);
     }
-    __syncthreads();
-#pragma unroll 1
-    for (int c = tid; c < 64 * CPR; c += NTHR) {
-      const int r = c / CPR, c8 = (c % CPR) * 8;
-      const int m = h * 64 + r;
-      const int col = nt * NCOL + c8;
-      if (m < m_rows && col < a.N) {
-        const float4 v0 = *reinterpret_cast<const float4*>(&ep[r * EPI_LD + c8]);
-        const float4 v1 = *reinterpret_cast<const float4*>(&ep[r * EPI_LD + c8 + 4]);
-        float f[8] = {v0.x, v0.y, v0.z, v0.w, v1.x, v1.y, v1.z, v1.w};
-        const int64_t orow = m_begin + m;
-        if constexpr (EPI == Epi::F32) {
-          float* out = static_cast<float*>(a.out) + kp * a.part_stride + orow * a.ldo + col;
-          if (col + 8 <= a.N && (a.ldo & 3) == 0) {
-            *reinterpret_cast<float4*>(out) = v0;
-            *reinterpret_cast<float4*>(out + 4) = v1;
-          } else {
-            for (int q = 0; q < 8 && col + q < a.N; ++q) out[q] = f[q];
-          }
-        } else {
-          int64_t drow = orow;
-          if constexpr (EPI == Epi::SCALED_SLOT) {
-            const int slot = a.perm[orow];
-            const float ws = a.topk_w[slot];
+  };
+
+  // K-step t lives in stage t % S.  Steps up to t + S - 2 are issued before step t is
+  // consumed, so before the barrier of step t a wave lets min(S - 2, n - 1 - t) stages
+  // of its copies stay outstanding.
+  const int kt0 = tp.kt0, n = tp.kt1 - tp.kt0;
 #pragma unroll
-            for (int q = 0; q < 8; ++q) f[q] *= ws;
-            drow = slot;
-          } else if constexpr (EPI == Epi::COMBINE) {
-            for (int jj = 0; jj < a.k; ++jj) {
-              const int64_t slot = orow * a.k + jj;
-              const int ex = a.idx[slot];
-              if (ex < 0 || ex >= a.E) continue;
-              const uint4 rv = ldg16(a.r + slot * a.N + col);
-              const uint32_t u[4] = {rv.x, rv.y, rv.z, rv.w};
-#pragma unroll
-              for (int q = 0; q < 4; ++q) {
-                f[2 * q] += __uint_as_float(u[q] << 16);
-                f[2 * q + 1] += __uint_as_float(u[q] & 0xffff0000u);
-              }
-            }
-          }
-          uint16_t* out = static_cast<uint16_t*>(a.out) + drow * a.ldo + col;
-          *reinterpret_cast<uint4*>(out) = make_uint4(pack_bf16x2(f[0], f[1]), pack_bf16x2(f[2], f[3]),
-                                                      pack_bf16x2(f[4], f[5]), pack_bf16x2(f[6], f[7]));
-        }
-      }
-    }
-    __syncthreads();
+  for (int p = 0; p < S - 1; ++p)
+    if (p < n) issue(p, kt0 + p);
+  int cur = 0, nxt = S - 1;  // stages of steps t and t + S - 1
+  for (int t = 0; t < n; ++t) {
+    const int ahead = n - 1 - t;
+    if (w < NHI)
+      copy_wait_ahead<J, S - 2>(ahead);
+    else
+      copy_wait_ahead<J - 1, S - 2>(ahead);
+    lds_barrier();
+    if (t + S - 1 < n) issue(nxt, kt0 + t + S - 1);
+    compute(cur);
+    cur = cur + 1 == S ? 0 : cur + 1;
+    nxt = nxt + 1 == S ? 0 : nxt + 1;
   }
+  copy_wait<0>();  // every wave is done reading the stages; all copies have landed
+  lds_barrier();
+  epilogue<NTHR, BN, 64, DUAL, EPI>(a, acc, reinterpret_cast<float*>(smem), tid, wm, wn, fr, fq, nt, tp.kp, m_begin,
+                                    m_rows);
+}
+
+// blocks of a launch: whole groups of M-tiles (extra tiles exit) x N-tiles x K-splits,
+// rounded up to the 8 XCDs
+inline int64_t grid_blocks(const TileArgs& a, int ncol) {
+  const int NT = (a.N + ncol - 1) / ncol;
+  const int G = a.group_m > 1 ? a.group_m : 1;  // (expert grouping: group_m <= 0, G = 1)
+  const int64_t mt_pad = (a.mtiles_bound + G - 1) / G * G;
+  const int64_t blocks = mt_pad * NT * (a.ksplit > 1 ? a.ksplit : 1);
+  return (blocks + 7) / 8 * 8;
 }
 
 template <int BN, int BK, WFmt WF, bool DUAL, AMode AM, Epi EPI>
 hipError_t launch_one(const TileArgs& a, hipStream_t s) {
-  constexpr int NCOL = DUAL ? BN / 2 : BN;
-  const int NT = (a.N + NCOL - 1) / NCOL;
-  const int G = a.group_m > 1 ? a.group_m : 1;
-  const int64_t mt_pad = (a.mtiles_bound + G - 1) / G * G;  // whole groups (extra tiles exit)
-  int64_t blocks = mt_pad * NT * (a.ksplit > 1 ? a.ksplit : 1);
-  blocks = (blocks + 7) / 8 * 8;
+  const int64_t blocks = grid_blocks(a, DUAL ? BN / 2 : BN);
   if (blocks <= 0) return hipSuccess;
   hipLaunchKernelGGL((k_tile<BN, BK, WF, DUAL, AM, EPI>), dim3(static_cast<unsigned>(blocks)), dim3(BN * 2), 0, s, a);
   return hipGetLastError();
 }
 
+template <int BN, int BK, int S, bool DUAL, AMode AM, Epi EPI>
+hipError_t launch_dma(const TileArgs& a, hipStream_t s) {
+  const int64_t blocks = grid_blocks(a, DUAL ? BN / 2 : BN);
+  if (blocks <= 0) return hipSuccess;
+  hipLaunchKernelGGL((k_tile_dma<BN, BK, S, DUAL, AM, EPI>), dim3(static_cast<unsigned>(blocks)), dim3(BN * 2), 0, s,
+                     a);
+  return hipGetLastError();
+}
+
+// Tile shapes of the copy pipeline (bf16 weights): 128 token rows x 512 weight rows,
+// K-step 64, two LDS stages (160 KB, 16 wavefronts, one block per CU).  A dense
+// single-matrix product with fewer such blocks than CUs takes 128 x 256 x 64 with
+// three stages instead (twice the blocks).
 template <WFmt WF, bool DUAL, AMode AM, Epi EPI>
 hipError_t launch_bn(const TileArgs& a, hipStream_t s) {
-  // Single-matrix products take the wide 8-wavefront tile (half the L2 -> LDS bytes
-  // per flop).  The gate/up product keeps the 4-wavefront 128 x 128 tile: measured
-  // faster on the workloads' shapes (two blocks per CU instead of one).
-  const bool wide = !DUAL && a.N >= 256;
-  // K-step: 32 for the wide tile (48 KB of LDS, several blocks per CU), 64 for the
-  // narrow one (measured best for each)
-  if (wide) return launch_one<256, 32, WF, DUAL, AM, EPI>(a, s);
-  return launch_one<128, 64, WF, DUAL, AM, EPI>(a, s);
+  if constexpr (WF == WFmt::BF16) {
+    if (!DUAL && !a.routed && grid_blocks(a, 512) < a.ncu) return launch_dma<256, 64, 3, DUAL, AM, EPI>(a, s);
+    return launch_dma<512, 64, 2, DUAL, AM, EPI>(a, s);
+  } else {
+    // u8 weights are dequantised in registers on their way to LDS.  Single-matrix
+    // products take the wide 8-wavefront tile (half the L2 -> LDS bytes per flop) with
+    // K-step 32 (48 KB of LDS, several blocks per CU); gate/up keeps 128 x 128 x 64.
+    if (!DUAL && a.N >= 256) return launch_one<256, 32, WF, DUAL, AM, EPI>(a, s);
+    return launch_one<128, 64, WF, DUAL, AM, EPI>(a, s);
+  }
 }
 
 }  // namespace
@@ -318,7 +602,7 @@ hipError_t launch_bn(const TileArgs& a, hipStream_t s) {
 hipError_t launch_tile_gemm(const TileArgs& a, AMode am, WFmt wf, Epi epi, hipStream_t s) {
   // the combinations the layer uses
   if (epi == Epi::F32 && am == AMode::DENSE && wf == WFmt::BF16)
-    return launch_one<128, 64, WFmt::BF16, false, AMode::DENSE, Epi::F32>(a, s);
+    return launch_dma<128, 64, 2, false, AMode::DENSE, Epi::F32>(a, s);
   if (epi == Epi::SWIGLU && am == AMode::GATHER && wf == WFmt::BF16)
     return launch_bn<WFmt::BF16, true, AMode::GATHER, Epi::SWIGLU>(a, s);
   if (epi == Epi::SWIGLU && am == AMode::GATHER && wf == WFmt::U8)

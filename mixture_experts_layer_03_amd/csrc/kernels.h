@@ -138,6 +138,7 @@ struct TileArgs {
   int ksplit;               // F32 epilogue only: K split into this many partial outputs
   int64_t part_stride;      // elements between partial outputs
   int group_m;              // M-tiles per block-order group (weight-panel reuse in L2)
+  int ncu;                  // compute units of the device (tile-shape choice)
 };
 hipError_t launch_tile_gemm(const TileArgs& a, AMode am, WFmt wf, Epi epi, hipStream_t s);
 

@@ -222,11 +222,11 @@ moe_status check_T(int64_t T) {
 moe_status check_ws(const moe_config& c, int64_t T, void* ws, size_t ws_bytes, Plan& p) {
   make_plan(c, T, p);
   if (!p.decode) {
-    // the tiled kernels address activation rows with 32-bit element offsets
+    // the tiled kernels address activation rows with 32-bit byte offsets
     int64_t kmax = c.hidden > c.moe_intermediate ? c.hidden : c.moe_intermediate;
     if (c.shared_intermediate > kmax) kmax = c.shared_intermediate;
-    if (T * c.top_k * kmax >= (int64_t(1) << 32))
-      return fail(MOE_EUNSUPPORTED, "T * top_k * max(hidden, intermediate) >= 2^32 on the tiled path; split the batch");
+    if (T * c.top_k * kmax * 2 >= (int64_t(1) << 32))
+      return fail(MOE_EUNSUPPORTED, "T * top_k * max(hidden, intermediate) * 2 bytes >= 2^32 on the tiled path; split the batch");
   }
   if (ws_bytes < p.total) return fail(MOE_EWORKSPACE, "workspace of %zu bytes < %zu required", ws_bytes, p.total);
   if (p.total > 0 && (!ws || !aligned(ws, 256))) return fail(MOE_EWORKSPACE, "workspace must be non-null and 256-byte aligned");
@@ -264,6 +264,7 @@ moe_status run_logits(const moe_config& c, const Plan& p, int64_t T, const void*
     g.ldo = static_cast<int>(c.num_experts);
     g.mtiles_bound = static_cast<int>((T + kTileM - 1) / kTileM);
   g.group_m = kGroupM;
+    g.ncu = device_cus();
     g.ksplit = p.P;
     g.part_stride = T * c.num_experts;
     MOE_LAUNCH_STAGE(MOE_STAGE_ROUTER, s, launch_tile_gemm(g, AMode::DENSE, WFmt::BF16, Epi::F32, s), "router logits (tiled)");
@@ -432,7 +433,8 @@ moe_status run_experts(const moe_config& c, const Plan& p, int64_t T, const void
   g.out = hm;
   g.ldo = I;
   g.mtiles_bound = p.mtiles_bound;
-  g.group_m = kGroupM;
+  g.group_m = 0;  // blocks grouped by expert
+  g.ncu = device_cus();
   MOE_LAUNCH_STAGE(MOE_STAGE_UP, s, launch_tile_gemm(g, AMode::GATHER, wf, Epi::SWIGLU, s), "expert gate/up (tiled)");
   TileArgs d{};
   d.A = static_cast<const uint16_t*>(hm);
@@ -452,7 +454,8 @@ moe_status run_experts(const moe_config& c, const Plan& p, int64_t T, const void
   d.ldo = H;
   d.topk_w = topk_w;
   d.mtiles_bound = p.mtiles_bound;
-  d.group_m = kGroupM;
+  d.group_m = 0;
+  d.ncu = g.ncu;
   MOE_LAUNCH_STAGE(MOE_STAGE_DOWN, s, launch_tile_gemm(d, AMode::DENSE, wf, Epi::SCALED_SLOT, s), "expert down (tiled)");
   (void)dmax;
   if (Is > 0) {
@@ -468,6 +471,7 @@ moe_status run_experts(const moe_config& c, const Plan& p, int64_t T, const void
     su.ldo = Is;
     su.mtiles_bound = static_cast<int>((T + kTileM - 1) / kTileM);
   su.group_m = kGroupM;
+    su.ncu = device_cus();
     MOE_LAUNCH_STAGE(MOE_STAGE_SHARED_UP, s, launch_tile_gemm(su, AMode::DENSE, WFmt::BF16, Epi::SWIGLU, s), "shared gate/up (tiled)");
     TileArgs sd{};
     sd.A = static_cast<const uint16_t*>(hs);
@@ -484,6 +488,7 @@ moe_status run_experts(const moe_config& c, const Plan& p, int64_t T, const void
     sd.E = E;
     sd.mtiles_bound = su.mtiles_bound;
   sd.group_m = kGroupM;
+    sd.ncu = su.ncu;
     MOE_LAUNCH_STAGE(MOE_STAGE_SHARED_DOWN, s, launch_tile_gemm(sd, AMode::DENSE, WFmt::BF16, Epi::COMBINE, s), "shared down + combine (tiled)");
   } else {
     CombineArgs cb{r, nullptr, idx, y, Ti, H, k, E, 1};
