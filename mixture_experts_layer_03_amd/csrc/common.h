@@ -68,4 +68,49 @@ __device__ __forceinline__ uint4 ld_stream(const void* p) {
   return make_uint4(v.x, v.y, v.z, v.w);
 }
 
+// ---- direct global -> LDS copies (global_load_lds_dwordx4), issued from inline asm so
+// the compiler's wait insertion does not track (and drain) them; users wait explicitly.
+// 16 bytes per lane from global memory to LDS at M0 + 16 * lane (M0 wave-uniform)
+__device__ __forceinline__ void copy_to_lds(const void* src, const uint16_t* lds_dst) {
+  const uint32_t m0 =
+      static_cast<uint32_t>(reinterpret_cast<uintptr_t>((const __attribute__((address_space(3))) void*)lds_dst));
+  asm volatile("global_load_lds_dwordx4 %0, off" ::"v"(src), "{m0}"(m0) : "memory");
+}
+// the same from a wave-uniform base plus a per-lane 32-bit byte offset
+__device__ __forceinline__ void copy_to_lds(const char* base, uint32_t off, const uint16_t* lds_dst) {
+  const uint32_t m0 =
+      static_cast<uint32_t>(reinterpret_cast<uintptr_t>((const __attribute__((address_space(3))) void*)lds_dst));
+  asm volatile("global_load_lds_dwordx4 %0, %1" ::"v"(off), "s"(base), "{m0}"(m0) : "memory");
+}
+// a pointer known to be the same in every lane, kept in scalar registers
+__device__ __forceinline__ const char* uniform_ptr(const void* p) {
+  const uint64_t v = reinterpret_cast<uint64_t>(p);
+  const uint32_t lo = __builtin_amdgcn_readfirstlane(static_cast<uint32_t>(v));
+  const uint32_t hi = __builtin_amdgcn_readfirstlane(static_cast<uint32_t>(v >> 32));
+  return reinterpret_cast<const char*>((static_cast<uint64_t>(hi) << 32) | lo);
+}
+
+// Wait until at most N of this wave's copies are outstanding and its LDS reads are
+// done.  Followed by lds_barrier(): afterwards every wave's copies older than its last
+// N have landed and no wave still reads a stage that is about to be refilled.
+template <int N>
+__device__ __forceinline__ void copy_wait() {
+  static_assert(N >= 0 && N < 64, "vmcnt range");
+  asm volatile("s_waitcnt vmcnt(%0) lgkmcnt(0)" ::"n"(N) : "memory");
+}
+__device__ __forceinline__ void lds_barrier() { asm volatile("s_barrier" ::: "memory"); }
+
+// copy_wait<min(ahead, A) * L>() for a runtime ahead >= 0
+template <int L, int A>
+__device__ __forceinline__ void copy_wait_ahead(int ahead) {
+  if constexpr (A == 0) {
+    copy_wait<0>();
+  } else {
+    if (ahead >= A)
+      copy_wait<A * L>();
+    else
+      copy_wait_ahead<L, A - 1>(ahead);
+  }
+}
+
 }  // namespace moe

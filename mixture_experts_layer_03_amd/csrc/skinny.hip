@@ -303,8 +303,8 @@ __global__ __launch_bounds__(256) void k_skinny_router(SkinnyRouterArgs a) {
       k0 = kk0 + ((kp * U / NWK) << 6);
       k1 = kk0 + (((kp + 1) * U / NWK) << 6);
     }
-    for (int t0 = 0; t0 < a.T; t0 += 64) {
-      const int ntok = min(64, a.T - t0);
+    for (int t0 = 0; t0 < a.T; t0 += 16 * MT) {
+      const int ntok = min(16 * MT, a.T - t0);
       Task<ACT, WF, 1, MT> tk;
       tk.wrow[0] = W + static_cast<int64_t>(row) * a.H;
       tk.mt_live = (ntok + 15) / 16;
@@ -352,7 +352,8 @@ __global__ __launch_bounds__(256) void k_skinny_up(SkinnyUpArgs a) {
   const int n = lane & 15;
   const int D = a.meta[0];
   const int CH = a.I / 16, CHs = a.Is / 16;
-  const int TC = (a.T + 63) / 64;
+  constexpr int TCH = 16 * MT;  // tokens per chunk
+  const int TC = (a.T + TCH - 1) / TCH;
   const int n_routed = D * CH;
   const int nitems = n_routed + CHs * TC;
   const AT* x = static_cast<const AT*>(a.x);
@@ -371,7 +372,7 @@ __global__ __launch_bounds__(256) void k_skinny_up(SkinnyUpArgs a) {
       off = a.offsets[e];
       ntot = a.counts[e];
       tc_begin = 0;
-      tc_end = (ntot + 63) / 64;
+      tc_end = (ntot + TCH - 1) / TCH;
     } else {
       const int si = it - n_routed;
       row0 = (si % CHs) * 16;
@@ -380,12 +381,12 @@ __global__ __launch_bounds__(256) void k_skinny_up(SkinnyUpArgs a) {
       ntot = a.T;
     }
     for (int tc = tc_begin; tc < tc_end; ++tc) {
-      const int ntok = min(64, ntot - tc * 64);
+      const int ntok = min(TCH, ntot - tc * TCH);
       Task<ACT, WF, 2, MT> tk;
       tk.mt_live = (ntok + 15) / 16;
 #pragma unroll
       for (int mt = 0; mt < MT; ++mt) {
-        const int m = tc * 64 + min(mt * 16 + n, ntok - 1);
+        const int m = tc * TCH + min(mt * 16 + n, ntok - 1);
         const int tok = shared ? m : a.perm[off + m] / a.k;
         tk.arow[mt] = x + static_cast<int64_t>(tok) * a.H;
       }
@@ -437,7 +438,7 @@ __global__ __launch_bounds__(256) void k_skinny_up(SkinnyUpArgs a) {
             const int m = mt * 16 + 4 * (lane >> 4) + v;
             if (m < ntok) {
               const float h = silu(acc[0][ai][v]) * acc[1][ai][v];
-              store_act<ACT>(out + (rbase + tc * 64 + m) * ld + row0 + n, h);
+              store_act<ACT>(out + (rbase + tc * TCH + m) * ld + row0 + n, h);
             }
           }
         }
@@ -458,7 +459,8 @@ __global__ __launch_bounds__(256) void k_skinny_down(SkinnyDownArgs a) {
   const int n = lane & 15;
   const int D = a.meta[0];
   const int CH = a.H / 16;
-  const int TC = (a.T + 63) / 64;
+  constexpr int TCH = 16 * MT;  // tokens per chunk
+  const int TC = (a.T + TCH - 1) / TCH;
   const int n_routed = D * CH;
   const int nitems = n_routed + (a.Is > 0 ? CH * TC : 0);
   const AT* hm = static_cast<const AT*>(a.hm);
@@ -478,7 +480,7 @@ __global__ __launch_bounds__(256) void k_skinny_down(SkinnyDownArgs a) {
       off = a.offsets[e];
       ntot = a.counts[e];
       tc_begin = 0;
-      tc_end = (ntot + 63) / 64;
+      tc_end = (ntot + TCH - 1) / TCH;
     } else {
       const int si = it - n_routed;
       row0 = (si % CH) * 16;
@@ -487,7 +489,7 @@ __global__ __launch_bounds__(256) void k_skinny_down(SkinnyDownArgs a) {
       ntot = a.T;
     }
     for (int tc = tc_begin; tc < tc_end; ++tc) {
-      const int ntok = min(64, ntot - tc * 64);
+      const int ntok = min(TCH, ntot - tc * TCH);
       f32x4 acc[1][MT];
       zero_acc(acc);
       const int mt_live = (ntok + 15) / 16;
@@ -497,7 +499,7 @@ __global__ __launch_bounds__(256) void k_skinny_down(SkinnyDownArgs a) {
           tk.mt_live = mt_live;
 #pragma unroll
           for (int mt = 0; mt < MT; ++mt)
-            tk.arow[mt] = hm + static_cast<int64_t>(off + tc * 64 + min(mt * 16 + n, ntok - 1)) * a.I;
+            tk.arow[mt] = hm + static_cast<int64_t>(off + tc * TCH + min(mt * 16 + n, ntok - 1)) * a.I;
           const int64_t ro = static_cast<int64_t>(e) * a.H + row0 + n;
           tk.wrow[0] = static_cast<const WT*>(a.down) + ro * a.I;
           if constexpr (WF == WFmt::U8) {
@@ -511,7 +513,7 @@ __global__ __launch_bounds__(256) void k_skinny_down(SkinnyDownArgs a) {
           ts.mt_live = mt_live;
 #pragma unroll
           for (int mt = 0; mt < MT; ++mt)
-            ts.arow[mt] = hs + static_cast<int64_t>(tc * 64 + min(mt * 16 + n, ntok - 1)) * a.Is;
+            ts.arow[mt] = hs + static_cast<int64_t>(tc * TCH + min(mt * 16 + n, ntok - 1)) * a.Is;
           ts.wrow[0] = static_cast<const ST*>(a.sdown) + static_cast<int64_t>(row0 + n) * a.Is;
           stream_rows(ts, k0, k1, acc);
         }
@@ -532,7 +534,7 @@ __global__ __launch_bounds__(256) void k_skinny_down(SkinnyDownArgs a) {
             const int m = mt * 16 + 4 * (lane >> 4) + v;
             if (m < ntok) {
               if (!shared) {
-                const int slot = a.perm[off + tc * 64 + m];
+                const int slot = a.perm[off + tc * TCH + m];
                 const float val = a.topk_w[slot] * acc[0][ai][v];
                 const int64_t o = static_cast<int64_t>(slot) * a.H + row0 + n;
                 if (a.r_bf16)
@@ -540,8 +542,275 @@ __global__ __launch_bounds__(256) void k_skinny_down(SkinnyDownArgs a) {
                 else
                   static_cast<float*>(a.r)[o] = val;
               } else {
-                a.rs[static_cast<int64_t>(tc * 64 + m) * a.H + row0 + n] = acc[0][ai][v];
+                a.rs[static_cast<int64_t>(tc * TCH + m) * a.H + row0 + n] = acc[0][ai][v];
               }
+            }
+          }
+        }
+      }
+    }
+  }
+}
+
+// ------------------------------------------- bf16 streaming through per-wave LDS rings
+// The same work items as above (16 weight rows of one matrix set x one 16-token
+// chunk), for bf16 activations and weights, with the operands brought in by direct
+// global -> LDS copies of whole 128-byte lines: one copy instruction moves 8 rows x 128
+// bytes (one 64-element K-step of 8 rows).  Each wavefront owns a ring of U K-steps in
+// LDS holding its NMAT x 16 weight rows and its 16 token rows, keeps U - 1 steps in
+// flight and reads MFMA fragments from the ring; wavefronts never wait for each other
+// inside the K loop.  Token rows are read once per K-step and item (they are shared by
+// the NMAT matrices), and every line of a weight row is requested once.
+//
+// Ring layout per step: rows [0, 16 NMAT) weights (matrix m: rows 16m ..), rows
+// [16 NMAT, 16 NMAT + 16) tokens; 128-byte rows with 16-byte chunks XOR-swizzled by
+// row % 8.  Lane l of a copy instruction covering rows [8h, 8h + 8) takes row 8h + l/8
+// and logical chunk (l % 8) ^ (l / 8).
+template <int NMAT>
+struct RingGeom {
+  static constexpr int ROWS = 16 * NMAT + 16;
+  static constexpr int SLOT = ROWS * 64;      // bf16 elements per K-step
+  static constexpr int CPS = 2 * NMAT + 2;    // copy instructions per K-step
+};
+
+// acc[m] += tokens x W_m^T over [k0, k1) (multiples of 64) with a U-step ring at `ring`.
+// wbase[m]: wave-uniform byte address of weight row 0 of matrix m (rows H_row bytes
+// apart, the stride folded into woff); woff[h]: this lane's byte offset of its row in
+// copy h (row 8h + l/8) plus its chunk; abase / aoff[h]: the same for the token rows.
+template <int NMAT, int U>
+__device__ __forceinline__ void ring_stream(const char* const (&wbase)[NMAT], const uint32_t (&woff)[2],
+                                            const char* abase, const uint32_t (&aoff)[2], int k0, int k1,
+                                            uint16_t* ring, f32x4 (&acc)[NMAT]) {
+  using G = RingGeom<NMAT>;
+  const int lane = lane_id();
+  const int n = (k1 - k0) >> 6;
+  auto issue = [&](int slot, int step) {
+    uint16_t* sl = ring + slot * G::SLOT;
+    const int kb = (k0 + 64 * step) * 2;
+#pragma unroll
+    for (int m = 0; m < NMAT; ++m)
+#pragma unroll
+      for (int h = 0; h < 2; ++h) copy_to_lds(uniform_ptr(wbase[m] + kb), woff[h], sl + (16 * m + 8 * h) * 64);
+#pragma unroll
+    for (int h = 0; h < 2; ++h) copy_to_lds(uniform_ptr(abase + kb), aoff[h], sl + (16 * NMAT + 8 * h) * 64);
+  };
+  const int r = lane & 15, q = lane >> 4;
+  auto compute = [&](int slot) {
+    const uint16_t* sl = ring + slot * G::SLOT;
+#pragma unroll
+    for (int ks = 0; ks < 2; ++ks) {
+      const int cc = ((ks * 4 + q) ^ (r & 7)) << 3;
+      const uint4 a = *reinterpret_cast<const uint4*>(sl + (16 * NMAT + r) * 64 + cc);
+#pragma unroll
+      for (int m = 0; m < NMAT; ++m) {
+        const uint4 w = *reinterpret_cast<const uint4*>(sl + (16 * m + r) * 64 + cc);
+        acc[m] = mfma16_bf16(a, w, acc[m]);
+      }
+    }
+  };
+#pragma unroll
+  for (int p = 0; p < U - 1; ++p)
+    if (p < n) issue(p, p);
+  int cur = 0, nxt = U - 1;
+  for (int t = 0; t < n; ++t) {
+    // this wave's copies of step t have landed (later steps may still be in flight) and
+    // its reads of the slot refilled next are done
+    copy_wait_ahead<G::CPS, U - 2>(n - 1 - t);
+    if (t + U - 1 < n) issue(nxt, t + U - 1);
+    compute(cur);
+    cur = cur + 1 == U ? 0 : cur + 1;
+    nxt = nxt + 1 == U ? 0 : nxt + 1;
+  }
+  copy_wait<0>();
+}
+
+// per-lane ring offsets: copy h covers rows 8h + l/8, logical chunk (l % 8) ^ (l / 8)
+__device__ __forceinline__ void ring_lane(int& row_in_copy, int& chunk) {
+  const int lane = lane_id();
+  row_in_copy = lane >> 3;
+  chunk = (lane & 7) ^ (lane >> 3);
+}
+
+template <int U, int NWK>
+__global__ __launch_bounds__(256) void k_stream_up(SkinnyUpArgs a) {
+  using G = RingGeom<2>;
+  constexpr int IPB = 4 / NWK;
+  __shared__ __attribute__((aligned(16))) uint16_t rings[4 * U * G::SLOT];
+  const int lane = lane_id(), w = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  const int n = lane & 15;
+  uint16_t* ring = rings + w * U * G::SLOT;
+  const int D = a.meta[0];
+  const int CH = a.I / 16, CHs = a.Is / 16;
+  const int TC = (a.T + 15) / 16;
+  const int n_routed = D * CH;
+  const int nitems = n_routed + CHs * TC;
+  int rr, ch;
+  ring_lane(rr, ch);
+  const char* xb = uniform_ptr(a.x);
+  for (int base = blockIdx.x * IPB; base < nitems; base += gridDim.x * IPB) {
+    const int item = base + w / NWK;
+    const bool live = item < nitems;
+    const int it = live ? item : 0;
+    const bool shared = it >= n_routed;
+    int k0 = 0, k1 = a.H;
+    if (NWK > 1) unit_range(a.H, w % NWK, NWK, k0, k1);
+    int e = 0, off = 0, ntot, row0, tc_begin, tc_end;
+    if (!shared) {
+      e = a.active[it / CH];
+      row0 = (it % CH) * 16;
+      off = a.offsets[e];
+      ntot = a.counts[e];
+      tc_begin = 0;
+      tc_end = (ntot + 15) / 16;
+    } else {
+      const int si = it - n_routed;
+      row0 = (si % CHs) * 16;
+      tc_begin = si / CHs;
+      tc_end = tc_begin + 1;
+      ntot = a.T;
+    }
+    const char* wb[2];
+    if (!shared) {
+      const int64_t ro = static_cast<int64_t>(e) * a.I + row0;
+      wb[0] = uniform_ptr(static_cast<const uint16_t*>(a.gate) + ro * a.H);
+      wb[1] = uniform_ptr(static_cast<const uint16_t*>(a.up) + ro * a.H);
+    } else {
+      wb[0] = uniform_ptr(static_cast<const uint16_t*>(a.sgate) + static_cast<int64_t>(row0) * a.H);
+      wb[1] = uniform_ptr(static_cast<const uint16_t*>(a.sup) + static_cast<int64_t>(row0) * a.H);
+    }
+    const uint32_t woff[2] = {static_cast<uint32_t>((rr * a.H + ch * 8) * 2),
+                              static_cast<uint32_t>(((8 + rr) * a.H + ch * 8) * 2)};
+    for (int tc = tc_begin; tc < tc_end; ++tc) {
+      const int ntok = min(16, ntot - tc * 16);
+      uint32_t aoff[2];
+#pragma unroll
+      for (int h = 0; h < 2; ++h) {
+        const int m = tc * 16 + min(8 * h + rr, ntok - 1);  // padded rows repeat the last token
+        const int tok = shared ? m : a.perm[off + m] / a.k;
+        aoff[h] = static_cast<uint32_t>(tok) * a.H * 2 + ch * 16;
+      }
+      f32x4 acc[2] = {f32x4{0.f, 0.f, 0.f, 0.f}, f32x4{0.f, 0.f, 0.f, 0.f}};
+      if (live) ring_stream<2, U>(wb, woff, xb, aoff, k0, k1, ring, acc);
+      if constexpr (NWK > 1) {
+        // K-split: partial sums through the (now idle) rings; wavefront 0 adds them
+        float* red = reinterpret_cast<float*>(rings);
+        __syncthreads();
+#pragma unroll
+        for (int m = 0; m < 2; ++m) *reinterpret_cast<f32x4*>(red + ((w * 2 + m) * 64 + lane) * 4) = acc[m];
+        __syncthreads();
+        if (w == 0) {
+#pragma unroll
+          for (int m = 0; m < 2; ++m) {
+            f32x4 sum = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+            for (int p = 0; p < 4; ++p) sum += *reinterpret_cast<const f32x4*>(red + ((p * 2 + m) * 64 + lane) * 4);
+            acc[m] = sum;
+          }
+        }
+        __syncthreads();
+      }
+      if (live && (NWK == 1 || w == 0)) {
+        uint16_t* out = static_cast<uint16_t*>(shared ? a.hs : a.hm);
+        const int ld = shared ? a.Is : a.I;
+        const int64_t rbase = shared ? 0 : off;
+#pragma unroll
+        for (int v = 0; v < 4; ++v) {
+          const int m = 4 * (lane >> 4) + v;
+          if (m < ntok) {
+            const float h = silu(acc[0][v]) * acc[1][v];
+            out[(rbase + tc * 16 + m) * ld + row0 + n] = f32_to_bf16(h);
+          }
+        }
+      }
+    }
+  }
+}
+
+template <int U, int NWK>
+__global__ __launch_bounds__(256) void k_stream_down(SkinnyDownArgs a) {
+  using G = RingGeom<1>;
+  constexpr int IPB = 4 / NWK;
+  __shared__ __attribute__((aligned(16))) uint16_t rings[4 * U * G::SLOT];
+  const int lane = lane_id(), w = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  const int n = lane & 15;
+  uint16_t* ring = rings + w * U * G::SLOT;
+  const int D = a.meta[0];
+  const int CH = a.H / 16;
+  const int TC = (a.T + 15) / 16;
+  const int n_routed = D * CH;
+  const int nitems = n_routed + (a.Is > 0 ? CH * TC : 0);
+  int rr, ch;
+  ring_lane(rr, ch);
+  for (int base = blockIdx.x * IPB; base < nitems; base += gridDim.x * IPB) {
+    const int item = base + w / NWK;
+    const bool live = item < nitems;
+    const int it = live ? item : 0;
+    const bool shared = it >= n_routed;
+    const int K = shared ? a.Is : a.I;
+    int k0 = 0, k1 = K;
+    if (NWK > 1) unit_range(K, w % NWK, NWK, k0, k1);
+    int e = 0, off = 0, ntot, row0, tc_begin, tc_end;
+    if (!shared) {
+      e = a.active[it / CH];
+      row0 = (it % CH) * 16;
+      off = a.offsets[e];
+      ntot = a.counts[e];
+      tc_begin = 0;
+      tc_end = (ntot + 15) / 16;
+    } else {
+      const int si = it - n_routed;
+      row0 = (si % CH) * 16;
+      tc_begin = si / CH;
+      tc_end = tc_begin + 1;
+      ntot = a.T;
+    }
+    const char* wb[1];
+    if (!shared)
+      wb[0] = uniform_ptr(static_cast<const uint16_t*>(a.down) + (static_cast<int64_t>(e) * a.H + row0) * a.I);
+    else
+      wb[0] = uniform_ptr(static_cast<const uint16_t*>(a.sdown) + static_cast<int64_t>(row0) * a.Is);
+    const uint32_t woff[2] = {static_cast<uint32_t>((rr * K + ch * 8) * 2),
+                              static_cast<uint32_t>(((8 + rr) * K + ch * 8) * 2)};
+    const char* ab = uniform_ptr(shared ? a.hs : a.hm);
+    for (int tc = tc_begin; tc < tc_end; ++tc) {
+      const int ntok = min(16, ntot - tc * 16);
+      uint32_t aoff[2];
+#pragma unroll
+      for (int h = 0; h < 2; ++h) {
+        const int m = tc * 16 + min(8 * h + rr, ntok - 1);
+        const int row = shared ? m : off + m;
+        aoff[h] = static_cast<uint32_t>(row) * K * 2 + ch * 16;
+      }
+      f32x4 acc[1] = {f32x4{0.f, 0.f, 0.f, 0.f}};
+      if (live) ring_stream<1, U>(wb, woff, ab, aoff, k0, k1, ring, acc);
+      if constexpr (NWK > 1) {
+        float* red = reinterpret_cast<float*>(rings);
+        __syncthreads();
+        *reinterpret_cast<f32x4*>(red + (w * 64 + lane) * 4) = acc[0];
+        __syncthreads();
+        if (w == 0) {
+          f32x4 sum = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+          for (int p = 0; p < 4; ++p) sum += *reinterpret_cast<const f32x4*>(red + (p * 64 + lane) * 4);
+          acc[0] = sum;
+        }
+        __syncthreads();
+      }
+      if (live && (NWK == 1 || w == 0)) {
+#pragma unroll
+        for (int v = 0; v < 4; ++v) {
+          const int m = 4 * (lane >> 4) + v;
+          if (m < ntok) {
+            if (!shared) {
+              const int slot = a.perm[off + tc * 16 + m];
+              const float val = a.topk_w[slot] * acc[0][v];
+              const int64_t o = static_cast<int64_t>(slot) * a.H + row0 + n;
+              if (a.r_bf16)
+                static_cast<uint16_t*>(a.r)[o] = f32_to_bf16(val);
+              else
+                static_cast<float*>(a.r)[o] = val;
+            } else {
+              a.rs[static_cast<int64_t>(tc * 16 + m) * a.H + row0 + n] = acc[0][v];
             }
           }
         }
@@ -606,6 +875,24 @@ int grid_for(int64_t items, int ipb, int ncu) {
   return static_cast<int>(blocks);
 }
 
+// K-steps per LDS ring (per wavefront) of the bf16 streaming kernels
+constexpr int kUpRing = 3, kDownRing = 4;
+
+// the ring kernels address activation rows with 32-bit byte offsets
+bool stream_ok(int64_t rows, int64_t cols, int64_t rows2, int64_t cols2) {
+  return rows * cols * 2 < (int64_t(1) << 31) && rows2 * cols2 * 2 < (int64_t(1) << 31);
+}
+
+// items < 4 * ncu: the four wavefronts of a block split K of one item; else one item each
+template <int U, typename Args>
+hipError_t launch_ring(void (*k1)(Args), void (*k4)(Args), int64_t items, int64_t small, int ncu, hipStream_t s,
+                       const Args& a) {
+  const bool split = items < small;
+  const int grid = grid_for(items, split ? 1 : 4, ncu);
+  hipLaunchKernelGGL(split ? k4 : k1, dim3(grid), dim3(256), 0, s, a);
+  return hipGetLastError();
+}
+
 }  // namespace
 
 #define MOE_DISPATCH_MT_NWK(KERNEL, ARGS, ITEMS, T_, NWK_SMALL_ITEMS, ...)                     \
@@ -645,12 +932,17 @@ hipError_t launch_skinny_up(const SkinnyUpArgs& a, Act act, WFmt wf, int ncu, hi
   if (a.T <= 0) return hipSuccess;
   const int64_t slots = static_cast<int64_t>(a.T) * a.k;
   const int64_t dmax = slots < a.E ? slots : a.E;
-  const int64_t items = dmax * (a.I / 16) + static_cast<int64_t>(a.Is / 16) * ((a.T + 63) / 64);
+  const int tch = 16 * pick_mt(a.T);
+  const int64_t items = dmax * (a.I / 16) + static_cast<int64_t>(a.Is / 16) * ((a.T + tch - 1) / tch);
   const int64_t small = 4ll * ncu;
   if (act == Act::F32)
     MOE_DISPATCH_MT_NWK(k_skinny_up, a, items, a.T, small, Act::F32, WFmt::F32);
   else if (wf == WFmt::U8)
     MOE_DISPATCH_MT_NWK(k_skinny_up, a, items, a.T, small, Act::BF16, WFmt::U8);
+  else if (stream_ok(a.T, a.H, a.T * a.k, a.I))
+    return launch_ring<kUpRing>(k_stream_up<kUpRing, 1>, k_stream_up<kUpRing, 4>,
+                                dmax * (a.I / 16) + static_cast<int64_t>(a.Is / 16) * ((a.T + 15) / 16), small, ncu,
+                                s, a);
   else
     MOE_DISPATCH_MT_NWK(k_skinny_up, a, items, a.T, small, Act::BF16, WFmt::BF16);
   return hipGetLastError();
@@ -660,12 +952,17 @@ hipError_t launch_skinny_down(const SkinnyDownArgs& a, Act act, WFmt wf, int ncu
   if (a.T <= 0) return hipSuccess;
   const int64_t slots = static_cast<int64_t>(a.T) * a.k;
   const int64_t dmax = slots < a.E ? slots : a.E;
-  const int64_t items = dmax * (a.H / 16) + (a.Is > 0 ? static_cast<int64_t>(a.H / 16) * ((a.T + 63) / 64) : 0);
+  const int tch = 16 * pick_mt(a.T);
+  const int64_t items = dmax * (a.H / 16) + (a.Is > 0 ? static_cast<int64_t>(a.H / 16) * ((a.T + tch - 1) / tch) : 0);
   const int64_t small = 4ll * ncu;
   if (act == Act::F32)
     MOE_DISPATCH_MT_NWK(k_skinny_down, a, items, a.T, small, Act::F32, WFmt::F32);
   else if (wf == WFmt::U8)
     MOE_DISPATCH_MT_NWK(k_skinny_down, a, items, a.T, small, Act::BF16, WFmt::U8);
+  else if (stream_ok(a.T * a.k, a.I, a.T, a.Is))
+    return launch_ring<kDownRing>(k_stream_down<kDownRing, 1>, k_stream_down<kDownRing, 4>,
+                                  dmax * (a.H / 16) + (a.Is > 0 ? static_cast<int64_t>(a.H / 16) * ((a.T + 15) / 16) : 0),
+                                  small, ncu, s, a);
   else
     MOE_DISPATCH_MT_NWK(k_skinny_down, a, items, a.T, small, Act::BF16, WFmt::BF16);
   return hipGetLastError();
