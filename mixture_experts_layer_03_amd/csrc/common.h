@@ -46,16 +46,64 @@ __device__ __forceinline__ f32x4 mfma16_f32(float a, float b, f32x4 c) {
   return __builtin_amdgcn_mfma_f32_16x16x4f32(a, b, c, 0, 0, 0);
 }
 
+// ---- wavefront reductions on the DPP lane network (register to register; a shuffle
+// through the LDS crossbar costs ~100 cycles per step)
+// update_dpp: lane value moved by CTRL; lanes the instruction does not write (rows or
+// banks masked off, source outside the row) return `old`
+template <int CTRL, int ROWM = 0xf, int BANKM = 0xf>
+__device__ __forceinline__ int dpp_i(int old, int v) {
+  return __builtin_amdgcn_update_dpp(old, v, CTRL, ROWM, BANKM, false);
+}
+template <int CTRL, int ROWM = 0xf, int BANKM = 0xf>
+__device__ __forceinline__ float dpp_f(float old, float v) {
+  return __int_as_float(dpp_i<CTRL, ROWM, BANKM>(__float_as_int(old), __float_as_int(v)));
+}
+// gfx9 DPP controls
+constexpr int kDppQuadXor1 = 0xB1;    // quad_perm [1,0,3,2]
+constexpr int kDppQuadXor2 = 0x4E;    // quad_perm [2,3,0,1]
+constexpr int kDppRowShr1 = 0x111, kDppRowShr2 = 0x112, kDppRowShr4 = 0x114, kDppRowShr8 = 0x118;
+constexpr int kDppRowMirror = 0x140, kDppRowHalfMirror = 0x141;
+constexpr int kDppRowBcast15 = 0x142, kDppRowBcast31 = 0x143;
+
+// Fold `op` over all 64 lanes toward lane 63 (row prefix by shifts 1, 2, 4, 8, then the
+// row totals by the row broadcasts), then broadcast lane 63.  `ident` is op's identity.
+template <typename F>
+__device__ __forceinline__ float wave_reduce(float v, float ident, F op) {
+  v = op(v, dpp_f<kDppRowShr1>(ident, v));
+  v = op(v, dpp_f<kDppRowShr2>(ident, v));
+  v = op(v, dpp_f<kDppRowShr4, 0xf, 0xe>(ident, v));
+  v = op(v, dpp_f<kDppRowShr8, 0xf, 0xc>(ident, v));
+  v = op(v, dpp_f<kDppRowBcast15, 0xa, 0xf>(ident, v));
+  v = op(v, dpp_f<kDppRowBcast31, 0xc, 0xf>(ident, v));
+  return __int_as_float(__builtin_amdgcn_readlane(__float_as_int(v), 63));
+}
+
 __device__ __forceinline__ float wave_sum(float v) {
-#pragma unroll
-  for (int o = 32; o > 0; o >>= 1) v += __shfl_xor(v, o, kWave);
-  return v;
+  return wave_reduce(v, 0.f, [](float x, float y) { return x + y; });
 }
 
 __device__ __forceinline__ float wave_max(float v) {
-#pragma unroll
-  for (int o = 32; o > 0; o >>= 1) v = fmaxf(v, __shfl_xor(v, o, kWave));
-  return v;
+  return wave_reduce(v, -__builtin_huge_valf(), [](float x, float y) { return fmaxf(x, y); });
+}
+
+// (v, i) with the largest v over the wavefront, equal v -> smaller i; in every lane
+__device__ __forceinline__ void wave_argmax(float& v, int& i) {
+  constexpr float ninf = -__builtin_huge_valf();
+  constexpr int imax = 0x7fffffff;
+  auto take = [&](float ov, int oi) {
+    if (ov > v || (ov == v && oi < i)) {
+      v = ov;
+      i = oi;
+    }
+  };
+  take(dpp_f<kDppRowShr1>(ninf, v), dpp_i<kDppRowShr1>(imax, i));
+  take(dpp_f<kDppRowShr2>(ninf, v), dpp_i<kDppRowShr2>(imax, i));
+  take(dpp_f<kDppRowShr4, 0xf, 0xe>(ninf, v), dpp_i<kDppRowShr4, 0xf, 0xe>(imax, i));
+  take(dpp_f<kDppRowShr8, 0xf, 0xc>(ninf, v), dpp_i<kDppRowShr8, 0xf, 0xc>(imax, i));
+  take(dpp_f<kDppRowBcast15, 0xa, 0xf>(ninf, v), dpp_i<kDppRowBcast15, 0xa, 0xf>(imax, i));
+  take(dpp_f<kDppRowBcast31, 0xc, 0xf>(ninf, v), dpp_i<kDppRowBcast31, 0xc, 0xf>(imax, i));
+  v = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(v), 63));
+  i = __builtin_amdgcn_readlane(i, 63);
 }
 
 __device__ __forceinline__ int lane_id() { return threadIdx.x & (kWave - 1); }
@@ -81,6 +129,12 @@ __device__ __forceinline__ void copy_to_lds(const char* base, uint32_t off, cons
   const uint32_t m0 =
       static_cast<uint32_t>(reinterpret_cast<uintptr_t>((const __attribute__((address_space(3))) void*)lds_dst));
   asm volatile("global_load_lds_dwordx4 %0, %1" ::"v"(off), "s"(base), "{m0}"(m0) : "memory");
+}
+// 4 bytes per lane to LDS at M0 + 4 * lane (M0 wave-uniform)
+__device__ __forceinline__ void copy4_to_lds(const void* src, const void* lds_dst) {
+  const uint32_t m0 =
+      static_cast<uint32_t>(reinterpret_cast<uintptr_t>((const __attribute__((address_space(3))) void*)lds_dst));
+  asm volatile("global_load_lds_dword %0, off" ::"v"(src), "{m0}"(m0) : "memory");
 }
 // a pointer known to be the same in every lane, kept in scalar registers
 __device__ __forceinline__ const char* uniform_ptr(const void* p) {

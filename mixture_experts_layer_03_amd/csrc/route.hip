@@ -104,43 +104,83 @@ __device__ void route_token(const TopkArgs& a, int t) {
   // grouped mask: keep the g groups with the largest top-2 sums, zero the rest
   if (a.G > 1 && a.g < a.G) {
     const int gs = E / a.G;
-    int grp[EPL];
-#pragma unroll
-    for (int i = 0; i < EPL; ++i) grp[i] = valid[i] ? (lane * EPL + i) / gs : -1;
-    float sig_mine = kNegInf;
-    for (int gr = 0; gr < a.G; ++gr) {
+    const int lpg = gs / EPL;  // lanes per group when a group spans whole lanes
+    if (gs % EPL == 0 && (lpg == 1 || lpg == 2 || lpg == 4 || lpg == 8 || lpg == 16) && a.G * lpg <= kWave) {
+      // each group is lpg consecutive lanes: top-2 per lane, then a butterfly inside the
+      // group on the DPP network (xor 1, xor 2 within quads; the half-row and row
+      // mirrors pair the 4- and 8-lane halves once those are uniform)
       float t1 = kNegInf, t2 = kNegInf;
 #pragma unroll
       for (int i = 0; i < EPL; ++i) {
-        if (grp[i] == gr) {
-          const float x = sel[i];
-          if (x > t1) {
-            t2 = t1;
-            t1 = x;
-          } else if (x > t2) {
-            t2 = x;
-          }
+        const float x = valid[i] ? sel[i] : kNegInf;
+        if (x > t1) {
+          t2 = t1;
+          t1 = x;
+        } else if (x > t2) {
+          t2 = x;
         }
       }
-#pragma unroll
-      for (int o = 32; o > 0; o >>= 1) {
-        const float o1 = __shfl_xor(t1, o, kWave), o2 = __shfl_xor(t2, o, kWave);
+      auto merge = [&](float o1, float o2) {
         const float hi = fmaxf(t1, o1);
-        const float lo = fmaxf(fminf(t1, o1), fmaxf(t2, o2));
+        t2 = fmaxf(fminf(t1, o1), fmaxf(t2, o2));
         t1 = hi;
-        t2 = lo;
+      };
+      if (lpg >= 2) merge(dpp_f<kDppQuadXor1>(t1, t1), dpp_f<kDppQuadXor1>(t2, t2));
+      if (lpg >= 4) merge(dpp_f<kDppQuadXor2>(t1, t1), dpp_f<kDppQuadXor2>(t2, t2));
+      if (lpg >= 8) merge(dpp_f<kDppRowHalfMirror>(t1, t1), dpp_f<kDppRowHalfMirror>(t2, t2));
+      if (lpg >= 16) merge(dpp_f<kDppRowMirror>(t1, t1), dpp_f<kDppRowMirror>(t2, t2));
+      const float mine = t1 + t2;
+      // rank of this lane's group among all groups (larger first, ties -> lower group)
+      const int gme = lane / lpg;
+      int rank = 0;
+      for (int gr = 0; gr < a.G; ++gr) {
+        const float o = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(mine), gr * lpg));
+        rank += (o > mine || (o == mine && gr < gme)) ? 1 : 0;
       }
-      if (lane == gr) sig_mine = t1 + t2;
-    }
-    int rank = 0;
-    for (int gr = 0; gr < a.G; ++gr) {
-      const float o = __shfl(sig_mine, gr, kWave);
-      rank += (o > sig_mine || (o == sig_mine && gr < lane)) ? 1 : 0;
-    }
-    const unsigned long long kept = __ballot(lane < a.G && rank < a.g);
+      if (rank >= a.g) {
 #pragma unroll
-    for (int i = 0; i < EPL; ++i)
-      if (grp[i] >= 0 && !((kept >> grp[i]) & 1ull)) sel[i] = 0.0f;
+        for (int i = 0; i < EPL; ++i)
+          if (valid[i]) sel[i] = 0.0f;
+      }
+    } else {
+      int grp[EPL];
+#pragma unroll
+      for (int i = 0; i < EPL; ++i) grp[i] = valid[i] ? (lane * EPL + i) / gs : -1;
+      float sig_mine = kNegInf;
+      for (int gr = 0; gr < a.G; ++gr) {
+        float t1 = kNegInf, t2 = kNegInf;
+#pragma unroll
+        for (int i = 0; i < EPL; ++i) {
+          if (grp[i] == gr) {
+            const float x = sel[i];
+            if (x > t1) {
+              t2 = t1;
+              t1 = x;
+            } else if (x > t2) {
+              t2 = x;
+            }
+          }
+        }
+#pragma unroll
+        for (int o = 32; o > 0; o >>= 1) {
+          const float o1 = __shfl_xor(t1, o, kWave), o2 = __shfl_xor(t2, o, kWave);
+          const float hi = fmaxf(t1, o1);
+          const float lo = fmaxf(fminf(t1, o1), fmaxf(t2, o2));
+          t1 = hi;
+          t2 = lo;
+        }
+        if (lane == gr) sig_mine = t1 + t2;
+      }
+      int rank = 0;
+      for (int gr = 0; gr < a.G; ++gr) {
+        const float o = __shfl(sig_mine, gr, kWave);
+        rank += (o > sig_mine || (o == sig_mine && gr < lane)) ? 1 : 0;
+      }
+      const unsigned long long kept = __ballot(lane < a.G && rank < a.g);
+#pragma unroll
+      for (int i = 0; i < EPL; ++i)
+        if (grp[i] >= 0 && !((kept >> grp[i]) & 1ull)) sel[i] = 0.0f;
+    }
   }
 
   // top-k: k rounds of wave arg-max, larger score first, equal scores -> lower index
@@ -158,20 +198,14 @@ __device__ void route_token(const TopkArgs& a, int t) {
         bo = s[i];
       }
     }
-#pragma unroll
-    for (int o = 32; o > 0; o >>= 1) {
-      const float ov = __shfl_xor(bv, o, kWave), oo = __shfl_xor(bo, o, kWave);
-      const int oi = __shfl_xor(bi, o, kWave);
-      if (ov > bv || (ov == bv && oi < bi)) {
-        bv = ov;
-        bi = oi;
-        bo = oo;
-      }
-    }
-    if (bi != 0x7fffffff && bi / EPL == lane) taken |= 1u << (bi - lane * EPL);
+    const int own = bi;
+    wave_argmax(bv, bi);
+    // the unbiased score of the winner, from the lane that holds it
+    const float wo = bi != 0x7fffffff ? __int_as_float(__builtin_amdgcn_readlane(__float_as_int(bo), bi / EPL)) : 0.f;
+    if (bi != 0x7fffffff && own == bi) taken |= 1u << (bi - lane * EPL);
     if (lane == j) {
       my_idx = bi;
-      my_w = bo;
+      my_w = wo;
     }
   }
 

@@ -12,6 +12,8 @@
 // unchanged.  Each 64-element step is mapped so that one load instruction covers 64
 // contiguous bytes of every one of its 16 rows (bf16: two instructions per step,
 // u8: one), i.e. whole cache-line halves.
+#include <initializer_list>
+
 #include "common.h"
 #include "kernels.h"
 
@@ -819,6 +821,340 @@ __global__ __launch_bounds__(256) void k_stream_down(SkinnyDownArgs a) {
   }
 }
 
+// ----------------------------------------------------- u8 weights through LDS rings
+// One ring step covers 128 elements of K (two quantisation groups), so a weight row's
+// codes for the step are one whole 128-byte line.  Slot layout (bytes): NMAT x 16 code
+// rows of 128 B, two token images of 16 rows x 128 B (elements 0..63 and 64..127 of the
+// step), then 256 B of group parameters: lane l of one 4-byte-per-lane copy brings the
+// two fp16 values (groups 2t, 2t + 1) of matrix l / 32, kind (l / 16) % 2 (scale,
+// zero), row l % 16.  Products per group are exact: codes minus the zero point are
+// integers in [-255, 255], exact in bf16; the group scale multiplies the fp32 result.
+template <int NMAT>
+struct RingGeomU8 {
+  static constexpr int W_BYTES = NMAT * 16 * 128;
+  static constexpr int A_BYTES = 2 * 16 * 128;
+  static constexpr int SLOT_BYTES = W_BYTES + A_BYTES + 256;
+  static constexpr int CPS = 2 * NMAT + 4 + 1;  // copy instructions per step
+};
+
+// codes: 8 u8 in (lo, hi) minus zero point -> 8 bf16
+__device__ __forceinline__ uint4 codes_minus_zero(uint2 c, float z) {
+  const uint32_t w[2] = {c.x, c.y};
+  uint32_t o[4];
+#pragma unroll
+  for (int i = 0; i < 2; ++i) {
+    o[2 * i] = pack_bf16x2(static_cast<float>(w[i] & 0xffu) - z, static_cast<float>((w[i] >> 8) & 0xffu) - z);
+    o[2 * i + 1] = pack_bf16x2(static_cast<float>((w[i] >> 16) & 0xffu) - z, static_cast<float>(w[i] >> 24) - z);
+  }
+  return make_uint4(o[0], o[1], o[2], o[3]);
+}
+
+// acc[m] += tokens x dequant(W_m)^T over [k0, k1) (multiples of 128).
+// wbase[m]: wave-uniform byte address of code row 0 of matrix m; woff[h]: lane offset of
+// its code row in copy h (row 8h + l/8, rows K bytes apart) plus its chunk.  sz_src: this
+// lane's group-parameter address for group 0 of the range (4 bytes, 2 groups).
+template <int NMAT, int U>
+__device__ __forceinline__ void ring_stream_u8(const char* const (&wbase)[NMAT], const uint32_t (&woff)[2],
+                                               const char* abase, const uint32_t (&aoff)[2], const uint16_t* sz_src,
+                                               int k0, int k1, char* ring, f32x4 (&acc)[NMAT]) {
+  using G = RingGeomU8<NMAT>;
+  const int lane = lane_id();
+  const int n = (k1 - k0) >> 7;
+  auto issue = [&](int slot, int step) {
+    char* sl = ring + slot * G::SLOT_BYTES;
+    const int kc = k0 + 128 * step;  // element index = code byte offset
+#pragma unroll
+    for (int m = 0; m < NMAT; ++m)
+#pragma unroll
+      for (int h = 0; h < 2; ++h)
+        copy_to_lds(uniform_ptr(wbase[m] + kc), woff[h], reinterpret_cast<uint16_t*>(sl + (16 * m + 8 * h) * 128));
+#pragma unroll
+    for (int half = 0; half < 2; ++half)
+#pragma unroll
+      for (int h = 0; h < 2; ++h)
+        copy_to_lds(uniform_ptr(abase + (kc + 64 * half) * 2), aoff[h],
+                    reinterpret_cast<uint16_t*>(sl + G::W_BYTES + half * 2048 + 8 * h * 128));
+    copy4_to_lds(sz_src + (kc >> 6), sl + G::W_BYTES + G::A_BYTES);
+  };
+  const int r = lane & 15, q = lane >> 4;
+  auto compute = [&](int slot) {
+    const char* sl = ring + slot * G::SLOT_BYTES;
+    const uint32_t* szp = reinterpret_cast<const uint32_t*>(sl + G::W_BYTES + G::A_BYTES);
+#pragma unroll
+    for (int g = 0; g < 2; ++g) {
+      f32x4 part[NMAT];
+      float zf[NMAT], sf[NMAT];
+#pragma unroll
+      for (int m = 0; m < NMAT; ++m) {
+        part[m] = f32x4{0.f, 0.f, 0.f, 0.f};
+        const uint32_t sv = szp[m * 32 + r], zv = szp[m * 32 + 16 + r];
+        sf[m] = f16_to_f32(static_cast<uint16_t>(g ? sv >> 16 : sv & 0xffffu));
+        zf[m] = f16_to_f32(static_cast<uint16_t>(g ? zv >> 16 : zv & 0xffffu));
+      }
+#pragma unroll
+      for (int ks = 0; ks < 2; ++ks) {
+        const int c = ks * 4 + q;  // logical 16-byte chunk of the 64-element token image
+        const uint4 av = *reinterpret_cast<const uint4*>(sl + G::W_BYTES + g * 2048 + r * 128 + ((c ^ (r & 7)) << 4));
+        const int cw = 4 * g + (c >> 1);  // 16-byte chunk of the code row holding codes 8c .. of group g
+#pragma unroll
+        for (int m = 0; m < NMAT; ++m) {
+          const uint2 cv =
+              *reinterpret_cast<const uint2*>(sl + (16 * m + r) * 128 + ((cw ^ (r & 7)) << 4) + (c & 1) * 8);
+          part[m] = mfma16_bf16(av, codes_minus_zero(cv, zf[m]), part[m]);
+        }
+      }
+#pragma unroll
+      for (int m = 0; m < NMAT; ++m) acc[m] += sf[m] * part[m];
+    }
+  };
+#pragma unroll
+  for (int p = 0; p < U - 1; ++p)
+    if (p < n) issue(p, p);
+  int cur = 0, nxt = U - 1;
+  for (int t = 0; t < n; ++t) {
+    copy_wait_ahead<G::CPS, U - 2>(n - 1 - t);
+    if (t + U - 1 < n) issue(nxt, t + U - 1);
+    compute(cur);
+    cur = cur + 1 == U ? 0 : cur + 1;
+    nxt = nxt + 1 == U ? 0 : nxt + 1;
+  }
+  copy_wait<0>();
+}
+
+// [k0, k1) of part `part` of `parts`, in 128-element units
+__device__ __forceinline__ void unit_range128(int K, int part, int parts, int& k0, int& k1) {
+  const int U = K >> 7;
+  k0 = (part * U / parts) << 7;
+  k1 = ((part + 1) * U / parts) << 7;
+}
+
+// lane's group-parameter source for the u8 ring: matrix l / 32 (NMAT = 2) or 0, scale
+// (kind 0) or zero point (kind 1) of row l % 16
+template <int NMAT>
+__device__ __forceinline__ const uint16_t* u8_param_row(const uint16_t* const (&s)[NMAT], const uint16_t* const (&z)[NMAT],
+                                                         int64_t row0, int K) {
+  const int lane = lane_id();
+  const int m = NMAT == 2 ? (lane >> 5) : 0;
+  const int kind = (lane >> 4) & 1;
+  const uint16_t* base = kind ? z[m] : s[m];
+  return base + (row0 + (lane & 15)) * (K / 64);
+}
+
+template <int U, int NWK>
+__global__ __launch_bounds__(256) void k_stream_up_u8(SkinnyUpArgs a) {
+  using G = RingGeomU8<2>;
+  using GB = RingGeom<2>;
+  constexpr int SLOTB = G::SLOT_BYTES > GB::SLOT * 2 ? G::SLOT_BYTES : GB::SLOT * 2;
+  constexpr int IPB = 4 / NWK;
+  __shared__ __attribute__((aligned(16))) char rings[4 * U * SLOTB];
+  const int lane = lane_id(), w = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  const int n = lane & 15;
+  char* ring = rings + w * U * SLOTB;
+  const int D = a.meta[0];
+  const int CH = a.I / 16, CHs = a.Is / 16;
+  const int TC = (a.T + 15) / 16;
+  const int n_routed = D * CH;
+  const int nitems = n_routed + CHs * TC;
+  int rr, ch;
+  ring_lane(rr, ch);
+  const char* xb = uniform_ptr(a.x);
+  for (int base = blockIdx.x * IPB; base < nitems; base += gridDim.x * IPB) {
+    const int item = base + w / NWK;
+    const bool live = item < nitems;
+    const int it = live ? item : 0;
+    const bool shared = it >= n_routed;
+    int k0 = 0, k1 = a.H;
+    if (NWK > 1) {
+      if (shared)
+        unit_range(a.H, w % NWK, NWK, k0, k1);
+      else
+        unit_range128(a.H, w % NWK, NWK, k0, k1);
+    }
+    int e = 0, off = 0, ntot, row0, tc_begin, tc_end;
+    if (!shared) {
+      e = a.active[it / CH];
+      row0 = (it % CH) * 16;
+      off = a.offsets[e];
+      ntot = a.counts[e];
+      tc_begin = 0;
+      tc_end = (ntot + 15) / 16;
+    } else {
+      const int si = it - n_routed;
+      row0 = (si % CHs) * 16;
+      tc_begin = si / CHs;
+      tc_end = tc_begin + 1;
+      ntot = a.T;
+    }
+    const int64_t ro = static_cast<int64_t>(e) * a.I + row0;
+    for (int tc = tc_begin; tc < tc_end; ++tc) {
+      const int ntok = min(16, ntot - tc * 16);
+      uint32_t aoff[2];
+#pragma unroll
+      for (int h = 0; h < 2; ++h) {
+        const int m = tc * 16 + min(8 * h + rr, ntok - 1);
+        const int tok = shared ? m : a.perm[off + m] / a.k;
+        aoff[h] = static_cast<uint32_t>(tok) * a.H * 2 + ch * 16;
+      }
+      f32x4 acc[2] = {f32x4{0.f, 0.f, 0.f, 0.f}, f32x4{0.f, 0.f, 0.f, 0.f}};
+      if (live) {
+        if (!shared) {
+          const char* wb[2] = {uniform_ptr(static_cast<const uint8_t*>(a.gate) + ro * a.H),
+                               uniform_ptr(static_cast<const uint8_t*>(a.up) + ro * a.H)};
+          const uint32_t woff[2] = {static_cast<uint32_t>(rr * a.H + ch * 16),
+                                    static_cast<uint32_t>((8 + rr) * a.H + ch * 16)};
+          const uint16_t* ss[2] = {a.gate_s, a.up_s};
+          const uint16_t* zz[2] = {a.gate_z, a.up_z};
+          ring_stream_u8<2, U>(wb, woff, xb, aoff, u8_param_row<2>(ss, zz, ro, a.H), k0, k1, ring, acc);
+        } else {
+          const char* wb[2] = {uniform_ptr(static_cast<const uint16_t*>(a.sgate) + static_cast<int64_t>(row0) * a.H),
+                               uniform_ptr(static_cast<const uint16_t*>(a.sup) + static_cast<int64_t>(row0) * a.H)};
+          const uint32_t woff[2] = {static_cast<uint32_t>((rr * a.H + ch * 8) * 2),
+                                    static_cast<uint32_t>(((8 + rr) * a.H + ch * 8) * 2)};
+          ring_stream<2, U>(wb, woff, xb, aoff, k0, k1, reinterpret_cast<uint16_t*>(ring), acc);
+        }
+      }
+      if constexpr (NWK > 1) {
+        float* red = reinterpret_cast<float*>(rings);
+        __syncthreads();
+#pragma unroll
+        for (int m = 0; m < 2; ++m) *reinterpret_cast<f32x4*>(red + ((w * 2 + m) * 64 + lane) * 4) = acc[m];
+        __syncthreads();
+        if (w == 0) {
+#pragma unroll
+          for (int m = 0; m < 2; ++m) {
+            f32x4 sum = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+            for (int p = 0; p < 4; ++p) sum += *reinterpret_cast<const f32x4*>(red + ((p * 2 + m) * 64 + lane) * 4);
+            acc[m] = sum;
+          }
+        }
+        __syncthreads();
+      }
+      if (live && (NWK == 1 || w == 0)) {
+        uint16_t* out = static_cast<uint16_t*>(shared ? a.hs : a.hm);
+        const int ld = shared ? a.Is : a.I;
+        const int64_t rbase = shared ? 0 : off;
+#pragma unroll
+        for (int v = 0; v < 4; ++v) {
+          const int m = 4 * (lane >> 4) + v;
+          if (m < ntok) {
+            const float h = silu(acc[0][v]) * acc[1][v];
+            out[(rbase + tc * 16 + m) * ld + row0 + n] = f32_to_bf16(h);
+          }
+        }
+      }
+    }
+  }
+}
+
+template <int U, int NWK>
+__global__ __launch_bounds__(256) void k_stream_down_u8(SkinnyDownArgs a) {
+  using G = RingGeomU8<1>;
+  using GB = RingGeom<1>;
+  constexpr int SLOTB = G::SLOT_BYTES > GB::SLOT * 2 ? G::SLOT_BYTES : GB::SLOT * 2;
+  constexpr int IPB = 4 / NWK;
+  __shared__ __attribute__((aligned(16))) char rings[4 * U * SLOTB];
+  const int lane = lane_id(), w = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  const int n = lane & 15;
+  char* ring = rings + w * U * SLOTB;
+  const int D = a.meta[0];
+  const int CH = a.H / 16;
+  const int TC = (a.T + 15) / 16;
+  const int n_routed = D * CH;
+  const int nitems = n_routed + (a.Is > 0 ? CH * TC : 0);
+  int rr, ch;
+  ring_lane(rr, ch);
+  for (int base = blockIdx.x * IPB; base < nitems; base += gridDim.x * IPB) {
+    const int item = base + w / NWK;
+    const bool live = item < nitems;
+    const int it = live ? item : 0;
+    const bool shared = it >= n_routed;
+    const int K = shared ? a.Is : a.I;
+    int k0 = 0, k1 = K;
+    if (NWK > 1) {
+      if (shared)
+        unit_range(K, w % NWK, NWK, k0, k1);
+      else
+        unit_range128(K, w % NWK, NWK, k0, k1);
+    }
+    int e = 0, off = 0, ntot, row0, tc_begin, tc_end;
+    if (!shared) {
+      e = a.active[it / CH];
+      row0 = (it % CH) * 16;
+      off = a.offsets[e];
+      ntot = a.counts[e];
+      tc_begin = 0;
+      tc_end = (ntot + 15) / 16;
+    } else {
+      const int si = it - n_routed;
+      row0 = (si % CH) * 16;
+      tc_begin = si / CH;
+      tc_end = tc_begin + 1;
+      ntot = a.T;
+    }
+    const char* ab = uniform_ptr(shared ? a.hs : a.hm);
+    const int64_t ro = static_cast<int64_t>(e) * a.H + row0;
+    for (int tc = tc_begin; tc < tc_end; ++tc) {
+      const int ntok = min(16, ntot - tc * 16);
+      uint32_t aoff[2];
+#pragma unroll
+      for (int h = 0; h < 2; ++h) {
+        const int m = tc * 16 + min(8 * h + rr, ntok - 1);
+        const int row = shared ? m : off + m;
+        aoff[h] = static_cast<uint32_t>(row) * K * 2 + ch * 16;
+      }
+      f32x4 acc[1] = {f32x4{0.f, 0.f, 0.f, 0.f}};
+      if (live) {
+        if (!shared) {
+          const char* wb[1] = {uniform_ptr(static_cast<const uint8_t*>(a.down) + ro * a.I)};
+          const uint32_t woff[2] = {static_cast<uint32_t>(rr * a.I + ch * 16),
+                                    static_cast<uint32_t>((8 + rr) * a.I + ch * 16)};
+          const uint16_t* ss[1] = {a.down_s};
+          const uint16_t* zz[1] = {a.down_z};
+          ring_stream_u8<1, U>(wb, woff, ab, aoff, u8_param_row<1>(ss, zz, ro, a.I), k0, k1, ring, acc);
+        } else {
+          const char* wb[1] = {uniform_ptr(static_cast<const uint16_t*>(a.sdown) + static_cast<int64_t>(row0) * a.Is)};
+          const uint32_t woff[2] = {static_cast<uint32_t>((rr * K + ch * 8) * 2),
+                                    static_cast<uint32_t>(((8 + rr) * K + ch * 8) * 2)};
+          ring_stream<1, U>(wb, woff, ab, aoff, k0, k1, reinterpret_cast<uint16_t*>(ring), acc);
+        }
+      }
+      if constexpr (NWK > 1) {
+        float* red = reinterpret_cast<float*>(rings);
+        __syncthreads();
+        *reinterpret_cast<f32x4*>(red + (w * 64 + lane) * 4) = acc[0];
+        __syncthreads();
+        if (w == 0) {
+          f32x4 sum = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+          for (int p = 0; p < 4; ++p) sum += *reinterpret_cast<const f32x4*>(red + (p * 64 + lane) * 4);
+          acc[0] = sum;
+        }
+        __syncthreads();
+      }
+      if (live && (NWK == 1 || w == 0)) {
+#pragma unroll
+        for (int v = 0; v < 4; ++v) {
+          const int m = 4 * (lane >> 4) + v;
+          if (m < ntok) {
+            if (!shared) {
+              const int slot = a.perm[off + tc * 16 + m];
+              const float val = a.topk_w[slot] * acc[0][v];
+              const int64_t o = static_cast<int64_t>(slot) * a.H + row0 + n;
+              if (a.r_bf16)
+                static_cast<uint16_t*>(a.r)[o] = f32_to_bf16(val);
+              else
+                static_cast<float*>(a.r)[o] = val;
+            } else {
+              a.rs[static_cast<int64_t>(tc * 16 + m) * a.H + row0 + n] = acc[0][v];
+            }
+          }
+        }
+      }
+    }
+  }
+}
+
 // y[t] = sum_j r[t*k + j] (valid experts only, fixed j order) + rs[t]
 template <Act ACT>
 __global__ __launch_bounds__(256) void k_combine(CombineArgs a) {
@@ -877,6 +1213,14 @@ int grid_for(int64_t items, int ipb, int ncu) {
 
 // K-steps per LDS ring (per wavefront) of the bf16 streaming kernels
 constexpr int kUpRing = 3, kDownRing = 4;
+constexpr int kUpRingU8 = 3, kDownRingU8 = 3;
+
+// the u8 ring kernels copy two fp16 group parameters at a time (4-byte copies)
+bool aligned4(std::initializer_list<const uint16_t*> ps) {
+  for (const uint16_t* p : ps)
+    if (reinterpret_cast<uintptr_t>(p) % 4) return false;
+  return true;
+}
 
 // the ring kernels address activation rows with 32-bit byte offsets
 bool stream_ok(int64_t rows, int64_t cols, int64_t rows2, int64_t cols2) {
@@ -937,6 +1281,11 @@ hipError_t launch_skinny_up(const SkinnyUpArgs& a, Act act, WFmt wf, int ncu, hi
   const int64_t small = 4ll * ncu;
   if (act == Act::F32)
     MOE_DISPATCH_MT_NWK(k_skinny_up, a, items, a.T, small, Act::F32, WFmt::F32);
+  else if (wf == WFmt::U8 && a.H % 128 == 0 && stream_ok(a.T, a.H, 0, 0) &&
+           aligned4({a.gate_s, a.gate_z, a.up_s, a.up_z}))
+    return launch_ring<kUpRingU8>(k_stream_up_u8<kUpRingU8, 1>, k_stream_up_u8<kUpRingU8, 4>,
+                                  dmax * (a.I / 16) + static_cast<int64_t>(a.Is / 16) * ((a.T + 15) / 16), small, ncu,
+                                  s, a);
   else if (wf == WFmt::U8)
     MOE_DISPATCH_MT_NWK(k_skinny_up, a, items, a.T, small, Act::BF16, WFmt::U8);
   else if (stream_ok(a.T, a.H, a.T * a.k, a.I))
@@ -957,6 +1306,11 @@ hipError_t launch_skinny_down(const SkinnyDownArgs& a, Act act, WFmt wf, int ncu
   const int64_t small = 4ll * ncu;
   if (act == Act::F32)
     MOE_DISPATCH_MT_NWK(k_skinny_down, a, items, a.T, small, Act::F32, WFmt::F32);
+  else if (wf == WFmt::U8 && a.I % 128 == 0 && stream_ok(a.T * a.k, a.I, a.T, a.Is) &&
+           aligned4({a.down_s, a.down_z}))
+    return launch_ring<kDownRingU8>(k_stream_down_u8<kDownRingU8, 1>, k_stream_down_u8<kDownRingU8, 4>,
+                                    dmax * (a.H / 16) + (a.Is > 0 ? static_cast<int64_t>(a.H / 16) * ((a.T + 15) / 16) : 0),
+                                    small, ncu, s, a);
   else if (wf == WFmt::U8)
     MOE_DISPATCH_MT_NWK(k_skinny_down, a, items, a.T, small, Act::BF16, WFmt::U8);
   else if (stream_ok(a.T * a.k, a.I, a.T, a.Is))
