@@ -71,6 +71,7 @@ struct SkinnyUpArgs {
   const int32_t* active;
   const int32_t* meta;
   int T, H, I, Is, k, E;
+  int part;                // items: 0 routed and shared, 1 routed only, 2 shared only (reads no routing)
 };
 hipError_t launch_skinny_up(const SkinnyUpArgs& a, Act act, WFmt wf, int ncu, hipStream_t s);
 
@@ -91,6 +92,7 @@ struct SkinnyDownArgs {
   const int32_t* active;
   const int32_t* meta;
   int T, H, I, Is, k, E;
+  int part;                // as SkinnyUpArgs::part
 };
 hipError_t launch_skinny_down(const SkinnyDownArgs& a, Act act, WFmt wf, int ncu, hipStream_t s);
 

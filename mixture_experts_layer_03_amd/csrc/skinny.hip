@@ -352,12 +352,12 @@ __global__ __launch_bounds__(256) void k_skinny_up(SkinnyUpArgs a) {
   __shared__ float red[NWK > 1 ? 4 * 2 * MT * 256 : 1];
   const int lane = lane_id(), w = threadIdx.x >> 6;
   const int n = lane & 15;
-  const int D = a.meta[0];
+  const int D = a.part == 2 ? 0 : a.meta[0];  // shared-only launches read no routing
   const int CH = a.I / 16, CHs = a.Is / 16;
   constexpr int TCH = 16 * MT;  // tokens per chunk
   const int TC = (a.T + TCH - 1) / TCH;
   const int n_routed = D * CH;
-  const int nitems = n_routed + CHs * TC;
+  const int nitems = n_routed + (a.part == 1 ? 0 : CHs * TC);
   const AT* x = static_cast<const AT*>(a.x);
   for (int base = blockIdx.x * IPB; base < nitems; base += gridDim.x * IPB) {
     const int item = base + w / NWK;
@@ -459,12 +459,12 @@ __global__ __launch_bounds__(256) void k_skinny_down(SkinnyDownArgs a) {
   __shared__ float red[NWK > 1 ? 4 * MT * 256 : 1];
   const int lane = lane_id(), w = threadIdx.x >> 6;
   const int n = lane & 15;
-  const int D = a.meta[0];
+  const int D = a.part == 2 ? 0 : a.meta[0];  // shared-only launches read no routing
   const int CH = a.H / 16;
   constexpr int TCH = 16 * MT;  // tokens per chunk
   const int TC = (a.T + TCH - 1) / TCH;
   const int n_routed = D * CH;
-  const int nitems = n_routed + (a.Is > 0 ? CH * TC : 0);
+  const int nitems = n_routed + (a.Is > 0 && a.part != 1 ? CH * TC : 0);
   const AT* hm = static_cast<const AT*>(a.hm);
   const AT* hs = static_cast<const AT*>(a.hs);
   for (int base = blockIdx.x * IPB; base < nitems; base += gridDim.x * IPB) {
@@ -641,11 +641,11 @@ __global__ __launch_bounds__(256) void k_stream_up(SkinnyUpArgs a) {
   const int lane = lane_id(), w = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   const int n = lane & 15;
   uint16_t* ring = rings + w * U * G::SLOT;
-  const int D = a.meta[0];
+  const int D = a.part == 2 ? 0 : a.meta[0];  // shared-only launches read no routing
   const int CH = a.I / 16, CHs = a.Is / 16;
   const int TC = (a.T + 15) / 16;
   const int n_routed = D * CH;
-  const int nitems = n_routed + CHs * TC;
+  const int nitems = n_routed + (a.part == 1 ? 0 : CHs * TC);
   int rr, ch;
   ring_lane(rr, ch);
   const char* xb = uniform_ptr(a.x);
@@ -736,11 +736,11 @@ __global__ __launch_bounds__(256) void k_stream_down(SkinnyDownArgs a) {
   const int lane = lane_id(), w = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   const int n = lane & 15;
   uint16_t* ring = rings + w * U * G::SLOT;
-  const int D = a.meta[0];
+  const int D = a.part == 2 ? 0 : a.meta[0];  // shared-only launches read no routing
   const int CH = a.H / 16;
   const int TC = (a.T + 15) / 16;
   const int n_routed = D * CH;
-  const int nitems = n_routed + (a.Is > 0 ? CH * TC : 0);
+  const int nitems = n_routed + (a.Is > 0 && a.part != 1 ? CH * TC : 0);
   int rr, ch;
   ring_lane(rr, ch);
   for (int base = blockIdx.x * IPB; base < nitems; base += gridDim.x * IPB) {
@@ -950,11 +950,11 @@ __global__ __launch_bounds__(256) void k_stream_up_u8(SkinnyUpArgs a) {
   const int lane = lane_id(), w = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   const int n = lane & 15;
   char* ring = rings + w * U * SLOTB;
-  const int D = a.meta[0];
+  const int D = a.part == 2 ? 0 : a.meta[0];  // shared-only launches read no routing
   const int CH = a.I / 16, CHs = a.Is / 16;
   const int TC = (a.T + 15) / 16;
   const int n_routed = D * CH;
-  const int nitems = n_routed + CHs * TC;
+  const int nitems = n_routed + (a.part == 1 ? 0 : CHs * TC);
   int rr, ch;
   ring_lane(rr, ch);
   const char* xb = uniform_ptr(a.x);
@@ -1057,11 +1057,11 @@ __global__ __launch_bounds__(256) void k_stream_down_u8(SkinnyDownArgs a) {
   const int lane = lane_id(), w = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   const int n = lane & 15;
   char* ring = rings + w * U * SLOTB;
-  const int D = a.meta[0];
+  const int D = a.part == 2 ? 0 : a.meta[0];  // shared-only launches read no routing
   const int CH = a.H / 16;
   const int TC = (a.T + 15) / 16;
   const int n_routed = D * CH;
-  const int nitems = n_routed + (a.Is > 0 ? CH * TC : 0);
+  const int nitems = n_routed + (a.Is > 0 && a.part != 1 ? CH * TC : 0);
   int rr, ch;
   ring_lane(rr, ch);
   for (int base = blockIdx.x * IPB; base < nitems; base += gridDim.x * IPB) {
@@ -1215,6 +1215,11 @@ int grid_for(int64_t items, int ipb, int ncu) {
 constexpr int kUpRing = 3, kDownRing = 4;
 constexpr int kUpRingU8 = 3, kDownRingU8 = 3;
 
+// work items of a launch covering `part` (see SkinnyUpArgs::part)
+int64_t part_items(int part, int64_t routed, int64_t shared) {
+  return (part == 2 ? 0 : routed) + (part == 1 ? 0 : shared);
+}
+
 // the u8 ring kernels copy two fp16 group parameters at a time (4-byte copies)
 bool aligned4(std::initializer_list<const uint16_t*> ps) {
   for (const uint16_t* p : ps)
@@ -1277,21 +1282,21 @@ hipError_t launch_skinny_up(const SkinnyUpArgs& a, Act act, WFmt wf, int ncu, hi
   const int64_t slots = static_cast<int64_t>(a.T) * a.k;
   const int64_t dmax = slots < a.E ? slots : a.E;
   const int tch = 16 * pick_mt(a.T);
-  const int64_t items = dmax * (a.I / 16) + static_cast<int64_t>(a.Is / 16) * ((a.T + tch - 1) / tch);
+  const int64_t items = part_items(a.part, dmax * (a.I / 16), static_cast<int64_t>(a.Is / 16) * ((a.T + tch - 1) / tch));
   const int64_t small = 4ll * ncu;
   if (act == Act::F32)
     MOE_DISPATCH_MT_NWK(k_skinny_up, a, items, a.T, small, Act::F32, WFmt::F32);
   else if (wf == WFmt::U8 && a.H % 128 == 0 && stream_ok(a.T, a.H, 0, 0) &&
            aligned4({a.gate_s, a.gate_z, a.up_s, a.up_z}))
     return launch_ring<kUpRingU8>(k_stream_up_u8<kUpRingU8, 1>, k_stream_up_u8<kUpRingU8, 4>,
-                                  dmax * (a.I / 16) + static_cast<int64_t>(a.Is / 16) * ((a.T + 15) / 16), small, ncu,
-                                  s, a);
+                                  part_items(a.part, dmax * (a.I / 16), static_cast<int64_t>(a.Is / 16) * ((a.T + 15) / 16)),
+                                  small, ncu, s, a);
   else if (wf == WFmt::U8)
     MOE_DISPATCH_MT_NWK(k_skinny_up, a, items, a.T, small, Act::BF16, WFmt::U8);
   else if (stream_ok(a.T, a.H, a.T * a.k, a.I))
     return launch_ring<kUpRing>(k_stream_up<kUpRing, 1>, k_stream_up<kUpRing, 4>,
-                                dmax * (a.I / 16) + static_cast<int64_t>(a.Is / 16) * ((a.T + 15) / 16), small, ncu,
-                                s, a);
+                                part_items(a.part, dmax * (a.I / 16), static_cast<int64_t>(a.Is / 16) * ((a.T + 15) / 16)),
+                                small, ncu, s, a);
   else
     MOE_DISPATCH_MT_NWK(k_skinny_up, a, items, a.T, small, Act::BF16, WFmt::BF16);
   return hipGetLastError();
@@ -1302,20 +1307,20 @@ hipError_t launch_skinny_down(const SkinnyDownArgs& a, Act act, WFmt wf, int ncu
   const int64_t slots = static_cast<int64_t>(a.T) * a.k;
   const int64_t dmax = slots < a.E ? slots : a.E;
   const int tch = 16 * pick_mt(a.T);
-  const int64_t items = dmax * (a.H / 16) + (a.Is > 0 ? static_cast<int64_t>(a.H / 16) * ((a.T + tch - 1) / tch) : 0);
+  const int64_t items = part_items(a.part, dmax * (a.H / 16), a.Is > 0 ? static_cast<int64_t>(a.H / 16) * ((a.T + tch - 1) / tch) : 0);
   const int64_t small = 4ll * ncu;
   if (act == Act::F32)
     MOE_DISPATCH_MT_NWK(k_skinny_down, a, items, a.T, small, Act::F32, WFmt::F32);
   else if (wf == WFmt::U8 && a.I % 128 == 0 && stream_ok(a.T * a.k, a.I, a.T, a.Is) &&
            aligned4({a.down_s, a.down_z}))
     return launch_ring<kDownRingU8>(k_stream_down_u8<kDownRingU8, 1>, k_stream_down_u8<kDownRingU8, 4>,
-                                    dmax * (a.H / 16) + (a.Is > 0 ? static_cast<int64_t>(a.H / 16) * ((a.T + 15) / 16) : 0),
+                                    part_items(a.part, dmax * (a.H / 16), a.Is > 0 ? static_cast<int64_t>(a.H / 16) * ((a.T + 15) / 16) : 0),
                                     small, ncu, s, a);
   else if (wf == WFmt::U8)
     MOE_DISPATCH_MT_NWK(k_skinny_down, a, items, a.T, small, Act::BF16, WFmt::U8);
   else if (stream_ok(a.T * a.k, a.I, a.T, a.Is))
     return launch_ring<kDownRing>(k_stream_down<kDownRing, 1>, k_stream_down<kDownRing, 4>,
-                                  dmax * (a.H / 16) + (a.Is > 0 ? static_cast<int64_t>(a.H / 16) * ((a.T + 15) / 16) : 0),
+                                  part_items(a.part, dmax * (a.H / 16), a.Is > 0 ? static_cast<int64_t>(a.H / 16) * ((a.T + 15) / 16) : 0),
                                   small, ncu, s, a);
   else
     MOE_DISPATCH_MT_NWK(k_skinny_down, a, items, a.T, small, Act::BF16, WFmt::BF16);
