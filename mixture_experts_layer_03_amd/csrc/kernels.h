@@ -42,7 +42,8 @@ struct PermuteArgs {
 constexpr int kPermChunk = 2048;   // slots per workgroup in the multi-block permutation
 constexpr int kPermSingleMax = 4096;  // up to this many slots one workgroup does everything
 hipError_t launch_permute(const PermuteArgs& a, hipStream_t s);
-// top-k of every token and the permutation in one workgroup (a.nslots <= kPermSingleMax)
+// top-k of every token and the permutation in one workgroup (a.nslots <= kFusedSlots)
+constexpr int kFusedSlots = 256;
 hipError_t launch_route_permute(const TopkArgs& t, const PermuteArgs& a, hipStream_t s);
 
 // -------------------------------------------------- weight-streaming (decode) path

@@ -758,7 +758,7 @@ moe_status moe_forward(const moe_config* cfg, int64_t T, const void* x, const mo
         join = aux->join;
       }
     }
-    if (p.decode && T <= kFusedRouteMaxT && T * cfg->top_k <= kPermSingleMax) {
+    if (p.decode && T <= kFusedRouteMaxT && T * cfg->top_k <= kFusedSlots) {
       // small batch: route and permute in one workgroup
       if ((s = run_logits(*cfg, p, T, x, w->router, ws, st)) != MOE_OK) return s;
       const TopkArgs ta = topk_args(*cfg, p, T, ws, w->router_bias, ebias, idx, wt);

@@ -24,8 +24,9 @@ constexpr float kNegInf = -__builtin_huge_valf();
 // Expert e lives in lane e / EPL, register e % EPL: each lane owns EPL consecutive
 // experts, so a row of logits is read with contiguous per-lane runs.
 // Routes token t with one wavefront (all 64 lanes active).
+// (lds_idx: optional copy of the token's k expert indices in LDS, at lds_idx[t * k + j])
 template <int EPL>
-__device__ void route_token(const TopkArgs& a, int t) {
+__device__ void route_token(const TopkArgs& a, int t, int* lds_idx = nullptr) {
   const int lane = lane_id();
   const int E = a.E;
 
@@ -36,19 +37,26 @@ __device__ void route_token(const TopkArgs& a, int t) {
     valid[i] = lane * EPL + i < E;
     s[i] = 0.f;
   }
-  // sum the P partial logits; every load of a partial is issued before any is used
+  // both biases and the P partial logits are loaded together (one memory round trip
+  // for P <= 8: a token's routing is a chain of dependent steps)
+  float rb[EPL], eb[EPL];
+#pragma unroll
+  for (int i = 0; i < EPL; ++i) {
+    rb[i] = (valid[i] && a.router_bias) ? a.router_bias[lane * EPL + i] : 0.f;
+    eb[i] = (valid[i] && a.use_ebias) ? a.expert_bias[lane * EPL + i] : 0.f;
+  }
   const float* row = a.logits + static_cast<int64_t>(t) * E + lane * EPL;
   if (EPL % 4 == 0 && (E % 4) == 0 && lane * EPL + EPL <= E) {
-    for (int q0 = 0; q0 < a.P; q0 += 4) {
-      float4 v[4][EPL / 4 > 0 ? EPL / 4 : 1];
+    for (int q0 = 0; q0 < a.P; q0 += 8) {
+      float4 v[8][EPL / 4 > 0 ? EPL / 4 : 1];
 #pragma unroll
-      for (int u = 0; u < 4; ++u)
+      for (int u = 0; u < 8; ++u)
 #pragma unroll
         for (int c = 0; c < EPL / 4; ++c)
           v[u][c] = q0 + u < a.P ? *reinterpret_cast<const float4*>(row + (q0 + u) * a.part_stride + 4 * c)
                                  : make_float4(0.f, 0.f, 0.f, 0.f);
 #pragma unroll
-      for (int u = 0; u < 4; ++u)
+      for (int u = 0; u < 8; ++u)
 #pragma unroll
         for (int c = 0; c < EPL / 4; ++c) {
           s[4 * c] += v[u][c].x;
@@ -58,19 +66,20 @@ __device__ void route_token(const TopkArgs& a, int t) {
         }
     }
   } else {
-    for (int q = 0; q < a.P; ++q) {
-      float v[EPL];
+    for (int q0 = 0; q0 < a.P; q0 += 8) {
+      float v[8][EPL];
 #pragma unroll
-      for (int i = 0; i < EPL; ++i) v[i] = valid[i] ? row[q * a.part_stride + i] : 0.f;
+      for (int u = 0; u < 8; ++u)
 #pragma unroll
-      for (int i = 0; i < EPL; ++i) s[i] += v[i];
+        for (int i = 0; i < EPL; ++i) v[u][i] = (valid[i] && q0 + u < a.P) ? row[(q0 + u) * a.part_stride + i] : 0.f;
+#pragma unroll
+      for (int u = 0; u < 8; ++u)
+#pragma unroll
+        for (int i = 0; i < EPL; ++i) s[i] += v[u][i];
     }
   }
-  if (a.router_bias) {
 #pragma unroll
-    for (int i = 0; i < EPL; ++i)
-      if (valid[i]) s[i] += a.router_bias[lane * EPL + i];
-  }
+  for (int i = 0; i < EPL; ++i) s[i] += rb[i];
 
   // scores
   if (a.score_sigmoid) {
@@ -95,11 +104,7 @@ __device__ void route_token(const TopkArgs& a, int t) {
 
   // selection copy (correction bias for selection only)
 #pragma unroll
-  for (int i = 0; i < EPL; ++i) {
-    const int e = lane * EPL + i;
-    float b = (valid[i] && a.use_ebias) ? a.expert_bias[e] : 0.f;
-    sel[i] = valid[i] ? s[i] + b : kNegInf;
-  }
+  for (int i = 0; i < EPL; ++i) sel[i] = valid[i] ? s[i] + eb[i] : kNegInf;
 
   // grouped mask: keep the g groups with the largest top-2 sums, zero the rest
   if (a.G > 1 && a.g < a.G) {
@@ -215,6 +220,7 @@ __device__ void route_token(const TopkArgs& a, int t) {
   if (lane < a.k) {
     a.idx[static_cast<int64_t>(t) * a.k + lane] = my_idx;
     a.w[static_cast<int64_t>(t) * a.k + lane] = my_w;
+    if (lds_idx) lds_idx[t * a.k + lane] = my_idx;
   }
 }
 
@@ -362,18 +368,31 @@ __global__ __launch_bounds__(kPermThreads) void k_permute(PermuteArgs a) {
 // them (one launch instead of two on the decode critical path).
 template <int EPL>
 __global__ __launch_bounds__(kPermThreads) void k_route_permute(TopkArgs ta, PermuteArgs a) {
+  // a.nslots <= kFusedSlots <= kPermThreads: thread s owns slot s, whose expert and
+  // rank stay in registers (no round trip through global memory between the phases)
   __shared__ int cnt[1024];
   __shared__ int off[1024];
   __shared__ int wtot[3][16];
   __shared__ int total_s;
+  __shared__ int s_idx[kFusedSlots];
   const int tid = threadIdx.x;
-  for (int t = tid >> 6; t < ta.T; t += kPermThreads / 64) route_token<EPL>(ta, t);
+  for (int t = tid >> 6; t < ta.T; t += kPermThreads / 64) route_token<EPL>(ta, t, s_idx);
   if (tid < a.E) cnt[tid] = 0;
-  __syncthreads();  // routing written by this workgroup is visible to it after the barrier
-  rank_slots(a, 0, a.nslots, cnt);
+  __syncthreads();
+  int e = -1, rank = -1;
+  if (tid < a.nslots) {
+    e = s_idx[tid];
+    if (e >= 0 && e < a.E) rank = atomicAdd(&cnt[e], 1);
+  }
   __syncthreads();
   scan_experts(a, tid < a.E ? cnt[tid] : 0, true, off, wtot, &total_s);
-  scatter_slots(a, 0, a.nslots, off);
+  if (rank >= 0) {
+    const int pos = off[e] + rank;
+    a.perm[pos] = tid;
+    a.slot_pos[tid] = pos;
+  } else if (tid < a.nslots) {
+    a.slot_pos[tid] = -1;
+  }
   for (int q = total_s + tid; q < a.nslots; q += kPermThreads) a.perm[q] = -1;
 }
 
@@ -433,6 +452,7 @@ hipError_t launch_topk(const TopkArgs& a, hipStream_t s) {
 }
 
 hipError_t launch_route_permute(const TopkArgs& t, const PermuteArgs& a, hipStream_t s) {
+  if (a.nslots > kFusedSlots || a.E > kPermThreads) return hipErrorInvalidValue;
   const int epl = (t.E + 63) / 64;
   const dim3 g(1), b(kPermThreads);
   if (epl <= 1)
