@@ -228,3 +228,33 @@ def test_deterministic():
         b = moe.forward(xd, W, moe_cfg(spec))
         torch.cuda.synchronize()
         assert torch.equal(a, b)
+
+
+@pytest.mark.parametrize("cid,T", [(2, 13), (2, 300), (5, 64), (4, 500)])
+def test_graph_replay_matches_eager(cid, T):
+    """The forward captured in a HIP graph (prefill runs the shared expert on a second
+    stream, joined inside the graph) gives the eager result on every replay, with other
+    eager work and synchronisations between the replays."""
+    import mixture_experts_layer_03_amd as moe
+    spec, L, W = layer(cid)
+    x, xd = xs(spec, T)
+    cfg = moe_cfg(spec)
+    log(f"graph replay cfg{cid} T={T}")
+    ws = torch.empty(cfg.workspace_size(T), dtype=torch.uint8, device="cuda")
+    y = torch.empty((T, spec.hidden), dtype=xd.dtype, device="cuda")
+    moe.forward(xd, W, cfg, ws=ws, out=y)  # eager call first (creates the library's second stream)
+    torch.cuda.synchronize()
+    ref = y.clone()
+    stream = torch.cuda.Stream()
+    stream.wait_stream(torch.cuda.current_stream())
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g, stream=stream):
+        moe.forward(xd, W, cfg, ws=ws, out=y)
+    for rep in range(3):
+        y.zero_()
+        noise = torch.randn_like(ref, dtype=torch.float32)  # eager work between replays
+        torch.cuda.synchronize()
+        g.replay()
+        torch.cuda.synchronize()
+        assert torch.equal(y, ref), f"replay {rep}"
+        del noise
