@@ -53,6 +53,13 @@ one named by the Ling-3.0-tiny-8bit-XL-mlx card ("XL Quantization Recipe")
 and by mlxcel #838 "Weight remap" (quant_predicate, group 64, 8 bits),
 written here in scale/zero-point form.
 
+4-bit routed experts (u4) use the same affine form per 64 elements with
+codes q in [0, 15] packed two per byte along each row's reduction axis,
+element 2i in the low nibble of byte i and element 2i+1 in the high nibble.
+The pages run routed experts at 4 bits (Ling-3.0-flash-GGUF card, conversion
+recipe: IQ4_XS; clm-0015 record, structural facts: Q4_K_M) without giving a
+layout; this plain affine int4 layout is a reading, listed with the others.
+
 Stored inputs are converted exactly to fp64 first: arrays of dtype uint16 are
 bf16 bit patterns (bits << 16 gives the fp32 value), float16/32/64 arrays are
 taken as they are.  Nothing is rounded afterwards.
@@ -129,6 +136,23 @@ def dequant_u8(q, scale, zero, group: int = 64) -> np.ndarray:
     qg = q.astype(np.float64).reshape(q.shape[:-1] + (n // group, group))
     w = s[..., None] * (qg - z[..., None])
     return w.reshape(q.shape)
+
+
+def unpack_u4(packed) -> np.ndarray:
+    """Two 4-bit codes per byte along the last axis -> one code per uint8 element:
+    element 2i is the low nibble of byte i, element 2i+1 its high nibble."""
+    p = np.asarray(packed)
+    if p.dtype != np.uint8:
+        raise TypeError("unpack_u4: packed codes must be uint8")
+    q = np.empty(p.shape[:-1] + (2 * p.shape[-1],), dtype=np.uint8)
+    q[..., 0::2] = p & 0x0F
+    q[..., 1::2] = p >> 4
+    return q
+
+
+def dequant_u4(packed, scale, zero, group: int = 64) -> np.ndarray:
+    """u4 affine dequantisation: unpack the nibbles, then w = s * (q - z) per group."""
+    return dequant_u8(unpack_u4(packed), scale, zero, group)
 
 
 # --------------------------------------------------------------------------
@@ -299,6 +323,9 @@ def expert_matrix(weights: dict, name: str, e: int, group: int) -> np.ndarray:
     if name + "_q" in weights:
         return dequant_u8(weights[name + "_q"][e], weights[name + "_scale"][e],
                           weights[name + "_zero"][e], group)
+    if name + "_q4" in weights:
+        return dequant_u4(weights[name + "_q4"][e], weights[name + "_scale"][e],
+                          weights[name + "_zero"][e], group)
     return to_f64(weights[name][e])
 
 
@@ -317,7 +344,7 @@ def forward(x, weights: dict, cfg: OracleConfig, tokens=None, forced_idx=None):
 
     weights keys: router [E,H], router_bias [E] or None, expert_bias [E] or
     None, gate/up [E,I,H] and down [E,H,I] (or gate_q/gate_scale/gate_zero...
-    for u8 experts), shared_gate/shared_up [I_s,H], shared_down [H,I_s] (absent
+    for u8 experts, gate_q4/... with [E,I,H/2] packed codes for u4 experts), shared_gate/shared_up [I_s,H], shared_down [H,I_s] (absent
     or None when there is no shared expert).
 
     tokens: optional list of token rows to evaluate (all when None).

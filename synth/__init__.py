@@ -17,7 +17,10 @@ stream per (layer seed, layer copy, tensor, expert), then encoded):
   * u8 experts  per 64 consecutive elements along a row's reduction axis:
               lo = min(min w, 0), hi = max(max w, 0),
               s = fp16 rounded up of (hi - lo) / 254, z = rint(-lo / s),
-              q = rint(w / s) + z  (always inside [0, 255]), z stored as fp16.
+              q = rint(w / s) + z  (always inside [0, 255]), z stored as fp16;
+  * u4 experts  the same with (hi - lo) / 14 (q inside [0, 15]), codes packed
+              two per byte along the row: element 2i in the low nibble of
+              byte i, element 2i+1 in the high nibble.
 """
 
 from __future__ import annotations
@@ -51,7 +54,7 @@ class LayerSpec:
     use_expert_bias: bool = False
     zipf_skew: float = 0.0            # 0 = no router bias
     act_dtype: str = "bf16"           # "f32" | "bf16"
-    expert_dtype: str = "bf16"        # "f32" | "bf16" | "u8"
+    expert_dtype: str = "bf16"        # "f32" | "bf16" | "u8" | "u4"
     quant_group: int = 64
     tokens: tuple = field(default=(1,))
     weight_std: float = 0.02
@@ -78,6 +81,8 @@ SPECS = {
 }
 # config 5 = config 4's layer with the routed experts stored u8-affine (same seeds)
 SPECS[5] = SPECS[4].variant("ling-3.0-flash-u8", 4, expert_dtype="u8", tokens=(1, 64, 8192))
+# config 4's layer with the routed experts stored as packed int4 affine (decode sizes)
+SPECS[6] = SPECS[4].variant("ling-3.0-flash-u4", 4, expert_dtype="u4", tokens=(1, 64))
 
 
 def _rng(*key) -> np.random.Generator:
@@ -122,6 +127,33 @@ def quantize_u8(w, group: int = 64):
     return (q.astype(np.uint8).reshape(w.shape), s16, z.astype(np.float16))
 
 
+def quantize_u4(w, group: int = 64):
+    """u4 affine encoding of fp32 values along the last axis (see module docstring).
+
+    Returns (packed uint8 [...,n/2], s float16 [...,n/group], z float16 [...,n/group]).
+    """
+    w = np.asarray(w, dtype=np.float32)
+    n = w.shape[-1]
+    if n % group or n % 2:
+        raise ValueError("row length must be a multiple of the quant group")
+    wg = w.reshape(w.shape[:-1] + (n // group, group)).astype(np.float64)
+    lo = np.minimum(wg.min(axis=-1), 0.0)
+    hi = np.maximum(wg.max(axis=-1), 0.0)
+    s64 = (hi - lo) / 14.0
+    s16 = s64.astype(np.float16)
+    up = s16.astype(np.float64) < s64
+    s16[up] = np.nextafter(s16[up], np.float16(np.inf))
+    s16 = np.maximum(s16, np.float16(2.0 ** -14))
+    s = s16.astype(np.float64)
+    z = np.rint(-lo / s)
+    q = (np.rint(wg / s[..., None]) + z[..., None]).reshape(w.shape)
+    if q.min() < 0 or q.max() > 15:
+        raise AssertionError("u4 encoder left [0, 15]")
+    q = q.astype(np.uint8)
+    packed = (q[..., 0::2] | (q[..., 1::2] << 4)).astype(np.uint8)
+    return packed, s16, z.astype(np.float16)
+
+
 def _threads(threads):
     if threads:
         return threads
@@ -143,7 +175,8 @@ def make_layer(spec: LayerSpec, copy: int = 0, threads=None) -> dict:
 
     Keys: router [E,H], router_bias [E] f32 or None, expert_bias [E] f32 or
     None, gate/up [E,I,H] and down [E,H,I] (or gate_q/gate_scale/gate_zero,
-    ... for u8 experts), shared_gate/shared_up [I_s,H], shared_down [H,I_s]
+    ... for u8 experts; gate_q4/... with packed [E,I,H/2] codes for u4 experts),
+    shared_gate/shared_up [I_s,H], shared_down [H,I_s]
     (None when there is no shared expert).
     """
     H, E, I, Is = spec.hidden, spec.num_experts, spec.moe_intermediate, spec.shared_intermediate
@@ -173,16 +206,18 @@ def make_layer(spec: LayerSpec, copy: int = 0, threads=None) -> dict:
                            ("down", _T_DOWN, (H, I))):
         arr = np.empty((E,) + shp, dtype=edt)
         _fill_expert_tensor(spec, copy, tid, shp, arr, E, threads)
-        if spec.expert_dtype == "u8":
-            q = np.empty((E,) + shp, dtype=np.uint8)
+        if spec.expert_dtype in ("u8", "u4"):
+            u4 = spec.expert_dtype == "u4"
+            q = np.empty((E, shp[0], shp[1] // 2 if u4 else shp[1]), dtype=np.uint8)
             s = np.empty((E, shp[0], shp[1] // spec.quant_group), dtype=np.float16)
             z = np.empty_like(s)
+            encode = quantize_u4 if u4 else quantize_u8
 
-            def enc(e, arr=arr, q=q, s=s, z=z):
-                q[e], s[e], z[e] = quantize_u8(bf16_values(arr[e]), spec.quant_group)
+            def enc(e, arr=arr, q=q, s=s, z=z, encode=encode):
+                q[e], s[e], z[e] = encode(bf16_values(arr[e]), spec.quant_group)
             with ThreadPoolExecutor(_threads(threads)) as ex:
                 list(ex.map(enc, range(E)))
-            L[name + "_q"], L[name + "_scale"], L[name + "_zero"] = q, s, z
+            L[name + ("_q4" if u4 else "_q")], L[name + "_scale"], L[name + "_zero"] = q, s, z
             del arr
         else:
             L[name] = arr
@@ -206,7 +241,8 @@ def make_x(spec: LayerSpec, T: int, stream: int = 0) -> np.ndarray:
 def layer_bytes(spec: LayerSpec) -> dict:
     """Stored bytes per routed expert, shared expert and router."""
     H, I, Is, E = spec.hidden, spec.moe_intermediate, spec.shared_intermediate, spec.num_experts
-    bw = {"f32": 4.0, "bf16": 2.0, "u8": 1.0 + 4.0 / spec.quant_group}[spec.expert_dtype]
+    bw = {"f32": 4.0, "bf16": 2.0, "u8": 1.0 + 4.0 / spec.quant_group,
+          "u4": 0.5 + 4.0 / spec.quant_group}[spec.expert_dtype]
     ba = 4.0 if spec.act_dtype == "f32" else 2.0
     return dict(expert=3 * I * H * bw, shared=3 * Is * H * ba, router=E * H * ba,
                 act=ba)

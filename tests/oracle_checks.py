@@ -363,7 +363,32 @@ def check_dequant(om):
     assert om.to_f64(bits).tolist() == [1.0, -2.0, 0.25, 0.0]
 
 
+# ------------------------------------------------------------- P14 u4 dequant
+def check_dequant_u4(om):
+    import synth
+    # hand-decoded bytes: 0x21 -> codes 1 (low nibble, element 0), 2 (element 1);
+    # 0xF0 -> 0, 15.  Group of 4, s = 0.5, z = 1: w = 0.5 * (q - 1)
+    p = np.array([[0x21, 0xF0]], dtype=np.uint8)
+    w = om.dequant_u4(p, np.array([[0.5]], dtype=np.float16), np.array([[1.0]], dtype=np.float16), 4)
+    assert w.tolist() == [[0.0, 0.5, -0.5, 7.0]]
+    # packing written out here independently: equals the u8 definition on the codes
+    rng = np.random.default_rng(31)
+    q = rng.integers(0, 16, size=(3, 128)).astype(np.uint8)
+    packed = (q[:, 0::2] | (q[:, 1::2] << 4)).astype(np.uint8)
+    s = (rng.random((3, 2)) * 0.01 + 1e-4).astype(np.float16)
+    z = rng.integers(0, 16, size=(3, 2)).astype(np.float16)
+    assert np.array_equal(om.dequant_u4(packed, s, z, 64), om.dequant_u8(q, s, z, 64))
+    # the synthetic encoder's codes decode to within half a step of the input
+    wv = rng.standard_normal((4, 256)).astype(np.float32) * 0.02
+    pk, sc, zp = synth.quantize_u4(wv, 64)
+    err = np.abs(om.dequant_u4(pk, sc, zp, 64) - wv.astype(np.float64)).reshape(4, 4, 64)
+    assert (err <= sc.astype(np.float64)[..., None] * 0.5 * (1 + 1e-6)).all()
+    # a routed expert stored packed is read through the u4 decoder
+    W = {"gate_q4": pk[None], "gate_scale": sc[None], "gate_zero": zp[None]}
+    assert np.array_equal(om.expert_matrix(W, "gate", 0, 64), om.dequant_u4(pk, sc, zp, 64))
+
+
 ALL_CHECKS = [check_logits, check_scores, check_plain_topk, check_bruteforce,
               check_bias_semantics, check_group_score_reading, check_zero_mask,
               check_renorm_scale, check_swiglu, check_hand_example, check_dense_mixture,
-              check_combine_invariants, check_dequant]
+              check_combine_invariants, check_dequant, check_dequant_u4]

@@ -38,8 +38,18 @@ def _m6_weighted_shared(mp):       # shared expert weighted by a routing weight
     mp.setattr(om, "combine", bad)
 
 
+def _m7_nibble_order(mp):          # u4: high nibble taken as the even element
+    def bad(packed):
+        p = np.asarray(packed)
+        q = np.empty(p.shape[:-1] + (2 * p.shape[-1],), dtype=np.uint8)
+        q[..., 0::2] = p >> 4
+        q[..., 1::2] = p & 0x0F
+        return q
+    mp.setattr(om, "unpack_u4", bad)
+
+
 MUTANTS = [_m1_bias_in_weights, _m2_renorm_unguarded, _m3_no_scaling, _m4_neg_inf_mask,
-           _m5_group_max, _m6_weighted_shared]
+           _m5_group_max, _m6_weighted_shared, _m7_nibble_order]
 
 
 @pytest.mark.parametrize("mutant", MUTANTS, ids=lambda f: f.__name__)
