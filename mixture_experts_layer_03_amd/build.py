@@ -44,12 +44,28 @@ def _compile(src: str) -> str:
     return obj
 
 
+def _check_isa(src: str) -> list:
+    """Device assembly of one source through the inline-asm wait-state check."""
+    from mixture_experts_layer_03_amd import isa_check
+    cmd = [hipcc(), *HIPCC_FLAGS, "--cuda-device-only", "-S", src, "-o", "-"]
+    r = subprocess.run(cmd, capture_output=True, text=True)
+    if r.returncode != 0:
+        raise RuntimeError(f"hipcc -S failed for {src}:\n{r.stderr[-8000:]}")
+    return isa_check.check(r.stdout)
+
+
 def build(verbose: bool = False) -> str:
-    """Compile every source (always) and link the shared library; returns its path."""
+    """Compile every source (always), check the wait states around the inline-asm
+    copies in the device assembly, and link the shared library; returns its path."""
     os.makedirs(BUILD_DIR, exist_ok=True)
     srcs = sorted(os.path.join(CSRC, f) for f in os.listdir(CSRC) if f.endswith(".hip"))
-    with ThreadPoolExecutor(max(1, min(len(srcs), os.cpu_count() or 1))) as ex:
-        objs = list(ex.map(_compile, srcs))
+    with ThreadPoolExecutor(max(1, min(2 * len(srcs), os.cpu_count() or 1))) as ex:
+        objs = ex.map(_compile, srcs)
+        isa = ex.map(_check_isa, srcs)
+        objs, isa = list(objs), list(isa)
+    bad = [v for vs in isa for v in vs]
+    if bad:
+        raise RuntimeError("wait-state check of the inline-asm copies failed:\n" + "\n".join(bad[:40]))
     tmp = OUT + ".tmp"
     cmd = [hipcc(), f"--offload-arch={ARCH}", "-shared", "-fPIC", *objs, "-o", tmp]
     r = subprocess.run(cmd, capture_output=True, text=True)

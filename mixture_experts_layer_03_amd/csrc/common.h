@@ -118,23 +118,35 @@ __device__ __forceinline__ uint4 ld_stream(const void* p) {
 
 // ---- direct global -> LDS copies (global_load_lds_dwordx4), issued from inline asm so
 // the compiler's wait insertion does not track (and drain) them; users wait explicitly.
+// The compiler's hazard recognizer does not look inside inline asm, so each block keeps
+// the CDNA wait-state rules itself:
+//  * a VMEM instruction reading an SGPR needs 5 wait states after a VALU write of it
+//    (e.g. v_readlane restoring a spilled base); the base is therefore first copied by
+//    s_mov_b64, an SALU read, which the hardware orders after any VALU write, and the
+//    load reads the copy;
+//  * a global load to LDS needs 1 wait state after an SALU write of M0 (the compiler
+//    writes M0 right before the block): the s_mov_b64, or an s_nop, provides it.
 // 16 bytes per lane from global memory to LDS at M0 + 16 * lane (M0 wave-uniform)
 __device__ __forceinline__ void copy_to_lds(const void* src, const uint16_t* lds_dst) {
   const uint32_t m0 =
       static_cast<uint32_t>(reinterpret_cast<uintptr_t>((const __attribute__((address_space(3))) void*)lds_dst));
-  asm volatile("global_load_lds_dwordx4 %0, off" ::"v"(src), "{m0}"(m0) : "memory");
+  asm volatile("s_nop 0\n\tglobal_load_lds_dwordx4 %0, off" ::"v"(src), "{m0}"(m0) : "memory");
 }
 // the same from a wave-uniform base plus a per-lane 32-bit byte offset
 __device__ __forceinline__ void copy_to_lds(const char* base, uint32_t off, const uint16_t* lds_dst) {
   const uint32_t m0 =
       static_cast<uint32_t>(reinterpret_cast<uintptr_t>((const __attribute__((address_space(3))) void*)lds_dst));
-  asm volatile("global_load_lds_dwordx4 %0, %1" ::"v"(off), "s"(base), "{m0}"(m0) : "memory");
+  const char* b;
+  asm volatile("s_mov_b64 %0, %2\n\tglobal_load_lds_dwordx4 %1, %0"
+               : "=&s"(b)
+               : "v"(off), "s"(base), "{m0}"(m0)
+               : "memory");
 }
 // 4 bytes per lane to LDS at M0 + 4 * lane (M0 wave-uniform)
 __device__ __forceinline__ void copy4_to_lds(const void* src, const void* lds_dst) {
   const uint32_t m0 =
       static_cast<uint32_t>(reinterpret_cast<uintptr_t>((const __attribute__((address_space(3))) void*)lds_dst));
-  asm volatile("global_load_lds_dword %0, off" ::"v"(src), "{m0}"(m0) : "memory");
+  asm volatile("s_nop 0\n\tglobal_load_lds_dword %0, off" ::"v"(src), "{m0}"(m0) : "memory");
 }
 // a pointer known to be the same in every lane, kept in scalar registers
 __device__ __forceinline__ const char* uniform_ptr(const void* p) {
