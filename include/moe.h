@@ -63,8 +63,13 @@ typedef enum { MOE_SCORE_SOFTMAX = 0, MOE_SCORE_SIGMOID = 1 } moe_score_fn;
 typedef enum {
   MOE_DT_F32 = 0,      /* IEEE fp32                                                  */
   MOE_DT_BF16 = 1,     /* bfloat16                                                    */
-  MOE_DT_U8_AFFINE = 2 /* u8 code q + fp16 scale s + fp16 zero z per quant_group      */
-                       /* consecutive elements of a row's reduction axis; w = s(q - z) */
+  MOE_DT_U8_AFFINE = 2, /* u8 code q + fp16 scale s + fp16 zero z per quant_group     */
+                        /* consecutive elements of a row's reduction axis; w = s(q - z) */
+  MOE_DT_U4_AFFINE = 3  /* the same with 4-bit codes q in [0, 15], two per byte along  */
+                        /* the row: element 2i in the low nibble of byte i, 2i+1 in the */
+                        /* high nibble.  Routed experts only; always runs the weight-   */
+                        /* streaming path [4-bit routed experts: Ling-3.0-flash-GGUF     */
+                        /* card, conversion recipe; the packing is not on the pages]     */
 } moe_dtype;
 
 typedef enum {
@@ -90,9 +95,9 @@ typedef struct {
   float routed_scaling_factor; /* always applied (default 1.0)                         */
   int32_t act_dtype;           /* x and y: MOE_DT_F32 or MOE_DT_BF16                   */
   int32_t router_dtype;        /* router weight: must equal act_dtype                  */
-  int32_t expert_dtype;        /* routed experts: act_dtype, or U8_AFFINE with bf16 x  */
+  int32_t expert_dtype;        /* routed experts: act_dtype, or U8/U4_AFFINE with bf16 x */
   int32_t shared_dtype;        /* shared expert: must equal act_dtype                  */
-  int64_t quant_group;         /* 64 when expert_dtype == MOE_DT_U8_AFFINE             */
+  int64_t quant_group;         /* 64 when expert_dtype is U8_AFFINE or U4_AFFINE       */
   int32_t path;                /* moe_path (default AUTO)                              */
 } moe_config;
 
@@ -102,9 +107,11 @@ typedef struct {
  *   router_bias  [E] fp32, nullable: added to the logits (the router's own bias)
  *   expert_bias  [E] fp32, the selection-only correction bias; required iff
  *                use_expert_bias
- *   gate, up     [E, I, H]; down [E, H, I]: expert_dtype (u8 codes when quantised)
+ *   gate, up     [E, I, H]; down [E, H, I]: expert_dtype (u8 codes when U8_AFFINE;
+ *                packed u4 codes, [E, I, H/2] and [E, H, I/2] bytes, when U4_AFFINE)
  *   *_scale, *_zero  fp16 [E, I, H/quant_group] (gate, up) / [E, H, I/quant_group]
- *                (down); required iff expert_dtype == MOE_DT_U8_AFFINE, else ignored
+ *                (down); required iff expert_dtype is U8_AFFINE or U4_AFFINE (then
+ *                4-byte aligned for U4_AFFINE), else ignored
  *   shared_gate, shared_up [I_s, H]; shared_down [H, I_s]: shared_dtype; required
  *                iff shared_intermediate > 0                                        */
 typedef struct {
@@ -137,9 +144,10 @@ moe_status moe_config_default(moe_config* cfg);
  *   E / G >= 2 (a group score needs two members), k <= g * E / G;
  *   score_function in {softmax, sigmoid}; routed_scaling_factor finite and > 0;
  *   flags in {0, 1}; dtype combination as documented in moe_config;
- *   quant_group == 64 for u8 experts.                 -> MOE_EINVAL_CONFIG
+ *   quant_group == 64 for u8 and u4 experts.          -> MOE_EINVAL_CONFIG
  * Valid layers the kernels do not cover -> MOE_EUNSUPPORTED: H, I, I_s not
- * multiples of 64; G > 64; forced PREFILL path with fp32 activations.
+ * multiples of 64; G > 64; forced PREFILL path with fp32 activations; u4 experts
+ * with H or I not multiples of 128, or with a forced PREFILL path.
  * Runs on the host only; needs no GPU.                                             */
 moe_status moe_validate_config(const moe_config* cfg);
 

@@ -15,7 +15,7 @@ LIB_PATH = os.path.join(HERE, "libmoe_mi355x.so")
 MOE_OK, MOE_EINVAL_CONFIG, MOE_EINVAL_ARG, MOE_EWORKSPACE, MOE_EUNSUPPORTED, MOE_EHIP = range(6)
 STATUS_NAMES = {0: "MOE_OK", 1: "MOE_EINVAL_CONFIG", 2: "MOE_EINVAL_ARG", 3: "MOE_EWORKSPACE",
                 4: "MOE_EUNSUPPORTED", 5: "MOE_EHIP"}
-DT_F32, DT_BF16, DT_U8_AFFINE = 0, 1, 2
+DT_F32, DT_BF16, DT_U8_AFFINE, DT_U4_AFFINE = 0, 1, 2, 3
 SCORE_SOFTMAX, SCORE_SIGMOID = 0, 1
 PATH_AUTO, PATH_DECODE, PATH_PREFILL = 0, 1, 2
 STAGES = {"router": 1, "topk": 2, "permute": 4, "up": 8, "down": 16, "shared_up": 32,

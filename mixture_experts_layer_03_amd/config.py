@@ -18,7 +18,7 @@ from dataclasses import dataclass, fields
 
 from . import _lib
 
-_DT = {"f32": _lib.DT_F32, "bf16": _lib.DT_BF16, "u8": _lib.DT_U8_AFFINE}
+_DT = {"f32": _lib.DT_F32, "bf16": _lib.DT_BF16, "u8": _lib.DT_U8_AFFINE, "u4": _lib.DT_U4_AFFINE}
 _SCORE = {"softmax": _lib.SCORE_SOFTMAX, "sigmoid": _lib.SCORE_SIGMOID}
 _PATH = {"auto": _lib.PATH_AUTO, "decode": _lib.PATH_DECODE, "prefill": _lib.PATH_PREFILL}
 
@@ -37,7 +37,7 @@ class MoEConfig:
     use_expert_bias: bool = False
     routed_scaling_factor: float = 1.0
     act_dtype: str = "bf16"        # x, y, router, shared expert: "bf16" | "f32"
-    expert_dtype: str = "bf16"     # routed experts: act_dtype or "u8" (affine, group 64)
+    expert_dtype: str = "bf16"     # routed experts: act_dtype, "u8" or "u4" (affine, group 64)
     quant_group: int = 64
     path: str = "auto"             # "auto" | "decode" | "prefill"
 

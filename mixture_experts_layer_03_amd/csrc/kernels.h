@@ -7,7 +7,7 @@
 namespace moe {
 
 enum class Act { F32 = 0, BF16 = 1 };
-enum class WFmt { F32 = 0, BF16 = 1, U8 = 2 };
+enum class WFmt { F32 = 0, BF16 = 1, U8 = 2, U4 = 3 };
 
 // ------------------------------------------------------------------ routing
 struct TopkArgs {

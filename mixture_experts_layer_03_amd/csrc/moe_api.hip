@@ -76,21 +76,32 @@ moe_status check_config(const moe_config* c) {
     return fail(MOE_EINVAL_CONFIG, "act_dtype=%d must be F32 or BF16", c->act_dtype);
   if (c->router_dtype != c->act_dtype) return fail(MOE_EINVAL_CONFIG, "router_dtype must equal act_dtype");
   if (c->shared_dtype != c->act_dtype) return fail(MOE_EINVAL_CONFIG, "shared_dtype must equal act_dtype");
-  if (c->expert_dtype != c->act_dtype && !(c->expert_dtype == MOE_DT_U8_AFFINE && c->act_dtype == MOE_DT_BF16))
-    return fail(MOE_EINVAL_CONFIG, "expert_dtype=%d must equal act_dtype or be U8_AFFINE with BF16 activations", c->expert_dtype);
-  if (c->expert_dtype == MOE_DT_U8_AFFINE && c->quant_group != 64)
-    return fail(MOE_EINVAL_CONFIG, "quant_group=%lld must be 64 for U8_AFFINE experts", (long long)c->quant_group);
+  const bool quantised = c->expert_dtype == MOE_DT_U8_AFFINE || c->expert_dtype == MOE_DT_U4_AFFINE;
+  if (c->expert_dtype != c->act_dtype && !(quantised && c->act_dtype == MOE_DT_BF16))
+    return fail(MOE_EINVAL_CONFIG, "expert_dtype=%d must equal act_dtype or be U8_AFFINE/U4_AFFINE with BF16 activations", c->expert_dtype);
+  if (quantised && c->quant_group != 64)
+    return fail(MOE_EINVAL_CONFIG, "quant_group=%lld must be 64 for quantised experts", (long long)c->quant_group);
   if (c->path < MOE_PATH_AUTO || c->path > MOE_PATH_PREFILL) return fail(MOE_EINVAL_CONFIG, "path=%d unknown", c->path);
   // valid, but outside what the gfx950 kernels implement
   if (c->hidden % 64 || c->moe_intermediate % 64 || c->shared_intermediate % 64)
     return fail(MOE_EUNSUPPORTED, "hidden, moe_intermediate and shared_intermediate must be multiples of 64");
   if (c->n_group > kMaxGroupsGpu) return fail(MOE_EUNSUPPORTED, "n_group=%lld > %lld", (long long)c->n_group, (long long)kMaxGroupsGpu);
+  if (c->expert_dtype == MOE_DT_U4_AFFINE && (c->hidden % 128 || c->moe_intermediate % 128))
+    return fail(MOE_EUNSUPPORTED, "u4 experts need hidden and moe_intermediate multiples of 128");
+  if (c->expert_dtype == MOE_DT_U4_AFFINE && c->path == MOE_PATH_PREFILL)
+    return fail(MOE_EUNSUPPORTED, "u4 experts run the weight-streaming path only (path must be AUTO or DECODE)");
   if (c->path == MOE_PATH_PREFILL && c->act_dtype == MOE_DT_F32)
     return fail(MOE_EUNSUPPORTED, "the tiled MFMA path needs BF16 activations");
   return MOE_OK;
 }
 
 size_t align256(size_t v) { return (v + 255) & ~size_t(255); }
+
+WFmt expert_fmt(const moe_config& c, Act act) {
+  if (c.expert_dtype == MOE_DT_U8_AFFINE) return WFmt::U8;
+  if (c.expert_dtype == MOE_DT_U4_AFFINE) return WFmt::U4;
+  return act == Act::F32 ? WFmt::F32 : WFmt::BF16;
+}
 
 struct Plan {
   bool decode;
@@ -121,7 +132,7 @@ int router_ksplit(const moe_config& c, int64_t T) {
 }
 
 void make_plan(const moe_config& c, int64_t T, Plan& p) {
-  p.decode = c.path == MOE_PATH_DECODE ||
+  p.decode = c.path == MOE_PATH_DECODE || c.expert_dtype == MOE_DT_U4_AFFINE ||
              (c.path == MOE_PATH_AUTO && (T <= kDecodeMaxT || c.act_dtype == MOE_DT_F32));
   const int64_t H = c.hidden, E = c.num_experts, k = c.top_k, I = c.moe_intermediate, Is = c.shared_intermediate;
   const size_t ab = c.act_dtype == MOE_DT_F32 ? 4 : 2;
@@ -253,6 +264,10 @@ moe_status check_ws(const moe_config& c, int64_t T, void* ws, size_t ws_bytes, P
     if (T * c.top_k * kmax * 2 >= (int64_t(1) << 32))
       return fail(MOE_EUNSUPPORTED, "T * top_k * max(hidden, intermediate) * 2 bytes >= 2^32 on the tiled path; split the batch");
   }
+  if (c.expert_dtype == MOE_DT_U4_AFFINE &&
+      (T * c.hidden * 2 >= (int64_t(1) << 31) || T * c.top_k * c.moe_intermediate * 2 >= (int64_t(1) << 31) ||
+       T * c.shared_intermediate * 2 >= (int64_t(1) << 31)))
+    return fail(MOE_EUNSUPPORTED, "u4 experts: T too large for one call (activations above 2 GB); split the batch");
   if (ws_bytes < p.total) return fail(MOE_EWORKSPACE, "workspace of %zu bytes < %zu required", ws_bytes, p.total);
   if (p.total > 0 && (!ws || !aligned(ws, 256))) return fail(MOE_EWORKSPACE, "workspace must be non-null and 256-byte aligned");
   return MOE_OK;
@@ -369,7 +384,7 @@ moe_status run_experts(const moe_config& c, const Plan& p, int64_t T, const void
                        const int32_t* idx, const float* topk_w, void* y, void* ws, hipStream_t s,
                        bool permuted = false, hipEvent_t shared_join = nullptr) {
   const Act act = c.act_dtype == MOE_DT_F32 ? Act::F32 : Act::BF16;
-  const WFmt wf = c.expert_dtype == MOE_DT_U8_AFFINE ? WFmt::U8 : (act == Act::F32 ? WFmt::F32 : WFmt::BF16);
+  const WFmt wf = expert_fmt(c, act);
   const int Ti = static_cast<int>(T), H = static_cast<int>(c.hidden), I = static_cast<int>(c.moe_intermediate),
             Is = static_cast<int>(c.shared_intermediate), k = static_cast<int>(c.top_k), E = static_cast<int>(c.num_experts);
   int32_t* counts = at<int32_t>(ws, p.o_counts);
@@ -541,7 +556,7 @@ moe_status run_experts(const moe_config& c, const Plan& p, int64_t T, const void
 moe_status run_shared(const moe_config& c, const Plan& p, int64_t T, const void* x, const moe_weights* w, void* ws,
                       hipStream_t s) {
   const Act act = c.act_dtype == MOE_DT_F32 ? Act::F32 : Act::BF16;
-  const WFmt wf = c.expert_dtype == MOE_DT_U8_AFFINE ? WFmt::U8 : (act == Act::F32 ? WFmt::F32 : WFmt::BF16);
+  const WFmt wf = expert_fmt(c, act);
   const int Ti = static_cast<int>(T), H = static_cast<int>(c.hidden), I = static_cast<int>(c.moe_intermediate),
             Is = static_cast<int>(c.shared_intermediate), k = static_cast<int>(c.top_k), E = static_cast<int>(c.num_experts);
   void* hs = at<void>(ws, p.o_hs);
@@ -599,13 +614,15 @@ moe_status check_weights(const moe_config& c, const moe_weights* w, bool need_ro
   REQUIRE_PTR(w->gate, 16, "weights.gate");
   REQUIRE_PTR(w->up, 16, "weights.up");
   REQUIRE_PTR(w->down, 16, "weights.down");
-  if (c.expert_dtype == MOE_DT_U8_AFFINE) {
-    REQUIRE_PTR(w->gate_scale, 2, "weights.gate_scale");
-    REQUIRE_PTR(w->gate_zero, 2, "weights.gate_zero");
-    REQUIRE_PTR(w->up_scale, 2, "weights.up_scale");
-    REQUIRE_PTR(w->up_zero, 2, "weights.up_zero");
-    REQUIRE_PTR(w->down_scale, 2, "weights.down_scale");
-    REQUIRE_PTR(w->down_zero, 2, "weights.down_zero");
+  if (c.expert_dtype == MOE_DT_U8_AFFINE || c.expert_dtype == MOE_DT_U4_AFFINE) {
+    // u4: the kernels copy two fp16 group parameters at a time
+    const int al = c.expert_dtype == MOE_DT_U4_AFFINE ? 4 : 2;
+    REQUIRE_PTR(w->gate_scale, al, "weights.gate_scale");
+    REQUIRE_PTR(w->gate_zero, al, "weights.gate_zero");
+    REQUIRE_PTR(w->up_scale, al, "weights.up_scale");
+    REQUIRE_PTR(w->up_zero, al, "weights.up_zero");
+    REQUIRE_PTR(w->down_scale, al, "weights.down_scale");
+    REQUIRE_PTR(w->down_zero, al, "weights.down_zero");
   }
   if (c.shared_intermediate > 0) {
     REQUIRE_PTR(w->shared_gate, 16, "weights.shared_gate");

@@ -921,6 +921,156 @@ __device__ __forceinline__ void ring_stream_u8(const char* const (&wbase)[NMAT],
   copy_wait<0>();
 }
 
+// ----------------------------------------------------- u4 weights through LDS rings
+// One ring step again covers 128 elements of K (two quantisation groups); a weight row's
+// codes for the step are 64 bytes, so one copy instruction moves all 16 rows of a
+// matrix.  Slot layout (bytes): NMAT x 16 code rows of 64 B (16-byte chunks XOR-swizzled
+// by (row / 4) % 4, which keeps the per-lane 4-byte fragment reads free of bank
+// conflicts), TR token rows of 256 B (the step's 128 elements, chunks swizzled by the
+// row), then the 256 B of group parameters laid out as for u8.  Only TR = 4, 8 or 16
+// token rows are copied, the fewest that hold the chunk's live tokens; MFMA rows beyond
+// TR reread row r % TR and their results are dropped.
+//
+// Dequantisation without per-element conversions: the bf16 pattern 0x4300 | q is the
+// exact value 128 + q, so a code dword turns into four bf16 pairs with one mask-and-or
+// each.  Taking elements (j, j + 4) into pair j fixes the order of the lane's 8 K values
+// as 0 4 1 5 2 6 3 7; the token fragment is permuted the same way, which leaves the dot
+// product unchanged.  Per group, sum_k a_k (q_k - z) = sum_k a_k (128 + q_k)
+// - (128 + z) sum_k a_k, with sum_k a_k from one more MFMA against ones.
+template <int NMAT, int TR>
+struct RingGeomU4 {
+  static constexpr int W_BYTES = NMAT * 16 * 64;
+  static constexpr int A_BYTES = TR * 256;
+  static constexpr int SLOT_BYTES = W_BYTES + A_BYTES + 256;
+  static constexpr int CPS = NMAT + TR / 4 + 1;  // copy instructions per step
+};
+constexpr int kU4MaxSlot = RingGeomU4<2, 16>::SLOT_BYTES;
+
+// code dword (8 nibbles, element j at bits 4j) -> bf16 pairs (128 + q_j, 128 + q_{j+4})
+__device__ __forceinline__ uint4 nibbles_biased(uint32_t w) {
+  constexpr uint32_t kMask = 0x000f000fu, kBias = 0x43004300u;
+  return make_uint4((w & kMask) | kBias, ((w >> 4) & kMask) | kBias, ((w >> 8) & kMask) | kBias,
+                    ((w >> 12) & kMask) | kBias);
+}
+
+// token fragment (a0 a1 | a2 a3 | a4 a5 | a6 a7) -> (a0 a4 | a1 a5 | a2 a6 | a3 a7)
+__device__ __forceinline__ uint4 pair_j_j4(uint4 a) {
+  return make_uint4((a.x & 0xffffu) | (a.z << 16), (a.x >> 16) | (a.z & 0xffff0000u), (a.y & 0xffffu) | (a.w << 16),
+                    (a.y >> 16) | (a.w & 0xffff0000u));
+}
+
+// lane's code-row offset for the u4 ring: row l / 4 of the 16, logical chunk
+// (l % 4) ^ (row / 4) % 4; rows `row_bytes` apart
+__device__ __forceinline__ uint32_t u4_code_off(int row_bytes) {
+  const int lane = lane_id();
+  const int row = lane >> 2;
+  return static_cast<uint32_t>(row * row_bytes + (((lane & 3) ^ ((row >> 2) & 3)) << 4));
+}
+
+// acc[m] += tokens x dequant(W_m)^T over [k0, k1) (multiples of 128), with a ring of as
+// many steps (at most 8) as RB bytes hold: fewer token rows leave room for more steps in
+// flight.  wbase[m]: wave-uniform byte address of code row 0 of matrix m; woff: this
+// lane's offset (u4_code_off).  abase / aoff[i]: token rows of copy i (rows 4i + l/16;
+// row byte offset plus 16 x logical chunk (l % 16) ^ row).  sz_src: as for the u8 ring.
+template <int NMAT, int RB, int TR>
+__device__ __forceinline__ void ring_stream_u4(const char* const (&wbase)[NMAT], uint32_t woff, const char* abase,
+                                               const uint32_t (&aoff)[TR / 4], const uint16_t* sz_src, int k0,
+                                               int k1, char* ring, f32x4 (&acc)[NMAT]) {
+  using G = RingGeomU4<NMAT, TR>;
+  constexpr int U = RB / G::SLOT_BYTES < 8 ? RB / G::SLOT_BYTES : 8;
+  static_assert(U >= 2, "ring too small");
+  const int lane = lane_id();
+  const int n = (k1 - k0) >> 7;
+  auto issue = [&](int slot, int step) {
+    char* sl = ring + slot * G::SLOT_BYTES;
+    const int kc = k0 + 128 * step;
+#pragma unroll
+    for (int m = 0; m < NMAT; ++m)
+      copy_to_lds(uniform_ptr(wbase[m] + (kc >> 1)), woff, reinterpret_cast<uint16_t*>(sl + m * 1024));
+#pragma unroll
+    for (int i = 0; i < TR / 4; ++i)
+      copy_to_lds(uniform_ptr(abase + kc * 2), aoff[i], reinterpret_cast<uint16_t*>(sl + G::W_BYTES + i * 1024));
+    copy4_to_lds(sz_src + (kc >> 6), sl + G::W_BYTES + G::A_BYTES);
+  };
+  const int r = lane & 15, q = lane >> 4;
+  const int tr = r & (TR - 1);
+  const uint4 ones = make_uint4(0x3f803f80u, 0x3f803f80u, 0x3f803f80u, 0x3f803f80u);
+  auto compute = [&](int slot) {
+    const char* sl = ring + slot * G::SLOT_BYTES;
+    const uint32_t* szp = reinterpret_cast<const uint32_t*>(sl + G::W_BYTES + G::A_BYTES);
+#pragma unroll
+    for (int g = 0; g < 2; ++g) {
+      f32x4 part[NMAT];
+      f32x4 asum = {0.f, 0.f, 0.f, 0.f};
+      float zf[NMAT], sf[NMAT];
+#pragma unroll
+      for (int m = 0; m < NMAT; ++m) {
+        part[m] = f32x4{0.f, 0.f, 0.f, 0.f};
+        const uint32_t sv = szp[m * 32 + r], zv = szp[m * 32 + 16 + r];
+        sf[m] = f16_to_f32(static_cast<uint16_t>(g ? sv >> 16 : sv & 0xffffu));
+        zf[m] = 128.f + f16_to_f32(static_cast<uint16_t>(g ? zv >> 16 : zv & 0xffffu));
+      }
+#pragma unroll
+      for (int ks = 0; ks < 2; ++ks) {
+        const int c = 8 * g + 4 * ks + q;  // 16-byte chunk of the 256-byte token row
+        const uint4 av = *reinterpret_cast<const uint4*>(sl + G::W_BYTES + tr * 256 + ((c ^ tr) << 4));
+        asum = mfma16_bf16(av, ones, asum);
+        const uint4 ap = pair_j_j4(av);
+        const int cw = 2 * g + ks;  // 16-byte chunk of the code row holding elements 32 cw ..
+#pragma unroll
+        for (int m = 0; m < NMAT; ++m) {
+          const uint32_t cv =
+              *reinterpret_cast<const uint32_t*>(sl + m * 1024 + r * 64 + ((cw ^ ((r >> 2) & 3)) << 4) + 4 * q);
+          part[m] = mfma16_bf16(ap, nibbles_biased(cv), part[m]);
+        }
+      }
+#pragma unroll
+      for (int m = 0; m < NMAT; ++m) acc[m] += sf[m] * (part[m] - zf[m] * asum);
+    }
+  };
+#pragma unroll
+  for (int p = 0; p < U - 1; ++p)
+    if (p < n) issue(p, p);
+  int cur = 0, nxt = U - 1;
+  for (int t = 0; t < n; ++t) {
+    copy_wait_ahead<G::CPS, U - 2>(n - 1 - t);
+    if (t + U - 1 < n) issue(nxt, t + U - 1);
+    compute(cur);
+    cur = cur + 1 == U ? 0 : cur + 1;
+    nxt = nxt + 1 == U ? 0 : nxt + 1;
+  }
+  copy_wait<0>();
+}
+
+// token-row copies of the u4 ring for the TR rows of a 16-token chunk: copy i, lane l
+// brings row j = 4i + l/16 (the chunk's token min(j, ntok - 1), whose byte offset in the
+// activation rows `row_of` gives), logical chunk (l % 16) ^ j
+template <int TR, typename F>
+__device__ __forceinline__ void u4_token_offsets(int ntok, F row_off, uint32_t (&aoff)[TR / 4]) {
+  const int lane = lane_id();
+#pragma unroll
+  for (int i = 0; i < TR / 4; ++i) {
+    const int j = 4 * i + (lane >> 4);
+    aoff[i] = row_off(min(j, ntok - 1)) + static_cast<uint32_t>(((lane & 15) ^ j) << 4);
+  }
+}
+
+template <int N>
+struct IntC {
+  static constexpr int value = N;
+};
+
+// calls f(IntC<TR>) with the fewest token rows (4, 8 or 16) covering ntok
+template <typename F>
+__device__ __forceinline__ void with_token_rows(int ntok, F f) {
+  if (ntok <= 4)
+    f(IntC<4>{});
+  else if (ntok <= 8)
+    f(IntC<8>{});
+  else
+    f(IntC<16>{});
+}
+
 // [k0, k1) of part `part` of `parts`, in 128-element units
 __device__ __forceinline__ void unit_range128(int K, int part, int parts, int& k0, int& k1) {
   const int U = K >> 7;
@@ -940,11 +1090,12 @@ __device__ __forceinline__ const uint16_t* u8_param_row(const uint16_t* const (&
   return base + (row0 + (lane & 15)) * (K / 64);
 }
 
-template <int U, int NWK>
-__global__ __launch_bounds__(256) void k_stream_up_u8(SkinnyUpArgs a) {
-  using G = RingGeomU8<2>;
+// quantised routed experts (BITS = 8: u8 ring, 4: u4 ring); shared items stream bf16
+template <int BITS, int U, int NWK>
+__global__ __launch_bounds__(256) void k_stream_up_q(SkinnyUpArgs a) {
+  constexpr int QSLOT = BITS == 8 ? RingGeomU8<2>::SLOT_BYTES : kU4MaxSlot;
   using GB = RingGeom<2>;
-  constexpr int SLOTB = G::SLOT_BYTES > GB::SLOT * 2 ? G::SLOT_BYTES : GB::SLOT * 2;
+  constexpr int SLOTB = QSLOT > GB::SLOT * 2 ? QSLOT : GB::SLOT * 2;
   constexpr int IPB = 4 / NWK;
   __shared__ __attribute__((aligned(16))) char rings[4 * U * SLOTB];
   const int lane = lane_id(), w = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
@@ -998,13 +1149,27 @@ __global__ __launch_bounds__(256) void k_stream_up_u8(SkinnyUpArgs a) {
       f32x4 acc[2] = {f32x4{0.f, 0.f, 0.f, 0.f}, f32x4{0.f, 0.f, 0.f, 0.f}};
       if (live) {
         if (!shared) {
-          const char* wb[2] = {uniform_ptr(static_cast<const uint8_t*>(a.gate) + ro * a.H),
-                               uniform_ptr(static_cast<const uint8_t*>(a.up) + ro * a.H)};
-          const uint32_t woff[2] = {static_cast<uint32_t>(rr * a.H + ch * 16),
-                                    static_cast<uint32_t>((8 + rr) * a.H + ch * 16)};
           const uint16_t* ss[2] = {a.gate_s, a.up_s};
           const uint16_t* zz[2] = {a.gate_z, a.up_z};
-          ring_stream_u8<2, U>(wb, woff, xb, aoff, u8_param_row<2>(ss, zz, ro, a.H), k0, k1, ring, acc);
+          const uint16_t* szs = u8_param_row<2>(ss, zz, ro, a.H);
+          if constexpr (BITS == 8) {
+            const char* wb[2] = {uniform_ptr(static_cast<const uint8_t*>(a.gate) + ro * a.H),
+                                 uniform_ptr(static_cast<const uint8_t*>(a.up) + ro * a.H)};
+            const uint32_t woff[2] = {static_cast<uint32_t>(rr * a.H + ch * 16),
+                                      static_cast<uint32_t>((8 + rr) * a.H + ch * 16)};
+            ring_stream_u8<2, U>(wb, woff, xb, aoff, szs, k0, k1, ring, acc);
+          } else {
+            const char* wb[2] = {uniform_ptr(static_cast<const uint8_t*>(a.gate) + ro * (a.H / 2)),
+                                 uniform_ptr(static_cast<const uint8_t*>(a.up) + ro * (a.H / 2))};
+            const uint32_t woff = u4_code_off(a.H / 2);
+            const int* prow = a.perm + off + tc * 16;
+            with_token_rows(ntok, [&](auto trc) {
+              constexpr int TR = decltype(trc)::value;
+              uint32_t ao[TR / 4];
+              u4_token_offsets<TR>(ntok, [&](int j) { return static_cast<uint32_t>(prow[j] / a.k) * a.H * 2; }, ao);
+              ring_stream_u4<2, U * SLOTB, TR>(wb, woff, xb, ao, szs, k0, k1, ring, acc);
+            });
+          }
         } else {
           const char* wb[2] = {uniform_ptr(static_cast<const uint16_t*>(a.sgate) + static_cast<int64_t>(row0) * a.H),
                                uniform_ptr(static_cast<const uint16_t*>(a.sup) + static_cast<int64_t>(row0) * a.H)};
@@ -1047,11 +1212,11 @@ __global__ __launch_bounds__(256) void k_stream_up_u8(SkinnyUpArgs a) {
   }
 }
 
-template <int U, int NWK>
-__global__ __launch_bounds__(256) void k_stream_down_u8(SkinnyDownArgs a) {
-  using G = RingGeomU8<1>;
+template <int BITS, int U, int NWK>
+__global__ __launch_bounds__(256) void k_stream_down_q(SkinnyDownArgs a) {
+  constexpr int QSLOT = BITS == 8 ? RingGeomU8<1>::SLOT_BYTES : RingGeomU4<1, 16>::SLOT_BYTES;
   using GB = RingGeom<1>;
-  constexpr int SLOTB = G::SLOT_BYTES > GB::SLOT * 2 ? G::SLOT_BYTES : GB::SLOT * 2;
+  constexpr int SLOTB = QSLOT > GB::SLOT * 2 ? QSLOT : GB::SLOT * 2;
   constexpr int IPB = 4 / NWK;
   __shared__ __attribute__((aligned(16))) char rings[4 * U * SLOTB];
   const int lane = lane_id(), w = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
@@ -1106,12 +1271,25 @@ __global__ __launch_bounds__(256) void k_stream_down_u8(SkinnyDownArgs a) {
       f32x4 acc[1] = {f32x4{0.f, 0.f, 0.f, 0.f}};
       if (live) {
         if (!shared) {
-          const char* wb[1] = {uniform_ptr(static_cast<const uint8_t*>(a.down) + ro * a.I)};
-          const uint32_t woff[2] = {static_cast<uint32_t>(rr * a.I + ch * 16),
-                                    static_cast<uint32_t>((8 + rr) * a.I + ch * 16)};
           const uint16_t* ss[1] = {a.down_s};
           const uint16_t* zz[1] = {a.down_z};
-          ring_stream_u8<1, U>(wb, woff, ab, aoff, u8_param_row<1>(ss, zz, ro, a.I), k0, k1, ring, acc);
+          const uint16_t* szs = u8_param_row<1>(ss, zz, ro, a.I);
+          if constexpr (BITS == 8) {
+            const char* wb[1] = {uniform_ptr(static_cast<const uint8_t*>(a.down) + ro * a.I)};
+            const uint32_t woff[2] = {static_cast<uint32_t>(rr * a.I + ch * 16),
+                                      static_cast<uint32_t>((8 + rr) * a.I + ch * 16)};
+            ring_stream_u8<1, U>(wb, woff, ab, aoff, szs, k0, k1, ring, acc);
+          } else {
+            const char* wb[1] = {uniform_ptr(static_cast<const uint8_t*>(a.down) + ro * (a.I / 2))};
+            const uint32_t woff = u4_code_off(a.I / 2);
+            const int row0t = off + tc * 16;
+            with_token_rows(ntok, [&](auto trc) {
+              constexpr int TR = decltype(trc)::value;
+              uint32_t ao[TR / 4];
+              u4_token_offsets<TR>(ntok, [&](int j) { return static_cast<uint32_t>(row0t + j) * a.I * 2; }, ao);
+              ring_stream_u4<1, U * SLOTB, TR>(wb, woff, ab, ao, szs, k0, k1, ring, acc);
+            });
+          }
         } else {
           const char* wb[1] = {uniform_ptr(static_cast<const uint16_t*>(a.sdown) + static_cast<int64_t>(row0) * a.Is)};
           const uint32_t woff[2] = {static_cast<uint32_t>((rr * K + ch * 8) * 2),
@@ -1214,6 +1392,7 @@ int grid_for(int64_t items, int ipb, int ncu) {
 // K-steps per LDS ring (per wavefront) of the bf16 streaming kernels
 constexpr int kUpRing = 3, kDownRing = 4;
 constexpr int kUpRingU8 = 3, kDownRingU8 = 3;
+constexpr int kUpRingU4 = 3, kDownRingU4 = 3;
 
 // work items of a launch covering `part` (see SkinnyUpArgs::part)
 int64_t part_items(int part, int64_t routed, int64_t shared) {
@@ -1284,11 +1463,19 @@ hipError_t launch_skinny_up(const SkinnyUpArgs& a, Act act, WFmt wf, int ncu, hi
   const int tch = 16 * pick_mt(a.T);
   const int64_t items = part_items(a.part, dmax * (a.I / 16), static_cast<int64_t>(a.Is / 16) * ((a.T + tch - 1) / tch));
   const int64_t small = 4ll * ncu;
+  if (wf == WFmt::U4) {
+    // the only u4 kernel: the configuration checks guarantee its conditions
+    if (act != Act::BF16 || a.H % 128 || !stream_ok(a.T, a.H, a.T, a.Is) || !aligned4({a.gate_s, a.gate_z, a.up_s, a.up_z}))
+      return hipErrorInvalidValue;
+    return launch_ring<kUpRingU4>(k_stream_up_q<4, kUpRingU4, 1>, k_stream_up_q<4, kUpRingU4, 4>,
+                                  part_items(a.part, dmax * (a.I / 16), static_cast<int64_t>(a.Is / 16) * ((a.T + 15) / 16)),
+                                  small, ncu, s, a);
+  }
   if (act == Act::F32)
     MOE_DISPATCH_MT_NWK(k_skinny_up, a, items, a.T, small, Act::F32, WFmt::F32);
   else if (wf == WFmt::U8 && a.H % 128 == 0 && stream_ok(a.T, a.H, 0, 0) &&
            aligned4({a.gate_s, a.gate_z, a.up_s, a.up_z}))
-    return launch_ring<kUpRingU8>(k_stream_up_u8<kUpRingU8, 1>, k_stream_up_u8<kUpRingU8, 4>,
+    return launch_ring<kUpRingU8>(k_stream_up_q<8, kUpRingU8, 1>, k_stream_up_q<8, kUpRingU8, 4>,
                                   part_items(a.part, dmax * (a.I / 16), static_cast<int64_t>(a.Is / 16) * ((a.T + 15) / 16)),
                                   small, ncu, s, a);
   else if (wf == WFmt::U8)
@@ -1309,11 +1496,18 @@ hipError_t launch_skinny_down(const SkinnyDownArgs& a, Act act, WFmt wf, int ncu
   const int tch = 16 * pick_mt(a.T);
   const int64_t items = part_items(a.part, dmax * (a.H / 16), a.Is > 0 ? static_cast<int64_t>(a.H / 16) * ((a.T + tch - 1) / tch) : 0);
   const int64_t small = 4ll * ncu;
+  if (wf == WFmt::U4) {
+    if (act != Act::BF16 || a.I % 128 || !stream_ok(a.T * a.k, a.I, a.T, a.Is) || !aligned4({a.down_s, a.down_z}))
+      return hipErrorInvalidValue;
+    return launch_ring<kDownRingU4>(k_stream_down_q<4, kDownRingU4, 1>, k_stream_down_q<4, kDownRingU4, 4>,
+                                    part_items(a.part, dmax * (a.H / 16), a.Is > 0 ? static_cast<int64_t>(a.H / 16) * ((a.T + 15) / 16) : 0),
+                                    small, ncu, s, a);
+  }
   if (act == Act::F32)
     MOE_DISPATCH_MT_NWK(k_skinny_down, a, items, a.T, small, Act::F32, WFmt::F32);
   else if (wf == WFmt::U8 && a.I % 128 == 0 && stream_ok(a.T * a.k, a.I, a.T, a.Is) &&
            aligned4({a.down_s, a.down_z}))
-    return launch_ring<kDownRingU8>(k_stream_down_u8<kDownRingU8, 1>, k_stream_down_u8<kDownRingU8, 4>,
+    return launch_ring<kDownRingU8>(k_stream_down_q<8, kDownRingU8, 1>, k_stream_down_q<8, kDownRingU8, 4>,
                                     part_items(a.part, dmax * (a.H / 16), a.Is > 0 ? static_cast<int64_t>(a.H / 16) * ((a.T + 15) / 16) : 0),
                                     small, ncu, s, a);
   else if (wf == WFmt::U8)

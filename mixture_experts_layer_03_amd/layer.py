@@ -57,12 +57,12 @@ def host_tensor_to_device(a, device):
 
 def weights_from_host(L: dict, device) -> MoEWeights:
     """Upload a dict of host arrays (names as in MoEWeights; u8 codes may be called
-    gate_q/up_q/down_q) to the device."""
+    gate_q/up_q/down_q, packed u4 codes gate_q4/up_q4/down_q4) to the device."""
     kw = {}
     for k, v in L.items():
         if v is None:
             continue
-        name = k[:-2] if k.endswith("_q") else k
+        name = k[:-2] if k.endswith("_q") else (k[:-3] if k.endswith("_q4") else k)
         kw[name] = host_tensor_to_device(v, device)
     return MoEWeights(**kw)
 
@@ -92,10 +92,11 @@ def check_weights(cfg: MoEConfig, w: MoEWeights, device, need_router=True, need_
         if cfg.use_expert_bias:
             _need(w.expert_bias, "expert_bias", (E,), torch.float32, device)
     if need_experts:
-        if cfg.expert_dtype == "u8":
+        if cfg.expert_dtype in ("u8", "u4"):
             G = cfg.quant_group
-            for n, shp, ss in (("gate", (E, I, H), (E, I, H // G)), ("up", (E, I, H), (E, I, H // G)),
-                               ("down", (E, H, I), (E, H, I // G))):
+            d = 2 if cfg.expert_dtype == "u4" else 1  # u4: two codes per byte along the row
+            for n, shp, ss in (("gate", (E, I, H // d), (E, I, H // G)), ("up", (E, I, H // d), (E, I, H // G)),
+                               ("down", (E, H, I // d), (E, H, I // G))):
                 _need(getattr(w, n), n, shp, torch.uint8, device)
                 _need(getattr(w, n + "_scale"), n + "_scale", ss, torch.float16, device)
                 _need(getattr(w, n + "_zero"), n + "_zero", ss, torch.float16, device)

@@ -39,6 +39,10 @@ SMALL = {
                                shared_intermediate=128),
 }
 SMALL[5] = SMALL[4].variant("ling-3.0-small-u8", 104, expert_dtype="u8")
+# packed int4 experts: more 128-element steps per row, fewer experts so that chunks of
+# 4, 8 and 16 tokens and several chunks per expert all occur
+SMALL[6] = SMALL[4].variant("ling-3.0-small-u4", 106, expert_dtype="u4", hidden=1024, moe_intermediate=384,
+                            shared_intermediate=256, num_experts=64)
 
 
 def log(msg: str) -> None:

@@ -84,6 +84,8 @@ def test_valid_configs_of_the_five_workloads():
     (dict(routed_scaling_factor=float("inf")), "routed_scaling_factor"),
     (dict(expert_dtype="u8", quant_group=32), "quant_group"),
     (dict(act_dtype="f32", expert_dtype="u8"), "expert_dtype"),
+    (dict(expert_dtype="u4", quant_group=128), "quant_group"),
+    (dict(act_dtype="f32", expert_dtype="u4"), "expert_dtype"),
     (dict(act_dtype="f32", expert_dtype="bf16"), "expert_dtype"),
 ])
 def test_invalid_config_rejected(kw, field):
@@ -117,6 +119,35 @@ def test_raw_struct_rejections():
 def test_unsupported_but_valid(kw):
     st, _ = status_of(good(**kw))
     assert st == _lib.MOE_EUNSUPPORTED
+
+
+U4 = dict(expert_dtype="u4", moe_intermediate=1024)
+
+
+@pytest.mark.parametrize("kw,word", [(dict(hidden=2048 + 64), "128"), (dict(moe_intermediate=1472), "128"),
+                                     (dict(path="prefill"), "streaming")])
+def test_u4_limits(kw, word):
+    """u4 experts: only the weight-streaming kernels exist, stepping 128 elements."""
+    st, msg = status_of(good(**{**U4, **kw}))
+    assert st == _lib.MOE_EUNSUPPORTED and word in msg, (st, msg)
+    assert status_of(good(**U4)) == (0, "")
+    assert status_of(good(**U4, path="decode")) == (0, "")
+
+
+def test_u4_weight_checks_before_any_launch():
+    """u4 group parameters are copied two at a time: 2-byte aligned is not enough."""
+    L = _lib.lib()
+    c = good(**U4).to_c()
+    fake = C.c_void_p(0x1000)
+    full = dict(router=0x1000, gate=0x1000, up=0x1000, down=0x1000, shared_gate=0x1000, shared_up=0x1000,
+                shared_down=0x1000, gate_scale=0x1000, gate_zero=0x1000, up_scale=0x1000, up_zero=0x1000,
+                down_scale=0x1000, down_zero=0x1000)
+    w = _lib.moe_weights(**{**full, "down_zero": None})
+    st = L.moe_experts(C.byref(c), 4, fake, C.byref(w), fake, fake, fake, fake, 1 << 30, None)
+    assert st == _lib.MOE_EINVAL_ARG and "down_zero" in L.moe_last_error().decode()
+    w = _lib.moe_weights(**{**full, "up_scale": 0x1002})
+    st = L.moe_experts(C.byref(c), 4, fake, C.byref(w), fake, fake, fake, fake, 1 << 30, None)
+    assert st == _lib.MOE_EINVAL_ARG and "up_scale" in L.moe_last_error().decode()
 
 
 def test_workspace_size_and_T_bounds():

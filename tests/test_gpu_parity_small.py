@@ -114,7 +114,8 @@ CASES = [(1, 16, "auto"), (1, 3, "auto"), (1, 100, "auto"),
          (4, 1, "auto"), (4, 40, "auto"), (4, 500, "auto"),
          (5, 1, "auto"), (5, 64, "auto"), (5, 500, "auto"),
          (2, 200, "decode"), (3, 100, "decode"), (5, 130, "decode"),
-         (2, 13, "prefill"), (3, 1, "prefill"), (5, 40, "prefill")]
+         (2, 13, "prefill"), (3, 1, "prefill"), (5, 40, "prefill"),
+         (6, 1, "auto"), (6, 7, "auto"), (6, 64, "auto"), (6, 300, "auto"), (6, 90, "decode")]
 
 
 @pytest.mark.parametrize("cid,T,path", CASES)
@@ -133,7 +134,7 @@ def test_forward(cid, T, path):
 
 
 @pytest.mark.parametrize("cid,T,path", [(2, 64, "decode"), (2, 64, "prefill"), (4, 300, "prefill"),
-                                        (4, 300, "decode"), (1, 16, "decode")])
+                                        (4, 300, "decode"), (1, 16, "decode"), (6, 300, "auto")])
 def test_experts_given_routing(cid, T, path):
     """The expert stage alone, fed the oracle's routing."""
     import mixture_experts_layer_03_amd as moe
@@ -230,7 +231,7 @@ def test_deterministic():
         assert torch.equal(a, b)
 
 
-@pytest.mark.parametrize("cid,T", [(2, 13), (2, 300), (5, 64), (4, 500)])
+@pytest.mark.parametrize("cid,T", [(2, 13), (2, 300), (5, 64), (4, 500), (6, 64)])
 def test_graph_replay_matches_eager(cid, T):
     """The forward captured in a HIP graph (prefill runs the shared expert on a second
     stream, joined inside the graph) gives the eager result on every replay, with other
