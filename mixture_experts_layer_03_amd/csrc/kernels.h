@@ -26,9 +26,9 @@ hipError_t launch_topk(const TopkArgs& a, hipStream_t s);
 
 struct PermuteArgs {
   const int32_t* idx;   // [nslots]
-  int nslots, E, BM;    // BM > 0: also build the M-tile map for tile GEMMs of BM rows
-  int small_max;        // experts with 1..small_max slots go to the active list (streaming
-                        // kernels); with BM > 0 only experts above it get M-tiles
+  int nslots, E, BM;    // BM > 0: also build the M-tile map (chunks of BM positions)
+  int small_max;        // experts with 1..small_max slots go to the active list
+  int tile_min;         // with BM > 0, experts with more than tile_min slots get M-tiles
   int32_t* counts;      // [E]
   int32_t* offsets;     // [E + 1]
   int32_t* perm;        // [nslots]  slot ids grouped by expert, -1 tail
@@ -57,6 +57,10 @@ struct SkinnyRouterArgs {
 };
 hipError_t launch_skinny_router(const SkinnyRouterArgs& a, Act act, int ncu, hipStream_t s);
 
+// Decode work is cut into chunks of at most kDecodeChunk positions of one expert (one
+// 16-row MFMA fragment of tokens), each chunk a separate work item.
+constexpr int kDecodeChunk = 16;
+
 struct SkinnyUpArgs {
   const void* x;           // [T, H]
   const void* gate;        // [E, I, H]
@@ -70,7 +74,9 @@ struct SkinnyUpArgs {
   const int32_t* offsets;
   const int32_t* perm;
   const int32_t* active;
-  const int32_t* meta;
+  const int32_t* meta;     // meta[0] active experts, meta[1] chunks in `tiles`
+  const int32_t* tiles;    // chunks of kDecodeChunk positions: (expert, first position)
+  int mtiles;              // upper bound on the chunks (grid sizing)
   int T, H, I, Is, k, E;
   int part;                // items: 0 routed and shared, 1 routed only, 2 shared only (reads no routing)
 };
@@ -92,6 +98,8 @@ struct SkinnyDownArgs {
   const int32_t* perm;
   const int32_t* active;
   const int32_t* meta;
+  const int32_t* tiles;    // as SkinnyUpArgs
+  int mtiles;
   int T, H, I, Is, k, E;
   int part;                // as SkinnyUpArgs::part
 };

@@ -139,7 +139,8 @@ void make_plan(const moe_config& c, int64_t T, Plan& p) {
   const int64_t slots = T * k;
   p.P = p.decode ? router_parts(c) : router_ksplit(c, T);
   const int64_t dmax = slots < E ? slots : E;
-  p.mtiles_bound = p.decode ? 0 : static_cast<int>((slots + dmax * (kTileM - 1)) / kTileM);
+  const int64_t bm = p.decode ? kDecodeChunk : kTileM;
+  p.mtiles_bound = static_cast<int>((slots + dmax * (bm - 1)) / bm);
   size_t o = 0;
   auto take = [&](size_t bytes) {
     const size_t at = o;
@@ -352,12 +353,16 @@ PermuteArgs permute_args(const moe_config& c, const Plan& p, int64_t T, const in
   a.idx = idx;
   a.nslots = static_cast<int>(T * c.top_k);
   a.E = static_cast<int>(c.num_experts);
-  a.BM = p.decode ? 0 : kTileM;
-  // decode: every active expert goes to the streaming kernels; tiled path: every
-  // active expert gets M-tiles.  (Sending experts with few tokens to the streaming
-  // kernels on the tiled path measured slower on the skewed workload: inside one tiled
-  // launch their memory-bound blocks overlap the large experts' MFMA-bound blocks.)
+  // decode: every active expert is in the active list (register-staged kernels) and
+  // cut into chunks of kDecodeChunk positions (ring kernels: one work item per chunk,
+  // so a popular expert's chunks run side by side instead of one after another);
+  // tiled path: every active expert gets M-tiles.  (Sending experts with few tokens to
+  // the streaming kernels on the tiled path measured slower on the skewed workload:
+  // inside one tiled launch their memory-bound blocks overlap the large experts'
+  // MFMA-bound blocks.)
+  a.BM = p.decode ? kDecodeChunk : kTileM;
   a.small_max = p.decode ? 0x7fffffff : 0;
+  a.tile_min = 0;
   a.counts = counts;
   a.offsets = offsets;
   a.perm = perm;
@@ -392,6 +397,7 @@ moe_status run_experts(const moe_config& c, const Plan& p, int64_t T, const void
   int32_t* perm = at<int32_t>(ws, p.o_perm);
   const int32_t* active = at<int32_t>(ws, p.o_active);
   const int32_t* meta = at<int32_t>(ws, p.o_meta);
+  const int32_t* tiles = at<int32_t>(ws, p.o_tiles);
   void* hm = at<void>(ws, p.o_hm);
   void* hs = at<void>(ws, p.o_hs);
   void* r = at<void>(ws, p.o_r);
@@ -419,6 +425,8 @@ moe_status run_experts(const moe_config& c, const Plan& p, int64_t T, const void
     u.perm = perm;
     u.active = active;
     u.meta = meta;
+    u.tiles = tiles;
+    u.mtiles = p.mtiles_bound;
     u.T = Ti;
     u.H = H;
     u.I = I;
@@ -443,6 +451,8 @@ moe_status run_experts(const moe_config& c, const Plan& p, int64_t T, const void
     d.perm = perm;
     d.active = active;
     d.meta = meta;
+    d.tiles = tiles;
+    d.mtiles = p.mtiles_bound;
     d.T = Ti;
     d.H = H;
     d.I = I;

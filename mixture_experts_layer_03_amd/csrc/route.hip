@@ -243,7 +243,7 @@ __device__ void scan_experts(const PermuteArgs& a, int c, bool write, int* off, 
   const int tid = threadIdx.x, lane = tid & 63, wv = tid >> 6;
   const int E = a.E;
   const int f = (c > 0 && c <= a.small_max) ? 1 : 0;
-  const int nt = (a.BM > 0 && c > a.small_max) ? (c + a.BM - 1) / a.BM : 0;
+  const int nt = (a.BM > 0 && c > a.tile_min) ? (c + a.BM - 1) / a.BM : 0;
   int ci = c, fi = f, ti = nt;
 #pragma unroll
   for (int o = 1; o < 64; o <<= 1) {

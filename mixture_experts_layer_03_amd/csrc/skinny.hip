@@ -641,10 +641,10 @@ __global__ __launch_bounds__(256) void k_stream_up(SkinnyUpArgs a) {
   const int lane = lane_id(), w = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   const int n = lane & 15;
   uint16_t* ring = rings + w * U * G::SLOT;
-  const int D = a.part == 2 ? 0 : a.meta[0];  // shared-only launches read no routing
+  const int NQ = a.part == 2 ? 0 : a.meta[1];  // chunks; shared-only launches read no routing
   const int CH = a.I / 16, CHs = a.Is / 16;
   const int TC = (a.T + 15) / 16;
-  const int n_routed = D * CH;
+  const int n_routed = NQ * CH;
   const int nitems = n_routed + (a.part == 1 ? 0 : CHs * TC);
   int rr, ch;
   ring_lane(rr, ch);
@@ -658,12 +658,23 @@ __global__ __launch_bounds__(256) void k_stream_up(SkinnyUpArgs a) {
     if (NWK > 1) unit_range(a.H, w % NWK, NWK, k0, k1);
     int e = 0, off = 0, ntot, row0, tc_begin, tc_end;
     if (!shared) {
-      e = a.active[it / CH];
-      row0 = (it % CH) * 16;
-      off = a.offsets[e];
-      ntot = a.counts[e];
+      // one chunk of at most 16 positions.  Expert e's chunks are chunk-list entries
+      // q0 .. q0 + nc - 1, and its items CH * q0 .. CH * (q0 + nc) - 1, ordered by row
+      // block and then chunk: the items of one expert are contiguous (neighbouring row
+      // blocks stream together) and a popular expert's chunks read the same rows side
+      // by side.  Any entry of the expert, such as it / CH, names it and its q0.
+      const int qa = it / CH;
+      e = a.tiles[2 * qa];
+      const int first = a.offsets[e];
+      const int q0 = qa - (a.tiles[2 * qa + 1] - first) / kDecodeChunk;
+      const int nc = (a.counts[e] + kDecodeChunk - 1) / kDecodeChunk;
+      const int local = it - q0 * CH;
+      const int c = local % nc;
+      row0 = (local / nc) * 16;
+      off = first + c * kDecodeChunk;
+      ntot = a.counts[e] - c * kDecodeChunk;
       tc_begin = 0;
-      tc_end = (ntot + 15) / 16;
+      tc_end = 1;
     } else {
       const int si = it - n_routed;
       row0 = (si % CHs) * 16;
@@ -736,10 +747,10 @@ __global__ __launch_bounds__(256) void k_stream_down(SkinnyDownArgs a) {
   const int lane = lane_id(), w = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   const int n = lane & 15;
   uint16_t* ring = rings + w * U * G::SLOT;
-  const int D = a.part == 2 ? 0 : a.meta[0];  // shared-only launches read no routing
+  const int NQ = a.part == 2 ? 0 : a.meta[1];  // chunks; shared-only launches read no routing
   const int CH = a.H / 16;
   const int TC = (a.T + 15) / 16;
-  const int n_routed = D * CH;
+  const int n_routed = NQ * CH;
   const int nitems = n_routed + (a.Is > 0 && a.part != 1 ? CH * TC : 0);
   int rr, ch;
   ring_lane(rr, ch);
@@ -753,12 +764,23 @@ __global__ __launch_bounds__(256) void k_stream_down(SkinnyDownArgs a) {
     if (NWK > 1) unit_range(K, w % NWK, NWK, k0, k1);
     int e = 0, off = 0, ntot, row0, tc_begin, tc_end;
     if (!shared) {
-      e = a.active[it / CH];
-      row0 = (it % CH) * 16;
-      off = a.offsets[e];
-      ntot = a.counts[e];
+      // one chunk of at most 16 positions.  Expert e's chunks are chunk-list entries
+      // q0 .. q0 + nc - 1, and its items CH * q0 .. CH * (q0 + nc) - 1, ordered by row
+      // block and then chunk: the items of one expert are contiguous (neighbouring row
+      // blocks stream together) and a popular expert's chunks read the same rows side
+      // by side.  Any entry of the expert, such as it / CH, names it and its q0.
+      const int qa = it / CH;
+      e = a.tiles[2 * qa];
+      const int first = a.offsets[e];
+      const int q0 = qa - (a.tiles[2 * qa + 1] - first) / kDecodeChunk;
+      const int nc = (a.counts[e] + kDecodeChunk - 1) / kDecodeChunk;
+      const int local = it - q0 * CH;
+      const int c = local % nc;
+      row0 = (local / nc) * 16;
+      off = first + c * kDecodeChunk;
+      ntot = a.counts[e] - c * kDecodeChunk;
       tc_begin = 0;
-      tc_end = (ntot + 15) / 16;
+      tc_end = 1;
     } else {
       const int si = it - n_routed;
       row0 = (si % CH) * 16;
@@ -1101,10 +1123,10 @@ __global__ __launch_bounds__(256) void k_stream_up_q(SkinnyUpArgs a) {
   const int lane = lane_id(), w = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   const int n = lane & 15;
   char* ring = rings + w * U * SLOTB;
-  const int D = a.part == 2 ? 0 : a.meta[0];  // shared-only launches read no routing
+  const int NQ = a.part == 2 ? 0 : a.meta[1];  // chunks; shared-only launches read no routing
   const int CH = a.I / 16, CHs = a.Is / 16;
   const int TC = (a.T + 15) / 16;
-  const int n_routed = D * CH;
+  const int n_routed = NQ * CH;
   const int nitems = n_routed + (a.part == 1 ? 0 : CHs * TC);
   int rr, ch;
   ring_lane(rr, ch);
@@ -1123,12 +1145,23 @@ __global__ __launch_bounds__(256) void k_stream_up_q(SkinnyUpArgs a) {
     }
     int e = 0, off = 0, ntot, row0, tc_begin, tc_end;
     if (!shared) {
-      e = a.active[it / CH];
-      row0 = (it % CH) * 16;
-      off = a.offsets[e];
-      ntot = a.counts[e];
+      // one chunk of at most 16 positions.  Expert e's chunks are chunk-list entries
+      // q0 .. q0 + nc - 1, and its items CH * q0 .. CH * (q0 + nc) - 1, ordered by row
+      // block and then chunk: the items of one expert are contiguous (neighbouring row
+      // blocks stream together) and a popular expert's chunks read the same rows side
+      // by side.  Any entry of the expert, such as it / CH, names it and its q0.
+      const int qa = it / CH;
+      e = a.tiles[2 * qa];
+      const int first = a.offsets[e];
+      const int q0 = qa - (a.tiles[2 * qa + 1] - first) / kDecodeChunk;
+      const int nc = (a.counts[e] + kDecodeChunk - 1) / kDecodeChunk;
+      const int local = it - q0 * CH;
+      const int c = local % nc;
+      row0 = (local / nc) * 16;
+      off = first + c * kDecodeChunk;
+      ntot = a.counts[e] - c * kDecodeChunk;
       tc_begin = 0;
-      tc_end = (ntot + 15) / 16;
+      tc_end = 1;
     } else {
       const int si = it - n_routed;
       row0 = (si % CHs) * 16;
@@ -1222,10 +1255,10 @@ __global__ __launch_bounds__(256) void k_stream_down_q(SkinnyDownArgs a) {
   const int lane = lane_id(), w = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   const int n = lane & 15;
   char* ring = rings + w * U * SLOTB;
-  const int D = a.part == 2 ? 0 : a.meta[0];  // shared-only launches read no routing
+  const int NQ = a.part == 2 ? 0 : a.meta[1];  // chunks; shared-only launches read no routing
   const int CH = a.H / 16;
   const int TC = (a.T + 15) / 16;
-  const int n_routed = D * CH;
+  const int n_routed = NQ * CH;
   const int nitems = n_routed + (a.Is > 0 && a.part != 1 ? CH * TC : 0);
   int rr, ch;
   ring_lane(rr, ch);
@@ -1244,12 +1277,23 @@ __global__ __launch_bounds__(256) void k_stream_down_q(SkinnyDownArgs a) {
     }
     int e = 0, off = 0, ntot, row0, tc_begin, tc_end;
     if (!shared) {
-      e = a.active[it / CH];
-      row0 = (it % CH) * 16;
-      off = a.offsets[e];
-      ntot = a.counts[e];
+      // one chunk of at most 16 positions.  Expert e's chunks are chunk-list entries
+      // q0 .. q0 + nc - 1, and its items CH * q0 .. CH * (q0 + nc) - 1, ordered by row
+      // block and then chunk: the items of one expert are contiguous (neighbouring row
+      // blocks stream together) and a popular expert's chunks read the same rows side
+      // by side.  Any entry of the expert, such as it / CH, names it and its q0.
+      const int qa = it / CH;
+      e = a.tiles[2 * qa];
+      const int first = a.offsets[e];
+      const int q0 = qa - (a.tiles[2 * qa + 1] - first) / kDecodeChunk;
+      const int nc = (a.counts[e] + kDecodeChunk - 1) / kDecodeChunk;
+      const int local = it - q0 * CH;
+      const int c = local % nc;
+      row0 = (local / nc) * 16;
+      off = first + c * kDecodeChunk;
+      ntot = a.counts[e] - c * kDecodeChunk;
       tc_begin = 0;
-      tc_end = (ntot + 15) / 16;
+      tc_end = 1;
     } else {
       const int si = it - n_routed;
       row0 = (si % CH) * 16;
@@ -1468,7 +1512,7 @@ hipError_t launch_skinny_up(const SkinnyUpArgs& a, Act act, WFmt wf, int ncu, hi
     if (act != Act::BF16 || a.H % 128 || !stream_ok(a.T, a.H, a.T, a.Is) || !aligned4({a.gate_s, a.gate_z, a.up_s, a.up_z}))
       return hipErrorInvalidValue;
     return launch_ring<kUpRingU4>(k_stream_up_q<4, kUpRingU4, 1>, k_stream_up_q<4, kUpRingU4, 4>,
-                                  part_items(a.part, dmax * (a.I / 16), static_cast<int64_t>(a.Is / 16) * ((a.T + 15) / 16)),
+                                  part_items(a.part, static_cast<int64_t>(a.mtiles) * (a.I / 16), static_cast<int64_t>(a.Is / 16) * ((a.T + 15) / 16)),
                                   small, ncu, s, a);
   }
   if (act == Act::F32)
@@ -1476,13 +1520,13 @@ hipError_t launch_skinny_up(const SkinnyUpArgs& a, Act act, WFmt wf, int ncu, hi
   else if (wf == WFmt::U8 && a.H % 128 == 0 && stream_ok(a.T, a.H, 0, 0) &&
            aligned4({a.gate_s, a.gate_z, a.up_s, a.up_z}))
     return launch_ring<kUpRingU8>(k_stream_up_q<8, kUpRingU8, 1>, k_stream_up_q<8, kUpRingU8, 4>,
-                                  part_items(a.part, dmax * (a.I / 16), static_cast<int64_t>(a.Is / 16) * ((a.T + 15) / 16)),
+                                  part_items(a.part, static_cast<int64_t>(a.mtiles) * (a.I / 16), static_cast<int64_t>(a.Is / 16) * ((a.T + 15) / 16)),
                                   small, ncu, s, a);
   else if (wf == WFmt::U8)
     MOE_DISPATCH_MT_NWK(k_skinny_up, a, items, a.T, small, Act::BF16, WFmt::U8);
   else if (stream_ok(a.T, a.H, a.T * a.k, a.I))
     return launch_ring<kUpRing>(k_stream_up<kUpRing, 1>, k_stream_up<kUpRing, 4>,
-                                part_items(a.part, dmax * (a.I / 16), static_cast<int64_t>(a.Is / 16) * ((a.T + 15) / 16)),
+                                part_items(a.part, static_cast<int64_t>(a.mtiles) * (a.I / 16), static_cast<int64_t>(a.Is / 16) * ((a.T + 15) / 16)),
                                 small, ncu, s, a);
   else
     MOE_DISPATCH_MT_NWK(k_skinny_up, a, items, a.T, small, Act::BF16, WFmt::BF16);
@@ -1500,7 +1544,7 @@ hipError_t launch_skinny_down(const SkinnyDownArgs& a, Act act, WFmt wf, int ncu
     if (act != Act::BF16 || a.I % 128 || !stream_ok(a.T * a.k, a.I, a.T, a.Is) || !aligned4({a.down_s, a.down_z}))
       return hipErrorInvalidValue;
     return launch_ring<kDownRingU4>(k_stream_down_q<4, kDownRingU4, 1>, k_stream_down_q<4, kDownRingU4, 4>,
-                                    part_items(a.part, dmax * (a.H / 16), a.Is > 0 ? static_cast<int64_t>(a.H / 16) * ((a.T + 15) / 16) : 0),
+                                    part_items(a.part, static_cast<int64_t>(a.mtiles) * (a.H / 16), a.Is > 0 ? static_cast<int64_t>(a.H / 16) * ((a.T + 15) / 16) : 0),
                                     small, ncu, s, a);
   }
   if (act == Act::F32)
@@ -1508,13 +1552,13 @@ hipError_t launch_skinny_down(const SkinnyDownArgs& a, Act act, WFmt wf, int ncu
   else if (wf == WFmt::U8 && a.I % 128 == 0 && stream_ok(a.T * a.k, a.I, a.T, a.Is) &&
            aligned4({a.down_s, a.down_z}))
     return launch_ring<kDownRingU8>(k_stream_down_q<8, kDownRingU8, 1>, k_stream_down_q<8, kDownRingU8, 4>,
-                                    part_items(a.part, dmax * (a.H / 16), a.Is > 0 ? static_cast<int64_t>(a.H / 16) * ((a.T + 15) / 16) : 0),
+                                    part_items(a.part, static_cast<int64_t>(a.mtiles) * (a.H / 16), a.Is > 0 ? static_cast<int64_t>(a.H / 16) * ((a.T + 15) / 16) : 0),
                                     small, ncu, s, a);
   else if (wf == WFmt::U8)
     MOE_DISPATCH_MT_NWK(k_skinny_down, a, items, a.T, small, Act::BF16, WFmt::U8);
   else if (stream_ok(a.T * a.k, a.I, a.T, a.Is))
     return launch_ring<kDownRing>(k_stream_down<kDownRing, 1>, k_stream_down<kDownRing, 4>,
-                                  part_items(a.part, dmax * (a.H / 16), a.Is > 0 ? static_cast<int64_t>(a.H / 16) * ((a.T + 15) / 16) : 0),
+                                  part_items(a.part, static_cast<int64_t>(a.mtiles) * (a.H / 16), a.Is > 0 ? static_cast<int64_t>(a.H / 16) * ((a.T + 15) / 16) : 0),
                                   small, ncu, s, a);
   else
     MOE_DISPATCH_MT_NWK(k_skinny_down, a, items, a.T, small, Act::BF16, WFmt::BF16);
