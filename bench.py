@@ -36,7 +36,7 @@ def parse():
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=20)
     ap.add_argument("--warmup", type=int, default=5)
-    ap.add_argument("--config", type=int, default=2, help="workload 1..6 (default 2: Ling-lite shape)")
+    ap.add_argument("--config", type=int, default=2, help="workload 1..7 (default 2: Ling-lite shape)")
     ap.add_argument("--tokens", type=int, default=4096, help="headline batch size T")
     ap.add_argument("--decode-tokens", default="1,64", help="extra decode batch sizes ('' = none)")
     ap.add_argument("--min-rotation-bytes", type=float, default=2e9,

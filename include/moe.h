@@ -197,6 +197,26 @@ moe_status moe_forward(const moe_config* cfg, int64_t T, const void* x, const mo
                        int32_t* expert_counts_out, void* ws, size_t ws_bytes,
                        moe_stream_t stream);
 
+/* Dense MLP of the layers in front of the MoE layers (`first_k_dense_replace`):
+ *   y = (silu(x W_gᵀ) ⊙ (x W_uᵀ)) W_dᵀ
+ * A plain gated MLP at the model's intermediate size [mlxcel #838 "Router: selection
+ * uses biased scores, ..." list: dense BailingMoeMLP layers before the MoE layers;
+ * Ling-2.6-flash-JANGTQ card, "Architecture" layer table: layer 0 is a dense MLP of
+ * intermediate 9216].  It is the shared expert's computation and runs on its kernels
+ * (weight streaming for T <= 64, tiled MFMA above, as for the layer).
+ *   cfg          hidden, act_dtype and path are read; routing and expert fields are not
+ *   intermediate MLP width I_d: a multiple of 64 in [64, 32768]
+ *   x [T, H] and y [T, H] act_dtype; gate, up [I_d, H] and down [H, I_d] act_dtype
+ *                (16-byte aligned device pointers)
+ *   ws           device workspace of ws_bytes >= moe_dense_workspace_size(cfg, I_d, T)
+ * Errors: MOE_EINVAL_CONFIG (hidden, act_dtype or path out of range), MOE_EUNSUPPORTED
+ * (hidden or I_d not a multiple of 64; PREFILL with fp32), MOE_EINVAL_ARG (null or
+ * misaligned pointers, I_d or T out of range), MOE_EWORKSPACE, MOE_ELAUNCH.        */
+moe_status moe_dense_workspace_size(const moe_config* cfg, int64_t intermediate, int64_t T, size_t* bytes);
+moe_status moe_dense_mlp(const moe_config* cfg, int64_t intermediate, int64_t T, const void* x,
+                         const void* gate, const void* up, const void* down, void* y, void* ws,
+                         size_t ws_bytes, moe_stream_t stream);
+
 /* Kernel timing with HIP events (for benchmarks).  While enabled, every launch of a
  * stage in `stage_mask` is bracketed by a pair of events recorded on its launch
  * stream, taken from a pool of `capacity` pairs created here (launches beyond the

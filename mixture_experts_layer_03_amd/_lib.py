@@ -72,6 +72,8 @@ def lib() -> C.CDLL:
         "moe_permute": [cfgp, I64, P, P, P, P, P, SZ, P],
         "moe_experts": [cfgp, I64, P, wp, P, P, P, P, SZ, P],
         "moe_forward": [cfgp, I64, P, wp, P, P, P, P, P, SZ, P],
+        "moe_dense_workspace_size": [cfgp, I64, I64, C.POINTER(SZ)],
+        "moe_dense_mlp": [cfgp, I64, I64, P, P, P, P, P, P, SZ, P],
     }
     for name, args in sigs.items():
         f = getattr(L, name)

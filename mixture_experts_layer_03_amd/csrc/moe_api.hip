@@ -642,6 +642,109 @@ moe_status check_weights(const moe_config& c, const moe_weights* w, bool need_ro
   return MOE_OK;
 }
 
+// ---- dense MLP (the shared expert's computation on its own)
+moe_status check_dense(const moe_config* c, int64_t I) {
+  if (!c) return fail(MOE_EINVAL_ARG, "cfg is null");
+  if (c->hidden < 1 || c->hidden > kMaxH)
+    return fail(MOE_EINVAL_CONFIG, "hidden=%lld outside [1, %lld]", (long long)c->hidden, (long long)kMaxH);
+  if (c->act_dtype != MOE_DT_F32 && c->act_dtype != MOE_DT_BF16)
+    return fail(MOE_EINVAL_CONFIG, "act_dtype=%d must be F32 or BF16", c->act_dtype);
+  if (c->path < MOE_PATH_AUTO || c->path > MOE_PATH_PREFILL) return fail(MOE_EINVAL_CONFIG, "path=%d unknown", c->path);
+  if (I < 1 || I > kMaxI) return fail(MOE_EINVAL_ARG, "intermediate=%lld outside [1, %lld]", (long long)I, (long long)kMaxI);
+  if (c->hidden % 64 || I % 64) return fail(MOE_EUNSUPPORTED, "hidden and intermediate must be multiples of 64");
+  if (c->path == MOE_PATH_PREFILL && c->act_dtype == MOE_DT_F32)
+    return fail(MOE_EUNSUPPORTED, "the tiled MFMA path needs BF16 activations");
+  return MOE_OK;
+}
+
+struct DensePlan {
+  bool decode;
+  size_t o_hs, o_rs, total;
+};
+
+void dense_plan(const moe_config& c, int64_t I, int64_t T, DensePlan& p) {
+  p.decode = c.path == MOE_PATH_DECODE || (c.path == MOE_PATH_AUTO && (T <= kDecodeMaxT || c.act_dtype == MOE_DT_F32));
+  const size_t ab = c.act_dtype == MOE_DT_F32 ? 4 : 2;
+  size_t o = 0;
+  auto take = [&](size_t bytes) {
+    const size_t at = o;
+    o += align256(bytes);
+    return at;
+  };
+  p.o_hs = take(T * I * ab);                           // silu(x W_g^T) * (x W_u^T)
+  p.o_rs = take(p.decode ? T * c.hidden * 4 : 0);      // fp32 output before rounding
+  p.total = o;
+}
+
+moe_status run_dense(const moe_config& c, const DensePlan& p, int64_t T, int64_t I, const void* x, const void* gate,
+                     const void* up, const void* down, void* y, void* ws, hipStream_t s) {
+  const Act act = c.act_dtype == MOE_DT_F32 ? Act::F32 : Act::BF16;
+  const WFmt wf = act == Act::F32 ? WFmt::F32 : WFmt::BF16;
+  const int Ti = static_cast<int>(T), H = static_cast<int>(c.hidden), Id = static_cast<int>(I);
+  void* hs = at<void>(ws, p.o_hs);
+  const int ncu = device_cus();
+  if (p.decode) {
+    // the shared-expert items of the streaming kernels (part 2 reads no routing)
+    SkinnyUpArgs u{};
+    u.x = x;
+    u.sgate = gate;
+    u.sup = up;
+    u.hs = hs;
+    u.T = Ti;
+    u.H = H;
+    u.I = Id;
+    u.Is = Id;
+    u.k = 1;
+    u.E = 1;
+    u.part = 2;
+    MOE_LAUNCH_STAGE(MOE_STAGE_SHARED_UP, s, launch_skinny_up(u, act, wf, ncu, s), "dense gate/up (streaming)");
+    SkinnyDownArgs d{};
+    d.hs = hs;
+    d.sdown = down;
+    d.rs = at<float>(ws, p.o_rs);
+    d.T = Ti;
+    d.H = H;
+    d.I = Id;
+    d.Is = Id;
+    d.k = 1;
+    d.E = 1;
+    d.part = 2;
+    MOE_LAUNCH_STAGE(MOE_STAGE_SHARED_DOWN, s, launch_skinny_down(d, act, wf, ncu, s), "dense down (streaming)");
+    CombineArgs cb{nullptr, d.rs, nullptr, y, Ti, H, 0, 0, 0};  // no routed terms: y = rounded output
+    MOE_LAUNCH_STAGE(MOE_STAGE_COMBINE, s, launch_combine(cb, act, s), "dense output");
+    return MOE_OK;
+  }
+  TileArgs su{};
+  su.A = static_cast<const uint16_t*>(x);
+  su.K = H;
+  su.B0 = gate;
+  su.B1 = up;
+  su.N = Id;
+  su.routed = 0;
+  su.M = Ti;
+  su.out = hs;
+  su.ldo = Id;
+  su.mtiles_bound = static_cast<int>((T + kTileM - 1) / kTileM);
+  su.group_m = kGroupM;
+  su.ncu = ncu;
+  MOE_LAUNCH_STAGE(MOE_STAGE_SHARED_UP, s, launch_tile_gemm(su, AMode::DENSE, WFmt::BF16, Epi::SWIGLU, s), "dense gate/up (tiled)");
+  TileArgs sd{};
+  sd.A = static_cast<const uint16_t*>(hs);
+  sd.K = Id;
+  sd.B0 = down;
+  sd.N = H;
+  sd.routed = 0;
+  sd.M = Ti;
+  sd.out = y;
+  sd.ldo = H;
+  sd.k = 0;  // the combine epilogue with no routed terms: y = rounded output
+  sd.mtiles_bound = su.mtiles_bound;
+  sd.group_m = kGroupM;
+  sd.ncu = ncu;
+  MOE_LAUNCH_STAGE(MOE_STAGE_SHARED_DOWN, s, launch_tile_gemm(sd, AMode::DENSE, WFmt::BF16, Epi::COMBINE, s), "dense down (tiled)");
+  return MOE_OK;
+}
+
 }  // namespace
 
 extern "C" {
@@ -807,6 +910,48 @@ moe_status moe_forward(const moe_config* cfg, int64_t T, const void* x, const mo
     return ok();
   } catch (...) {
     return fail(MOE_EINVAL_ARG, "internal error in moe_forward");
+  }
+}
+
+moe_status moe_dense_workspace_size(const moe_config* cfg, int64_t intermediate, int64_t T, size_t* bytes) {
+  try {
+    moe_status s = check_dense(cfg, intermediate);
+    if (s != MOE_OK) return s;
+    if ((s = check_T(T)) != MOE_OK) return s;
+    if (!bytes) return fail(MOE_EINVAL_ARG, "bytes is null");
+    DensePlan p;
+    dense_plan(*cfg, intermediate, T, p);
+    *bytes = p.total;
+    return ok();
+  } catch (...) {
+    return fail(MOE_EINVAL_ARG, "internal error while sizing");
+  }
+}
+
+moe_status moe_dense_mlp(const moe_config* cfg, int64_t intermediate, int64_t T, const void* x, const void* gate,
+                         const void* up, const void* down, void* y, void* ws, size_t ws_bytes, moe_stream_t stream) {
+  try {
+    moe_status s = check_dense(cfg, intermediate);
+    if (s != MOE_OK) return s;
+    if ((s = check_T(T)) != MOE_OK) return s;
+    if (T == 0) return ok();
+    REQUIRE_PTR(x, 16, "x");
+    REQUIRE_PTR(y, 16, "y");
+    REQUIRE_PTR(gate, 16, "gate");
+    REQUIRE_PTR(up, 16, "up");
+    REQUIRE_PTR(down, 16, "down");
+    DensePlan p;
+    dense_plan(*cfg, intermediate, T, p);
+    const int64_t kmax = cfg->hidden > intermediate ? cfg->hidden : intermediate;
+    if (!p.decode && T * kmax * 2 >= (int64_t(1) << 32))
+      return fail(MOE_EUNSUPPORTED, "T * max(hidden, intermediate) * 2 bytes >= 2^32 on the tiled path; split the batch");
+    if (ws_bytes < p.total) return fail(MOE_EWORKSPACE, "workspace of %zu bytes < %zu required", ws_bytes, p.total);
+    if (p.total > 0 && (!ws || !aligned(ws, 256))) return fail(MOE_EWORKSPACE, "workspace must be non-null and 256-byte aligned");
+    if ((s = run_dense(*cfg, p, T, intermediate, x, gate, up, down, y, ws, static_cast<hipStream_t>(stream))) != MOE_OK)
+      return s;
+    return ok();
+  } catch (...) {
+    return fail(MOE_EINVAL_ARG, "internal error in moe_dense_mlp");
   }
 }
 

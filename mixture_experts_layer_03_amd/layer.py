@@ -241,3 +241,38 @@ def forward(x: torch.Tensor, weights: MoEWeights, cfg: MoEConfig, return_routing
     if return_routing:
         return y, (idx, wt, counts)
     return y
+
+
+def dense_workspace_size(cfg: MoEConfig, intermediate: int, T: int) -> int:
+    n = C.c_size_t(0)
+    c = cfg.to_c()
+    _lib.check(_lib.lib().moe_dense_workspace_size(C.byref(c), intermediate, T, C.byref(n)))
+    return n.value
+
+
+def dense_mlp(x: torch.Tensor, gate: torch.Tensor, up: torch.Tensor, down: torch.Tensor, cfg: MoEConfig,
+              ws=None, out=None):
+    """Dense MLP of the layers before the MoE layers: y = (silu(x Wg^T) * (x Wu^T)) Wd^T.
+    Uses cfg.hidden, cfg.act_dtype and cfg.path; the width is gate.shape[0]."""
+    _x_checks(cfg, x)
+    T, H = x.shape
+    I = gate.shape[0] if gate is not None and gate.dim() == 2 else -1
+    adt = _TORCH_DT[cfg.act_dtype]
+    _need(gate, "gate", (I, H), adt, x.device)
+    _need(up, "up", (I, H), adt, x.device)
+    _need(down, "down", (H, I), adt, x.device)
+    y = out if out is not None else torch.empty_like(x)
+    if out is not None:
+        _need(out, "out", tuple(x.shape), x.dtype, x.device)
+    if T == 0:
+        return y
+    need = dense_workspace_size(cfg, I, T)
+    if ws is None:
+        ws = _WS.get(x.device, need)
+    elif ws.numel() * ws.element_size() < need:
+        raise ValueError(f"workspace of {ws.numel() * ws.element_size()} bytes < {need}")
+    c = cfg.to_c()
+    _lib.check(_lib.lib().moe_dense_mlp(C.byref(c), I, T, x.data_ptr(), gate.data_ptr(), up.data_ptr(),
+                                        down.data_ptr(), y.data_ptr(), ws.data_ptr(), ws.numel(),
+                                        _stream(x.device)))
+    return y

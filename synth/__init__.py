@@ -1,4 +1,4 @@
-"""Seeded synthetic inputs for the MoE layer: the five workload shapes and their tensors.
+"""Seeded synthetic inputs for the MoE layer: the workload shapes and their tensors.
 
 This module is shared by the tests, the benchmark and the smoke check.  It
 holds none of the layer's arithmetic: only shapes, seeded random streams,
@@ -64,7 +64,7 @@ class LayerSpec:
         return replace(self, name=name, seed_id=seed_id, **kw)
 
 
-# The five workloads (hidden, experts, routing and storage per the model pages' families).
+# The workloads (hidden, experts, routing and storage per the model pages' families).
 SPECS = {
     1: LayerSpec("toy-f32", 1, hidden=256, num_experts=8, top_k=2, moe_intermediate=128,
                  shared_intermediate=128, act_dtype="f32", expert_dtype="f32", tokens=(16,)),
@@ -83,6 +83,45 @@ SPECS = {
 SPECS[5] = SPECS[4].variant("ling-3.0-flash-u8", 4, expert_dtype="u8", tokens=(1, 64, 8192))
 # config 4's layer with the routed experts stored as packed int4 affine (decode sizes)
 SPECS[6] = SPECS[4].variant("ling-3.0-flash-u4", 4, expert_dtype="u4", tokens=(1, 64))
+# Ling-3.0-tiny: 128 routed + 1 shared experts, 8 active, 24 layers, 7.9B total / 1.3B
+# active.  The hidden size is not given; hidden 2048 with expert width 384 reproduces
+# both totals (routed experts 24 x 128 x 3 x 2048 x 384 = 7.25B, active experts
+# 24 x 9 x 3 x 2048 x 384 = 0.51B, the rest attention and embeddings).  Routing as the
+# Ling-3.0 family's flash model (sigmoid, 8 groups keep 4, correction bias).
+SPECS[7] = LayerSpec("ling-3.0-tiny", 7, hidden=2048, num_experts=128, top_k=8, moe_intermediate=384,
+                     shared_intermediate=384, score_function="sigmoid", n_group=8, topk_group=4,
+                     use_expert_bias=True, tokens=(1, 64, 4096))
+
+
+@dataclass(frozen=True)
+class DenseSpec:
+    """A dense gated MLP: the layers in front of the MoE layers (first_k_dense_replace)."""
+
+    name: str
+    seed_id: int
+    hidden: int
+    intermediate: int
+    act_dtype: str = "bf16"
+    tokens: tuple = field(default=(1,))
+    weight_std: float = 0.02
+
+
+# Ling-2.6-flash layer 0: dense MLP of intermediate 9216 (hidden 4096 as the MoE layers)
+DENSE = {
+    "ling-2.6-flash-dense0": DenseSpec("ling-2.6-flash-dense0", 31, hidden=4096, intermediate=9216,
+                                       tokens=(1, 64, 4096)),
+}
+
+
+def make_dense(spec: DenseSpec, copy: int = 0) -> dict:
+    """gate/up [I,H] and down [H,I] of a dense MLP (bf16 bit patterns, or fp32)."""
+    H, I = spec.hidden, spec.intermediate
+    out = {}
+    for name, tid, shp in (("gate", _T_SGATE, (I, H)), ("up", _T_SUP, (I, H)), ("down", _T_SDOWN, (H, I))):
+        v = _rng(spec.seed_id, copy, tid, 0).standard_normal(shp, dtype=np.float32)
+        v *= np.float32(spec.weight_std)
+        out[name] = v if spec.act_dtype == "f32" else bf16_bits(v)
+    return out
 
 
 def _rng(*key) -> np.random.Generator:
@@ -232,8 +271,9 @@ def make_layer(spec: LayerSpec, copy: int = 0, threads=None) -> dict:
     return L
 
 
-def make_x(spec: LayerSpec, T: int, stream: int = 0) -> np.ndarray:
-    """Hidden states [T,H] ~ N(0,1): bf16 bit patterns (fp32 values for the toy layer)."""
+def make_x(spec, T: int, stream: int = 0) -> np.ndarray:
+    """Hidden states [T,H] ~ N(0,1): bf16 bit patterns (fp32 values for the toy layer).
+    `spec` is a LayerSpec or a DenseSpec."""
     v = _rng(spec.seed_id, stream, _T_X, T).standard_normal((T, spec.hidden), dtype=np.float32)
     return v if spec.act_dtype == "f32" else bf16_bits(v)
 

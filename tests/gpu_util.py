@@ -27,7 +27,7 @@ MARGIN = 1e-5
 W_TOL = 1e-5
 Y_TOL = {"bf16": 2e-2, "f32": 1e-4}
 
-# Reduced layers with the routing structure of the five workloads: sizes the
+# Reduced layers with the routing structure of the workloads: sizes the
 # oracle finishes in seconds that still span several tiles and ragged tails.
 SMALL = {
     1: synth.SPECS[1],
@@ -43,6 +43,8 @@ SMALL[5] = SMALL[4].variant("ling-3.0-small-u8", 104, expert_dtype="u8")
 # 4, 8 and 16 tokens and several chunks per expert all occur
 SMALL[6] = SMALL[4].variant("ling-3.0-small-u4", 106, expert_dtype="u4", hidden=1024, moe_intermediate=384,
                             shared_intermediate=256, num_experts=64)
+SMALL[7] = synth.SPECS[7].variant("ling-3.0-tiny-small", 107, hidden=256, moe_intermediate=128,
+                                  shared_intermediate=128)
 
 
 def log(msg: str) -> None:

@@ -59,7 +59,7 @@ def status_of(cfg):
     return _lib.lib().moe_validate_config(C.byref(c)), _lib.lib().moe_last_error().decode()
 
 
-def test_valid_configs_of_the_five_workloads():
+def test_valid_configs_of_every_workload():
     import synth
     for spec in synth.SPECS.values():
         assert status_of(moe.MoEConfig.from_object(spec)) == (0, "")
@@ -257,3 +257,56 @@ def test_python_shape_checks_use_real_shapes():
     w = moe.MoEWeights(router=torch.zeros(4, 128, dtype=torch.float32))
     with pytest.raises(ValueError, match="dtype"):
         check_weights(cfg, w, torch.device("cpu"), need_router=True, need_experts=False)
+
+
+# ------------------------------------------------------------ dense MLP entry points
+def dense_status(cfg, I, T=4):
+    n = C.c_size_t(0)
+    c = cfg.to_c()
+    return _lib.lib().moe_dense_workspace_size(C.byref(c), I, T, C.byref(n)), _lib.lib().moe_last_error().decode(), n.value
+
+
+def test_dense_workspace_and_validation():
+    assert dense_status(good(), 9216)[0] == 0
+    assert dense_status(good(), 9216, T=0)[0] == 0
+    st, msg, _ = dense_status(good(), 100)
+    assert st == _lib.MOE_EUNSUPPORTED and "multiples of 64" in msg
+    st, msg, _ = dense_status(good(), 0)
+    assert st == _lib.MOE_EINVAL_ARG and "intermediate" in msg
+    st, msg, _ = dense_status(good(), 32768 + 64)
+    assert st == _lib.MOE_EINVAL_ARG
+    st, msg, _ = dense_status(good(act_dtype="f32", expert_dtype="f32", path="prefill"), 256)
+    assert st == _lib.MOE_EUNSUPPORTED and "BF16" in msg
+    st, _, _ = dense_status(good(), 256, T=-1)
+    assert st == _lib.MOE_EINVAL_ARG
+    # routing fields are not read: a configuration the layer would reject is fine here
+    c = good().to_c()
+    c.top_k = 99
+    n = C.c_size_t(0)
+    assert _lib.lib().moe_dense_workspace_size(C.byref(c), 256, 4, C.byref(n)) == 0
+    # decode (T <= 64) keeps an fp32 output buffer, the tiled path does not
+    assert dense_status(good(), 256, T=64)[2] > dense_status(good(), 256, T=65)[2]
+    assert _lib.lib().moe_dense_workspace_size(None, 256, 4, C.byref(n)) == _lib.MOE_EINVAL_ARG
+
+
+def test_dense_rejects_bad_arguments_before_any_launch():
+    L = _lib.lib()
+    c = good().to_c()
+    fake = C.c_void_p(0x1000)
+    need = dense_status(good(), 256)[2]
+    st = L.moe_dense_mlp(C.byref(c), 256, 4, None, fake, fake, fake, fake, fake, need, None)
+    assert st == _lib.MOE_EINVAL_ARG and "x" in L.moe_last_error().decode()
+    st = L.moe_dense_mlp(C.byref(c), 256, 4, fake, C.c_void_p(0x1008), fake, fake, fake, fake, need, None)
+    assert st == _lib.MOE_EINVAL_ARG and "gate" in L.moe_last_error().decode()
+    st = L.moe_dense_mlp(C.byref(c), 256, 4, fake, fake, fake, None, fake, fake, need, None)
+    assert st == _lib.MOE_EINVAL_ARG and "down" in L.moe_last_error().decode()
+    st = L.moe_dense_mlp(C.byref(c), 256, 4, fake, fake, fake, fake, fake, fake, need - 1, None)
+    assert st == _lib.MOE_EWORKSPACE
+    st = L.moe_dense_mlp(C.byref(c), 256, 4, fake, fake, fake, fake, fake, C.c_void_p(0x1010), need, None)
+    assert st == _lib.MOE_EWORKSPACE
+    assert L.moe_dense_mlp(C.byref(c), 256, 0, None, None, None, None, None, None, 0, None) == 0
+    # the tiled path's 32-bit operand offsets
+    big = 1 << 20
+    st = L.moe_dense_mlp(C.byref(good(path="prefill").to_c()), 32768, big, fake, fake, fake, fake, fake, fake,
+                         1 << 62, None)
+    assert st == _lib.MOE_EUNSUPPORTED

@@ -15,7 +15,7 @@ from gpu_util import check_forward, check_route, device_weights, log, moe_cfg, t
 
 pytestmark = [pytest.mark.gpu, pytest.mark.timeout(900)]
 
-CASES = [(cid, T) for cid in (2, 3, 4, 5, 6) for T in synth.SPECS[cid].tokens]
+CASES = [(cid, T) for cid in (2, 3, 4, 5, 6, 7) for T in synth.SPECS[cid].tokens]
 _STATE = {}
 
 

@@ -1,4 +1,4 @@
-"""GPU parity on reduced layers (same routing structure as the five workloads,
+"""GPU parity on reduced layers (same routing structure as the workloads,
 small hidden/intermediate sizes) against the fp64 oracle, through the C ABI.
 
 Every case spans several tiles and ragged tails; the oracle runs on every token.
@@ -30,7 +30,7 @@ def xs(spec, T):
     return x, to_dev(x)
 
 
-@pytest.mark.parametrize("cid", [1, 2, 3, 4, 5])
+@pytest.mark.parametrize("cid", [1, 2, 3, 4, 5, 7])
 @pytest.mark.parametrize("T", [1, 7, 64, 300])
 def test_route(cid, T):
     import mixture_experts_layer_03_amd as moe
@@ -115,7 +115,8 @@ CASES = [(1, 16, "auto"), (1, 3, "auto"), (1, 100, "auto"),
          (5, 1, "auto"), (5, 64, "auto"), (5, 500, "auto"),
          (2, 200, "decode"), (3, 100, "decode"), (5, 130, "decode"),
          (2, 13, "prefill"), (3, 1, "prefill"), (5, 40, "prefill"),
-         (6, 1, "auto"), (6, 7, "auto"), (6, 64, "auto"), (6, 300, "auto"), (6, 90, "decode")]
+         (6, 1, "auto"), (6, 7, "auto"), (6, 64, "auto"), (6, 300, "auto"), (6, 90, "decode"),
+         (7, 1, "auto"), (7, 13, "auto"), (7, 64, "auto"), (7, 300, "auto")]
 
 
 @pytest.mark.parametrize("cid,T,path", CASES)
