@@ -300,7 +300,9 @@ def main():
             key = f"up_stream_cfg{args.config}_T{args.tokens}"
             roof = dict(bound="hbm", achieved=ach, peak=HBM_PEAK_GBPS, unit="GB/s",
                         frac=ach / HBM_PEAK_GBPS, traffic=recorded_traffic(key, digest),
-                        kernel="routed+shared gate/up weight streaming + SwiGLU (k_skinny_up)",
+                        kernel="routed+shared gate/up weight streaming + SwiGLU (" + {
+                            "bf16": "k_stream_up", "u8": "k_stream_up_q<8>", "u4": "k_stream_up_q<4>",
+                            "f32": "k_skinny_up"}[spec.expert_dtype] + ")",
                         avg_ms=up_ms, algorithmic_bytes=alg["up_bytes_decode"])
 
     cpu = None

@@ -538,12 +538,16 @@ hipError_t launch_dma(const TileArgs& a, hipStream_t s) {
 
 // Tile shapes of the copy pipeline (bf16 weights): 128 token rows x 512 weight rows,
 // K-step 64, two LDS stages (160 KB, 16 wavefronts, one block per CU).  A dense
-// single-matrix product with fewer such blocks than CUs takes 128 x 256 x 64 with
-// three stages instead (twice the blocks).
+// single-matrix product with fewer such blocks than CUs, and a gate/up product whose
+// last 256-column tile would be mostly padding, take 128 x 256 x 64 with three stages
+// instead.
 template <WFmt WF, bool DUAL, AMode AM, Epi EPI>
 hipError_t launch_bn(const TileArgs& a, hipStream_t s) {
   if constexpr (WF == WFmt::BF16) {
     if (!DUAL && !a.routed && grid_blocks(a, 512) < a.ncu) return launch_dma<256, 64, 3, DUAL, AM, EPI>(a, s);
+    // gate/up whose width leaves more than an eighth of the last 256-column tile empty
+    // (e.g. 384 = 256 + 128) takes 128-column tiles
+    if (DUAL && (a.N + 255) / 256 * 256 - a.N > a.N / 8) return launch_dma<256, 64, 3, DUAL, AM, EPI>(a, s);
     return launch_dma<512, 64, 2, DUAL, AM, EPI>(a, s);
   } else {
     // u8 weights are dequantised in registers on their way to LDS.  Single-matrix

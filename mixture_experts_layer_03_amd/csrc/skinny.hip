@@ -676,9 +676,10 @@ __global__ __launch_bounds__(256) void k_stream_up(SkinnyUpArgs a) {
       tc_begin = 0;
       tc_end = 1;
     } else {
+      // shared item: the chunks of one row block are neighbours (they share its rows)
       const int si = it - n_routed;
-      row0 = (si % CHs) * 16;
-      tc_begin = si / CHs;
+      row0 = (si / TC) * 16;
+      tc_begin = si % TC;
       tc_end = tc_begin + 1;
       ntot = a.T;
     }
@@ -782,9 +783,10 @@ __global__ __launch_bounds__(256) void k_stream_down(SkinnyDownArgs a) {
       tc_begin = 0;
       tc_end = 1;
     } else {
+      // shared item: the chunks of one row block are neighbours (they share its rows)
       const int si = it - n_routed;
-      row0 = (si % CH) * 16;
-      tc_begin = si / CH;
+      row0 = (si / TC) * 16;
+      tc_begin = si % TC;
       tc_end = tc_begin + 1;
       ntot = a.T;
     }
@@ -1163,9 +1165,10 @@ __global__ __launch_bounds__(256) void k_stream_up_q(SkinnyUpArgs a) {
       tc_begin = 0;
       tc_end = 1;
     } else {
+      // shared item: the chunks of one row block are neighbours (they share its rows)
       const int si = it - n_routed;
-      row0 = (si % CHs) * 16;
-      tc_begin = si / CHs;
+      row0 = (si / TC) * 16;
+      tc_begin = si % TC;
       tc_end = tc_begin + 1;
       ntot = a.T;
     }
@@ -1295,9 +1298,10 @@ __global__ __launch_bounds__(256) void k_stream_down_q(SkinnyDownArgs a) {
       tc_begin = 0;
       tc_end = 1;
     } else {
+      // shared item: the chunks of one row block are neighbours (they share its rows)
       const int si = it - n_routed;
-      row0 = (si % CH) * 16;
-      tc_begin = si / CH;
+      row0 = (si / TC) * 16;
+      tc_begin = si % TC;
       tc_end = tc_begin + 1;
       ntot = a.T;
     }
