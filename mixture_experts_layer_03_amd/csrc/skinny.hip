@@ -1511,13 +1511,20 @@ hipError_t launch_skinny_up(const SkinnyUpArgs& a, Act act, WFmt wf, int ncu, hi
   const int tch = 16 * pick_mt(a.T);
   const int64_t items = part_items(a.part, dmax * (a.I / 16), static_cast<int64_t>(a.Is / 16) * ((a.T + tch - 1) / tch));
   const int64_t small = 4ll * ncu;
+  // Gate/up ring kernels split K over the four wavefronts of a block at every size
+  // (measured faster on the bf16 and u4 layers from 1 to 64 tokens: finer work units
+  // even out the last round), except for u8 weights, whose rings leave one block per CU,
+  // and shared-only launches (the dense MLP), whose token chunks of one row block share
+  // its rows best inside one block: these split only when their items cannot occupy the
+  // CUs otherwise.
+  const int64_t split_up = wf == WFmt::U8 || a.part == 2 ? small : int64_t(1) << 62;
   if (wf == WFmt::U4) {
     // the only u4 kernel: the configuration checks guarantee its conditions
     if (act != Act::BF16 || a.H % 128 || !stream_ok(a.T, a.H, a.T, a.Is) || !aligned4({a.gate_s, a.gate_z, a.up_s, a.up_z}))
       return hipErrorInvalidValue;
     return launch_ring<kUpRingU4>(k_stream_up_q<4, kUpRingU4, 1>, k_stream_up_q<4, kUpRingU4, 4>,
                                   part_items(a.part, static_cast<int64_t>(a.mtiles) * (a.I / 16), static_cast<int64_t>(a.Is / 16) * ((a.T + 15) / 16)),
-                                  small, ncu, s, a);
+                                  split_up, ncu, s, a);
   }
   if (act == Act::F32)
     MOE_DISPATCH_MT_NWK(k_skinny_up, a, items, a.T, small, Act::F32, WFmt::F32);
@@ -1525,13 +1532,13 @@ hipError_t launch_skinny_up(const SkinnyUpArgs& a, Act act, WFmt wf, int ncu, hi
            aligned4({a.gate_s, a.gate_z, a.up_s, a.up_z}))
     return launch_ring<kUpRingU8>(k_stream_up_q<8, kUpRingU8, 1>, k_stream_up_q<8, kUpRingU8, 4>,
                                   part_items(a.part, static_cast<int64_t>(a.mtiles) * (a.I / 16), static_cast<int64_t>(a.Is / 16) * ((a.T + 15) / 16)),
-                                  small, ncu, s, a);
+                                  split_up, ncu, s, a);
   else if (wf == WFmt::U8)
     MOE_DISPATCH_MT_NWK(k_skinny_up, a, items, a.T, small, Act::BF16, WFmt::U8);
   else if (stream_ok(a.T, a.H, a.T * a.k, a.I))
     return launch_ring<kUpRing>(k_stream_up<kUpRing, 1>, k_stream_up<kUpRing, 4>,
                                 part_items(a.part, static_cast<int64_t>(a.mtiles) * (a.I / 16), static_cast<int64_t>(a.Is / 16) * ((a.T + 15) / 16)),
-                                small, ncu, s, a);
+                                split_up, ncu, s, a);
   else
     MOE_DISPATCH_MT_NWK(k_skinny_up, a, items, a.T, small, Act::BF16, WFmt::BF16);
   return hipGetLastError();
