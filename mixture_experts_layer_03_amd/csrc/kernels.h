@@ -79,6 +79,7 @@ struct SkinnyUpArgs {
   int mtiles;              // upper bound on the chunks (grid sizing)
   int T, H, I, Is, k, E;
   int part;                // items: 0 routed and shared, 1 routed only, 2 shared only (reads no routing)
+  int dense;               // 1: the dense MLP (shared items only, its own split rule)
 };
 hipError_t launch_skinny_up(const SkinnyUpArgs& a, Act act, WFmt wf, int ncu, hipStream_t s);
 

@@ -583,6 +583,7 @@ moe_status run_shared(const moe_config& c, const Plan& p, int64_t T, const void*
     u.Is = Is;
     u.k = k;
     u.E = E;
+    u.mtiles = p.mtiles_bound;  // the whole layer's counts decide the K split
     u.part = 2;
     MOE_LAUNCH_STAGE(MOE_STAGE_SHARED_UP, s, launch_skinny_up(u, act, wf, ncu, s), "shared gate/up (streaming)");
     SkinnyDownArgs d{};
@@ -595,6 +596,7 @@ moe_status run_shared(const moe_config& c, const Plan& p, int64_t T, const void*
     d.Is = Is;
     d.k = k;
     d.E = E;
+    d.mtiles = p.mtiles_bound;
     d.part = 2;
     MOE_LAUNCH_STAGE(MOE_STAGE_SHARED_DOWN, s, launch_skinny_down(d, act, wf, ncu, s), "shared down (streaming)");
     return MOE_OK;
@@ -697,6 +699,7 @@ moe_status run_dense(const moe_config& c, const DensePlan& p, int64_t T, int64_t
     u.k = 1;
     u.E = 1;
     u.part = 2;
+    u.dense = 1;
     MOE_LAUNCH_STAGE(MOE_STAGE_SHARED_UP, s, launch_skinny_up(u, act, wf, ncu, s), "dense gate/up (streaming)");
     SkinnyDownArgs d{};
     d.hs = hs;
@@ -876,10 +879,12 @@ moe_status moe_forward(const moe_config* cfg, int64_t T, const void* x, const mo
     // prefill: the shared expert's gate/up GEMM, which needs no routing, runs on a second
     // stream beside the router, top-k, permutation and routed GEMMs (measured: the
     // Ling-lite shape at 4096 tokens 0.906 -> 0.873 ms).  Decode keeps one stream: there
-    // the two extra launches and the join cost more than the overlap gains.
+    // the two extra launches and the join cost more than the overlap gains, eagerly and
+    // as graph branches alike (Ling-lite at 1 token: graph replay 55 -> 72 us forked).
     hipEvent_t join = nullptr;
-    if (cfg->shared_intermediate > 0 && !p.decode) {
-      if (AuxStream* aux = aux_stream(st)) {
+    AuxStream* aux = cfg->shared_intermediate > 0 && !p.decode ? aux_stream(st) : nullptr;
+    if (aux) {
+      {
         hipError_t e = hipEventRecord(aux->fork, st);
         if (e == hipSuccess) e = hipStreamWaitEvent(aux->s, aux->fork, 0);
         if (e != hipSuccess) return hip_fail(e, "fork of the shared expert");

@@ -1462,11 +1462,10 @@ bool stream_ok(int64_t rows, int64_t cols, int64_t rows2, int64_t cols2) {
   return rows * cols * 2 < (int64_t(1) << 31) && rows2 * cols2 * 2 < (int64_t(1) << 31);
 }
 
-// items < 4 * ncu: the four wavefronts of a block split K of one item; else one item each
+// split: the four wavefronts of a block share one item's K; else one item each
 template <int U, typename Args>
-hipError_t launch_ring(void (*k1)(Args), void (*k4)(Args), int64_t items, int64_t small, int ncu, hipStream_t s,
+hipError_t launch_ring(void (*k1)(Args), void (*k4)(Args), int64_t items, bool split, int ncu, hipStream_t s,
                        const Args& a) {
-  const bool split = items < small;
   const int grid = grid_for(items, split ? 1 : 4, ncu);
   hipLaunchKernelGGL(split ? k4 : k1, dim3(grid), dim3(256), 0, s, a);
   return hipGetLastError();
@@ -1474,10 +1473,10 @@ hipError_t launch_ring(void (*k1)(Args), void (*k4)(Args), int64_t items, int64_
 
 }  // namespace
 
-#define MOE_DISPATCH_MT_NWK(KERNEL, ARGS, ITEMS, T_, NWK_SMALL_ITEMS, ...)                     \
+#define MOE_DISPATCH_MT_NWK(KERNEL, ARGS, ITEMS, T_, SPLIT, ...)                                \
   do {                                                                                          \
     const int mt_ = pick_mt(T_);                                                                \
-    const bool k4_ = (ITEMS) < (NWK_SMALL_ITEMS);                                               \
+    const bool k4_ = (SPLIT);                                                                   \
     const int grid_ = grid_for((ITEMS), k4_ ? 1 : 4, ncu);                                      \
     if (k4_) {                                                                                  \
       if (mt_ == 1)                                                                             \
@@ -1501,49 +1500,53 @@ hipError_t launch_skinny_router(const SkinnyRouterArgs& a, Act act, int ncu, hip
   const int64_t items = static_cast<int64_t>((a.E + 15) / 16) * a.P;
   const int64_t small = 4ll * ncu;
   if (act == Act::BF16)
-    MOE_DISPATCH_MT_NWK(k_skinny_router, a, items, a.T, small, Act::BF16);
+    MOE_DISPATCH_MT_NWK(k_skinny_router, a, items, a.T, items < small, Act::BF16);
   else
-    MOE_DISPATCH_MT_NWK(k_skinny_router, a, items, a.T, small, Act::F32);
+    MOE_DISPATCH_MT_NWK(k_skinny_router, a, items, a.T, items < small, Act::F32);
   return hipGetLastError();
 }
 
+// Split decisions are taken from the item count of the whole layer (routed and shared
+// items), never from `part`, so that a layer launched in one piece and one whose shared
+// expert runs as a separate launch (a graph branch) do the same arithmetic.
 hipError_t launch_skinny_up(const SkinnyUpArgs& a, Act act, WFmt wf, int ncu, hipStream_t s) {
   if (a.T <= 0) return hipSuccess;
   const int64_t slots = static_cast<int64_t>(a.T) * a.k;
   const int64_t dmax = slots < a.E ? slots : a.E;
   const int tch = 16 * pick_mt(a.T);
-  const int64_t items = part_items(a.part, dmax * (a.I / 16), static_cast<int64_t>(a.Is / 16) * ((a.T + tch - 1) / tch));
+  const int64_t shared_skinny = static_cast<int64_t>(a.Is / 16) * ((a.T + tch - 1) / tch);
+  const int64_t items = part_items(a.part, dmax * (a.I / 16), shared_skinny);
   const int64_t small = 4ll * ncu;
+  const bool split_skinny = part_items(0, dmax * (a.I / 16), shared_skinny) < small;
+  // ring kernels: one item = 16 weight rows x one chunk of 16 tokens
+  const int64_t shared_ring = static_cast<int64_t>(a.Is / 16) * ((a.T + 15) / 16);
+  const int64_t ring = part_items(a.part, static_cast<int64_t>(a.mtiles) * (a.I / 16), shared_ring);
+  const int64_t ring_all = part_items(0, static_cast<int64_t>(a.mtiles) * (a.I / 16), shared_ring);
   // Gate/up ring kernels split K over the four wavefronts of a block at every size
   // (measured faster on the bf16 and u4 layers from 1 to 64 tokens: finer work units
   // even out the last round), except for u8 weights, whose rings leave one block per CU,
-  // and shared-only launches (the dense MLP), whose token chunks of one row block share
-  // its rows best inside one block: these split only when their items cannot occupy the
-  // CUs otherwise.
-  const int64_t split_up = wf == WFmt::U8 || a.part == 2 ? small : int64_t(1) << 62;
+  // and the dense MLP, whose token chunks of one row block share its rows best inside
+  // one block: these split only when their items cannot occupy the CUs otherwise.
+  const bool split_ring = wf == WFmt::U8 || a.dense ? ring_all < small : true;
   if (wf == WFmt::U4) {
     // the only u4 kernel: the configuration checks guarantee its conditions
     if (act != Act::BF16 || a.H % 128 || !stream_ok(a.T, a.H, a.T, a.Is) || !aligned4({a.gate_s, a.gate_z, a.up_s, a.up_z}))
       return hipErrorInvalidValue;
-    return launch_ring<kUpRingU4>(k_stream_up_q<4, kUpRingU4, 1>, k_stream_up_q<4, kUpRingSplitU4, 4>,
-                                  part_items(a.part, static_cast<int64_t>(a.mtiles) * (a.I / 16), static_cast<int64_t>(a.Is / 16) * ((a.T + 15) / 16)),
-                                  split_up, ncu, s, a);
+    return launch_ring<kUpRingU4>(k_stream_up_q<4, kUpRingU4, 1>, k_stream_up_q<4, kUpRingSplitU4, 4>, ring,
+                                  split_ring, ncu, s, a);
   }
   if (act == Act::F32)
-    MOE_DISPATCH_MT_NWK(k_skinny_up, a, items, a.T, small, Act::F32, WFmt::F32);
+    MOE_DISPATCH_MT_NWK(k_skinny_up, a, items, a.T, split_skinny, Act::F32, WFmt::F32);
   else if (wf == WFmt::U8 && a.H % 128 == 0 && stream_ok(a.T, a.H, 0, 0) &&
            aligned4({a.gate_s, a.gate_z, a.up_s, a.up_z}))
-    return launch_ring<kUpRingU8>(k_stream_up_q<8, kUpRingU8, 1>, k_stream_up_q<8, kUpRingU8, 4>,
-                                  part_items(a.part, static_cast<int64_t>(a.mtiles) * (a.I / 16), static_cast<int64_t>(a.Is / 16) * ((a.T + 15) / 16)),
-                                  split_up, ncu, s, a);
+    return launch_ring<kUpRingU8>(k_stream_up_q<8, kUpRingU8, 1>, k_stream_up_q<8, kUpRingU8, 4>, ring, split_ring,
+                                  ncu, s, a);
   else if (wf == WFmt::U8)
-    MOE_DISPATCH_MT_NWK(k_skinny_up, a, items, a.T, small, Act::BF16, WFmt::U8);
+    MOE_DISPATCH_MT_NWK(k_skinny_up, a, items, a.T, split_skinny, Act::BF16, WFmt::U8);
   else if (stream_ok(a.T, a.H, a.T * a.k, a.I))
-    return launch_ring<kUpRing>(k_stream_up<kUpRing, 1>, k_stream_up<kUpRing, 4>,
-                                part_items(a.part, static_cast<int64_t>(a.mtiles) * (a.I / 16), static_cast<int64_t>(a.Is / 16) * ((a.T + 15) / 16)),
-                                split_up, ncu, s, a);
+    return launch_ring<kUpRing>(k_stream_up<kUpRing, 1>, k_stream_up<kUpRing, 4>, ring, split_ring, ncu, s, a);
   else
-    MOE_DISPATCH_MT_NWK(k_skinny_up, a, items, a.T, small, Act::BF16, WFmt::BF16);
+    MOE_DISPATCH_MT_NWK(k_skinny_up, a, items, a.T, split_skinny, Act::BF16, WFmt::BF16);
   return hipGetLastError();
 }
 
@@ -1552,30 +1555,33 @@ hipError_t launch_skinny_down(const SkinnyDownArgs& a, Act act, WFmt wf, int ncu
   const int64_t slots = static_cast<int64_t>(a.T) * a.k;
   const int64_t dmax = slots < a.E ? slots : a.E;
   const int tch = 16 * pick_mt(a.T);
-  const int64_t items = part_items(a.part, dmax * (a.H / 16), a.Is > 0 ? static_cast<int64_t>(a.H / 16) * ((a.T + tch - 1) / tch) : 0);
+  const int64_t shared_skinny = a.Is > 0 ? static_cast<int64_t>(a.H / 16) * ((a.T + tch - 1) / tch) : 0;
+  const int64_t items = part_items(a.part, dmax * (a.H / 16), shared_skinny);
   const int64_t small = 4ll * ncu;
+  const bool split_skinny = part_items(0, dmax * (a.H / 16), shared_skinny) < small;
+  const int64_t shared_ring = a.Is > 0 ? static_cast<int64_t>(a.H / 16) * ((a.T + 15) / 16) : 0;
+  const int64_t ring = part_items(a.part, static_cast<int64_t>(a.mtiles) * (a.H / 16), shared_ring);
+  // down, whose K is the expert width, splits only when its items cannot occupy the CUs
+  const bool split_ring = part_items(0, static_cast<int64_t>(a.mtiles) * (a.H / 16), shared_ring) < small;
   if (wf == WFmt::U4) {
     if (act != Act::BF16 || a.I % 128 || !stream_ok(a.T * a.k, a.I, a.T, a.Is) || !aligned4({a.down_s, a.down_z}))
       return hipErrorInvalidValue;
-    return launch_ring<kDownRingU4>(k_stream_down_q<4, kDownRingU4, 1>, k_stream_down_q<4, kDownRingU4, 4>,
-                                    part_items(a.part, static_cast<int64_t>(a.mtiles) * (a.H / 16), a.Is > 0 ? static_cast<int64_t>(a.H / 16) * ((a.T + 15) / 16) : 0),
-                                    small, ncu, s, a);
+    return launch_ring<kDownRingU4>(k_stream_down_q<4, kDownRingU4, 1>, k_stream_down_q<4, kDownRingU4, 4>, ring,
+                                    split_ring, ncu, s, a);
   }
   if (act == Act::F32)
-    MOE_DISPATCH_MT_NWK(k_skinny_down, a, items, a.T, small, Act::F32, WFmt::F32);
+    MOE_DISPATCH_MT_NWK(k_skinny_down, a, items, a.T, split_skinny, Act::F32, WFmt::F32);
   else if (wf == WFmt::U8 && a.I % 128 == 0 && stream_ok(a.T * a.k, a.I, a.T, a.Is) &&
            aligned4({a.down_s, a.down_z}))
-    return launch_ring<kDownRingU8>(k_stream_down_q<8, kDownRingU8, 1>, k_stream_down_q<8, kDownRingU8, 4>,
-                                    part_items(a.part, static_cast<int64_t>(a.mtiles) * (a.H / 16), a.Is > 0 ? static_cast<int64_t>(a.H / 16) * ((a.T + 15) / 16) : 0),
-                                    small, ncu, s, a);
+    return launch_ring<kDownRingU8>(k_stream_down_q<8, kDownRingU8, 1>, k_stream_down_q<8, kDownRingU8, 4>, ring,
+                                    split_ring, ncu, s, a);
   else if (wf == WFmt::U8)
-    MOE_DISPATCH_MT_NWK(k_skinny_down, a, items, a.T, small, Act::BF16, WFmt::U8);
+    MOE_DISPATCH_MT_NWK(k_skinny_down, a, items, a.T, split_skinny, Act::BF16, WFmt::U8);
   else if (stream_ok(a.T * a.k, a.I, a.T, a.Is))
-    return launch_ring<kDownRing>(k_stream_down<kDownRing, 1>, k_stream_down<kDownRing, 4>,
-                                  part_items(a.part, static_cast<int64_t>(a.mtiles) * (a.H / 16), a.Is > 0 ? static_cast<int64_t>(a.H / 16) * ((a.T + 15) / 16) : 0),
-                                  small, ncu, s, a);
+    return launch_ring<kDownRing>(k_stream_down<kDownRing, 1>, k_stream_down<kDownRing, 4>, ring, split_ring, ncu, s,
+                                  a);
   else
-    MOE_DISPATCH_MT_NWK(k_skinny_down, a, items, a.T, small, Act::BF16, WFmt::BF16);
+    MOE_DISPATCH_MT_NWK(k_skinny_down, a, items, a.T, split_skinny, Act::BF16, WFmt::BF16);
   return hipGetLastError();
 }
 
