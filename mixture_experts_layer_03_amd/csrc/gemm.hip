@@ -170,16 +170,25 @@ __device__ __forceinline__ void epilogue(const TileArgs& a, f32x4 (&acc)[4][4], 
             for (int q = 0; q < 8; ++q) f[q] *= ws;
             drow = slot;
           } else if constexpr (EPI == Epi::COMBINE) {
-            for (int jj = 0; jj < a.k; ++jj) {
-              const int64_t slot = orow * a.k + jj;
-              const int ex = a.idx[slot];
-              if (ex < 0 || ex >= a.E) continue;
-              const uint4 rv = ldg16(a.r + slot * a.N + col);
-              const uint32_t u[4] = {rv.x, rv.y, rv.z, rv.w};
+            // the k routed terms of the token in slot order, four slots per batch: their
+            // indices, then their rows, are loaded together (one memory latency per batch)
+            for (int j0 = 0; j0 < a.k; j0 += 4) {
+              int ex[4];
+              uint4 rv[4];
+#pragma unroll
+              for (int q = 0; q < 4; ++q) ex[q] = j0 + q < a.k ? a.idx[orow * a.k + j0 + q] : -1;
+#pragma unroll
+              for (int q = 0; q < 4; ++q)
+                rv[q] = ex[q] >= 0 && ex[q] < a.E ? ldg16(a.r + (orow * a.k + j0 + q) * a.N + col) : make_uint4(0, 0, 0, 0);
 #pragma unroll
               for (int q = 0; q < 4; ++q) {
-                f[2 * q] += __uint_as_float(u[q] << 16);
-                f[2 * q + 1] += __uint_as_float(u[q] & 0xffff0000u);
+                if (ex[q] < 0 || ex[q] >= a.E) continue;
+                const uint32_t u[4] = {rv[q].x, rv[q].y, rv[q].z, rv[q].w};
+#pragma unroll
+                for (int h = 0; h < 4; ++h) {
+                  f[2 * h] += __uint_as_float(u[h] << 16);
+                  f[2 * h + 1] += __uint_as_float(u[h] & 0xffff0000u);
+                }
               }
             }
           }
