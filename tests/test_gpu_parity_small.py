@@ -116,7 +116,8 @@ CASES = [(1, 16, "auto"), (1, 3, "auto"), (1, 100, "auto"),
          (2, 200, "decode"), (3, 100, "decode"), (5, 130, "decode"),
          (2, 13, "prefill"), (3, 1, "prefill"), (5, 40, "prefill"),
          (6, 1, "auto"), (6, 7, "auto"), (6, 64, "auto"), (6, 300, "auto"), (6, 90, "decode"),
-         (7, 1, "auto"), (7, 13, "auto"), (7, 64, "auto"), (7, 300, "auto")]
+         (7, 1, "auto"), (7, 13, "auto"), (7, 64, "auto"), (7, 300, "auto"),
+         (2, 16, "auto"), (4, 16, "auto")]
 
 
 @pytest.mark.parametrize("cid,T,path", CASES)
@@ -232,7 +233,7 @@ def test_deterministic():
         assert torch.equal(a, b)
 
 
-@pytest.mark.parametrize("cid,T", [(2, 13), (2, 300), (5, 64), (4, 500), (6, 64)])
+@pytest.mark.parametrize("cid,T", [(2, 13), (2, 300), (5, 64), (4, 500), (6, 64), (3, 1), (7, 16)])
 def test_graph_replay_matches_eager(cid, T):
     """The forward captured in a HIP graph (prefill runs the shared expert on a second
     stream, joined inside the graph) gives the eager result on every replay, with other
@@ -260,3 +261,29 @@ def test_graph_replay_matches_eager(cid, T):
         torch.cuda.synchronize()
         assert torch.equal(y, ref), f"replay {rep}"
         del noise
+
+
+@pytest.mark.parametrize("cid,T", [(2, 1), (4, 5)])
+def test_small_batches_on_two_streams(cid, T):
+    """Small batches issued on two streams at once, each stream with its own workspace,
+    give the single-stream result on every call."""
+    import mixture_experts_layer_03_amd as moe
+    spec, L, W = layer(cid)
+    cfg = moe_cfg(spec)
+    x, xd = xs(spec, T)
+    ref = moe.forward(xd, W, cfg)
+    torch.cuda.synchronize()
+    streams = [torch.cuda.Stream(), torch.cuda.Stream()]
+    wss = [torch.empty(cfg.workspace_size(T), dtype=torch.uint8, device="cuda") for _ in streams]
+    outs = [[torch.empty_like(ref) for _ in range(8)] for _ in streams]
+    log(f"two streams cfg{cid} T={T}")
+    for st in streams:
+        st.wait_stream(torch.cuda.current_stream())
+    for i in range(8):
+        for j, st in enumerate(streams):
+            with torch.cuda.stream(st):
+                moe.forward(xd, W, cfg, ws=wss[j], out=outs[j][i])
+    torch.cuda.synchronize()
+    for j in range(2):
+        for i in range(8):
+            assert torch.equal(outs[j][i], ref), f"stream {j} call {i}"
