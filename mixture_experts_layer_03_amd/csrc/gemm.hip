@@ -63,10 +63,12 @@ __device__ __forceinline__ uint4 ldg16(const void* p) { return *reinterpret_cast
 struct TilePos {
   int nt, kp, e, m_begin, m_rows, kt0, kt1;
 };
+// nblocks: the blocks of the launch that take such tiles (a multiple of 8, numbered
+// from 0); NT: the N-tiles they cover (0: all of N).
 template <int NCOL, int BK, int TBM = BM>
-__device__ __forceinline__ bool tile_pos(const TileArgs& a, TilePos& p) {
-  const int NT = (a.N + NCOL - 1) / NCOL;
-  const int per = gridDim.x / 8;
+__device__ __forceinline__ bool tile_pos(const TileArgs& a, TilePos& p, int nblocks, int NT = 0) {
+  if (NT <= 0) NT = (a.N + NCOL - 1) / NCOL;
+  const int per = nblocks / 8;
   const int KS = a.ksplit > 1 ? a.ksplit : 1;
   const int Lx = (blockIdx.x % 8) * per + blockIdx.x / 8;
   p.kp = Lx % KS;
@@ -218,7 +220,7 @@ __global__ __launch_bounds__(BN * 2) void k_tile(TileArgs a) {
 
   const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
   TilePos tp;
-  if (!tile_pos<NCOL, BK>(a, tp)) return;
+  if (!tile_pos<NCOL, BK>(a, tp, gridDim.x)) return;
   const int nt = tp.nt, kp = tp.kp, e = tp.e, m_begin = tp.m_begin, m_rows = tp.m_rows;
   const int K = a.K;
   const int kt0 = tp.kt0, kt1 = tp.kt1;
@@ -380,29 +382,34 @@ __global__ __launch_bounds__(BN * 2) void k_tile(TileArgs a) {
 // The stage image is BM + BN rows of BK elements: Q = (BM + BN) / RPI copy
 // instructions of 1 KB (A rows first, then B rows), dealt round-robin to the NW
 // wavefronts, so wave w issues instructions w, w + NW, ... and waits on its own count.
-template <int BN, int BK, int S, bool DUAL, AMode AM, Epi EPI>
-__global__ __launch_bounds__(BN * 2) void k_tile_dma(TileArgs a) {
-  constexpr int NW = BN / 32;                   // wavefronts (each a 64 x 64 sub-tile)
+// LDS elements of a copy-pipeline tile shape: S stages, or the epilogue's 64 fp32 rows
+template <int TBM, int BN, int BK, int S, bool DUAL>
+constexpr int dma_smem_elems() {
+  constexpr int NCOL = DUAL ? BN / 2 : BN;
+  constexpr int STAGE_ELEMS = (TBM + BN) * BK;
+  constexpr int EPI_ELEMS = 64 * (NCOL + 4) * 2;
+  return S * STAGE_ELEMS > EPI_ELEMS ? S * STAGE_ELEMS : EPI_ELEMS;
+}
+
+// One TBM x BN tile of the copy pipeline at position tp, with (TBM / 64) x (BN / 64)
+// wavefronts (the block's) and dma_smem_elems() elements of LDS at smem.
+template <int TBM, int BN, int BK, int S, bool DUAL, AMode AM, Epi EPI>
+__device__ __forceinline__ void tile_dma_body(const TileArgs& a, const TilePos& tp, uint16_t* smem) {
+  constexpr int WN = BN / 64;
+  constexpr int NW = (TBM / 64) * WN;           // wavefronts (each a 64 x 64 sub-tile)
   constexpr int NTHR = NW * 64;
   constexpr int CPRK = BK / 8;                  // 16-byte chunks per LDS row
   constexpr int RPI = 64 / CPRK;                // tile rows per copy instruction
-  constexpr int QA = BM / RPI, Q = (BM + BN) / RPI;
+  constexpr int QA = TBM / RPI, Q = (TBM + BN) / RPI;
   constexpr int J = (Q + NW - 1) / NW;          // copy slots per wave
   constexpr int NHI = Q % NW == 0 ? NW : Q % NW;  // waves with J copies (the rest J - 1)
-  constexpr int WN = BN / 64;
   constexpr int NCOL = DUAL ? BN / 2 : BN;
-  constexpr int STAGE_ELEMS = (BM + BN) * BK;
-  constexpr int EPI_LD = NCOL + 4;
-  constexpr int EPI_ELEMS = 64 * EPI_LD * 2;   // 64 fp32 rows of the epilogue
-  constexpr int SMEM_ELEMS = S * STAGE_ELEMS > EPI_ELEMS ? S * STAGE_ELEMS : EPI_ELEMS;
-  static_assert(S >= 2 && BM % RPI == 0 && BN % RPI == 0, "pipeline shape");
+  constexpr int STAGE_ELEMS = (TBM + BN) * BK;
+  static_assert(S >= 2 && TBM % 64 == 0 && TBM % RPI == 0 && BN % RPI == 0 && NTHR <= 1024, "pipeline shape");
   static_assert(J * (S - 1) < 64, "vmcnt range");
-  __shared__ __attribute__((aligned(16))) uint16_t smem[SMEM_ELEMS];
 
   const int tid = threadIdx.x, lane = tid & 63;
   const int w = __builtin_amdgcn_readfirstlane(tid >> 6);
-  TilePos tp;
-  if (!tile_pos<NCOL, BK>(a, tp)) return;
   const int nt = tp.nt, e = tp.e, m_begin = tp.m_begin, m_rows = tp.m_rows;
   const int K = a.K;
 
@@ -476,7 +483,7 @@ __global__ __launch_bounds__(BN * 2) void k_tile_dma(TileArgs a) {
   const int a_rd = (wm * 64 + fr) * BK, b_rd = (wn * 64 + fr) * BK;
   auto compute = [&](int stage) {
     const uint16_t* As = smem + stage * STAGE_ELEMS;
-    const uint16_t* Bs = As + BM * BK;
+    const uint16_t* Bs = As + TBM * BK;
 #pragma unroll
     for (int ks = 0; ks < BK / 32; ++ks) {
       const int cc = ((ks * 4 + fq) ^ swz<BK>(fr)) << 3;
@@ -514,14 +521,52 @@ __global__ __launch_bounds__(BN * 2) void k_tile_dma(TileArgs a) {
   }
   copy_wait<0>();  // every wave is done reading the stages; all copies have landed
   lds_barrier();
-  epilogue<NTHR, BN, 64, DUAL, EPI>(a, acc, reinterpret_cast<float*>(smem), tid, wm, wn, fr, fq, nt, tp.kp, m_begin,
-                                    m_rows);
+  epilogue<NTHR, BN, 64, DUAL, EPI, TBM>(a, acc, reinterpret_cast<float*>(smem), tid, wm, wn, fr, fq, nt, tp.kp,
+                                         m_begin, m_rows);
+}
+
+template <int BN, int BK, int S, bool DUAL, AMode AM, Epi EPI>
+__global__ __launch_bounds__(BN * 2) void k_tile_dma(TileArgs a) {
+  __shared__ __attribute__((aligned(16))) uint16_t smem[dma_smem_elems<BM, BN, BK, S, DUAL>()];
+  TilePos tp;
+  if (!tile_pos<DUAL ? BN / 2 : BN, BK>(a, tp, gridDim.x)) return;
+  tile_dma_body<BM, BN, BK, S, DUAL, AM, EPI>(a, tp, smem);
+}
+
+// Routed gate/up (SwiGLU) whose last 256-column N-tile is at most half full (e.g. 1408
+// = 5 x 256 + 128 columns).  Blocks [0, a.rem_first) take 128 x 512 tiles of the full
+// N-tiles [0, N / 256); the blocks past it take the last N % 256 columns as 256 x 256
+// tiles (128 columns of gate and of up) over chunks of 256 positions (tiles2), so
+// those columns cost 512 rows of copies per K-step instead of 640 for half the useful
+// work.  The remainder blocks come last, as the smallest units of the final round.
+template <AMode AM>
+__global__ __launch_bounds__(1024) void k_tile_dma_split(TileArgs a, int rem_first) {
+  constexpr int SM_MAIN = dma_smem_elems<BM, 512, 64, 2, true>();
+  constexpr int SM_REM = dma_smem_elems<256, 256, 64, 2, true>();
+  __shared__ __attribute__((aligned(16))) uint16_t smem[SM_MAIN > SM_REM ? SM_MAIN : SM_REM];
+  const int nt_main = a.N / 256;
+  TilePos tp;
+  if (static_cast<int>(blockIdx.x) < rem_first) {
+    if (!tile_pos<256, 64>(a, tp, rem_first, nt_main)) return;
+    tile_dma_body<BM, 512, 64, 2, true, AM, Epi::SWIGLU>(a, tp, smem);
+    return;
+  }
+  const int r = blockIdx.x - rem_first;
+  if (r >= a.meta[3]) return;
+  tp.e = a.tiles2[2 * r];
+  tp.m_begin = a.tiles2[2 * r + 1];
+  tp.m_rows = min(256, a.offsets[tp.e + 1] - tp.m_begin);
+  tp.nt = 2 * nt_main;  // 128-column tiles: column base nt_main * 256
+  tp.kp = 0;
+  tp.kt0 = 0;
+  tp.kt1 = a.K / 64;
+  tile_dma_body<256, 256, 64, 2, true, AM, Epi::SWIGLU>(a, tp, smem);
 }
 
 // blocks of a launch: whole groups of M-tiles (extra tiles exit) x N-tiles x K-splits,
-// rounded up to the 8 XCDs
-inline int64_t grid_blocks(const TileArgs& a, int ncol) {
-  const int NT = (a.N + ncol - 1) / ncol;
+// rounded up to the 8 XCDs (NT: the N-tiles, 0 for all of N)
+inline int64_t grid_blocks(const TileArgs& a, int ncol, int NT = 0) {
+  if (NT <= 0) NT = (a.N + ncol - 1) / ncol;
   const int G = a.group_m > 1 ? a.group_m : 1;  // (expert grouping: group_m <= 0, G = 1)
   const int64_t mt_pad = (a.mtiles_bound + G - 1) / G * G;
   const int64_t blocks = mt_pad * NT * (a.ksplit > 1 ? a.ksplit : 1);
@@ -550,6 +595,16 @@ hipError_t launch_dma(const TileArgs& a, hipStream_t s) {
 // single-matrix product with fewer such blocks than CUs, and a gate/up product whose
 // last 256-column tile would be mostly padding, take 128 x 256 x 64 with three stages
 // instead.
+template <AMode AM>
+hipError_t launch_split(const TileArgs& a, hipStream_t s) {
+  const int64_t main_blocks = grid_blocks(a, 256, a.N / 256);
+  const int64_t blocks = main_blocks + a.mtiles2_bound;
+  if (blocks <= 0) return hipSuccess;
+  hipLaunchKernelGGL(k_tile_dma_split<AM>, dim3(static_cast<unsigned>(blocks)), dim3(1024), 0, s, a,
+                     static_cast<int>(main_blocks));
+  return hipGetLastError();
+}
+
 template <WFmt WF, bool DUAL, AMode AM, Epi EPI>
 hipError_t launch_bn(const TileArgs& a, hipStream_t s) {
   if constexpr (WF == WFmt::BF16) {
@@ -557,6 +612,13 @@ hipError_t launch_bn(const TileArgs& a, hipStream_t s) {
     // gate/up whose width leaves more than an eighth of the last 256-column tile empty
     // (e.g. 384 = 256 + 128) takes 128-column tiles
     if (DUAL && (a.N + 255) / 256 * 256 - a.N > a.N / 8) return launch_dma<256, 64, 3, DUAL, AM, EPI>(a, s);
+    // routed gate/up whose last 256-column tile is at most half full (e.g. 1408 = 5 x 256
+    // + 128): that tile over 256-position chunks (measured on the Ling-lite shape at 4096
+    // tokens: 463 -> 420 us; the 384-wide tiny shape stays on 128-column tiles, 194 vs
+    // 200 us)
+    if constexpr (DUAL && EPI == Epi::SWIGLU)
+      if (a.routed && a.tiles2 && a.N > 256 && a.N % 256 != 0 && a.N % 256 <= 128)
+        return launch_split<AM>(a, s);
     return launch_dma<512, 64, 2, DUAL, AM, EPI>(a, s);
   } else {
     // u8 weights are dequantised in registers on their way to LDS.  Single-matrix

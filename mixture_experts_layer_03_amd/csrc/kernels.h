@@ -35,7 +35,9 @@ struct PermuteArgs {
   int32_t* slot_pos;    // [nslots]  position of each slot in perm, -1 if dropped
   int32_t* active;      // [E]       experts with 1..small_max slots, ascending
   int32_t* tiles;       // [max_tiles * 2] (expert, start position)
-  int32_t* meta;        // [4]: D, number of M-tiles, valid slots
+  int BM2;              // > 0: also a map of chunks of BM2 positions (tiles2, meta[3])
+  int32_t* tiles2;      // [max_tiles2 * 2] (expert, start position)
+  int32_t* meta;        // [4]: D, number of M-tiles, valid slots, number of BM2 chunks
   int32_t* counts_copy; // optional extra copy of counts (caller output) or null
   int32_t* hist;        // [ceil(nslots / kPermChunk)][E] per-block histograms (multi-block form)
 };
@@ -151,6 +153,10 @@ struct TileArgs {
   int64_t part_stride;      // elements between partial outputs
   int group_m;              // M-tiles per block-order group (weight-panel reuse in L2)
   int ncu;                  // compute units of the device (tile-shape choice)
+  // routed SwiGLU products whose last 256-column N-tile is at most half full: that
+  // tile's columns are computed over chunks of 256 positions (tiles2, count meta[3])
+  const int32_t* tiles2;    // or null
+  int mtiles2_bound;        // grid bound on the 256-position chunks
 };
 hipError_t launch_tile_gemm(const TileArgs& a, AMode am, WFmt wf, Epi epi, hipStream_t s);
 

@@ -107,7 +107,8 @@ struct Plan {
   bool decode;
   int P;
   int mtiles_bound;
-  size_t o_logits, o_idx, o_w, o_counts, o_offsets, o_perm, o_slotpos, o_active, o_meta, o_tiles, o_hist,
+  int mtiles2_bound;  // prefill: chunks of 256 positions (last N-tile of a half-full gate/up)
+  size_t o_logits, o_idx, o_w, o_counts, o_offsets, o_perm, o_slotpos, o_active, o_meta, o_tiles, o_tiles2, o_hist,
       o_hm, o_hs, o_r, o_rs, total;
 };
 
@@ -141,6 +142,7 @@ void make_plan(const moe_config& c, int64_t T, Plan& p) {
   const int64_t dmax = slots < E ? slots : E;
   const int64_t bm = p.decode ? kDecodeChunk : kTileM;
   p.mtiles_bound = static_cast<int>((slots + dmax * (bm - 1)) / bm);
+  p.mtiles2_bound = p.decode ? 0 : static_cast<int>((slots + dmax * 255) / 256);
   size_t o = 0;
   auto take = [&](size_t bytes) {
     const size_t at = o;
@@ -157,6 +159,7 @@ void make_plan(const moe_config& c, int64_t T, Plan& p) {
   p.o_active = take(E * 4);
   p.o_meta = take(64);
   p.o_tiles = take(size_t(p.mtiles_bound) * 8);
+  p.o_tiles2 = take(size_t(p.mtiles2_bound) * 8);
   p.o_hist = take(slots > kPermSingleMax ? size_t((slots + kPermChunk - 1) / kPermChunk) * E * 4 : 0);
   p.o_hm = take(slots * I * ab);
   p.o_hs = take(T * Is * ab);
@@ -369,6 +372,8 @@ PermuteArgs permute_args(const moe_config& c, const Plan& p, int64_t T, const in
   a.slot_pos = at<int32_t>(ws, p.o_slotpos);
   a.active = at<int32_t>(ws, p.o_active);
   a.tiles = at<int32_t>(ws, p.o_tiles);
+  a.BM2 = p.mtiles2_bound > 0 ? 256 : 0;
+  a.tiles2 = p.mtiles2_bound > 0 ? at<int32_t>(ws, p.o_tiles2) : nullptr;
   a.meta = at<int32_t>(ws, p.o_meta);
   a.counts_copy = counts_copy;
   a.hist = p.o_hist && T * c.top_k > kPermSingleMax ? at<int32_t>(ws, p.o_hist) : nullptr;
@@ -492,6 +497,8 @@ moe_status run_experts(const moe_config& c, const Plan& p, int64_t T, const void
   g.out = hm;
   g.ldo = I;
   g.mtiles_bound = p.mtiles_bound;
+  g.tiles2 = p.mtiles2_bound > 0 ? at<int32_t>(ws, p.o_tiles2) : nullptr;
+  g.mtiles2_bound = p.mtiles2_bound;
   g.group_m = 0;  // blocks grouped by expert
   g.ncu = device_cus();
   MOE_LAUNCH_STAGE(MOE_STAGE_UP, s, launch_tile_gemm(g, AMode::GATHER, wf, Epi::SWIGLU, s), "expert gate/up (tiled)");

@@ -235,34 +235,39 @@ constexpr int kPermThreads = 1024;
 constexpr int kPermUnroll = 4;
 
 // Exclusive scans over the experts of: counts c[e], small-expert flags (1..small_max
-// slots: handled by the streaming kernels) and M-tiles of the larger experts.  Fills
-// off[e] (LDS) with each expert's first position; when `write` is set, also stores
-// counts, offsets, the small-expert list, the M-tile map and meta.
+// slots: handled by the streaming kernels), M-tiles of the larger experts and their
+// chunks of BM2 positions.  Fills off[e] (LDS) with each expert's first position; when
+// `write` is set, also stores counts, offsets, the small-expert list, both tile maps
+// and meta.
 // Called by all kPermThreads threads with c = this thread's expert count (0 past E).
 __device__ void scan_experts(const PermuteArgs& a, int c, bool write, int* off, int (*wtot)[16], int* total_s) {
   const int tid = threadIdx.x, lane = tid & 63, wv = tid >> 6;
   const int E = a.E;
   const int f = (c > 0 && c <= a.small_max) ? 1 : 0;
   const int nt = (a.BM > 0 && c > a.tile_min) ? (c + a.BM - 1) / a.BM : 0;
-  int ci = c, fi = f, ti = nt;
+  const int nt2 = (a.BM2 > 0 && c > a.tile_min) ? (c + a.BM2 - 1) / a.BM2 : 0;
+  int ci = c, fi = f, ti = nt, t2 = nt2;
 #pragma unroll
   for (int o = 1; o < 64; o <<= 1) {
-    const int x = __shfl_up(ci, o, kWave), y = __shfl_up(fi, o, kWave), z = __shfl_up(ti, o, kWave);
+    const int x = __shfl_up(ci, o, kWave), y = __shfl_up(fi, o, kWave), z = __shfl_up(ti, o, kWave),
+              u = __shfl_up(t2, o, kWave);
     if (lane >= o) {
       ci += x;
       fi += y;
       ti += z;
+      t2 += u;
     }
   }
   if (lane == 63) {
     wtot[0][wv] = ci;
     wtot[1][wv] = fi;
     wtot[2][wv] = ti;
+    wtot[3][wv] = t2;
   }
   __syncthreads();
   if (wv == 0) {
 #pragma unroll
-    for (int q = 0; q < 3; ++q) {
+    for (int q = 0; q < 4; ++q) {
       const int v = lane < 16 ? wtot[q][lane] : 0;
       int inc = v;
 #pragma unroll
@@ -277,6 +282,7 @@ __device__ void scan_experts(const PermuteArgs& a, int c, bool write, int* off, 
   const int ce = ci - c + wtot[0][wv];
   const int fe = fi - f + wtot[1][wv];
   const int te = ti - nt + wtot[2][wv];
+  const int te2 = t2 - nt2 + wtot[3][wv];
   if (tid < E) {
     off[tid] = ce;
     if (write) {
@@ -288,6 +294,10 @@ __device__ void scan_experts(const PermuteArgs& a, int c, bool write, int* off, 
         a.tiles[2 * (te + q)] = tid;
         a.tiles[2 * (te + q) + 1] = ce + q * a.BM;
       }
+      for (int q = 0; q < nt2; ++q) {
+        a.tiles2[2 * (te2 + q)] = tid;
+        a.tiles2[2 * (te2 + q) + 1] = ce + q * a.BM2;
+      }
     }
   }
   if (tid == E - 1) {
@@ -296,6 +306,7 @@ __device__ void scan_experts(const PermuteArgs& a, int c, bool write, int* off, 
       a.meta[0] = fe + f;
       a.meta[1] = te + nt;
       a.meta[2] = ce + c;
+      a.meta[3] = te2 + nt2;
     }
     *total_s = ce + c;
   }
@@ -352,7 +363,7 @@ __device__ void scatter_slots(const PermuteArgs& a, int s0, int s1, const int* b
 __global__ __launch_bounds__(kPermThreads) void k_permute(PermuteArgs a) {
   __shared__ int cnt[1024];
   __shared__ int off[1024];
-  __shared__ int wtot[3][16];
+  __shared__ int wtot[4][16];
   __shared__ int total_s;
   const int tid = threadIdx.x;
   if (tid < a.E) cnt[tid] = 0;
@@ -372,7 +383,7 @@ __global__ __launch_bounds__(kPermThreads) void k_route_permute(TopkArgs ta, Per
   // rank stay in registers (no round trip through global memory between the phases)
   __shared__ int cnt[1024];
   __shared__ int off[1024];
-  __shared__ int wtot[3][16];
+  __shared__ int wtot[4][16];
   __shared__ int total_s;
   __shared__ int s_idx[kFusedSlots];
   const int tid = threadIdx.x;
@@ -412,7 +423,7 @@ __global__ __launch_bounds__(kPermThreads) void k_perm_count(PermuteArgs a) {
 // them), adds the counts of earlier chunks, and scatters its own chunk.
 __global__ __launch_bounds__(kPermThreads) void k_perm_scatter(PermuteArgs a) {
   __shared__ int off[1024];
-  __shared__ int wtot[3][16];
+  __shared__ int wtot[4][16];
   __shared__ int total_s;
   const int tid = threadIdx.x;
   const int nb = gridDim.x, b = blockIdx.x;

@@ -287,3 +287,24 @@ def test_small_batches_on_two_streams(cid, T):
     for j in range(2):
         for i in range(8):
             assert torch.equal(outs[j][i], ref), f"stream {j} call {i}"
+
+
+@pytest.mark.parametrize("I", [1152, 2112])
+def test_gate_up_last_tile_over_256_position_chunks(I):
+    """Prefill gate/up whose last 256-column tile is at most half full but holds no more
+    than an eighth of padding (1152 = 4 x 256 + 128; 2112 = 8 x 256 + 64, whose last
+    tile also has rows past N): those columns are computed over chunks of 256
+    positions of each expert, the others over 128-position tiles; experts with one to
+    three chunks."""
+    import mixture_experts_layer_03_amd as moe
+    spec = SMALL[2].variant(f"split-I{I}", 152, moe_intermediate=I)
+    L = synth.make_layer(spec)
+    W = device_weights(L)
+    for T in (700, 90):
+        x = synth.make_x(spec, T)
+        log(f"prefill I={I} T={T}")
+        y, (idx, w, _) = moe.forward(to_dev(x), W, moe_cfg(spec, "prefill"), return_routing=True)
+        torch.cuda.synchronize()
+        idx_h = idx.cpu().numpy()
+        check_route(spec, idx_h, w.cpu().numpy(), L, x)
+        check_forward(spec, y_to_f64(y), idx_h, L, x)
