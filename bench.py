@@ -293,7 +293,8 @@ def main():
             key = f"up_tiled_cfg{args.config}_T{args.tokens}"
             roof = dict(bound="mfma", achieved=ach, peak=BF16_PEAK_TFLOPS, unit="TFLOP/s",
                         frac=ach / BF16_PEAK_TFLOPS, traffic=recorded_traffic(key, digest),
-                        kernel="routed gate/up grouped GEMM + SwiGLU (k_tile_dma, gather, dual)",
+                        kernel="routed gate/up grouped GEMM + SwiGLU (copy-pipeline tiles: k_tile_dma_split "
+                               "when the last 256-column tile is at most half full, else k_tile_dma; gather, dual)",
                         avg_ms=up_ms, algorithmic_flops=alg["up_flops"])
         else:
             ach = alg["up_bytes_decode"] / (up_ms * 1e-3) / 1e9
