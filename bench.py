@@ -37,6 +37,9 @@ def parse():
     ap.add_argument("--steps", type=int, default=20)
     ap.add_argument("--warmup", type=int, default=5)
     ap.add_argument("--config", type=int, default=2, help="workload 1..7 (default 2: Ling-lite shape)")
+    ap.add_argument("--dense", action="store_true",
+                    help="time the dense MLP in front of the MoE layers (Ling-2.6-flash layer 0: "
+                         "hidden 4096, intermediate 9216) instead of a MoE workload")
     ap.add_argument("--tokens", type=int, default=4096, help="headline batch size T")
     ap.add_argument("--decode-tokens", default="1,64", help="extra decode batch sizes ('' = none)")
     ap.add_argument("--min-rotation-bytes", type=float, default=2e9,
@@ -209,6 +212,148 @@ def recorded_traffic(kernel_key, digest, launch_div=1.0):
     return k.get("hbm_bytes_per_launch")
 
 
+def bench_dense(args):
+    """The dense gated MLP (moe_dense_mlp) on the Ling-2.6-flash layer-0 shape: same timing
+    protocol and JSON line as the MoE workloads (eager and graph replay over rotated weight
+    copies; roofline of the gate/up kernel; the oracle's gated MLP as the CPU baseline)."""
+    import torch
+    import synth
+    import mixture_experts_layer_03_amd as moe
+    from mixture_experts_layer_03_amd import _lib
+    import oracle.moe_oracle as om
+    spec = synth.DENSE["ling-2.6-flash-dense0"]
+    H, I = spec.hidden, spec.intermediate
+    dev = torch.device("cuda:0")
+    t_gen = time.perf_counter()
+    W_host = synth.make_dense(spec)
+    copies = [{k: moe.host_tensor_to_device(v, dev) for k, v in W_host.items()}]
+    gen_s = time.perf_counter() - t_gen
+    w_bytes = 3 * I * H * 2
+    ncp = max(1, min(args.max_copies, int(np.ceil(args.min_rotation_bytes / w_bytes))))
+    g = torch.Generator(device=dev)
+    g.manual_seed(7919 + spec.seed_id)
+    while len(copies) < ncp:   # timing-only copies drawn on the GPU with the same distribution
+        copies.append({k: (torch.randn(t.shape, generator=g, device=dev) * spec.weight_std).to(torch.bfloat16)
+                       for k, t in copies[0].items()})
+    cfg = moe.MoEConfig(hidden=H, num_experts=8, top_k=2, moe_intermediate=64, shared_intermediate=0)
+    digest = source_digest()
+    Ts = [args.tokens] + [int(t) for t in args.decode_tokens.split(",") if t.strip()]
+    results, head_x = {}, None
+    for T in Ts:
+        x_host = synth.make_x(spec, T)
+        x = moe.host_tensor_to_device(x_host, dev)
+        if T == args.tokens:
+            head_x = x_host
+        y = torch.empty_like(x)
+        ws = torch.empty(moe.dense_workspace_size(cfg, I, T), dtype=torch.uint8, device=dev)
+        steps = args.steps if T == args.tokens else max(args.steps, 100)
+
+        def call(i, out=y, wsp=ws):
+            W = copies[i % len(copies)]
+            moe.dense_mlp(x, W["gate"], W["up"], W["down"], cfg, ws=wsp, out=out)
+        for i in range(args.warmup):
+            call(i)
+        torch.cuda.synchronize()
+        mask = _lib.STAGES["shared_up"]
+        _lib.check(moe.lib().moe_profile_enable(mask, max(8, 16 * steps)))
+        torch.cuda.synchronize()
+        t0 = time.perf_counter()
+        for i in range(steps):
+            call(i)
+        torch.cuda.synchronize()
+        secs = time.perf_counter() - t0
+        st = stage_times(moe, mask)
+        _lib.check(moe.lib().moe_profile_disable())
+        t_step = secs / steps
+        byt = w_bytes + 2 * T * H * 2
+        fl = 6.0 * T * H * I
+        r = dict(T=T, copies=len(copies), ms_per_step=t_step * 1e3, tokens_per_s=T / t_step,
+                 hbm_gbps=byt / t_step / 1e9, mfma_tflops=fl / t_step / 1e12,
+                 up_ms=st.get("shared_up"), path="decode" if T <= 64 else "prefill")
+        r["hbm_frac"] = r["hbm_gbps"] / HBM_PEAK_GBPS
+        r["mfma_frac"] = r["mfma_tflops"] / BF16_PEAK_TFLOPS
+        r["roofline_frac"] = max(byt / (HBM_PEAK_GBPS * 1e9), fl / (BF16_PEAK_TFLOPS * 1e12)) / t_step
+        if not args.no_graph:
+            L = len(copies)
+            ys = [torch.empty_like(x) for _ in range(L)]
+            wss = [torch.empty_like(ws) for _ in range(L)]
+            for i in range(L):
+                call(i, ys[i], wss[i])
+            torch.cuda.synchronize()
+            ref = [t.clone() for t in ys]
+            graphs, s = [], torch.cuda.Stream()
+            s.wait_stream(torch.cuda.current_stream())
+            with torch.cuda.stream(s):
+                for i in range(L):
+                    gr = torch.cuda.CUDAGraph()
+                    with torch.cuda.graph(gr, stream=s):
+                        call(i, ys[i], wss[i])
+                    graphs.append(gr)
+            torch.cuda.current_stream().wait_stream(s)
+            torch.cuda.synchronize()
+            for i in range(max(args.warmup, L)):
+                graphs[i % L].replay()
+            torch.cuda.synchronize()
+            ok = all(torch.equal(ys[i], ref[i]) for i in range(L))
+            t0 = time.perf_counter()
+            for i in range(steps):
+                graphs[i % L].replay()
+            torch.cuda.synchronize()
+            gt = (time.perf_counter() - t0) / steps
+            r.update(graph_ms_per_step=gt * 1e3, graph_tokens_per_s=T / gt,
+                     graph_roofline_frac=max(byt / (HBM_PEAK_GBPS * 1e9), fl / (BF16_PEAK_TFLOPS * 1e12)) / gt,
+                     graph_matches_eager=ok)
+        results[T] = r
+    head = results[args.tokens]
+    T = args.tokens
+    roof = None
+    if head.get("up_ms"):
+        up_s = head["up_ms"] * 1e-3
+        if head["path"] == "prefill":
+            ach = 4.0 * T * H * I / up_s / 1e12
+            roof = dict(bound="mfma", achieved=ach, peak=BF16_PEAK_TFLOPS, unit="TFLOP/s",
+                        frac=ach / BF16_PEAK_TFLOPS, traffic=None, avg_ms=head["up_ms"],
+                        kernel="dense gate/up GEMM + SwiGLU (copy-pipeline tiles)", algorithmic_flops=4.0 * T * H * I)
+        else:
+            ub = 2 * I * H * 2 + T * H * 2 + T * I * 2
+            ach = ub / up_s / 1e9
+            roof = dict(bound="hbm", achieved=ach, peak=HBM_PEAK_GBPS, unit="GB/s", frac=ach / HBM_PEAK_GBPS,
+                        traffic=None, avg_ms=head["up_ms"], kernel="dense gate/up weight streaming + SwiGLU",
+                        algorithmic_bytes=ub)
+    cpu = None
+    if not args.no_cpu_baseline:
+        try:
+            from threadpoolctl import threadpool_info
+            cores = max((i.get("num_threads", 1) for i in threadpool_info()), default=1)
+        except Exception:
+            cores = os.cpu_count() or 1
+        n = min(args.cpu_sample_tokens, T)
+        X = om.to_f64(head_x[:n])
+        Wg, Wu, Wd = (om.to_f64(W_host[k]) for k in ("gate", "up", "down"))
+        passes, t0 = 0, time.perf_counter()
+        while True:
+            om.swiglu_mlp(X, Wg, Wu, Wd)
+            passes += 1
+            dt = time.perf_counter() - t0
+            if dt >= 10.0 or passes >= 20:
+                break
+        cpu = dict(value=passes * n / dt, unit="tokens/s", cores=int(cores), kind="oracle",
+                   sample=f"fp64 oracle gated MLP (NumPy/BLAS) on {n} tokens of the T={T} batch, "
+                          f"{passes} passes, {dt:.1f} s on {cores} threads")
+    line = {
+        "metric": METRIC, "value": head["tokens_per_s"], "unit": "tokens/s", "n_gpus": 1,
+        "steps": args.steps, "warmup": args.warmup, "ms_per_step": head["ms_per_step"],
+        "higher_is_better": True, "scaling": "weak", "vs_baseline": None, "dtype": "bf16", "data": "synthetic",
+        "config": {"workload": f"{spec.name} dense gated MLP: hidden {H}, intermediate {I}; T={T}",
+                   "tokens": T, "layer_gb": round(w_bytes / 1e9, 4)},
+        "roofline": roof, "cpu_baseline": cpu, "hbm_gbps": head["hbm_gbps"], "mfma_frac": head["mfma_frac"],
+        "roofline_frac": head["roofline_frac"],
+        "per_T": [{k: (round(v, 5) if isinstance(v, float) else v) for k, v in results[t].items()} for t in Ts],
+        "source_digest": digest, "gen_seconds": round(gen_s, 2),
+    }
+    print(json.dumps(line), flush=True)
+
+
 def main():
     args = parse()
     world = int(os.environ.get("WORLD_SIZE", "1"))
@@ -217,6 +362,9 @@ def main():
               "(expert-parallel sharding is a design note only); use --gpus 1.", file=sys.stderr)
         sys.exit(2)
     sys.path.insert(0, ROOT)
+    if args.dense:
+        bench_dense(args)
+        return
     import torch
     import synth
     import mixture_experts_layer_03_amd as moe
