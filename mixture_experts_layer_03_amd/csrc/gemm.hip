@@ -563,6 +563,175 @@ __global__ __launch_bounds__(1024) void k_tile_dma_split(TileArgs a, int rem_fir
   tile_dma_body<256, 256, 64, 2, true, AM, Epi::SWIGLU>(a, tp, smem);
 }
 
+// ---------------------------------------------------------------------------------
+// u8 weights through the copy pipeline: a 128 x 512 x 64 tile (16 wavefronts of 64 x
+// 64) whose weight operand stays as codes in LDS.  Two stages of (bytes):
+//   A   128 token rows x 128 B (bf16, 16-byte chunks XOR-swizzled by row % 8), 16 KB;
+//   Bq  512 weight rows x 64 B of codes (16-byte chunk c of row r at slot
+//       c ^ (r / 2) % 4, which spreads the 8-byte fragment reads of 16 rows over the
+//       bank lines), 32 KB;
+// and, double-buffered per window of 8 K-steps, the fp16 scales and zero points of the
+// 512 rows for those 8 groups (16 bytes per row and kind, one copy lane each), 16 KB.
+// Copying a row's parameters once per 8 K-steps keeps their line requests at an eighth
+// of the rows per step (per-step copies touched one line per row, more lines than the
+// codes and tokens together).  Each wavefront issues three copies per K-step (8 token
+// rows, twice 16 code rows) and, at the first step of a window, one parameter copy for
+// the next window (64 rows of scales or of zero points; those rows span a gate block
+// and an up block, so the lanes carry their own 64-bit addresses).  A B fragment (16
+// rows x 8 codes per lane) is dequantised in registers as s * (q - z), rounded to bf16
+// (the values the register-staged kernel stores), right before its MFMAs.
+constexpr int kQ8Stage = 128 * 128 + 512 * 64;
+constexpr int kQ8Params = 2 * 512 * 16;  // one window: scales, then zero points
+
+template <bool DUAL, AMode AM, Epi EPI>
+__global__ __launch_bounds__(1024) void k_tile_dma_q8(TileArgs a) {
+  constexpr int TBM = BM, BN = 512, BK = 64, S = 2, WIN = 8;
+  constexpr int WN = BN / 64, NTHR = 1024;
+  constexpr int NCOL = DUAL ? BN / 2 : BN;
+  constexpr int A_BYTES = TBM * BK * 2;
+  static_assert(A_BYTES + BN * BK == kQ8Stage, "stage layout");
+  constexpr int PIPE_BYTES = S * kQ8Stage + 2 * kQ8Params;
+  constexpr int SMEM_BYTES = PIPE_BYTES > 64 * (NCOL + 4) * 4 ? PIPE_BYTES : 64 * (NCOL + 4) * 4;
+  __shared__ __attribute__((aligned(16))) uint16_t smem[SMEM_BYTES / 2];
+  char* const sm = reinterpret_cast<char*>(smem);
+  char* const pm = sm + S * kQ8Stage;  // parameter windows
+
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int w = __builtin_amdgcn_readfirstlane(tid >> 6);
+  TilePos tp;
+  if (!tile_pos<NCOL, BK>(a, tp, gridDim.x)) return;
+  const int nt = tp.nt, e = tp.e, m_begin = tp.m_begin, m_rows = tp.m_rows;
+  const int K = a.K, G = K / 64;
+
+  // weight row of B tile row r (and whether it is an up row)
+  auto weight_row = [&](int r, bool& second) {
+    if (DUAL) {
+      const int blk = r >> 5;
+      second = blk & 1;
+      return min(nt * NCOL + (blk >> 1) * 32 + (r & 31), a.N - 1);  // past N: computed, never stored
+    }
+    second = false;
+    return min(nt * BN + r, a.N - 1);
+  };
+  const int64_t erow = static_cast<int64_t>(e) * a.N;  // first weight row of this expert
+  const char* a_base = uniform_ptr(a.A);
+  const char* q0_base = uniform_ptr(static_cast<const uint8_t*>(a.B0) + erow * K);
+  const char* q1_base = DUAL ? uniform_ptr(static_cast<const uint8_t*>(a.B1) + erow * K) : q0_base;
+
+  // copy 0: A rows 8w + l/8
+  uint32_t a_off;
+  {
+    const int lr = lane >> 3, r = min(8 * w + lr, m_rows - 1);
+    int row;
+    if constexpr (AM == AMode::GATHER)
+      row = a.perm[m_begin + r] / a.k;
+    else
+      row = m_begin + r;
+    a_off = (static_cast<uint32_t>(row) * K + (((lane & 7) ^ (lr & 7)) << 3)) * 2;
+  }
+  // copies 1, 2: code rows 16 q + l/4 for q = w and 16 + w
+  uint32_t q_off[2];
+  const char* q_base[2];
+#pragma unroll
+  for (int h = 0; h < 2; ++h) {
+    const int q = 16 * h + w;
+    const int r = 16 * q + (lane >> 2);
+    bool second;
+    const int n = weight_row(r, second);
+    q_off[h] = static_cast<uint32_t>(n) * K + (((lane & 3) ^ ((r >> 1) & 3)) << 4);
+    bool sec0;
+    weight_row(16 * q, sec0);  // the instruction's 16 rows lie in one 32-row block
+    q_base[h] = sec0 ? q1_base : q0_base;
+  }
+  // parameter copy: rows 64 (w % 8) + l, scales for w < 8, zero points otherwise
+  const uint16_t* p_src;
+  {
+    const int r = 64 * (w & 7) + lane;
+    bool second;
+    const int n = weight_row(r, second);
+    const uint16_t* arr = (w < 8) ? (second ? a.B1s : a.B0s) : (second ? a.B1z : a.B0z);
+    p_src = arr + (erow + n) * G;
+  }
+  auto issue = [&](int stage, int kt) {
+    char* st = sm + stage * kQ8Stage;
+    copy_to_lds(a_base + kt * BK * 2, a_off, reinterpret_cast<uint16_t*>(st + w * 1024));
+#pragma unroll
+    for (int h = 0; h < 2; ++h)
+      copy_to_lds(q_base[h] + kt * BK, q_off[h], reinterpret_cast<uint16_t*>(st + A_BYTES + (16 * h + w) * 1024));
+  };
+  auto issue_params = [&](int win) {  // groups [8 win, 8 win + 8)
+    copy_to_lds(p_src + WIN * win, reinterpret_cast<uint16_t*>(pm + (win & 1) * kQ8Params + w * 1024));
+  };
+
+  f32x4 acc[4][4];
+#pragma unroll
+  for (int i = 0; i < 4; ++i)
+#pragma unroll
+    for (int j = 0; j < 4; ++j) acc[i][j] = f32x4{0.f, 0.f, 0.f, 0.f};
+
+  const int wm = w / WN, wn = w % WN;
+  const int fr = lane & 15, fq = lane >> 4;
+  const int a_rd = (wm * 64 + fr) * BK;
+  auto compute = [&](int stage, int kt) {
+    const char* st = sm + stage * kQ8Stage;
+    const uint16_t* As = reinterpret_cast<const uint16_t*>(st);
+    const char* Bq = st + A_BYTES;
+    const uint16_t* Ps = reinterpret_cast<const uint16_t*>(pm + ((kt / WIN) & 1) * kQ8Params);
+    const uint16_t* Pz = Ps + BN * WIN;
+    float sf[4], zf[4];
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      const int r = wn * 64 + j * 16 + fr;
+      sf[j] = f16_to_f32(Ps[r * WIN + kt % WIN]);
+      zf[j] = f16_to_f32(Pz[r * WIN + kt % WIN]);
+    }
+#pragma unroll
+    for (int ks = 0; ks < BK / 32; ++ks) {
+      const int cc = ((ks * 4 + fq) ^ (fr & 7)) << 3;
+      uint4 af[4];
+#pragma unroll
+      for (int i = 0; i < 4; ++i) af[i] = *reinterpret_cast<const uint4*>(&As[a_rd + cc + i * 16 * BK]);
+      const int o = ks * 4 + fq;  // 8-code group of the row
+#pragma unroll
+      for (int j = 0; j < 4; ++j) {
+        const int r = wn * 64 + j * 16 + fr;
+        const uint2 c =
+            *reinterpret_cast<const uint2*>(Bq + r * 64 + (((o >> 1) ^ ((r >> 1) & 3)) << 4) + ((o & 1) << 3));
+        const float sj = sf[j], zj = zf[j];
+        uint4 bfr;
+        bfr.x = pack_bf16x2(sj * (static_cast<float>(c.x & 0xffu) - zj), sj * (static_cast<float>((c.x >> 8) & 0xffu) - zj));
+        bfr.y = pack_bf16x2(sj * (static_cast<float>((c.x >> 16) & 0xffu) - zj), sj * (static_cast<float>(c.x >> 24) - zj));
+        bfr.z = pack_bf16x2(sj * (static_cast<float>(c.y & 0xffu) - zj), sj * (static_cast<float>((c.y >> 8) & 0xffu) - zj));
+        bfr.w = pack_bf16x2(sj * (static_cast<float>((c.y >> 16) & 0xffu) - zj), sj * (static_cast<float>(c.y >> 24) - zj));
+#pragma unroll
+        for (int i = 0; i < 4; ++i) acc[i][j] = mfma16_bf16(af[i], bfr, acc[i][j]);
+      }
+    }
+  };
+
+  // Two stages: the copies of K-step t + 1 (and, at the first step of a window, the next
+  // window's parameters) are issued after the barrier of step t and have all landed
+  // before the barrier of step t + 1.  A window's parameter buffer is refilled two
+  // windows later, after every wave has passed the barrier of the step that follows its
+  // last step.
+  const int nk = tp.kt1 - tp.kt0;  // the whole K (no split): windows start at steps 0, 8, ..
+  if (nk > 0) {
+    issue_params(0);
+    issue(0, 0);
+  }
+  for (int t = 0; t < nk; ++t) {
+    copy_wait<0>();
+    lds_barrier();
+    if (t + 1 < nk) issue((t + 1) & 1, t + 1);
+    if (t % WIN == 0 && t + WIN < nk) issue_params(t / WIN + 1);
+    compute(t & 1, t);
+  }
+  copy_wait<0>();
+  lds_barrier();
+  epilogue<NTHR, BN, 64, DUAL, EPI>(a, acc, reinterpret_cast<float*>(smem), tid, wm, wn, fr, fq, nt, tp.kp, m_begin,
+                                    m_rows);
+}
+
 // blocks of a launch: whole groups of M-tiles (extra tiles exit) x N-tiles x K-splits,
 // rounded up to the 8 XCDs (NT: the N-tiles, 0 for all of N)
 inline int64_t grid_blocks(const TileArgs& a, int ncol, int NT = 0) {
@@ -621,9 +790,23 @@ hipError_t launch_bn(const TileArgs& a, hipStream_t s) {
         return launch_split<AM>(a, s);
     return launch_dma<512, 64, 2, DUAL, AM, EPI>(a, s);
   } else {
-    // u8 weights are dequantised in registers on their way to LDS.  Single-matrix
-    // products take the wide 8-wavefront tile (half the L2 -> LDS bytes per flop) with
-    // K-step 32 (48 KB of LDS, several blocks per CU); gate/up keeps 128 x 128 x 64.
+    // u8 weights.  Gate/up: codes through the copy pipeline (k_tile_dma_q8) when every
+    // row's parameters of 8 groups can be copied as one aligned 16-byte chunk (K a
+    // multiple of 512, 16-byte aligned parameter arrays); measured on the Ling-3.0-flash
+    // shape at 8192 tokens 3237 -> 2754 us.  Otherwise, and for single-matrix products
+    // (the same kernel measured 1461 -> 1541 us on that down product), the weights are
+    // dequantised in registers on their way to LDS: single-matrix products take the wide
+    // 8-wavefront tile with K-step 32, gate/up 128 x 128 x 64.
+    if constexpr (DUAL) {
+      const bool al16 = (reinterpret_cast<uintptr_t>(a.B0s) | reinterpret_cast<uintptr_t>(a.B0z) |
+                         reinterpret_cast<uintptr_t>(a.B1s) | reinterpret_cast<uintptr_t>(a.B1z)) % 16 == 0;
+      if (a.K % 512 == 0 && al16 && a.ksplit <= 1) {
+        const int64_t blocks = grid_blocks(a, 256);
+        if (blocks <= 0) return hipSuccess;
+        hipLaunchKernelGGL((k_tile_dma_q8<DUAL, AM, EPI>), dim3(static_cast<unsigned>(blocks)), dim3(1024), 0, s, a);
+        return hipGetLastError();
+      }
+    }
     if (!DUAL && a.N >= 256) return launch_one<256, 32, WF, DUAL, AM, EPI>(a, s);
     return launch_one<128, 64, WF, DUAL, AM, EPI>(a, s);
   }
