@@ -1439,7 +1439,10 @@ int grid_for(int64_t items, int ipb, int ncu) {
 
 // K-steps per LDS ring (per wavefront) of the bf16 streaming kernels
 constexpr int kUpRing = 3, kDownRing = 4;
-constexpr int kUpRingU8 = 3, kDownRingU8 = 3;
+// u8 gate/up: a two-step ring (two blocks per CU) split over the four wavefronts
+// measured 3-6% faster than three steps unsplit on the Ling-3.0-flash shape at 1 to 64
+// tokens (graph replay at 64 tokens 338.5 -> 317 us)
+constexpr int kUpRingU8 = 2, kDownRingU8 = 3;
 constexpr int kUpRingU4 = 3, kDownRingU4 = 3;
 // the split u4 gate/up kernel: a two-slot budget (still 3-5 steps in flight with 4-8
 // token rows) lets three blocks share a CU (measured 5-7% faster at 8-64 tokens)
@@ -1523,11 +1526,11 @@ hipError_t launch_skinny_up(const SkinnyUpArgs& a, Act act, WFmt wf, int ncu, hi
   const int64_t ring = part_items(a.part, static_cast<int64_t>(a.mtiles) * (a.I / 16), shared_ring);
   const int64_t ring_all = part_items(0, static_cast<int64_t>(a.mtiles) * (a.I / 16), shared_ring);
   // Gate/up ring kernels split K over the four wavefronts of a block at every size
-  // (measured faster on the bf16 and u4 layers from 1 to 64 tokens: finer work units
-  // even out the last round), except for u8 weights, whose rings leave one block per CU,
-  // and the dense MLP, whose token chunks of one row block share its rows best inside
-  // one block: these split only when their items cannot occupy the CUs otherwise.
-  const bool split_ring = wf == WFmt::U8 || a.dense ? ring_all < small : true;
+  // (measured faster on the bf16, u8 and u4 layers from 1 to 64 tokens: finer work units
+  // even out the last round), except for the dense MLP, whose token chunks of one row
+  // block share its rows best inside one block: it splits only when its items cannot
+  // occupy the CUs otherwise.
+  const bool split_ring = a.dense ? ring_all < small : true;
   if (wf == WFmt::U4) {
     // the only u4 kernel: the configuration checks guarantee its conditions
     if (act != Act::BF16 || a.H % 128 || !stream_ok(a.T, a.H, a.T, a.Is) || !aligned4({a.gate_s, a.gate_z, a.up_s, a.up_z}))
