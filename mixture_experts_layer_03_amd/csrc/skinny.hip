@@ -1443,7 +1443,9 @@ constexpr int kUpRing = 3, kDownRing = 4;
 // measured 3-6% faster than three steps unsplit on the Ling-3.0-flash shape at 1 to 64
 // tokens (graph replay at 64 tokens 338.5 -> 317 us)
 constexpr int kUpRingU8 = 2, kDownRingU8 = 3;
-constexpr int kUpRingU4 = 3, kDownRingU4 = 3;
+// u4 down: two steps (measured 3-5% faster than three on the Ling-3.0-flash u4 shape
+// at 1 to 64 tokens, graph replay at 64 tokens 260.8 -> 248.4 us)
+constexpr int kUpRingU4 = 3, kDownRingU4 = 2;
 // the split u4 gate/up kernel: a two-slot budget (still 3-5 steps in flight with 4-8
 // token rows) lets three blocks share a CU (measured 5-7% faster at 8-64 tokens)
 constexpr int kUpRingSplitU4 = 2;
