@@ -18,12 +18,16 @@
 // per K-step it is paced by the number of wavefronts issuing copies and by the average
 // L2 latency, so the tile moving the fewest bytes per flop with the most wavefronts
 // wins.  Dense single-matrix products too small to fill the chip with such blocks take
-// 128 x 256 x 64 with three stages.  The router product (fp32 out, split over K) takes
-// 128 x 128 x 64.
+// 128 x 256 x 64 with three stages, and so does a gate/up whose last 256-column tile
+// would be mostly padding.  A routed gate/up whose last tile is at most half full
+// (k_tile_dma_split) runs that tile's columns as 256 x 256 tiles over chunks of 256
+// positions.  The router product (fp32 out, split over K) takes 128 x 128 x 64.
 //
-// u8 weights (k_tile): operands are staged global -> registers -> LDS (double buffered),
-// the weight codes dequantised to bf16 (s * (q - z), rounded to nearest even) on the
-// way, eight codes per thread and chunk.
+// u8 weights: gate/up (k_tile_dma_q8) copies the codes and their group parameters to
+// LDS the same way and dequantises each B fragment in registers; the down product
+// (k_tile) stages them global -> registers -> LDS (double buffered), dequantised to
+// bf16 (s * (q - z), rounded to nearest even) on the way, eight codes per thread and
+// chunk.
 //
 // Epilogues stage 64-row slices of the tile through LDS as fp32 and write 16-byte
 // chunks, so every output, gather and scatter is coalesced.  Blocks are numbered so that

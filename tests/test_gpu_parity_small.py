@@ -308,3 +308,23 @@ def test_gate_up_last_tile_over_256_position_chunks(I):
         idx_h = idx.cpu().numpy()
         check_route(spec, idx_h, w.cpu().numpy(), L, x)
         check_forward(spec, y_to_f64(y), idx_h, L, x)
+
+
+@pytest.mark.parametrize("H,I", [(512, 192), (1024, 320)])
+def test_u8_gate_up_copy_pipeline(H, I):
+    """Prefill gate/up with u8 experts and a hidden size that is a multiple of 512: codes
+    and group parameters copied to LDS (parameters once per 8 K-steps, both buffers of
+    the window in use when K spans several windows), dequantised per fragment; every
+    token against the oracle."""
+    import mixture_experts_layer_03_amd as moe
+    spec = SMALL[5].variant(f"u8-dma-H{H}", 153, hidden=H, moe_intermediate=I)
+    L = synth.make_layer(spec)
+    W = device_weights(L)
+    for T in (300, 70):
+        x = synth.make_x(spec, T)
+        log(f"u8 prefill H={H} I={I} T={T}")
+        y, (idx, w, _) = moe.forward(to_dev(x), W, moe_cfg(spec, "prefill"), return_routing=True)
+        torch.cuda.synchronize()
+        idx_h = idx.cpu().numpy()
+        check_route(spec, idx_h, w.cpu().numpy(), L, x)
+        check_forward(spec, y_to_f64(y), idx_h, L, x)
