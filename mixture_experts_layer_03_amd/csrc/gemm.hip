@@ -23,11 +23,10 @@
 // (k_tile_dma_split) runs that tile's columns as 256 x 256 tiles over chunks of 256
 // positions.  The router product (fp32 out, split over K) takes 128 x 128 x 64.
 //
-// u8 weights: gate/up (k_tile_dma_q8) copies the codes and their group parameters to
-// LDS the same way and dequantises each B fragment in registers; the down product
-// (k_tile) stages them global -> registers -> LDS (double buffered), dequantised to
-// bf16 (s * (q - z), rounded to nearest even) on the way, eight codes per thread and
-// chunk.
+// u8 weights (k_tile_dma_q8) copy the codes and their group parameters to LDS the same
+// way and dequantise each B fragment in registers; shapes it does not take (k_tile)
+// stage them global -> registers -> LDS (double buffered), dequantised to bf16
+// (s * (q - z), rounded to nearest even) on the way, eight codes per thread and chunk.
 //
 // Epilogues stage 64-row slices of the tile through LDS as fp32 and write 16-byte
 // chunks, so every output, gather and scatter is coalesced.  Blocks are numbered so that
@@ -114,6 +113,71 @@ __device__ __forceinline__ bool tile_pos(const TileArgs& a, TilePos& p, int nblo
   return true;
 }
 
+// Write-out of one epilogue pass: rows [h*RP, h*RP + RP) of the NCOL-column result,
+// staged in LDS as fp32 (row stride NCOL + 4), go out as 16-byte chunks of 8 columns
+// (fp32, or bf16 after the epilogue's scaling, scatter or combine).
+template <int NTHR, int NCOL, int RP, Epi EPI>
+__device__ __forceinline__ void epilogue_write(const TileArgs& a, const float* ep, int tid, int h, int nt, int kp,
+                                               int m_begin, int m_rows) {
+  constexpr int EPI_LD = NCOL + 4;
+  constexpr int CPR = NCOL / 8;
+#pragma unroll 1
+  for (int c = tid; c < RP * CPR; c += NTHR) {
+    const int r = c / CPR, c8 = (c % CPR) * 8;
+    const int m = h * RP + r;
+    const int col = nt * NCOL + c8;
+    if (m < m_rows && col < a.N) {
+      const float4 v0 = *reinterpret_cast<const float4*>(&ep[r * EPI_LD + c8]);
+      const float4 v1 = *reinterpret_cast<const float4*>(&ep[r * EPI_LD + c8 + 4]);
+      float f[8] = {v0.x, v0.y, v0.z, v0.w, v1.x, v1.y, v1.z, v1.w};
+      const int64_t orow = m_begin + m;
+      if constexpr (EPI == Epi::F32) {
+        float* out = static_cast<float*>(a.out) + kp * a.part_stride + orow * a.ldo + col;
+        if (col + 8 <= a.N && (a.ldo & 3) == 0) {
+          *reinterpret_cast<float4*>(out) = v0;
+          *reinterpret_cast<float4*>(out + 4) = v1;
+        } else {
+          for (int q = 0; q < 8 && col + q < a.N; ++q) out[q] = f[q];
+        }
+      } else {
+        int64_t drow = orow;
+        if constexpr (EPI == Epi::SCALED_SLOT) {
+          const int slot = a.perm[orow];
+          const float ws = a.topk_w[slot];
+#pragma unroll
+          for (int q = 0; q < 8; ++q) f[q] *= ws;
+          drow = slot;
+        } else if constexpr (EPI == Epi::COMBINE) {
+          // the k routed terms of the token in slot order, four slots per batch: their
+          // indices, then their rows, are loaded together (one memory latency per batch)
+          for (int j0 = 0; j0 < a.k; j0 += 4) {
+            int ex[4];
+            uint4 rv[4];
+#pragma unroll
+            for (int q = 0; q < 4; ++q) ex[q] = j0 + q < a.k ? a.idx[orow * a.k + j0 + q] : -1;
+#pragma unroll
+            for (int q = 0; q < 4; ++q)
+              rv[q] = ex[q] >= 0 && ex[q] < a.E ? ldg16(a.r + (orow * a.k + j0 + q) * a.N + col) : make_uint4(0, 0, 0, 0);
+#pragma unroll
+            for (int q = 0; q < 4; ++q) {
+              if (ex[q] < 0 || ex[q] >= a.E) continue;
+              const uint32_t u[4] = {rv[q].x, rv[q].y, rv[q].z, rv[q].w};
+#pragma unroll
+              for (int h = 0; h < 4; ++h) {
+                f[2 * h] += __uint_as_float(u[h] << 16);
+                f[2 * h + 1] += __uint_as_float(u[h] & 0xffff0000u);
+              }
+            }
+          }
+        }
+        uint16_t* out = static_cast<uint16_t*>(a.out) + drow * a.ldo + col;
+        *reinterpret_cast<uint4*>(out) = make_uint4(pack_bf16x2(f[0], f[1]), pack_bf16x2(f[2], f[3]),
+                                                    pack_bf16x2(f[4], f[5]), pack_bf16x2(f[6], f[7]));
+      }
+    }
+  }
+}
+
 // Epilogue shared by the tile kernels: the TBM x NCOL result goes through LDS as fp32
 // in passes of RP rows (RP = 64, 32 or 16, whatever the LDS area holds), then every
 // thread writes 16-byte chunks of 8 columns.  Caller: all LDS reads of the main loop
@@ -123,7 +187,6 @@ __device__ __forceinline__ void epilogue(const TileArgs& a, f32x4 (&acc)[4][4], 
                                          int fr, int fq, int nt, int kp, int m_begin, int m_rows) {
   constexpr int NCOL = DUAL ? BN / 2 : BN;
   constexpr int EPI_LD = NCOL + 4;  // fp32 row stride (bank spread)
-  constexpr int CPR = NCOL / 8;     // 8-column chunks per row
   static_assert(RP == 64 || RP == 32 || RP == 16, "rows per pass");
 #pragma unroll 1
   for (int h = 0; h < TBM / RP && h * RP < m_rows; ++h) {
@@ -149,61 +212,7 @@ __device__ __forceinline__ void epilogue(const TileArgs& a, f32x4 (&acc)[4][4], 
       }
     }
     __syncthreads();
-#pragma unroll 1
-    for (int c = tid; c < RP * CPR; c += NTHR) {
-      const int r = c / CPR, c8 = (c % CPR) * 8;
-      const int m = h * RP + r;
-      const int col = nt * NCOL + c8;
-      if (m < m_rows && col < a.N) {
-        const float4 v0 = *reinterpret_cast<const float4*>(&ep[r * EPI_LD + c8]);
-        const float4 v1 = *reinterpret_cast<const float4*>(&ep[r * EPI_LD + c8 + 4]);
-        float f[8] = {v0.x, v0.y, v0.z, v0.w, v1.x, v1.y, v1.z, v1.w};
-        const int64_t orow = m_begin + m;
-        if constexpr (EPI == Epi::F32) {
-          float* out = static_cast<float*>(a.out) + kp * a.part_stride + orow * a.ldo + col;
-          if (col + 8 <= a.N && (a.ldo & 3) == 0) {
-            *reinterpret_cast<float4*>(out) = v0;
-            *reinterpret_cast<float4*>(out + 4) = v1;
-          } else {
-            for (int q = 0; q < 8 && col + q < a.N; ++q) out[q] = f[q];
-          }
-        } else {
-          int64_t drow = orow;
-          if constexpr (EPI == Epi::SCALED_SLOT) {
-            const int slot = a.perm[orow];
-            const float ws = a.topk_w[slot];
-#pragma unroll
-            for (int q = 0; q < 8; ++q) f[q] *= ws;
-            drow = slot;
-          } else if constexpr (EPI == Epi::COMBINE) {
-            // the k routed terms of the token in slot order, four slots per batch: their
-            // indices, then their rows, are loaded together (one memory latency per batch)
-            for (int j0 = 0; j0 < a.k; j0 += 4) {
-              int ex[4];
-              uint4 rv[4];
-#pragma unroll
-              for (int q = 0; q < 4; ++q) ex[q] = j0 + q < a.k ? a.idx[orow * a.k + j0 + q] : -1;
-#pragma unroll
-              for (int q = 0; q < 4; ++q)
-                rv[q] = ex[q] >= 0 && ex[q] < a.E ? ldg16(a.r + (orow * a.k + j0 + q) * a.N + col) : make_uint4(0, 0, 0, 0);
-#pragma unroll
-              for (int q = 0; q < 4; ++q) {
-                if (ex[q] < 0 || ex[q] >= a.E) continue;
-                const uint32_t u[4] = {rv[q].x, rv[q].y, rv[q].z, rv[q].w};
-#pragma unroll
-                for (int h = 0; h < 4; ++h) {
-                  f[2 * h] += __uint_as_float(u[h] << 16);
-                  f[2 * h + 1] += __uint_as_float(u[h] & 0xffff0000u);
-                }
-              }
-            }
-          }
-          uint16_t* out = static_cast<uint16_t*>(a.out) + drow * a.ldo + col;
-          *reinterpret_cast<uint4*>(out) = make_uint4(pack_bf16x2(f[0], f[1]), pack_bf16x2(f[2], f[3]),
-                                                      pack_bf16x2(f[4], f[5]), pack_bf16x2(f[6], f[7]));
-        }
-      }
-    }
+    epilogue_write<NTHR, NCOL, RP, EPI>(a, ep, tid, h, nt, kp, m_begin, m_rows);
     __syncthreads();
   }
 }
@@ -568,8 +577,12 @@ __global__ __launch_bounds__(1024) void k_tile_dma_split(TileArgs a, int rem_fir
 }
 
 // ---------------------------------------------------------------------------------
-// u8 weights through the copy pipeline: a 128 x 512 x 64 tile (16 wavefronts of 64 x
-// 64) whose weight operand stays as codes in LDS.  Two stages of (bytes):
+// u8 weights through the copy pipeline: a 128 x 512 x 64 tile whose weight operand
+// stays as codes in LDS.  Each of the 16 wavefronts owns all 128 token rows and 32
+// weight rows (8 x 2 MFMA tiles), so every weight fragment is dequantised by exactly
+// one wavefront; gate/up interleave gate and up rows in 16-row blocks, so a
+// wavefront's two fragments are the gate and up rows of the same 16 output columns.
+// Two stages of (bytes):
 //   A   128 token rows x 128 B (bf16, 16-byte chunks XOR-swizzled by row % 8), 16 KB;
 //   Bq  512 weight rows x 64 B of codes (16-byte chunk c of row r at slot
 //       c ^ (r / 2) % 4, which spreads the 8-byte fragment reads of 16 rows over the
@@ -580,22 +593,22 @@ __global__ __launch_bounds__(1024) void k_tile_dma_split(TileArgs a, int rem_fir
 // of the rows per step (per-step copies touched one line per row, more lines than the
 // codes and tokens together).  Each wavefront issues three copies per K-step (8 token
 // rows, twice 16 code rows) and, at the first step of a window, one parameter copy for
-// the next window (64 rows of scales or of zero points; those rows span a gate block
-// and an up block, so the lanes carry their own 64-bit addresses).  A B fragment (16
-// rows x 8 codes per lane) is dequantised in registers as s * (q - z), rounded to bf16
-// (the values the register-staged kernel stores), right before its MFMAs.
+// the next window (64 rows of scales or of zero points; those rows span gate and up
+// blocks, so the lanes carry their own 64-bit addresses).  A fragment (16 rows x 8
+// codes per lane) is dequantised in registers as s * (q - z), rounded to bf16 (the
+// values the register-staged kernel stores), right before its MFMAs.
 constexpr int kQ8Stage = 128 * 128 + 512 * 64;
 constexpr int kQ8Params = 2 * 512 * 16;  // one window: scales, then zero points
 
 template <bool DUAL, AMode AM, Epi EPI>
 __global__ __launch_bounds__(1024) void k_tile_dma_q8(TileArgs a) {
-  constexpr int TBM = BM, BN = 512, BK = 64, S = 2, WIN = 8;
-  constexpr int WN = BN / 64, NTHR = 1024;
+  constexpr int TBM = BM, BN = 512, BK = 64, S = 2, WIN = 8, NTHR = 1024;
   constexpr int NCOL = DUAL ? BN / 2 : BN;
+  constexpr int EPI_LD = NCOL + 4;
   constexpr int A_BYTES = TBM * BK * 2;
   static_assert(A_BYTES + BN * BK == kQ8Stage, "stage layout");
   constexpr int PIPE_BYTES = S * kQ8Stage + 2 * kQ8Params;
-  constexpr int SMEM_BYTES = PIPE_BYTES > 64 * (NCOL + 4) * 4 ? PIPE_BYTES : 64 * (NCOL + 4) * 4;
+  constexpr int SMEM_BYTES = PIPE_BYTES > 64 * EPI_LD * 4 ? PIPE_BYTES : 64 * EPI_LD * 4;
   __shared__ __attribute__((aligned(16))) uint16_t smem[SMEM_BYTES / 2];
   char* const sm = reinterpret_cast<char*>(smem);
   char* const pm = sm + S * kQ8Stage;  // parameter windows
@@ -610,9 +623,9 @@ __global__ __launch_bounds__(1024) void k_tile_dma_q8(TileArgs a) {
   // weight row of B tile row r (and whether it is an up row)
   auto weight_row = [&](int r, bool& second) {
     if (DUAL) {
-      const int blk = r >> 5;
+      const int blk = r >> 4;
       second = blk & 1;
-      return min(nt * NCOL + (blk >> 1) * 32 + (r & 31), a.N - 1);  // past N: computed, never stored
+      return min(nt * NCOL + (blk >> 1) * 16 + (r & 15), a.N - 1);  // past N: computed, never stored
     }
     second = false;
     return min(nt * BN + r, a.N - 1);
@@ -633,7 +646,7 @@ __global__ __launch_bounds__(1024) void k_tile_dma_q8(TileArgs a) {
       row = m_begin + r;
     a_off = (static_cast<uint32_t>(row) * K + (((lane & 7) ^ (lr & 7)) << 3)) * 2;
   }
-  // copies 1, 2: code rows 16 q + l/4 for q = w and 16 + w
+  // copies 1, 2: code rows 16 q + l/4 for q = w and 16 + w (one 16-row block: one matrix)
   uint32_t q_off[2];
   const char* q_base[2];
 #pragma unroll
@@ -643,9 +656,7 @@ __global__ __launch_bounds__(1024) void k_tile_dma_q8(TileArgs a) {
     bool second;
     const int n = weight_row(r, second);
     q_off[h] = static_cast<uint32_t>(n) * K + (((lane & 3) ^ ((r >> 1) & 3)) << 4);
-    bool sec0;
-    weight_row(16 * q, sec0);  // the instruction's 16 rows lie in one 32-row block
-    q_base[h] = sec0 ? q1_base : q0_base;
+    q_base[h] = second ? q1_base : q0_base;
   }
   // parameter copy: rows 64 (w % 8) + l, scales for w < 8, zero points otherwise
   const uint16_t* p_src;
@@ -667,38 +678,36 @@ __global__ __launch_bounds__(1024) void k_tile_dma_q8(TileArgs a) {
     copy_to_lds(p_src + WIN * win, reinterpret_cast<uint16_t*>(pm + (win & 1) * kQ8Params + w * 1024));
   };
 
-  f32x4 acc[4][4];
+  f32x4 acc[8][2];
 #pragma unroll
-  for (int i = 0; i < 4; ++i)
+  for (int i = 0; i < 8; ++i)
 #pragma unroll
-    for (int j = 0; j < 4; ++j) acc[i][j] = f32x4{0.f, 0.f, 0.f, 0.f};
+    for (int j = 0; j < 2; ++j) acc[i][j] = f32x4{0.f, 0.f, 0.f, 0.f};
 
-  const int wm = w / WN, wn = w % WN;
   const int fr = lane & 15, fq = lane >> 4;
-  const int a_rd = (wm * 64 + fr) * BK;
   auto compute = [&](int stage, int kt) {
     const char* st = sm + stage * kQ8Stage;
     const uint16_t* As = reinterpret_cast<const uint16_t*>(st);
     const char* Bq = st + A_BYTES;
     const uint16_t* Ps = reinterpret_cast<const uint16_t*>(pm + ((kt / WIN) & 1) * kQ8Params);
     const uint16_t* Pz = Ps + BN * WIN;
-    float sf[4], zf[4];
+    float sf[2], zf[2];
 #pragma unroll
-    for (int j = 0; j < 4; ++j) {
-      const int r = wn * 64 + j * 16 + fr;
+    for (int j = 0; j < 2; ++j) {
+      const int r = 32 * w + 16 * j + fr;
       sf[j] = f16_to_f32(Ps[r * WIN + kt % WIN]);
       zf[j] = f16_to_f32(Pz[r * WIN + kt % WIN]);
     }
 #pragma unroll
     for (int ks = 0; ks < BK / 32; ++ks) {
       const int cc = ((ks * 4 + fq) ^ (fr & 7)) << 3;
-      uint4 af[4];
+      uint4 af[8];
 #pragma unroll
-      for (int i = 0; i < 4; ++i) af[i] = *reinterpret_cast<const uint4*>(&As[a_rd + cc + i * 16 * BK]);
+      for (int i = 0; i < 8; ++i) af[i] = *reinterpret_cast<const uint4*>(&As[(i * 16 + fr) * BK + cc]);
       const int o = ks * 4 + fq;  // 8-code group of the row
 #pragma unroll
-      for (int j = 0; j < 4; ++j) {
-        const int r = wn * 64 + j * 16 + fr;
+      for (int j = 0; j < 2; ++j) {
+        const int r = 32 * w + 16 * j + fr;
         const uint2 c =
             *reinterpret_cast<const uint2*>(Bq + r * 64 + (((o >> 1) ^ ((r >> 1) & 3)) << 4) + ((o & 1) << 3));
         const float sj = sf[j], zj = zf[j];
@@ -708,7 +717,7 @@ __global__ __launch_bounds__(1024) void k_tile_dma_q8(TileArgs a) {
         bfr.z = pack_bf16x2(sj * (static_cast<float>(c.y & 0xffu) - zj), sj * (static_cast<float>((c.y >> 8) & 0xffu) - zj));
         bfr.w = pack_bf16x2(sj * (static_cast<float>((c.y >> 16) & 0xffu) - zj), sj * (static_cast<float>(c.y >> 24) - zj));
 #pragma unroll
-        for (int i = 0; i < 4; ++i) acc[i][j] = mfma16_bf16(af[i], bfr, acc[i][j]);
+        for (int i = 0; i < 8; ++i) acc[i][j] = mfma16_bf16(af[i], bfr, acc[i][j]);
       }
     }
   };
@@ -732,8 +741,29 @@ __global__ __launch_bounds__(1024) void k_tile_dma_q8(TileArgs a) {
   }
   copy_wait<0>();
   lds_barrier();
-  epilogue<NTHR, BN, 64, DUAL, EPI>(a, acc, reinterpret_cast<float*>(smem), tid, wm, wn, fr, fq, nt, tp.kp, m_begin,
-                                    m_rows);
+  // epilogue in two passes of 64 rows: every wavefront stages its 16 (SwiGLU) or 32
+  // columns of the pass's rows, then the block writes them out
+  float* ep = reinterpret_cast<float*>(smem);
+#pragma unroll 1
+  for (int h = 0; h < 2 && h * 64 < m_rows; ++h) {
+#pragma unroll
+    for (int i = 0; i < 8; ++i) {
+      if ((i >> 2) != h) continue;
+#pragma unroll
+      for (int v = 0; v < 4; ++v) {
+        const int r = (i - 4 * h) * 16 + 4 * fq + v;
+        if constexpr (DUAL) {
+          ep[r * EPI_LD + 16 * w + fr] = silu(acc[i][0][v]) * acc[i][1][v];
+        } else {
+#pragma unroll
+          for (int j = 0; j < 2; ++j) ep[r * EPI_LD + 32 * w + 16 * j + fr] = acc[i][j][v];
+        }
+      }
+    }
+    __syncthreads();
+    epilogue_write<NTHR, NCOL, 64, EPI>(a, ep, tid, h, nt, tp.kp, m_begin, m_rows);
+    __syncthreads();
+  }
 }
 
 // blocks of a launch: whole groups of M-tiles (extra tiles exit) x N-tiles x K-splits,
@@ -794,18 +824,17 @@ hipError_t launch_bn(const TileArgs& a, hipStream_t s) {
         return launch_split<AM>(a, s);
     return launch_dma<512, 64, 2, DUAL, AM, EPI>(a, s);
   } else {
-    // u8 weights.  Gate/up: codes through the copy pipeline (k_tile_dma_q8) when every
-    // row's parameters of 8 groups can be copied as one aligned 16-byte chunk (K a
-    // multiple of 512, 16-byte aligned parameter arrays); measured on the Ling-3.0-flash
-    // shape at 8192 tokens 3237 -> 2754 us.  Otherwise, and for single-matrix products
-    // (the same kernel measured 1461 -> 1541 us on that down product), the weights are
-    // dequantised in registers on their way to LDS: single-matrix products take the wide
-    // 8-wavefront tile with K-step 32, gate/up 128 x 128 x 64.
-    if constexpr (DUAL) {
+    // u8 weights: codes through the copy pipeline (k_tile_dma_q8) when every row's
+    // parameters of 8 groups can be copied as one aligned 16-byte chunk (K a multiple
+    // of 512, 16-byte aligned parameter arrays); measured on the Ling-3.0-flash shape at
+    // 8192 tokens: gate/up 3251 -> 2131 us, down 1462 -> 1236 us.  Otherwise the weights
+    // are dequantised in registers on their way to LDS: single-matrix products take the
+    // wide 8-wavefront tile with K-step 32, gate/up 128 x 128 x 64.
+    {
       const bool al16 = (reinterpret_cast<uintptr_t>(a.B0s) | reinterpret_cast<uintptr_t>(a.B0z) |
-                         reinterpret_cast<uintptr_t>(a.B1s) | reinterpret_cast<uintptr_t>(a.B1z)) % 16 == 0;
+                         (DUAL ? reinterpret_cast<uintptr_t>(a.B1s) | reinterpret_cast<uintptr_t>(a.B1z) : 0)) % 16 == 0;
       if (a.K % 512 == 0 && al16 && a.ksplit <= 1) {
-        const int64_t blocks = grid_blocks(a, 256);
+        const int64_t blocks = grid_blocks(a, DUAL ? 256 : 512);
         if (blocks <= 0) return hipSuccess;
         hipLaunchKernelGGL((k_tile_dma_q8<DUAL, AM, EPI>), dim3(static_cast<unsigned>(blocks)), dim3(1024), 0, s, a);
         return hipGetLastError();

@@ -310,12 +310,12 @@ def test_gate_up_last_tile_over_256_position_chunks(I):
         check_forward(spec, y_to_f64(y), idx_h, L, x)
 
 
-@pytest.mark.parametrize("H,I", [(512, 192), (1024, 320)])
-def test_u8_gate_up_copy_pipeline(H, I):
-    """Prefill gate/up with u8 experts and a hidden size that is a multiple of 512: codes
-    and group parameters copied to LDS (parameters once per 8 K-steps, both buffers of
-    the window in use when K spans several windows), dequantised per fragment; every
-    token against the oracle."""
+@pytest.mark.parametrize("H,I", [(512, 192), (1024, 512)])
+def test_u8_copy_pipeline(H, I):
+    """Prefill with u8 experts whose reduction sizes are multiples of 512 (gate/up: H;
+    down: I, in the second case): codes and group parameters copied to LDS (parameters
+    once per 8 K-steps, both buffers in use when K spans several windows), dequantised
+    per fragment; every token against the oracle."""
     import mixture_experts_layer_03_amd as moe
     spec = SMALL[5].variant(f"u8-dma-H{H}", 153, hidden=H, moe_intermediate=I)
     L = synth.make_layer(spec)
