@@ -108,6 +108,8 @@ struct SkinnyDownArgs {
 };
 hipError_t launch_skinny_down(const SkinnyDownArgs& a, Act act, WFmt wf, int ncu, hipStream_t s);
 
+// largest top_k the library accepts (the combine kernel keeps a token's k terms in registers)
+constexpr int kMaxTopK = 16;
 struct CombineArgs {
   const void* r;            // [T*k, H] slot order (fp32 or bf16)
   const float* rs;          // [T, H] fp32 or null

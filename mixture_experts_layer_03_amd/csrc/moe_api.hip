@@ -33,7 +33,7 @@ moe_status ok() {
   return MOE_OK;
 }
 
-constexpr int64_t kMaxH = 16384, kMaxE = 1024, kMaxI = 32768, kMaxT = int64_t(1) << 20, kMaxK = 16;
+constexpr int64_t kMaxH = 16384, kMaxE = 1024, kMaxI = 32768, kMaxT = int64_t(1) << 20, kMaxK = kMaxTopK;
 constexpr int64_t kMaxGroupsGpu = 64;
 constexpr int kDecodeMaxT = 64;
 constexpr int kFusedRouteMaxT = 16;  // one workgroup routes and permutes up to this many tokens

@@ -1389,31 +1389,42 @@ __global__ __launch_bounds__(256) void k_combine(CombineArgs a) {
   for (int64_t i = blockIdx.x * 256ll + threadIdx.x; i < nvec; i += static_cast<int64_t>(gridDim.x) * 256) {
     const int t = static_cast<int>(i / (a.H / 4));
     const int h = static_cast<int>(i % (a.H / 4)) * 4;
+    // the token's k indices, its k routed rows and its shared row are loaded together
+    // (one memory latency; a row whose index is invalid is loaded but not added: its
+    // slot holds no routed term), then added in slot order
     float4 s = make_float4(0.f, 0.f, 0.f, 0.f);
-    for (int j = 0; j < a.k; ++j) {
-      const int64_t slot = static_cast<int64_t>(t) * a.k + j;
-      const int e = a.idx[slot];
-      if (e < 0 || e >= a.E) continue;
+    const int64_t slot0 = static_cast<int64_t>(t) * a.k;
+    int ex[kMaxTopK];
+    float4 rv[kMaxTopK];
+#pragma unroll
+    for (int j = 0; j < kMaxTopK; ++j)
+      if (j < a.k) ex[j] = a.idx[slot0 + j];
+#pragma unroll
+    for (int j = 0; j < kMaxTopK; ++j) {
+      if (j >= a.k) continue;
       if (a.r_bf16) {
-        const uint2 v = *reinterpret_cast<const uint2*>(static_cast<const uint16_t*>(a.r) + slot * a.H + h);
-        s.x += __uint_as_float(v.x << 16);
-        s.y += __uint_as_float(v.x & 0xffff0000u);
-        s.z += __uint_as_float(v.y << 16);
-        s.w += __uint_as_float(v.y & 0xffff0000u);
+        const uint2 v = *reinterpret_cast<const uint2*>(static_cast<const uint16_t*>(a.r) + (slot0 + j) * a.H + h);
+        rv[j] = make_float4(__uint_as_float(v.x << 16), __uint_as_float(v.x & 0xffff0000u),
+                            __uint_as_float(v.y << 16), __uint_as_float(v.y & 0xffff0000u));
       } else {
-        const float4 v = *reinterpret_cast<const float4*>(static_cast<const float*>(a.r) + slot * a.H + h);
-        s.x += v.x;
-        s.y += v.y;
-        s.z += v.z;
-        s.w += v.w;
+        rv[j] = *reinterpret_cast<const float4*>(static_cast<const float*>(a.r) + (slot0 + j) * a.H + h);
       }
     }
+    const float4 vs = a.rs ? *reinterpret_cast<const float4*>(a.rs + static_cast<int64_t>(t) * a.H + h)
+                           : make_float4(0.f, 0.f, 0.f, 0.f);
+#pragma unroll
+    for (int j = 0; j < kMaxTopK; ++j) {
+      if (j >= a.k || ex[j] < 0 || ex[j] >= a.E) continue;
+      s.x += rv[j].x;
+      s.y += rv[j].y;
+      s.z += rv[j].z;
+      s.w += rv[j].w;
+    }
     if (a.rs) {
-      const float4 v = *reinterpret_cast<const float4*>(a.rs + static_cast<int64_t>(t) * a.H + h);
-      s.x += v.x;
-      s.y += v.y;
-      s.z += v.z;
-      s.w += v.w;
+      s.x += vs.x;
+      s.y += vs.y;
+      s.z += vs.z;
+      s.w += vs.w;
     }
     AT* y = static_cast<AT*>(a.y) + static_cast<int64_t>(t) * a.H + h;
     if constexpr (ACT == Act::BF16) {
