@@ -8,13 +8,15 @@
 // the weight operand rows are the output features and K runs along memory.
 //
 // Block tile 128 (tokens) x BN (weight rows) x BK with BN/32 wavefronts, each owning a
-// 64 x 64 sub-tile (a 4 x 4 grid of v_mfma_f32_16x16x32_bf16).  LDS tiles hold 16-byte
+// 64 x 64 sub-tile (a 4 x 4 grid of v_mfma_f32_16x16x32_bf16); the routed gate/up of
+// the copy pipeline takes BN/64 wavefronts of 64 x 128 (4 x 8).  LDS tiles hold 16-byte
 // chunks XOR-swizzled by row, so fragment reads do not collide on banks.
 //
 // bf16 weights (k_tile_dma): both operands go HBM/L2 -> LDS through the load unit's
 // direct copy (global_load_lds_dwordx4), S LDS stages deep, with explicit waits.  The
 // layer's products take 128 x 512 x 64 with two stages (160 KB of LDS, 16 wavefronts,
-// four per SIMD): measured on this chip, the load path is what bounds these GEMMs, and
+// four per SIMD; 8 wider ones for the routed gate/up): measured on this chip, the load
+// path is what bounds these GEMMs, and
 // per K-step it is paced by the number of wavefronts issuing copies and by the average
 // L2 latency, so the tile moving the fewest bytes per flop with the most wavefronts
 // wins.  Dense single-matrix products too small to fill the chip with such blocks take
@@ -182,8 +184,10 @@ __device__ __forceinline__ void epilogue_write(const TileArgs& a, const float* e
 // in passes of RP rows (RP = 64, 32 or 16, whatever the LDS area holds), then every
 // thread writes 16-byte chunks of 8 columns.  Caller: all LDS reads of the main loop
 // are finished (a barrier) before the first pass.
-template <int NTHR, int BN, int RP, bool DUAL, Epi EPI, int TBM = BM>
-__device__ __forceinline__ void epilogue(const TileArgs& a, f32x4 (&acc)[4][4], float* ep, int tid, int wm, int wn,
+// A wavefront's result is NH 64 x 64 sub-tiles side by side along N (acc[hh]): sub-tile
+// hh is placed as the 64-column band wn * NH + hh.
+template <int NTHR, int BN, int RP, bool DUAL, Epi EPI, int TBM = BM, int NH = 1>
+__device__ __forceinline__ void epilogue(const TileArgs& a, f32x4 (&acc)[NH][4][4], float* ep, int tid, int wm, int wn,
                                          int fr, int fq, int nt, int kp, int m_begin, int m_rows) {
   constexpr int NCOL = DUAL ? BN / 2 : BN;
   constexpr int EPI_LD = NCOL + 4;  // fp32 row stride (bank spread)
@@ -195,18 +199,22 @@ __device__ __forceinline__ void epilogue(const TileArgs& a, f32x4 (&acc)[4][4], 
     const int i0 = ((h * RP) & 63) >> 4;
     if (wm == (h * RP) >> 6) {
 #pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        if (i < i0 || i >= i0 + RP / 16) continue;
+      for (int hh = 0; hh < NH; ++hh) {
+        const int band = wn * NH + hh;
 #pragma unroll
-        for (int v = 0; v < 4; ++v) {
-          const int r = (i - i0) * 16 + 4 * fq + v;
-          if constexpr (DUAL) {
+        for (int i = 0; i < 4; ++i) {
+          if (i < i0 || i >= i0 + RP / 16) continue;
 #pragma unroll
-            for (int j = 0; j < 2; ++j)
-              ep[r * EPI_LD + wn * 32 + j * 16 + fr] = silu(acc[i][j][v]) * acc[i][j + 2][v];
-          } else {
+          for (int v = 0; v < 4; ++v) {
+            const int r = (i - i0) * 16 + 4 * fq + v;
+            if constexpr (DUAL) {
 #pragma unroll
-            for (int j = 0; j < 4; ++j) ep[r * EPI_LD + wn * 64 + j * 16 + fr] = acc[i][j][v];
+              for (int j = 0; j < 2; ++j)
+                ep[r * EPI_LD + band * 32 + j * 16 + fr] = silu(acc[hh][i][j][v]) * acc[hh][i][j + 2][v];
+            } else {
+#pragma unroll
+              for (int j = 0; j < 4; ++j) ep[r * EPI_LD + band * 64 + j * 16 + fr] = acc[hh][i][j][v];
+            }
           }
         }
       }
@@ -373,8 +381,8 @@ __global__ __launch_bounds__(BN * 2) void k_tile(TileArgs a) {
     __syncthreads();
   }
 
-  epilogue<NTHR, BN, 64, DUAL, EPI>(a, acc, reinterpret_cast<float*>(smem), tid, wm, wn, fr, fq, nt, kp, m_begin,
-                                      m_rows);
+  epilogue<NTHR, BN, 64, DUAL, EPI>(a, reinterpret_cast<f32x4(&)[1][4][4]>(acc), reinterpret_cast<float*>(smem), tid,
+                                    wm, wn, fr, fq, nt, kp, m_begin, m_rows);
 }
 
 // ---------------------------------------------------------------------------------
@@ -404,12 +412,23 @@ constexpr int dma_smem_elems() {
   return S * STAGE_ELEMS > EPI_ELEMS ? S * STAGE_ELEMS : EPI_ELEMS;
 }
 
-// One TBM x BN tile of the copy pipeline at position tp, with (TBM / 64) x (BN / 64)
-// wavefronts (the block's) and dma_smem_elems() elements of LDS at smem.
-template <int TBM, int BN, int BK, int S, bool DUAL, AMode AM, Epi EPI>
+// Wavefronts of a copy-pipeline tile: (TBM / 64) x (BN / WT), each 64 token rows x WT
+// weight rows.
+template <int TBM, int BN, int WT>
+constexpr int dma_threads() {
+  return (TBM / 64) * (BN / WT) * 64;
+}
+
+// One TBM x BN tile of the copy pipeline at position tp, with dma_threads() threads
+// (the block's) and dma_smem_elems() elements of LDS at smem.  A wavefront computes
+// 64 x WT (WT = 64 or 128: 4 x 4 or 4 x 8 MFMA tiles).  Per K-step a wavefront reads
+// (64 + WT) rows of fragments from LDS, so the wider tile reads a quarter less of the
+// LDS per flop, with half as many wavefronts issuing copies.
+template <int TBM, int BN, int BK, int S, bool DUAL, AMode AM, Epi EPI, int WT = 64>
 __device__ __forceinline__ void tile_dma_body(const TileArgs& a, const TilePos& tp, uint16_t* smem) {
-  constexpr int WN = BN / 64;
-  constexpr int NW = (TBM / 64) * WN;           // wavefronts (each a 64 x 64 sub-tile)
+  constexpr int NH = WT / 64;                   // 64-column sub-tiles per wavefront
+  constexpr int WN = BN / WT;
+  constexpr int NW = (TBM / 64) * WN;           // wavefronts
   constexpr int NTHR = NW * 64;
   constexpr int CPRK = BK / 8;                  // 16-byte chunks per LDS row
   constexpr int RPI = 64 / CPRK;                // tile rows per copy instruction
@@ -419,6 +438,7 @@ __device__ __forceinline__ void tile_dma_body(const TileArgs& a, const TilePos& 
   constexpr int NCOL = DUAL ? BN / 2 : BN;
   constexpr int STAGE_ELEMS = (TBM + BN) * BK;
   static_assert(S >= 2 && TBM % 64 == 0 && TBM % RPI == 0 && BN % RPI == 0 && NTHR <= 1024, "pipeline shape");
+  static_assert((WT == 64 || WT == 128) && BN % WT == 0, "wavefront tile");
   static_assert(J * (S - 1) < 64, "vmcnt range");
 
   const int tid = threadIdx.x, lane = tid & 63;
@@ -485,30 +505,34 @@ __device__ __forceinline__ void tile_dma_body(const TileArgs& a, const TilePos& 
     }
   };
 
-  f32x4 acc[4][4];
+  f32x4 acc[NH][4][4];
 #pragma unroll
-  for (int i = 0; i < 4; ++i)
+  for (int hh = 0; hh < NH; ++hh)
 #pragma unroll
-    for (int j = 0; j < 4; ++j) acc[i][j] = f32x4{0.f, 0.f, 0.f, 0.f};
+    for (int i = 0; i < 4; ++i)
+#pragma unroll
+      for (int j = 0; j < 4; ++j) acc[hh][i][j] = f32x4{0.f, 0.f, 0.f, 0.f};
 
   const int wm = w / WN, wn = w % WN;
   const int fr = lane & 15, fq = lane >> 4;
-  const int a_rd = (wm * 64 + fr) * BK, b_rd = (wn * 64 + fr) * BK;
+  const int a_rd = (wm * 64 + fr) * BK, b_rd = (wn * WT + fr) * BK;
   auto compute = [&](int stage) {
     const uint16_t* As = smem + stage * STAGE_ELEMS;
     const uint16_t* Bs = As + TBM * BK;
 #pragma unroll
     for (int ks = 0; ks < BK / 32; ++ks) {
       const int cc = ((ks * 4 + fq) ^ swz<BK>(fr)) << 3;
-      uint4 af[4], bf[4];
+      uint4 af[4], bf[4 * NH];
 #pragma unroll
       for (int i = 0; i < 4; ++i) af[i] = *reinterpret_cast<const uint4*>(&As[a_rd + cc + i * 16 * BK]);
 #pragma unroll
-      for (int j = 0; j < 4; ++j) bf[j] = *reinterpret_cast<const uint4*>(&Bs[b_rd + cc + j * 16 * BK]);
+      for (int j = 0; j < 4 * NH; ++j) bf[j] = *reinterpret_cast<const uint4*>(&Bs[b_rd + cc + j * 16 * BK]);
 #pragma unroll
-      for (int i = 0; i < 4; ++i)
+      for (int hh = 0; hh < NH; ++hh)
 #pragma unroll
-        for (int j = 0; j < 4; ++j) acc[i][j] = mfma16_bf16(af[i], bf[j], acc[i][j]);
+        for (int i = 0; i < 4; ++i)
+#pragma unroll
+          for (int j = 0; j < 4; ++j) acc[hh][i][j] = mfma16_bf16(af[i], bf[hh * 4 + j], acc[hh][i][j]);
     }
   };
 
@@ -534,16 +558,16 @@ __device__ __forceinline__ void tile_dma_body(const TileArgs& a, const TilePos& 
   }
   copy_wait<0>();  // every wave is done reading the stages; all copies have landed
   lds_barrier();
-  epilogue<NTHR, BN, 64, DUAL, EPI, TBM>(a, acc, reinterpret_cast<float*>(smem), tid, wm, wn, fr, fq, nt, tp.kp,
+  epilogue<NTHR, BN, 64, DUAL, EPI, TBM, NH>(a, acc, reinterpret_cast<float*>(smem), tid, wm, wn, fr, fq, nt, tp.kp,
                                          m_begin, m_rows);
 }
 
-template <int BN, int BK, int S, bool DUAL, AMode AM, Epi EPI>
-__global__ __launch_bounds__(BN * 2) void k_tile_dma(TileArgs a) {
+template <int BN, int BK, int S, bool DUAL, AMode AM, Epi EPI, int WT>
+__global__ __launch_bounds__((dma_threads<BM, BN, WT>())) void k_tile_dma(TileArgs a) {
   __shared__ __attribute__((aligned(16))) uint16_t smem[dma_smem_elems<BM, BN, BK, S, DUAL>()];
   TilePos tp;
   if (!tile_pos<DUAL ? BN / 2 : BN, BK>(a, tp, gridDim.x)) return;
-  tile_dma_body<BM, BN, BK, S, DUAL, AM, EPI>(a, tp, smem);
+  tile_dma_body<BM, BN, BK, S, DUAL, AM, EPI, WT>(a, tp, smem);
 }
 
 // Routed gate/up (SwiGLU) whose last 256-column N-tile is at most half full (e.g. 1408
@@ -552,8 +576,9 @@ __global__ __launch_bounds__(BN * 2) void k_tile_dma(TileArgs a) {
 // tiles (128 columns of gate and of up) over chunks of 256 positions (tiles2), so
 // those columns cost 512 rows of copies per K-step instead of 640 for half the useful
 // work.  The remainder blocks come last, as the smallest units of the final round.
-template <AMode AM>
-__global__ __launch_bounds__(1024) void k_tile_dma_split(TileArgs a, int rem_first) {
+template <AMode AM, int WT>
+__global__ __launch_bounds__((dma_threads<BM, 512, WT>())) void k_tile_dma_split(TileArgs a, int rem_first) {
+  static_assert(dma_threads<BM, 512, WT>() == dma_threads<256, 256, WT>(), "one block size for both tile shapes");
   constexpr int SM_MAIN = dma_smem_elems<BM, 512, 64, 2, true>();
   constexpr int SM_REM = dma_smem_elems<256, 256, 64, 2, true>();
   __shared__ __attribute__((aligned(16))) uint16_t smem[SM_MAIN > SM_REM ? SM_MAIN : SM_REM];
@@ -561,7 +586,7 @@ __global__ __launch_bounds__(1024) void k_tile_dma_split(TileArgs a, int rem_fir
   TilePos tp;
   if (static_cast<int>(blockIdx.x) < rem_first) {
     if (!tile_pos<256, 64>(a, tp, rem_first, nt_main)) return;
-    tile_dma_body<BM, 512, 64, 2, true, AM, Epi::SWIGLU>(a, tp, smem);
+    tile_dma_body<BM, 512, 64, 2, true, AM, Epi::SWIGLU, WT>(a, tp, smem);
     return;
   }
   const int r = blockIdx.x - rem_first;
@@ -573,7 +598,7 @@ __global__ __launch_bounds__(1024) void k_tile_dma_split(TileArgs a, int rem_fir
   tp.kp = 0;
   tp.kt0 = 0;
   tp.kt1 = a.K / 64;
-  tile_dma_body<256, 256, 64, 2, true, AM, Epi::SWIGLU>(a, tp, smem);
+  tile_dma_body<256, 256, 64, 2, true, AM, Epi::SWIGLU, WT>(a, tp, smem);
 }
 
 // ---------------------------------------------------------------------------------
@@ -784,17 +809,31 @@ hipError_t launch_one(const TileArgs& a, hipStream_t s) {
   return hipGetLastError();
 }
 
+// Wavefront tile width (weight rows).  The routed gate/up takes 64 x 128 wavefront
+// tiles (8 wavefronts per 128 x 512 block, a quarter fewer LDS fragment reads per
+// flop); measured against 64 x 64 tiles (16 wavefronts) on the MI355X: Ling-lite at
+// 4096 tokens 419 -> 409 us, Ling-3.0-flash at 8192 tokens 2036-2061 -> 2028-2031 us.
+// The single-matrix products keep 64 x 64 (routed down with 64 x 128: 224 -> 233 us
+// and 673 -> 717 us on the Ling-lite and Ling-2.6-flash shapes), and so does the
+// dense gate/up (the shared expert: 160 -> 165 us on the Ling-3.0-flash shape).
+constexpr int kWaveGateUp = 128;
+template <int BN, bool DUAL, AMode AM>
+constexpr int wave_width() {
+  return BN == 512 && DUAL && AM == AMode::GATHER ? kWaveGateUp : 64;
+}
+
 template <int BN, int BK, int S, bool DUAL, AMode AM, Epi EPI>
 hipError_t launch_dma(const TileArgs& a, hipStream_t s) {
+  constexpr int WT = wave_width<BN, DUAL, AM>();
   const int64_t blocks = grid_blocks(a, DUAL ? BN / 2 : BN);
   if (blocks <= 0) return hipSuccess;
-  hipLaunchKernelGGL((k_tile_dma<BN, BK, S, DUAL, AM, EPI>), dim3(static_cast<unsigned>(blocks)), dim3(BN * 2), 0, s,
-                     a);
+  hipLaunchKernelGGL((k_tile_dma<BN, BK, S, DUAL, AM, EPI, WT>), dim3(static_cast<unsigned>(blocks)),
+                     dim3(dma_threads<BM, BN, WT>()), 0, s, a);
   return hipGetLastError();
 }
 
 // Tile shapes of the copy pipeline (bf16 weights): 128 token rows x 512 weight rows,
-// K-step 64, two LDS stages (160 KB, 16 wavefronts, one block per CU).  A dense
+// K-step 64, two LDS stages (160 KB, one block per CU).  A dense
 // single-matrix product with fewer such blocks than CUs, and a gate/up product whose
 // last 256-column tile would be mostly padding, take 128 x 256 x 64 with three stages
 // instead.
@@ -803,7 +842,8 @@ hipError_t launch_split(const TileArgs& a, hipStream_t s) {
   const int64_t main_blocks = grid_blocks(a, 256, a.N / 256);
   const int64_t blocks = main_blocks + a.mtiles2_bound;
   if (blocks <= 0) return hipSuccess;
-  hipLaunchKernelGGL(k_tile_dma_split<AM>, dim3(static_cast<unsigned>(blocks)), dim3(1024), 0, s, a,
+  hipLaunchKernelGGL((k_tile_dma_split<AM, kWaveGateUp>), dim3(static_cast<unsigned>(blocks)),
+                     dim3(dma_threads<BM, 512, kWaveGateUp>()), 0, s, a,
                      static_cast<int>(main_blocks));
   return hipGetLastError();
 }
