@@ -213,6 +213,66 @@ def test_odd_expert_count_and_single_group():
         check_forward(spec, y_to_f64(y), idx.cpu().numpy(), L, x)
 
 
+_SPEC_CACHE = {}
+
+
+def layer_of(spec):
+    if spec.name not in _SPEC_CACHE:
+        L = synth.make_layer(spec)
+        _SPEC_CACHE[spec.name] = (L, device_weights(L))
+    return _SPEC_CACHE[spec.name]
+
+
+@pytest.mark.parametrize("path,T", [("decode", 1), ("decode", 40), ("prefill", 33), ("prefill", 300),
+                                    ("auto", 100)])
+def test_top_k_16(path, T):
+    """The largest top_k the library takes: sixteen routed terms per token through the
+    routing, the permutation and both combines (the decode kernel and the shared-down
+    epilogue)."""
+    import mixture_experts_layer_03_amd as moe
+    spec = SMALL[2].variant("top16", 152, num_experts=48, top_k=16)
+    L, W = layer_of(spec)
+    x = synth.make_x(spec, T)
+    log(f"forward top_k=16 E=48 T={T} path={path}")
+    y, (idx, w, _) = moe.forward(to_dev(x), W, moe_cfg(spec, path), return_routing=True)
+    torch.cuda.synchronize()
+    check_route(spec, idx.cpu().numpy(), w.cpu().numpy(), L, x)
+    check_forward(spec, y_to_f64(y), idx.cpu().numpy(), L, x)
+
+
+@pytest.mark.parametrize("I,T,path", [(1024, 700, "prefill"), (1152, 700, "prefill"), (1024, 64, "decode")])
+def test_every_token_on_one_expert(I, T, path):
+    """The most skewed routing: one expert among every token's picks, so it holds all T
+    tokens (six 128-row M-tiles and three 256-position chunks of one expert at 700
+    tokens; the 128 x 512 gate/up tiles at I = 1024, the split kernel at I = 1152, four
+    16-token chunks in the decode kernels).  The oracle's forced-routing mode gives the
+    weights of those sets."""
+    import mixture_experts_layer_03_amd as moe
+    spec = SMALL[2].variant(f"one-expert-{I}", 153, moe_intermediate=I)
+    L, W = layer_of(spec)
+    x = synth.make_x(spec, T)
+    ocfg = oracle_cfg(spec)
+    _, d0 = om.forward(x, L, ocfg)
+    hot = 5
+    forced = d0["idx"].copy()
+    for t in range(T):
+        row = [int(e) for e in forced[t]]
+        if hot in row:
+            row.remove(hot)
+        else:
+            row.pop()
+        forced[t] = [hot] + row
+    y_o, d = om.forward(x, L, ocfg, forced_idx=forced)
+    assert (d["idx"] == hot).any(axis=1).all()
+    log(f"experts with every token on expert {hot}: I={I} T={T} path={path}")
+    idx = torch.from_numpy(d["idx"].astype(np.int32)).cuda()
+    wt = torch.from_numpy(d["w"].astype(np.float32)).cuda()
+    y = moe.experts(to_dev(x), W, idx, wt, moe_cfg(spec, path))
+    torch.cuda.synchronize()
+    rel = np.abs(y_to_f64(y) - y_o).max(axis=1) / np.abs(y_o).max(axis=1)
+    assert rel.max() <= 2e-2, rel.max()
+
+
 def test_zero_tokens_is_noop():
     import mixture_experts_layer_03_amd as moe
     spec, L, W = layer(2)
