@@ -83,6 +83,13 @@ def check_plain_topk(om):
         assert set(r.idx.tolist()) == set(ref.tolist()), "n_group=1 must be plain top-k"
         py = sorted(range(E), key=lambda e: (-l[e], e))[:k]
         assert r.idx.tolist() == py, "order: descending score, ties to the lower index"
+    # exact ties (a reading, R4: the pages' argpartition leaves their order open):
+    # equal scores go to the lower expert index
+    l = np.array([0.5, 2.0, 2.0, -1.0, 2.0, 2.0])
+    for k, want in ((1, [1]), (2, [1, 2]), (3, [1, 2, 4]), (5, [1, 2, 4, 5, 0])):
+        for fn in ("sigmoid", "softmax"):
+            r = om.route_token(l, _cfg(om, num_experts=6, top_k=k, score_function=fn))
+            assert r.idx.tolist() == want, f"ties to the lower index ({fn}, k={k})"
 
 
 # ------------------------------------------------ P4 brute-force enumeration

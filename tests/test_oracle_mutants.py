@@ -48,8 +48,80 @@ def _m7_nibble_order(mp):          # u4: high nibble taken as the even element
     mp.setattr(om, "unpack_u4", bad)
 
 
+def _m8_router_bias_dropped(mp):   # the router's own bias left out of the logits
+    mp.setattr(om, "router_logits", lambda x, W, b=None: om.to_f64(x) @ om.to_f64(W).T)
+
+
+def _m9_sigmoid_sign(mp):          # sigmoid of -l
+    orig = om.score
+
+    def bad(l, fn):
+        return 1.0 / (1.0 + np.exp(np.asarray(l, dtype=np.float64))) if fn == "sigmoid" else orig(l, fn)
+    mp.setattr(om, "score", bad)
+
+
+def _m10_gate_without_silu(mp):    # sigmoid(a) in place of a * sigmoid(a)
+    mp.setattr(om, "silu", lambda a: 1.0 / (1.0 + np.exp(-a)))
+
+
+def _m11_down_from_up(mp):         # wrong operand: the up matrix as the down projection
+    def bad(X, Wg, Wu, Wd):
+        h = om.silu(X @ Wg.T) * (X @ Wu.T)
+        return h @ Wu if Wu.shape[::-1] == Wd.shape else h @ Wd
+    mp.setattr(om, "swiglu_mlp", bad)
+
+
+def _m12_zero_point_sign(mp):      # s * (q + z)
+    orig = om.dequant_u8
+
+    def bad(q, s, z, group=64):
+        return orig(q, s, -om.to_f64(z), group)
+    mp.setattr(om, "dequant_u8", bad)
+
+
+def _m13_ties_to_higher_index(mp):  # equal selection scores: the higher expert index first
+    def bad(sel, k):
+        n = sel.shape[0]
+        order = np.argsort(-sel[::-1], kind="stable")
+        return (n - 1 - order)[:k]
+    mp.setattr(om, "select_topk", bad)
+
+
+def _m14_shared_dropped(mp):       # the shared expert left out of the sum
+    orig = om.combine
+    mp.setattr(om, "combine", lambda terms, w_row, y_s: orig(terms, w_row, None))
+
+
+def _m15_worst_groups_kept(mp):    # the lowest-scoring groups kept
+    orig = om.kept_groups
+
+    def bad(sel, G, g):
+        keep, sigma = orig(sel, G, G)
+        return keep[G - g:], sigma
+    mp.setattr(om, "kept_groups", bad)
+
+
+def _m16_renorm_without_epsilon(mp):  # w / sum(w), no 1e-20
+    mp.setattr(om, "normalize", lambda w, k, norm: w / w.sum() if (k > 1 and norm) else w)
+
+
+def _m17_softmax_over_tokens(mp):  # softmax taken over the wrong axis
+    orig = om.score
+
+    def bad(l, fn):
+        if fn != "softmax":
+            return orig(l, fn)
+        a = np.asarray(l, dtype=np.float64)
+        p = np.exp(a - a.max(axis=0, keepdims=True))
+        return p / p.sum(axis=0, keepdims=True)
+    mp.setattr(om, "score", bad)
+
+
 MUTANTS = [_m1_bias_in_weights, _m2_renorm_unguarded, _m3_no_scaling, _m4_neg_inf_mask,
-           _m5_group_max, _m6_weighted_shared, _m7_nibble_order]
+           _m5_group_max, _m6_weighted_shared, _m7_nibble_order, _m8_router_bias_dropped,
+           _m9_sigmoid_sign, _m10_gate_without_silu, _m11_down_from_up, _m12_zero_point_sign,
+           _m13_ties_to_higher_index, _m14_shared_dropped, _m15_worst_groups_kept,
+           _m16_renorm_without_epsilon, _m17_softmax_over_tokens]
 
 
 @pytest.mark.parametrize("mutant", MUTANTS, ids=lambda f: f.__name__)
