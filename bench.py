@@ -436,7 +436,7 @@ def main():
         r = dict(T=T, copies=ncp, ms_per_step=t_step * 1e3, tokens_per_s=T / t_step,
                  hbm_gbps=alg["bytes"] / t_step / 1e9, mfma_tflops=alg["flops"] / t_step / 1e12,
                  distinct_experts=alg["D"], stage_ms=stages, alg=alg,
-                 path="decode" if T <= 64 else "prefill")
+                 path=cfg.kernel_path(T))
         r["hbm_frac"] = r["hbm_gbps"] / HBM_PEAK_GBPS
         r["mfma_frac"] = r["mfma_tflops"] / BF16_PEAK_TFLOPS
         r["roofline_frac"] = max(alg["bytes"] / (HBM_PEAK_GBPS * 1e9),

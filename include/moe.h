@@ -73,7 +73,9 @@ typedef enum {
 } moe_dtype;
 
 typedef enum {
-  MOE_PATH_AUTO = 0,    /* T <= 64: weight-streaming decode path; else tiled MFMA path */
+  MOE_PATH_AUTO = 0,    /* T <= 64 or T*top_k <= 10*num_experts (at most 10 routed tokens
+                           per expert on average): weight-streaming decode path; else the
+                           tiled MFMA path */
   MOE_PATH_DECODE = 1,  /* force the weight-streaming path (any T)                      */
   MOE_PATH_PREFILL = 2  /* force the tiled grouped-GEMM path (bf16 activations only)    */
 } moe_path;
@@ -155,6 +157,14 @@ moe_status moe_validate_config(const moe_config* cfg);
  * moe_route / moe_permute / moe_experts / moe_forward; one size fits all four).
  * 0 <= T <= 2^20.  Needs no GPU.                                                   */
 moe_status moe_workspace_size(const moe_config* cfg, int64_t T, size_t* bytes);
+
+/* The kernels a call with T tokens runs: *path_out = MOE_PATH_DECODE (weight-streaming
+ * kernels) or MOE_PATH_PREFILL (tiled MFMA GEMMs), after cfg->path, the expert storage
+ * (u4 experts always stream) and, for MOE_PATH_AUTO, the batch size rule documented
+ * at moe_path.  Only the selected experts' weights are read on either path [Ling-3.0-
+ * flash-GGUF card, "Measured performance"]; the choice changes speed, not results
+ * beyond rounding.  Checks as moe_workspace_size.  Needs no GPU.                     */
+moe_status moe_select_path(const moe_config* cfg, int64_t T, int32_t* path_out);
 
 /* Router (steps: logits, scoring, correction bias, grouped mask, top-k, weights).
  *   x          [T, H] act_dtype

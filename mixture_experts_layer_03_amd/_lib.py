@@ -68,6 +68,7 @@ def lib() -> C.CDLL:
         "moe_config_default": [cfgp],
         "moe_validate_config": [cfgp],
         "moe_workspace_size": [cfgp, I64, C.POINTER(SZ)],
+        "moe_select_path": [cfgp, I64, C.POINTER(C.c_int32)],
         "moe_route": [cfgp, I64, P, P, P, P, P, P, P, SZ, P],
         "moe_permute": [cfgp, I64, P, P, P, P, P, SZ, P],
         "moe_experts": [cfgp, I64, P, wp, P, P, P, P, SZ, P],

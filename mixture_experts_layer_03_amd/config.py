@@ -111,5 +111,13 @@ class MoEConfig:
         _lib.check(_lib.lib().moe_workspace_size(C.byref(c), int(T), C.byref(n)))
         return int(n.value)
 
+    def kernel_path(self, T: int) -> str:
+        """"decode" (weight-streaming kernels) or "prefill" (tiled GEMMs): the kernels a
+        call with T tokens runs under this configuration."""
+        c = self.to_c()
+        v = C.c_int32(-1)
+        _lib.check(_lib.lib().moe_select_path(C.byref(c), int(T), C.byref(v)))
+        return "decode" if v.value == _lib.PATH_DECODE else "prefill"
+
     def as_dict(self) -> dict:
         return {f.name: getattr(self, f.name) for f in fields(self)}

@@ -36,6 +36,15 @@ moe_status ok() {
 constexpr int64_t kMaxH = 16384, kMaxE = 1024, kMaxI = 32768, kMaxT = int64_t(1) << 20, kMaxK = kMaxTopK;
 constexpr int64_t kMaxGroupsGpu = 64;
 constexpr int kDecodeMaxT = 64;
+// The automatic path also streams (decode) while a batch averages at most this many
+// routed tokens per expert (T * top_k <= 10 * num_experts).  There the tiled GEMMs'
+// 128-row M-tiles are mostly padding and read the selected experts' weights at ~2 TB/s,
+// while the streaming kernels read them at 5-6 TB/s.  Measured on the MI355X, the
+// streaming path stays faster up to about 20 tokens per expert on the Ling-lite and
+// Ling-3.0-tiny shapes (T ~ 210 and ~ 320), 10-11 on the Ling-2.6-flash and
+// Ling-3.0-flash shapes (T ~ 330 and ~ 700) and 14 on the u8 Ling-3.0-flash shape;
+// e.g. Ling-3.0-flash at 256 tokens: 0.92 ms streamed against 1.70 ms tiled.
+constexpr int kDecodeTokensPerExpert = 10;
 constexpr int kFusedRouteMaxT = 16;  // one workgroup routes and permutes up to this many tokens
 constexpr int kGroupM = 4;           // M-tiles per block-order group of the tiled GEMMs
 
@@ -134,7 +143,8 @@ int router_ksplit(const moe_config& c, int64_t T) {
 
 void make_plan(const moe_config& c, int64_t T, Plan& p) {
   p.decode = c.path == MOE_PATH_DECODE || c.expert_dtype == MOE_DT_U4_AFFINE ||
-             (c.path == MOE_PATH_AUTO && (T <= kDecodeMaxT || c.act_dtype == MOE_DT_F32));
+             (c.path == MOE_PATH_AUTO && (T <= kDecodeMaxT || c.act_dtype == MOE_DT_F32 ||
+                                          T * c.top_k <= kDecodeTokensPerExpert * c.num_experts));
   const int64_t H = c.hidden, E = c.num_experts, k = c.top_k, I = c.moe_intermediate, Is = c.shared_intermediate;
   const size_t ab = c.act_dtype == MOE_DT_F32 ? 4 : 2;
   const int64_t slots = T * k;
@@ -795,6 +805,21 @@ moe_status moe_workspace_size(const moe_config* cfg, int64_t T, size_t* bytes) {
     return ok();
   } catch (...) {
     return fail(MOE_EINVAL_ARG, "internal error while sizing");
+  }
+}
+
+moe_status moe_select_path(const moe_config* cfg, int64_t T, int32_t* path_out) {
+  try {
+    moe_status s = check_config(cfg);
+    if (s != MOE_OK) return s;
+    if ((s = check_T(T)) != MOE_OK) return s;
+    if (!path_out) return fail(MOE_EINVAL_ARG, "path_out is null");
+    Plan p;
+    make_plan(*cfg, T, p);
+    *path_out = p.decode ? MOE_PATH_DECODE : MOE_PATH_PREFILL;
+    return ok();
+  } catch (...) {
+    return fail(MOE_EINVAL_ARG, "internal error while choosing the path");
   }
 }
 

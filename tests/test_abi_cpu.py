@@ -162,6 +162,27 @@ def test_workspace_size_and_T_bounds():
         cfg.workspace_size((1 << 20) + 1)
 
 
+def test_path_choice():
+    """The automatic path streams up to 64 tokens or at most 10 routed tokens per
+    expert on average (T * top_k <= 10 * E); u4 experts and fp32 layers always stream;
+    a forced path is kept."""
+    import synth
+    spec2, spec4 = synth.SPECS[2], synth.SPECS[4]           # E 64 k 6; E 512 k 8
+    c2, c4 = moe.MoEConfig.from_object(spec2), moe.MoEConfig.from_object(spec4)
+    assert [c2.kernel_path(T) for T in (1, 64, 106, 107, 4096)] == \
+        ["decode", "decode", "decode", "prefill", "prefill"]
+    assert [c4.kernel_path(T) for T in (8, 640, 641, 8192)] == ["decode", "decode", "prefill", "prefill"]
+    assert moe.MoEConfig.from_object(synth.SPECS[6]).kernel_path(8192) == "decode"   # u4
+    assert moe.MoEConfig.from_object(synth.SPECS[1]).kernel_path(4096) == "decode"   # fp32
+    assert moe.MoEConfig.from_object(spec2, path="prefill").kernel_path(1) == "prefill"
+    assert moe.MoEConfig.from_object(spec2, path="decode").kernel_path(4096) == "decode"
+    c = c2.to_c()
+    v = C.c_int32(-1)
+    assert _lib.lib().moe_select_path(C.byref(c), 64, None) == _lib.MOE_EINVAL_ARG
+    assert _lib.lib().moe_select_path(C.byref(c), -1, C.byref(v)) == _lib.MOE_EINVAL_ARG
+    assert _lib.lib().moe_select_path(None, 64, C.byref(v)) == _lib.MOE_EINVAL_ARG
+
+
 def test_entry_points_reject_bad_arguments_before_any_launch():
     """Null pointers, too-small workspace: refused on the host, nothing touches a device."""
     L = _lib.lib()

@@ -117,7 +117,10 @@ CASES = [(1, 16, "auto"), (1, 3, "auto"), (1, 100, "auto"),
          (2, 13, "prefill"), (3, 1, "prefill"), (5, 40, "prefill"),
          (6, 1, "auto"), (6, 7, "auto"), (6, 64, "auto"), (6, 300, "auto"), (6, 90, "decode"),
          (7, 1, "auto"), (7, 13, "auto"), (7, 64, "auto"), (7, 300, "auto"),
-         (2, 16, "auto"), (4, 16, "auto")]
+         (2, 16, "auto"), (4, 16, "auto"),
+         # the automatic choice streams these (at most 10 routed tokens per expert):
+         # the same batches through the tiled kernels
+         (3, 300, "prefill"), (4, 500, "prefill"), (5, 500, "prefill")]
 
 
 @pytest.mark.parametrize("cid,T,path", CASES)
@@ -284,7 +287,7 @@ def test_zero_tokens_is_noop():
 def test_deterministic():
     import mixture_experts_layer_03_amd as moe
     spec, L, W = layer(4)
-    for T in (37, 400):
+    for T in (37, 400, 700):
         x, xd = xs(spec, T)
         log(f"determinism T={T}")
         a = moe.forward(xd, W, moe_cfg(spec))
@@ -293,7 +296,7 @@ def test_deterministic():
         assert torch.equal(a, b)
 
 
-@pytest.mark.parametrize("cid,T", [(2, 13), (2, 300), (5, 64), (4, 500), (6, 64), (3, 1), (7, 16)])
+@pytest.mark.parametrize("cid,T", [(2, 13), (2, 300), (5, 64), (4, 500), (4, 700), (6, 64), (3, 1), (7, 16)])
 def test_graph_replay_matches_eager(cid, T):
     """The forward captured in a HIP graph (prefill runs the shared expert on a second
     stream, joined inside the graph) gives the eager result on every replay, with other
