@@ -29,6 +29,7 @@ HBM_PEAK_GBPS = 8000.0          # MI355X HBM3E, published
 BF16_PEAK_TFLOPS = 2500.0       # MI355X dense bf16 MFMA, published
 METRIC = "MoE-layer tokens/s at T=1/64/4096; achieved HBM GB/s & MFMA % of peak"
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "traffic_counters.json")
+DENSE_STREAM_MAX_T = 192        # moe_dense_mlp streams up to this many tokens (include/moe.h)
 
 
 def parse():
@@ -299,7 +300,7 @@ def bench_dense(args):
         fl = 6.0 * T * H * I
         r = dict(T=T, copies=len(copies), ms_per_step=t_step * 1e3, tokens_per_s=T / t_step,
                  hbm_gbps=byt / t_step / 1e9, mfma_tflops=fl / t_step / 1e12,
-                 up_ms=st.get("shared_up"), path="decode" if T <= 64 else "prefill")
+                 up_ms=st.get("shared_up"), path="decode" if T <= DENSE_STREAM_MAX_T else "prefill")
         r["hbm_frac"] = r["hbm_gbps"] / HBM_PEAK_GBPS
         r["mfma_frac"] = r["mfma_tflops"] / BF16_PEAK_TFLOPS
         r["roofline_frac"] = max(byt / (HBM_PEAK_GBPS * 1e9), fl / (BF16_PEAK_TFLOPS * 1e12)) / t_step

@@ -213,7 +213,7 @@ moe_status moe_forward(const moe_config* cfg, int64_t T, const void* x, const mo
  * uses biased scores, ..." list: dense BailingMoeMLP layers before the MoE layers;
  * Ling-2.6-flash-JANGTQ card, "Architecture" layer table: layer 0 is a dense MLP of
  * intermediate 9216].  It is the shared expert's computation and runs on its kernels
- * (weight streaming for T <= 64, tiled MFMA above, as for the layer).
+ * (weight streaming for T <= 192, tiled MFMA above).
  *   cfg          hidden, act_dtype and path are read; routing and expert fields are not
  *   intermediate MLP width I_d: a multiple of 64 in [64, 32768]
  *   x [T, H] and y [T, H] act_dtype; gate, up [I_d, H] and down [H, I_d] act_dtype

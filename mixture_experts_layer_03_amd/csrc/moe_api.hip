@@ -45,6 +45,11 @@ constexpr int kDecodeMaxT = 64;
 // Ling-3.0-flash shapes (T ~ 330 and ~ 700) and 14 on the u8 Ling-3.0-flash shape;
 // e.g. Ling-3.0-flash at 256 tokens: 0.92 ms streamed against 1.70 ms tiled.
 constexpr int kDecodeTokensPerExpert = 10;
+// The dense MLP streams up to this many tokens.  Measured on the MI355X at the
+// Ling-2.6-flash layer-0 shape (H 4096, I 9216): streaming 99.5 / 149.6 / 163.4 /
+// 219.6 / 284.5 us at 64 / 96 / 128 / 192 / 256 tokens against 243-261 us tiled (one
+// or two 128-row M-tiles leave most CUs idle).
+constexpr int kDenseDecodeMaxT = 192;
 constexpr int kFusedRouteMaxT = 16;  // one workgroup routes and permutes up to this many tokens
 constexpr int kGroupM = 4;           // M-tiles per block-order group of the tiled GEMMs
 
@@ -682,7 +687,8 @@ struct DensePlan {
 };
 
 void dense_plan(const moe_config& c, int64_t I, int64_t T, DensePlan& p) {
-  p.decode = c.path == MOE_PATH_DECODE || (c.path == MOE_PATH_AUTO && (T <= kDecodeMaxT || c.act_dtype == MOE_DT_F32));
+  p.decode = c.path == MOE_PATH_DECODE ||
+             (c.path == MOE_PATH_AUTO && (T <= kDenseDecodeMaxT || c.act_dtype == MOE_DT_F32));
   const size_t ab = c.act_dtype == MOE_DT_F32 ? 4 : 2;
   size_t o = 0;
   auto take = [&](size_t bytes) {

@@ -305,8 +305,8 @@ def test_dense_workspace_and_validation():
     c.top_k = 99
     n = C.c_size_t(0)
     assert _lib.lib().moe_dense_workspace_size(C.byref(c), 256, 4, C.byref(n)) == 0
-    # decode (T <= 64) keeps an fp32 output buffer, the tiled path does not
-    assert dense_status(good(), 256, T=64)[2] > dense_status(good(), 256, T=65)[2]
+    # the streaming path (T <= 192) keeps an fp32 output buffer, the tiled path does not
+    assert dense_status(good(), 256, T=192)[2] > dense_status(good(), 256, T=193)[2]
     assert _lib.lib().moe_dense_workspace_size(None, 256, 4, C.byref(n)) == _lib.MOE_EINVAL_ARG
 
 

@@ -51,8 +51,9 @@ def check(spec, T, path, tokens=None):
     assert rel.max() <= TOL[spec.act_dtype], rel.max()
 
 
-@pytest.mark.parametrize("T,path", [(1, "auto"), (7, "auto"), (64, "auto"), (65, "auto"), (300, "auto"),
-                                    (40, "prefill"), (200, "decode")])
+@pytest.mark.parametrize("T,path", [(1, "auto"), (7, "auto"), (64, "auto"), (65, "auto"), (192, "auto"),
+                                    (193, "auto"), (300, "auto"), (40, "prefill"), (65, "prefill"),
+                                    (200, "decode")])
 def test_dense_small(T, path):
     check(SMALL["bf16"], T, path)
 
