@@ -73,8 +73,9 @@ typedef enum {
 } moe_dtype;
 
 typedef enum {
-  MOE_PATH_AUTO = 0,    /* T <= 64 or T*top_k <= 10*num_experts (at most 10 routed tokens
-                           per expert on average): weight-streaming decode path; else the
+  MOE_PATH_AUTO = 0,    /* T <= 64, or at most min(20, 40960/hidden) routed tokens per
+                           expert on average (T*top_k*max(hidden, 2048) <=
+                           40960*num_experts): weight-streaming decode path; else the
                            tiled MFMA path */
   MOE_PATH_DECODE = 1,  /* force the weight-streaming path (any T)                      */
   MOE_PATH_PREFILL = 2  /* force the tiled grouped-GEMM path (bf16 activations only)    */

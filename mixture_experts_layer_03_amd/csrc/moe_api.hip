@@ -6,6 +6,7 @@
 // before divisibility checks, routing bounds (1 <= top_k <= experts; with groups,
 // experts divisible by n_group and 1 <= topk_group <= n_group), sizes taken from
 // the caller's real arguments, and no exception or abort ever crossing the ABI.
+#include <algorithm>
 #include <cmath>
 #include <cstdarg>
 #include <cstdio>
@@ -36,15 +37,17 @@ moe_status ok() {
 constexpr int64_t kMaxH = 16384, kMaxE = 1024, kMaxI = 32768, kMaxT = int64_t(1) << 20, kMaxK = kMaxTopK;
 constexpr int64_t kMaxGroupsGpu = 64;
 constexpr int kDecodeMaxT = 64;
-// The automatic path also streams (decode) while a batch averages at most this many
-// routed tokens per expert (T * top_k <= 10 * num_experts).  There the tiled GEMMs'
-// 128-row M-tiles are mostly padding and read the selected experts' weights at ~2 TB/s,
-// while the streaming kernels read them at 5-6 TB/s.  Measured on the MI355X, the
-// streaming path stays faster up to about 20 tokens per expert on the Ling-lite and
-// Ling-3.0-tiny shapes (T ~ 210 and ~ 320), 10-11 on the Ling-2.6-flash and
-// Ling-3.0-flash shapes (T ~ 330 and ~ 700) and 14 on the u8 Ling-3.0-flash shape;
-// e.g. Ling-3.0-flash at 256 tokens: 0.92 ms streamed against 1.70 ms tiled.
-constexpr int kDecodeTokensPerExpert = 10;
+// The automatic path also streams (decode) while a batch averages at most
+// min(20, 40960 / hidden) routed tokens per expert: T * top_k * max(hidden, 2048)
+// <= 40960 * num_experts, i.e. 20 at hidden 2048 (and below) and 10 at hidden 4096.  There the
+// tiled GEMMs' 128-row M-tiles are mostly padding and read the selected experts'
+// weights at ~2 TB/s, while the streaming kernels read them at 5-6 TB/s.  Measured on
+// the MI355X, the streaming path stays faster up to about 20 tokens per expert on the
+// Ling-lite and Ling-3.0-tiny shapes (hidden 2048; T ~ 210 and ~ 320), 10-11 on the
+// Ling-2.6-flash and Ling-3.0-flash shapes (hidden 4096; T ~ 330 and ~ 700) and 14 on
+// the u8 Ling-3.0-flash shape; e.g. Ling-3.0-flash at 256 tokens: 0.92 ms streamed
+// against 1.70 ms tiled.
+constexpr int64_t kDecodeTokensTimesHidden = 40960, kDecodeHiddenFloor = 2048;
 // The dense MLP streams up to this many tokens.  Measured on the MI355X at the
 // Ling-2.6-flash layer-0 shape (H 4096, I 9216): streaming 99.5 / 149.6 / 163.4 /
 // 219.6 / 284.5 us at 64 / 96 / 128 / 192 / 256 tokens against 243-261 us tiled (one
@@ -149,7 +152,8 @@ int router_ksplit(const moe_config& c, int64_t T) {
 void make_plan(const moe_config& c, int64_t T, Plan& p) {
   p.decode = c.path == MOE_PATH_DECODE || c.expert_dtype == MOE_DT_U4_AFFINE ||
              (c.path == MOE_PATH_AUTO && (T <= kDecodeMaxT || c.act_dtype == MOE_DT_F32 ||
-                                          T * c.top_k <= kDecodeTokensPerExpert * c.num_experts));
+                                          T * c.top_k * std::max(c.hidden, kDecodeHiddenFloor) <=
+                                              kDecodeTokensTimesHidden * c.num_experts));
   const int64_t H = c.hidden, E = c.num_experts, k = c.top_k, I = c.moe_intermediate, Is = c.shared_intermediate;
   const size_t ab = c.act_dtype == MOE_DT_F32 ? 4 : 2;
   const int64_t slots = T * k;

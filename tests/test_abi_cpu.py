@@ -163,13 +163,13 @@ def test_workspace_size_and_T_bounds():
 
 
 def test_path_choice():
-    """The automatic path streams up to 64 tokens or at most 10 routed tokens per
-    expert on average (T * top_k <= 10 * E); u4 experts and fp32 layers always stream;
-    a forced path is kept."""
+    """The automatic path streams up to 64 tokens or at most min(20, 40960 / H) routed
+    tokens per expert on average (20 at hidden 2048, 10 at 4096); u4 experts and fp32
+    layers always stream; a forced path is kept."""
     import synth
-    spec2, spec4 = synth.SPECS[2], synth.SPECS[4]           # E 64 k 6; E 512 k 8
+    spec2, spec4 = synth.SPECS[2], synth.SPECS[4]           # H 2048 E 64 k 6; H 4096 E 512 k 8
     c2, c4 = moe.MoEConfig.from_object(spec2), moe.MoEConfig.from_object(spec4)
-    assert [c2.kernel_path(T) for T in (1, 64, 106, 107, 4096)] == \
+    assert [c2.kernel_path(T) for T in (1, 64, 213, 214, 4096)] == \
         ["decode", "decode", "decode", "prefill", "prefill"]
     assert [c4.kernel_path(T) for T in (8, 640, 641, 8192)] == ["decode", "decode", "prefill", "prefill"]
     assert moe.MoEConfig.from_object(synth.SPECS[6]).kernel_path(8192) == "decode"   # u4

@@ -1,6 +1,6 @@
 """GPU parity at the workloads' full sizes, in the launch configuration the
-benchmark times (auto path: streaming kernels for T <= 64 or at most 10 routed
-tokens per expert, tiled MFMA above).
+benchmark times (auto path: streaming kernels for T <= 64 or few routed tokens per
+expert, tiled MFMA above).
 
 Routing is compared on every token; outputs on a seeded sample of tokens the
 oracle computes one by one (first, last and random rows).

@@ -118,9 +118,9 @@ CASES = [(1, 16, "auto"), (1, 3, "auto"), (1, 100, "auto"),
          (6, 1, "auto"), (6, 7, "auto"), (6, 64, "auto"), (6, 300, "auto"), (6, 90, "decode"),
          (7, 1, "auto"), (7, 13, "auto"), (7, 64, "auto"), (7, 300, "auto"),
          (2, 16, "auto"), (4, 16, "auto"),
-         # the automatic choice streams these (at most 10 routed tokens per expert):
+         # the automatic choice streams these (at most 20 routed tokens per expert):
          # the same batches through the tiled kernels
-         (3, 300, "prefill"), (4, 500, "prefill"), (5, 500, "prefill")]
+         (3, 300, "prefill"), (4, 500, "prefill"), (5, 500, "prefill"), (7, 300, "prefill")]
 
 
 @pytest.mark.parametrize("cid,T,path", CASES)
@@ -207,10 +207,10 @@ def test_odd_expert_count_and_single_group():
     spec = SMALL[3].variant("odd-E", 151, num_experts=40, n_group=4, topk_group=4, top_k=5)
     L = synth.make_layer(spec)
     W = device_weights(L)
-    for T in (3, 150):
+    for T, path in ((3, "auto"), (150, "auto"), (150, "prefill")):
         x = synth.make_x(spec, T)
-        log(f"forward E=40 G=g=4 T={T}")
-        y, (idx, w, _) = moe.forward(to_dev(x), W, moe_cfg(spec), return_routing=True)
+        log(f"forward E=40 G=g=4 T={T} path={path}")
+        y, (idx, w, _) = moe.forward(to_dev(x), W, moe_cfg(spec, path), return_routing=True)
         torch.cuda.synchronize()
         check_route(spec, idx.cpu().numpy(), w.cpu().numpy(), L, x)
         check_forward(spec, y_to_f64(y), idx.cpu().numpy(), L, x)
@@ -287,25 +287,26 @@ def test_zero_tokens_is_noop():
 def test_deterministic():
     import mixture_experts_layer_03_amd as moe
     spec, L, W = layer(4)
-    for T in (37, 400, 700):
+    for T, path in ((37, "auto"), (400, "auto"), (700, "prefill")):
         x, xd = xs(spec, T)
-        log(f"determinism T={T}")
-        a = moe.forward(xd, W, moe_cfg(spec))
-        b = moe.forward(xd, W, moe_cfg(spec))
+        log(f"determinism T={T} path={path}")
+        a = moe.forward(xd, W, moe_cfg(spec, path))
+        b = moe.forward(xd, W, moe_cfg(spec, path))
         torch.cuda.synchronize()
         assert torch.equal(a, b)
 
 
-@pytest.mark.parametrize("cid,T", [(2, 13), (2, 300), (5, 64), (4, 500), (4, 700), (6, 64), (3, 1), (7, 16)])
-def test_graph_replay_matches_eager(cid, T):
+@pytest.mark.parametrize("cid,T,path", [(2, 13, "auto"), (2, 300, "auto"), (5, 64, "auto"), (4, 500, "auto"),
+                                        (4, 700, "prefill"), (6, 64, "auto"), (3, 1, "auto"), (7, 16, "auto")])
+def test_graph_replay_matches_eager(cid, T, path):
     """The forward captured in a HIP graph (prefill runs the shared expert on a second
     stream, joined inside the graph) gives the eager result on every replay, with other
     eager work and synchronisations between the replays."""
     import mixture_experts_layer_03_amd as moe
     spec, L, W = layer(cid)
     x, xd = xs(spec, T)
-    cfg = moe_cfg(spec)
-    log(f"graph replay cfg{cid} T={T}")
+    cfg = moe_cfg(spec, path)
+    log(f"graph replay cfg{cid} T={T} path={path}")
     ws = torch.empty(cfg.workspace_size(T), dtype=torch.uint8, device="cuda")
     y = torch.empty((T, spec.hidden), dtype=xd.dtype, device="cuda")
     moe.forward(xd, W, cfg, ws=ws, out=y)  # eager call first (creates the library's second stream)
