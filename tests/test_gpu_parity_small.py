@@ -276,6 +276,27 @@ def test_every_token_on_one_expert(I, T, path):
     assert rel.max() <= 2e-2, rel.max()
 
 
+@pytest.mark.parametrize("cid,path,T", [(5, "decode", 40), (5, "prefill", 300), (6, "auto", 64), (6, "auto", 7)])
+def test_fractional_zero_points(cid, path, T):
+    """Zero points are fp16 and need not be integers (the synthetic quantiser writes
+    integers): every zero point shifted by 0.375, against the oracle, which takes
+    s * (q - z) exactly."""
+    import mixture_experts_layer_03_amd as moe
+    spec = SMALL[cid]
+    L = dict(synth.make_layer(spec))
+    for n in ("gate_zero", "up_zero", "down_zero"):
+        L[n] = (np.asarray(L[n], dtype=np.float32) + np.float32(0.375)).astype(np.float16)
+    W = device_weights(L)
+    x = synth.make_x(spec, T)
+    log(f"fractional zero points cfg{cid} T={T} path={path}")
+    y, (idx, w, _) = moe.forward(to_dev(x), W, moe_cfg(spec, path), return_routing=True)
+    torch.cuda.synchronize()
+    idx_h = idx.cpu().numpy()
+    check_route(spec, idx_h, w.cpu().numpy(), L, x)
+    st = check_forward(spec, y_to_f64(y), idx_h, L, x)
+    log(f"  ok: max rel err {st['max_rel']:.3e}")
+
+
 def test_zero_tokens_is_noop():
     import mixture_experts_layer_03_amd as moe
     spec, L, W = layer(2)
