@@ -156,7 +156,13 @@ moe_status moe_validate_config(const moe_config* cfg);
 
 /* Bytes of device workspace a call with T tokens needs (the largest of
  * moe_route / moe_permute / moe_experts / moe_forward; one size fits all four).
- * 0 <= T <= 2^20.  Needs no GPU.                                                   */
+ * The workspace is how this interface keeps the pages' ownership rule for the
+ * native side: the caller owns every buffer and the library holds no device memory
+ * of its own, so nothing is allocated, resized or freed behind the caller's back
+ * [mlxcel #838 "Defensive requirements": validate at load, no failure at run time].
+ * 0 <= T <= 2^20; the same config checks as moe_validate_config first.
+ * Errors: MOE_EINVAL_CONFIG / MOE_EUNSUPPORTED (config), MOE_EINVAL_ARG (T out of
+ * range, bytes null).  Needs no GPU.                                               */
 moe_status moe_workspace_size(const moe_config* cfg, int64_t T, size_t* bytes);
 
 /* The kernels a call with T tokens runs: *path_out = MOE_PATH_DECODE (weight-streaming
@@ -167,42 +173,63 @@ moe_status moe_workspace_size(const moe_config* cfg, int64_t T, size_t* bytes);
  * beyond rounding.  Checks as moe_workspace_size.  Needs no GPU.                     */
 moe_status moe_select_path(const moe_config* cfg, int64_t T, int32_t* path_out);
 
-/* Router (steps: logits, scoring, correction bias, grouped mask, top-k, weights).
+/* Router (steps: logits, scoring, correction bias, grouped mask, top-k, weights)
+ * [mlxcel #838 "Router: selection uses biased scores, weights come from unbiased
+ * scores" (the correction bias enters the selection copy only; renormalisation by
+ * sum + 1e-20 when top_k > 1); "moe_router_enable_routed_scaling is dead code
+ * upstream" (the factor is always applied); "Architecture notes" (groups kept,
+ * the rest zeroed before top-k); Ling-2.6-flash-JANGTQ card, "Architecture
+ * (bailing_hybrid)" (sigmoid, 8 groups -> top-4 groups -> top-8 experts)].
  *   x          [T, H] act_dtype
  *   router_w   [E, H] router_dtype; router_bias [E] fp32 nullable;
  *   expert_bias [E] fp32, required iff use_expert_bias
  *   topk_idx   [T, k] int32 out: experts by descending masked selection score,
  *              equal scores -> lower index first
  *   topk_w     [T, k] fp32 out: final routing weights (kept in fp32)
- *   ws         device workspace of ws_bytes >= moe_workspace_size(cfg, T)          */
+ *   ws         device workspace of ws_bytes >= moe_workspace_size(cfg, T)
+ * Errors: MOE_EINVAL_CONFIG / MOE_EUNSUPPORTED (config), MOE_EINVAL_ARG (T out of
+ * range; x or router_w null or not 16-byte aligned; a bias, topk_idx or topk_w null
+ * where required or not 4-byte aligned), MOE_EWORKSPACE (ws null, not 256-byte
+ * aligned or too small), MOE_EHIP (a launch failed).                               */
 moe_status moe_route(const moe_config* cfg, int64_t T, const void* x, const void* router_w,
                      const float* router_bias, const float* expert_bias, int32_t* topk_idx,
                      float* topk_w, void* ws, size_t ws_bytes, moe_stream_t stream);
 
-/* Token permutation by expert (histogram, exclusive scan, scatter).
+/* Token permutation by expert (histogram, exclusive scan, scatter): the grouping that
+ * lets each selected expert's weights be read once per call [Ling-3.0-flash-GGUF
+ * card, "Measured performance": decode reads only the selected experts].
  *   topk_idx  [T, k] int32 in; entries outside [0, E) are dropped (not counted)
  *   counts    [E] int32 out: slots routed to each expert
  *   offsets   [E + 1] int32 out: exclusive prefix sum of counts
  *   perm      [T * k] int32 out: slot ids t*k + j grouped by expert, expert e's run
  *             being perm[offsets[e] .. offsets[e+1]); the order inside a run is
- *             unspecified (the set is exact).  Trailing entries of dropped slots = -1. */
+ *             unspecified (the set is exact).  Trailing entries of dropped slots = -1.
+ * Errors: as moe_route (topk_idx, counts, offsets, perm: non-null, 4-byte aligned).  */
 moe_status moe_permute(const moe_config* cfg, int64_t T, const int32_t* topk_idx,
                        int32_t* counts, int32_t* offsets, int32_t* perm, void* ws,
                        size_t ws_bytes, moe_stream_t stream);
 
 /* Expert stage with routing given by the caller (permutation, routed SwiGLU experts,
- * shared expert, weighted combine).
+ * shared expert, weighted combine) [mlxcel #838 "Validation checkpoint" and "Weight
+ * remap" (per-expert gate/up/down, gate_proj the SwiGLU gate); "Shared experts are
+ * one wide MLP, not N separate experts" (weight 1.0, no routing)].
  *   x [T, H] act_dtype; w: layer weights (router fields unused);
  *   topk_idx [T, k] int32 (entries outside [0, E) contribute nothing);
- *   topk_w [T, k] fp32; y [T, H] act_dtype out.                                     */
+ *   topk_w [T, k] fp32; y [T, H] act_dtype out.
+ * Errors: as moe_route; weight pointers null or misaligned (16 bytes for matrices,
+ * 2 bytes for u8 and 4 bytes for u4 scales and zero points) -> MOE_EINVAL_ARG.      */
 moe_status moe_experts(const moe_config* cfg, int64_t T, const void* x, const moe_weights* w,
                        const int32_t* topk_idx, const float* topk_w, void* y, void* ws,
                        size_t ws_bytes, moe_stream_t stream);
 
-/* The whole layer: y = MoE(x).
+/* The whole layer: y = MoE(x) = sum_j w_j expert_{S_j}(x) + shared(x)
+ * [mlxcel #838 "Architecture notes" (router, routed experts and the shared expert of
+ * one MoE layer) and "Shared experts are one wide MLP, not N separate experts" (the
+ * shared output added at weight 1.0); the router as in moe_route].
  *   x [T, H] act_dtype; y [T, H] act_dtype out;
  *   topk_idx_out [T, k] int32, topk_w_out [T, k] fp32, expert_counts_out [E] int32:
- *   optional copies of the routing (nullable).                                       */
+ *   optional copies of the routing (nullable).
+ * Errors: as moe_experts, plus the router pointers as moe_route.                     */
 moe_status moe_forward(const moe_config* cfg, int64_t T, const void* x, const moe_weights* w,
                        void* y, int32_t* topk_idx_out, float* topk_w_out,
                        int32_t* expert_counts_out, void* ws, size_t ws_bytes,
@@ -210,8 +237,8 @@ moe_status moe_forward(const moe_config* cfg, int64_t T, const void* x, const mo
 
 /* Dense MLP of the layers in front of the MoE layers (`first_k_dense_replace`):
  *   y = (silu(x W_gᵀ) ⊙ (x W_uᵀ)) W_dᵀ
- * A plain gated MLP at the model's intermediate size [mlxcel #838 "Router: selection
- * uses biased scores, ..." list: dense BailingMoeMLP layers before the MoE layers;
+ * A plain gated MLP at the model's intermediate size [mlxcel #838 "Architecture
+ * notes": the first_k_dense_replace layers before the MoE layers are dense MLPs;
  * Ling-2.6-flash-JANGTQ card, "Architecture" layer table: layer 0 is a dense MLP of
  * intermediate 9216].  It is the shared expert's computation and runs on its kernels
  * (weight streaming for T <= 192, tiled MFMA above).
@@ -222,7 +249,7 @@ moe_status moe_forward(const moe_config* cfg, int64_t T, const void* x, const mo
  *   ws           device workspace of ws_bytes >= moe_dense_workspace_size(cfg, I_d, T)
  * Errors: MOE_EINVAL_CONFIG (hidden, act_dtype or path out of range), MOE_EUNSUPPORTED
  * (hidden or I_d not a multiple of 64; PREFILL with fp32), MOE_EINVAL_ARG (null or
- * misaligned pointers, I_d or T out of range), MOE_EWORKSPACE, MOE_ELAUNCH.        */
+ * misaligned pointers, I_d or T out of range), MOE_EWORKSPACE, MOE_EHIP.           */
 moe_status moe_dense_workspace_size(const moe_config* cfg, int64_t intermediate, int64_t T, size_t* bytes);
 moe_status moe_dense_mlp(const moe_config* cfg, int64_t intermediate, int64_t T, const void* x,
                          const void* gate, const void* up, const void* down, void* y, void* ws,
@@ -250,10 +277,16 @@ moe_status moe_profile_collect(int32_t stage, float* total_ms, int32_t* launches
 moe_status moe_profile_disable(void);
 moe_status moe_profile_reset(void); /* forget recorded pairs, keep the pool and mask */
 
-/* Static description of a status code.                                             */
+/* Static description of a status code.  Every entry point reports failure as a
+ * status value, never by throwing or aborting [mlxcel #838 "Defensive requirements":
+ * invalid input is rejected when it is loaded, with an error, instead of failing
+ * later].                                                                          */
 const char* moe_status_str(moe_status s);
 
-/* Message of the last failed call on this thread ("" when none).                   */
+/* Message of the last failed call on this thread ("" when none).  It names the
+ * offending config field or argument and the value it had [mlxcel #838 "Defensive
+ * requirements": the error names the actual field].  The string stays valid until
+ * the next call on this thread.                                                     */
 const char* moe_last_error(void);
 
 /* ABI version (incremented on any change of the structs or signatures).            */

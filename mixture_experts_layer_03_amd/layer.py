@@ -112,16 +112,23 @@ def check_weights(cfg: MoEConfig, w: MoEWeights, device, need_router=True, need_
 
 
 class Workspace:
-    """Per-device scratch buffer that grows on demand (one per stream for concurrent use)."""
+    """Scratch buffers that grow on demand, one per (device, stream).
+
+    Calls on different streams get different buffers, so they never race on one.
+    A buffer is allocated while its stream is current, so the caching allocator ties
+    it to that stream: when a larger buffer replaces it, the old memory is reused
+    only by work ordered after everything already queued on the same stream."""
 
     def __init__(self):
         self._buf = {}
 
     def get(self, device, nbytes: int) -> torch.Tensor:
-        key = str(device)
+        stream = torch.cuda.current_stream(device)
+        key = (str(device), stream.cuda_stream)
         b = self._buf.get(key)
         if b is None or b.numel() < nbytes:
-            b = torch.empty(max(nbytes, 256), dtype=torch.uint8, device=device)
+            with torch.cuda.stream(stream):
+                b = torch.empty(max(nbytes, 256), dtype=torch.uint8, device=device)
             self._buf[key] = b
         return b
 

@@ -395,7 +395,134 @@ def check_dequant_u4(om):
     assert np.array_equal(om.expert_matrix(W, "gate", 0, 64), om.dequant_u4(pk, sc, zp, 64))
 
 
+# ------------------------------------------- P15 the batch router route()
+def _route_by_definition(x, W, b_r, beta, cfg):
+    """One token's routing written out from the definition: fsum logits (plus the
+    router bias), the score function, the biased copy for selection, the kept groups
+    and the selected set by enumeration of subsets, weights from the unbiased scores
+    renormalised and scaled, and the decision margin."""
+    E, H = W.shape
+    l = np.array([math.fsum(x[h] * W[e, h] for h in range(H)) + (b_r[e] if b_r is not None else 0.0)
+                  for e in range(E)])
+    if cfg.score_function == "sigmoid":
+        s = np.array([1.0 / (1.0 + math.exp(-v)) for v in l])
+    else:
+        m = max(l)
+        ex = [math.exp(v - m) for v in l]
+        tot = math.fsum(ex)
+        s = np.array([v / tot for v in ex])
+    sel = s + beta if cfg.use_expert_bias else s.copy()
+    G, g, k = cfg.n_group, cfg.topk_group, cfg.top_k
+    winners, gtie = _brute_route(sel, E, G, g, k)
+    margin = math.inf
+    masked = sel.copy()
+    if G > 1 and g < G:
+        gs = E // G
+        sig = sorted((max(sel[q * gs + a] + sel[q * gs + b]
+                          for a, b in itertools.combinations(range(gs), 2)) for q in range(G)), reverse=True)
+        margin = sig[g - 1] - sig[g]
+        # the kept groups are the ones holding the winning set's best pair sums; rebuild
+        # the masked scores from the g largest group scores (no ties on random inputs)
+        best = sorted(range(G), key=lambda q: -max(sel[q * gs + a] + sel[q * gs + b]
+                                                   for a, b in itertools.combinations(range(gs), 2)))[:g]
+        masked = np.zeros(E)
+        for q in best:
+            masked[q * gs:(q + 1) * gs] = sel[q * gs:(q + 1) * gs]
+    if k < E:
+        srt = sorted(masked, reverse=True)
+        margin = min(margin, srt[k - 1] - srt[k])
+    return s, winners, gtie, margin
+
+
+def check_route(om):
+    """route() -- the batch entry every GPU routing comparison is checked against --
+    equals routing written out from the definition on random layers (router bias,
+    correction bias, groups, both score functions), its tokens= subset selects the
+    same rows, and it agrees with forward()'s routing."""
+    rng = np.random.default_rng(37)
+    cases = [
+        dict(E=12, H=6, G=3, g=2, k=3, sf="sigmoid", bias=True, rsf=2.5, rb=True),
+        dict(E=10, H=5, G=1, g=1, k=4, sf="softmax", bias=False, rsf=1.0, rb=True),
+        dict(E=8, H=7, G=4, g=2, k=2, sf="softmax", bias=True, rsf=1.7, rb=False),
+    ]
+    for c in cases:
+        E, H, T = c["E"], c["H"], 9
+        W = rng.standard_normal((E, H))
+        b_r = rng.standard_normal(E) * 0.5 if c["rb"] else None
+        beta = rng.standard_normal(E) * 0.3
+        x = rng.standard_normal((T, H))
+        cfg = om.OracleConfig(hidden=H, num_experts=E, top_k=c["k"], moe_intermediate=1, n_group=c["G"],
+                              topk_group=c["g"], score_function=c["sf"], use_expert_bias=c["bias"],
+                              routed_scaling_factor=c["rsf"])
+        eb = beta if c["bias"] else None
+        idx, w, margin, masked = om.route(x, W, cfg, router_bias=b_r, expert_bias=eb)
+        assert idx.shape == (T, c["k"]) and w.shape == (T, c["k"])
+        for t in range(T):
+            s, winners, gtie, mg = _route_by_definition(x[t], W, b_r, beta, cfg)
+            assert not gtie
+            assert set(idx[t].tolist()) in winners, f"route(): token {t} set {idx[t]} not optimal"
+            raw = s[idx[t]]
+            want = c["rsf"] * raw / (raw.sum() + 1e-20)
+            assert np.allclose(w[t], want, rtol=1e-13, atol=0), "route(): weights"
+            assert abs(margin[t] - mg) <= 1e-13, f"route(): margin {margin[t]} vs {mg}"
+        sub = [7, 0, 4, 4]
+        i2, w2, m2, k2 = om.route(x, W, cfg, router_bias=b_r, expert_bias=eb, tokens=sub)
+        assert np.array_equal(i2, idx[sub]) and np.array_equal(w2, w[sub]) and np.array_equal(m2, margin[sub])
+        Wl = dict(router=W, router_bias=b_r, expert_bias=eb, gate=np.zeros((E, 1, H)), up=np.zeros((E, 1, H)),
+                  down=np.zeros((E, H, 1)))
+        _, d = om.forward(x, Wl, cfg, tokens=sub)
+        assert np.array_equal(d["idx"], i2) and np.allclose(d["w"], w2, rtol=1e-15, atol=0)
+    # the expert bias is refused when enabled but missing
+    try:
+        om.route(x, W, om.OracleConfig(hidden=H, num_experts=E, top_k=2, moe_intermediate=1,
+                                       use_expert_bias=True))
+    except ValueError:
+        pass
+    else:
+        raise AssertionError("route(): a missing correction bias must be rejected")
+
+
+# ------------------------------------------- P16 u8 routed experts in forward()
+def check_u8_layer(om):
+    """forward() on a layer whose routed experts are stored u8 (code, fp16 scale and
+    fp16 zero point per 64 elements of each row's reduction axis) equals forward() on
+    the same layer stored as the values s * (q - z), expanded here group by group.
+    Every matrix has its own scale and zero-point arrays, so reading one matrix's
+    parameters for another changes the result."""
+    rng = np.random.default_rng(41)
+    E, H, I, Is, T = 4, 128, 64, 64, 6
+    shapes = dict(gate=(E, I, H), up=(E, I, H), down=(E, H, I))
+    Wq, Wf = {}, {}
+    for n, shp in shapes.items():
+        q = rng.integers(0, 256, size=shp).astype(np.uint8)
+        sc = (rng.random(shp[:-1] + (shp[-1] // 64,)) * 0.002 + 1e-4).astype(np.float16)
+        zp = rng.integers(0, 256, size=sc.shape).astype(np.float16)
+        Wq[n + "_q"], Wq[n + "_scale"], Wq[n + "_zero"] = q, sc, zp
+        full = np.empty(shp)
+        for gi in range(shp[-1] // 64):
+            cols = slice(64 * gi, 64 * gi + 64)
+            full[..., cols] = sc[..., gi:gi + 1].astype(np.float64) * (
+                q[..., cols].astype(np.float64) - zp[..., gi:gi + 1].astype(np.float64))
+        Wf[n] = full
+    common = dict(router=rng.standard_normal((E, H)), router_bias=None, expert_bias=None,
+                  shared_gate=rng.standard_normal((Is, H)) * 0.1, shared_up=rng.standard_normal((Is, H)) * 0.1,
+                  shared_down=rng.standard_normal((H, Is)) * 0.1)
+    Wq.update(common)
+    Wf.update(common)
+    cfg = om.OracleConfig(hidden=H, num_experts=E, top_k=2, moe_intermediate=I, shared_intermediate=Is,
+                          quant_group=64)
+    x = rng.standard_normal((T, H))
+    yq, dq = om.forward(x, Wq, cfg)
+    yf, df = om.forward(x, Wf, cfg)
+    assert np.array_equal(dq["idx"], df["idx"])
+    assert np.allclose(yq, yf, rtol=1e-12, atol=1e-12), "u8 experts must read as s * (q - z)"
+    assert np.abs(yq).max() > 1e-3
+    for n in shapes:
+        assert np.array_equal(om.expert_matrix(Wq, n, 1, 64), Wf[n][1])
+
+
 ALL_CHECKS = [check_logits, check_scores, check_plain_topk, check_bruteforce,
               check_bias_semantics, check_group_score_reading, check_zero_mask,
               check_renorm_scale, check_swiglu, check_hand_example, check_dense_mixture,
-              check_combine_invariants, check_dequant, check_dequant_u4]
+              check_combine_invariants, check_dequant, check_dequant_u4, check_route,
+              check_u8_layer]

@@ -1,0 +1,141 @@
+"""Exact ties in the routing decision, on the GPU, through the C ABI.
+
+The pages leave the order of equal scores open (argpartition); the library's
+reading is that equal selection scores go to the lower expert index and equal
+group scores to the lower group (include/moe.h, moe_route).  Seeded random
+inputs never tie exactly, so these layers are built to tie:
+
+  * twin experts: router rows 2i and 2i+1 (and their correction biases) are
+    equal, so every expert's score has an exact twin.  With an odd top_k the
+    boundary of the selected set falls inside a twin pair for most tokens, and
+    only the lower twin may be taken; twins taken together come lower first.
+  * twin groups: the router rows and biases of group 3 repeat those of group 1,
+    so the two group scores are equal, and whenever only one of the two can be
+    kept it must be group 1.
+
+Each token's set is compared with the oracle's (which sorts stably: equal values
+keep ascending index) whenever every score across the decision boundary that is not
+an exact twin lies more than 1e-5 away; tokens closer than that are counted,
+and even then the lower-twin rule is checked.
+"""
+import numpy as np
+import pytest
+import torch
+
+import oracle.moe_oracle as om
+import synth
+from gpu_util import MARGIN, device_weights, log, moe_cfg, oracle_cfg, to_dev
+
+pytestmark = pytest.mark.gpu
+
+
+def _twin_layer(spec, twin_groups=False):
+    L = synth.make_layer(spec)
+    E, G = spec.num_experts, spec.n_group
+    out = {}
+    for key in ("router", "router_bias", "expert_bias"):   # router rows and both biases
+        v = None if L[key] is None else L[key].copy()
+        if v is not None:
+            if twin_groups:
+                gs = E // G
+                v[3 * gs:4 * gs] = v[1 * gs:2 * gs]
+            else:
+                v[1::2] = v[0::2]
+        out[key] = v
+    L.update(out)
+    return L
+
+
+def _robust_gaps(sel_m, sigma, S, keep, G):
+    """Smallest distance across the decision boundary between values that are not
+    exactly equal: selected vs unselected masked scores, kept vs dropped group scores."""
+    E = sel_m.shape[0]
+    inset = np.zeros(E, dtype=bool)
+    inset[S] = True
+    a, b = sel_m[inset], sel_m[~inset]
+    d = np.abs(a[:, None] - b[None, :])
+    gap = d[d > 0].min() if (d > 0).any() else np.inf
+    if sigma is not None:
+        kept = np.zeros(G, dtype=bool)
+        kept[keep] = True
+        dg = np.abs(sigma[kept][:, None] - sigma[~kept][None, :])
+        if (dg > 0).any():
+            gap = min(gap, dg[dg > 0].min())
+    return gap
+
+
+CASES = [
+    # (name, spec, twin_groups, T, path)
+    ("twin experts, softmax, G=1, k=5", 2, False, 5, 1, "auto"),
+    ("twin experts, softmax, G=1, k=5", 2, False, 5, 40, "auto"),
+    ("twin experts, softmax, G=1, k=5", 2, False, 5, 300, "prefill"),
+    ("twin experts, sigmoid+bias, 8 groups keep 4, k=7", 3, False, 7, 13, "auto"),
+    ("twin experts, sigmoid+bias, 8 groups keep 4, k=7", 3, False, 7, 300, "prefill"),
+    ("twin groups, sigmoid+bias, 8 groups keep 4, k=8", 4, True, 8, 64, "auto"),
+    ("twin groups, sigmoid+bias, 8 groups keep 4, k=8", 4, True, 8, 300, "prefill"),
+]
+
+
+@pytest.mark.parametrize("name,cid,twin_groups,k,T,path", CASES)
+def test_exact_ties_go_to_the_lower_index(name, cid, twin_groups, k, T, path):
+    import mixture_experts_layer_03_amd as moe
+    base = {2: synth.SPECS[2].variant("ties-lite", 202, hidden=512, moe_intermediate=192,
+                                      shared_intermediate=384, num_experts=16),
+            3: synth.SPECS[3].variant("ties-2.6", 203, hidden=256, moe_intermediate=128,
+                                      shared_intermediate=128, num_experts=64),
+            4: synth.SPECS[4].variant("ties-3.0", 204, hidden=256, moe_intermediate=128,
+                                      shared_intermediate=128, num_experts=64)}[cid]
+    spec = base.variant(base.name, base.seed_id, top_k=k)
+    L = _twin_layer(spec, twin_groups)
+    W = device_weights(L)
+    x = synth.make_x(spec, T)
+    log(f"exact ties: {name}, T={T}, path {path}")
+    cfg = moe_cfg(spec, path=path)
+    log(f"  kernels: {cfg.kernel_path(T)}")
+    y, (idx, _, _) = moe.forward(to_dev(x), W, cfg, return_routing=True)
+    idx_r, _ = moe.route(to_dev(x), W.router, cfg, W.router_bias, W.expert_bias)
+    torch.cuda.synchronize()
+    idx_h = idx.cpu().numpy()
+    assert np.array_equal(idx_h, idx_r.cpu().numpy()), "moe_forward and moe_route disagree"
+    ocfg = oracle_cfg(spec)
+    logits = om.router_logits(x, L["router"], L.get("router_bias"))
+    E, G, g = spec.num_experts, spec.n_group, spec.topk_group
+    gs = E // G
+
+    def twin_below(e):
+        """The expert with the same router row and bias and a lower index, if any."""
+        if not twin_groups:
+            return e - 1 if e % 2 == 1 else None
+        return e - 2 * gs if e // gs == 3 else None
+    checked = near = twin_boundary = 0
+    for t in range(T):
+        s = om.score(logits[t][None, :], ocfg.score_function)[0]
+        sel = om.selection_scores(s, L["expert_bias"], ocfg.use_expert_bias)
+        r = om.route_token(logits[t], ocfg, L["expert_bias"])
+        sigma = keep = None
+        if G > 1 and g < G:
+            keep, sigma = om.kept_groups(sel, G, g)
+        got = idx_h[t].tolist()
+        assert len(set(got)) == k and all(0 <= e < E for e in got), f"token {t}: {got}"
+        # equal scores inside the returned list: lower index first
+        for a, b in zip(got, got[1:]):
+            if r.sel_masked[a] == r.sel_masked[b]:
+                assert a < b, f"token {t}: equal scores out of index order {got}"
+        # an upper twin never taken without its lower twin when their scores are equal
+        for e in got:
+            lo = twin_below(e)
+            if lo is not None and lo not in got:
+                assert r.sel_masked[lo] != r.sel_masked[e], f"token {t}: twin {e} taken over {lo}: {got}"
+        if twin_groups:
+            kept_g = {e // gs for e in got}
+            assert not (3 in kept_g and 1 not in kept_g and sigma[1] == sigma[3]), \
+                f"token {t}: twin group 3 kept over group 1: {got}"
+        twin_boundary += int(r.margin == 0.0)
+        if _robust_gaps(r.sel_masked, sigma, r.idx, keep, G) > MARGIN:
+            assert set(got) == set(r.idx.tolist()), f"token {t}: gpu {sorted(got)} oracle {sorted(r.idx.tolist())}"
+            checked += 1
+        else:
+            near += 1
+    log(f"  ok: {checked}/{T} tokens with the oracle's set, {twin_boundary} with an exact tie "
+        f"on the boundary, {near} near-ties")
+    assert twin_boundary > 0, "the constructed layer produced no exact tie on the boundary"

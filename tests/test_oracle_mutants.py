@@ -117,11 +117,40 @@ def _m17_softmax_over_tokens(mp):  # softmax taken over the wrong axis
     mp.setattr(om, "score", bad)
 
 
+def _m18_route_bias_arguments_swapped(mp):  # router bias taken as the correction bias and back
+    orig = om.route
+
+    def bad(x, W_r, cfg, router_bias=None, expert_bias=None, tokens=None):
+        return orig(x, W_r, cfg, router_bias=expert_bias, expert_bias=router_bias, tokens=tokens)
+    mp.setattr(om, "route", bad)
+
+
+def _m19_route_tokens_off_by_one(mp):  # the tokens= subset shifted by one row
+    orig = om.route
+
+    def bad(x, W_r, cfg, router_bias=None, expert_bias=None, tokens=None):
+        if tokens is not None:
+            tokens = (np.asarray(tokens) + 1) % np.asarray(x).shape[0]
+        return orig(x, W_r, cfg, router_bias=router_bias, expert_bias=expert_bias, tokens=tokens)
+    mp.setattr(om, "route", bad)
+
+
+def _m20_gate_reads_up_scale(mp):  # u8 gate codes dequantised with the up matrix's scales
+    orig = om.expert_matrix
+
+    def bad(weights, name, e, group):
+        if name == "gate" and "gate_q" in weights:
+            weights = dict(weights, gate_scale=weights["up_scale"])
+        return orig(weights, name, e, group)
+    mp.setattr(om, "expert_matrix", bad)
+
+
 MUTANTS = [_m1_bias_in_weights, _m2_renorm_unguarded, _m3_no_scaling, _m4_neg_inf_mask,
            _m5_group_max, _m6_weighted_shared, _m7_nibble_order, _m8_router_bias_dropped,
            _m9_sigmoid_sign, _m10_gate_without_silu, _m11_down_from_up, _m12_zero_point_sign,
            _m13_ties_to_higher_index, _m14_shared_dropped, _m15_worst_groups_kept,
-           _m16_renorm_without_epsilon, _m17_softmax_over_tokens]
+           _m16_renorm_without_epsilon, _m17_softmax_over_tokens, _m18_route_bias_arguments_swapped,
+           _m19_route_tokens_off_by_one, _m20_gate_reads_up_scale]
 
 
 @pytest.mark.parametrize("mutant", MUTANTS, ids=lambda f: f.__name__)
