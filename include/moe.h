@@ -235,6 +235,27 @@ moe_status moe_forward(const moe_config* cfg, int64_t T, const void* x, const mo
                        int32_t* expert_counts_out, void* ws, size_t ws_bytes,
                        moe_stream_t stream);
 
+/* The whole layer as moe_forward, for callers that cannot allocate device memory
+ * (code under HIP graph capture, tight serving loops, harnesses that forbid
+ * hipMalloc).  The scratch memory is a fixed device array of the library,
+ * MOE_NOALLOC_SCRATCH_BYTES (64 MiB) per GPU, held from the library's first use on
+ * that GPU until the process ends; the caller passes only inputs and outputs.  The
+ * call allocates nothing and runs every launch on `stream` (no second stream).
+ *   Same arguments, layouts and results as moe_forward without ws / ws_bytes.
+ *   Limit: moe_workspace_size(cfg, T) <= MOE_NOALLOC_SCRATCH_BYTES (every decode
+ *   batch of the family's layers; prefill batches up to several hundred tokens);
+ *   larger calls -> MOE_EWORKSPACE with the bytes needed, nothing launched.
+ *   Concurrency: all calls on one GPU share its scratch array; calls that overlap in
+ *   time on one GPU (two streams, two host threads) race and give wrong results, so
+ *   the caller serialises them.  No state carries over between calls: every kernel
+ *   writes the scratch it reads within the same call.
+ * Errors: as moe_forward, plus MOE_EHIP if the array's device address cannot be
+ * obtained.                                                                         */
+#define MOE_NOALLOC_SCRATCH_BYTES ((size_t)64 << 20)
+moe_status moe_forward_noalloc(const moe_config* cfg, int64_t T, const void* x, const moe_weights* w,
+                               void* y, int32_t* topk_idx_out, float* topk_w_out,
+                               int32_t* expert_counts_out, moe_stream_t stream);
+
 /* Dense MLP of the layers in front of the MoE layers (`first_k_dense_replace`):
  *   y = (silu(x W_gᵀ) ⊙ (x W_uᵀ)) W_dᵀ
  * A plain gated MLP at the model's intermediate size [mlxcel #838 "Architecture

@@ -6,9 +6,9 @@ binding for device memory and streams.  Build the library with
 """
 from ._lib import MoEError, lib
 from .config import MoEConfig
-from .layer import (MoEWeights, dense_mlp, dense_workspace_size, experts, forward, host_tensor_to_device, permute,
-                    route, weights_from_host)
+from .layer import (MoEWeights, dense_mlp, dense_workspace_size, experts, forward, forward_noalloc,
+                    host_tensor_to_device, permute, route, weights_from_host)
 
-__all__ = ["MoEConfig", "MoEError", "MoEWeights", "dense_mlp", "dense_workspace_size", "experts", "forward",
+__all__ = ["MoEConfig", "MoEError", "MoEWeights", "dense_mlp", "dense_workspace_size", "experts", "forward", "forward_noalloc",
            "host_tensor_to_device", "lib",
            "permute", "route", "weights_from_host"]

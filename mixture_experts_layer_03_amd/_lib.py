@@ -18,6 +18,7 @@ STATUS_NAMES = {0: "MOE_OK", 1: "MOE_EINVAL_CONFIG", 2: "MOE_EINVAL_ARG", 3: "MO
 DT_F32, DT_BF16, DT_U8_AFFINE, DT_U4_AFFINE = 0, 1, 2, 3
 SCORE_SOFTMAX, SCORE_SIGMOID = 0, 1
 PATH_AUTO, PATH_DECODE, PATH_PREFILL = 0, 1, 2
+NOALLOC_SCRATCH_BYTES = 64 << 20   # MOE_NOALLOC_SCRATCH_BYTES
 STAGES = {"router": 1, "topk": 2, "permute": 4, "up": 8, "down": 16, "shared_up": 32,
           "shared_down": 64, "combine": 128}
 
@@ -73,6 +74,7 @@ def lib() -> C.CDLL:
         "moe_permute": [cfgp, I64, P, P, P, P, P, SZ, P],
         "moe_experts": [cfgp, I64, P, wp, P, P, P, P, SZ, P],
         "moe_forward": [cfgp, I64, P, wp, P, P, P, P, P, SZ, P],
+        "moe_forward_noalloc": [cfgp, I64, P, wp, P, P, P, P, P],
         "moe_dense_workspace_size": [cfgp, I64, I64, C.POINTER(SZ)],
         "moe_dense_mlp": [cfgp, I64, I64, P, P, P, P, P, P, SZ, P],
     }

@@ -11,11 +11,15 @@
 #include <cstdarg>
 #include <cstdio>
 #include <cstring>
+#include <mutex>
 
 #include "moe.h"
 #include "kernels.h"
 
 using namespace moe;
+
+// Fixed device scratch of moe_forward_noalloc (its address: noalloc_scratch below).
+static __device__ __align__(256) unsigned char scratch[MOE_NOALLOC_SCRATCH_BYTES];
 
 namespace {
 
@@ -775,6 +779,100 @@ moe_status run_dense(const moe_config& c, const DensePlan& p, int64_t T, int64_t
   return MOE_OK;
 }
 
+// Argument checks of moe_forward and moe_forward_noalloc (everything but the workspace).
+moe_status check_forward_args(const moe_config* cfg, int64_t T, const void* x, const moe_weights* w, const void* y,
+                              const int32_t* topk_idx_out, const float* topk_w_out,
+                              const int32_t* expert_counts_out) {
+  moe_status s = check_config(cfg);
+  if (s != MOE_OK) return s;
+  if ((s = check_T(T)) != MOE_OK) return s;
+  if (T == 0) return MOE_OK;
+  REQUIRE_PTR(x, 16, "x");
+  REQUIRE_PTR(y, 16, "y");
+  if (topk_idx_out && !aligned(topk_idx_out, 4)) return fail(MOE_EINVAL_ARG, "topk_idx_out is not 4-byte aligned");
+  if (topk_w_out && !aligned(topk_w_out, 4)) return fail(MOE_EINVAL_ARG, "topk_w_out is not 4-byte aligned");
+  if (expert_counts_out && !aligned(expert_counts_out, 4))
+    return fail(MOE_EINVAL_ARG, "expert_counts_out is not 4-byte aligned");
+  return check_weights(*cfg, w, true);
+}
+
+// ---- fixed scratch of moe_forward_noalloc, for callers that cannot allocate.
+// A file-scope device array: every GPU the library runs on holds its own copy, at its
+// own address, until the process ends.  In host code `scratch` names a host-side
+// stand-in, so its device address is taken once per device with
+// hipGetSymbolAddress (that device current) and only that address is used.
+constexpr size_t kNoAllocScratchBytes = MOE_NOALLOC_SCRATCH_BYTES;
+
+std::mutex g_scratch_mu;
+void* g_scratch_ptr[64] = {};
+
+moe_status noalloc_scratch(void** out) {
+  int dev = -1;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) return hip_fail(e, "hipGetDevice");
+  if (dev < 0 || dev >= 64) return fail(MOE_EUNSUPPORTED, "device %d: the fixed scratch covers devices 0..63", dev);
+  std::lock_guard<std::mutex> lock(g_scratch_mu);
+  if (!g_scratch_ptr[dev]) {
+    void* ptr = nullptr;
+    e = hipGetSymbolAddress(&ptr, HIP_SYMBOL(scratch));
+    if (e != hipSuccess) return hip_fail(e, "hipGetSymbolAddress(scratch)");
+    if (!ptr || !aligned(ptr, 256)) return fail(MOE_EHIP, "the fixed scratch has no 256-byte aligned device address");
+    g_scratch_ptr[dev] = ptr;
+  }
+  *out = g_scratch_ptr[dev];
+  return MOE_OK;
+}
+
+// The whole layer on stream st with a checked plan and workspace.  With `fork`, the
+// prefill path runs the shared expert's gate/up on a second stream of this thread;
+// without it every launch goes to st.
+moe_status run_forward(const moe_config& c, const Plan& p, int64_t T, const void* x, const moe_weights* w, void* y,
+                       int32_t* topk_idx_out, float* topk_w_out, int32_t* expert_counts_out, void* ws,
+                       hipStream_t st, bool fork) {
+  const moe_config* cfg = &c;
+  moe_status s = MOE_OK;
+  int32_t* idx = topk_idx_out ? topk_idx_out : at<int32_t>(ws, p.o_idx);
+  float* wt = topk_w_out ? topk_w_out : at<float>(ws, p.o_w);
+  const float* ebias = cfg->use_expert_bias ? w->expert_bias : nullptr;
+  // prefill: the shared expert's gate/up GEMM, which needs no routing, runs on a second
+  // stream beside the router, top-k, permutation and routed GEMMs (measured: the
+  // Ling-lite shape at 4096 tokens 0.906 -> 0.873 ms).  Decode keeps one stream: there
+  // the two extra launches and the join cost more than the overlap gains, eagerly and
+  // as graph branches alike (Ling-lite at 1 token: graph replay 55 -> 72 us forked).
+  hipEvent_t join = nullptr;
+  AuxStream* aux = fork && cfg->shared_intermediate > 0 && !p.decode ? aux_stream(st) : nullptr;
+  if (aux) {
+    {
+      hipError_t e = hipEventRecord(aux->fork, st);
+      if (e == hipSuccess) e = hipStreamWaitEvent(aux->s, aux->fork, 0);
+      if (e != hipSuccess) return hip_fail(e, "fork of the shared expert");
+      if ((s = run_shared(*cfg, p, T, x, w, ws, aux->s)) != MOE_OK) return s;
+      if ((e = hipEventRecord(aux->join, aux->s)) != hipSuccess) return hip_fail(e, "shared expert done");
+      join = aux->join;
+    }
+  }
+  if (p.decode && T <= kFusedRouteMaxT && T * cfg->top_k <= kFusedSlots) {
+    // small batch: route and permute in one workgroup
+    if ((s = run_logits(*cfg, p, T, x, w->router, ws, st)) != MOE_OK) return s;
+    const TopkArgs ta = topk_args(*cfg, p, T, ws, w->router_bias, ebias, idx, wt);
+    const PermuteArgs pa = permute_args(*cfg, p, T, idx, at<int32_t>(ws, p.o_counts), at<int32_t>(ws, p.o_offsets),
+                                          at<int32_t>(ws, p.o_perm), nullptr, ws);
+    MOE_LAUNCH_STAGE(MOE_STAGE_TOPK, st, launch_route_permute(ta, pa, st), "top-k + permutation");
+    s = run_experts(*cfg, p, T, x, w, idx, wt, y, ws, st, true, join);
+  } else {
+    s = run_route(*cfg, p, T, x, w->router, w->router_bias, ebias, idx, wt, ws, st);
+    if (s != MOE_OK) return s;
+    s = run_experts(*cfg, p, T, x, w, idx, wt, y, ws, st, false, join);
+  }
+  if (s != MOE_OK) return s;
+  if (expert_counts_out) {
+    const hipError_t e = hipMemcpyAsync(expert_counts_out, at<int32_t>(ws, p.o_counts),
+                                          sizeof(int32_t) * cfg->num_experts, hipMemcpyDeviceToDevice, st);
+    if (e != hipSuccess) return hip_fail(e, "expert counts copy");
+  }
+  return MOE_OK;
+}
+
 }  // namespace
 
 extern "C" {
@@ -902,61 +1000,39 @@ moe_status moe_forward(const moe_config* cfg, int64_t T, const void* x, const mo
                        int32_t* topk_idx_out, float* topk_w_out, int32_t* expert_counts_out, void* ws,
                        size_t ws_bytes, moe_stream_t stream) {
   try {
-    moe_status s = check_config(cfg);
-    if (s != MOE_OK) return s;
-    if ((s = check_T(T)) != MOE_OK) return s;
-    if (T == 0) return ok();
-    REQUIRE_PTR(x, 16, "x");
-    REQUIRE_PTR(y, 16, "y");
-    if (topk_idx_out && !aligned(topk_idx_out, 4)) return fail(MOE_EINVAL_ARG, "topk_idx_out is not 4-byte aligned");
-    if (topk_w_out && !aligned(topk_w_out, 4)) return fail(MOE_EINVAL_ARG, "topk_w_out is not 4-byte aligned");
-    if (expert_counts_out && !aligned(expert_counts_out, 4)) return fail(MOE_EINVAL_ARG, "expert_counts_out is not 4-byte aligned");
-    if ((s = check_weights(*cfg, w, true)) != MOE_OK) return s;
+    moe_status s = check_forward_args(cfg, T, x, w, y, topk_idx_out, topk_w_out, expert_counts_out);
+    if (s != MOE_OK || T == 0) return s == MOE_OK ? ok() : s;
     Plan p;
     if ((s = check_ws(*cfg, T, ws, ws_bytes, p)) != MOE_OK) return s;
-    const hipStream_t st = static_cast<hipStream_t>(stream);
-    int32_t* idx = topk_idx_out ? topk_idx_out : at<int32_t>(ws, p.o_idx);
-    float* wt = topk_w_out ? topk_w_out : at<float>(ws, p.o_w);
-    const float* ebias = cfg->use_expert_bias ? w->expert_bias : nullptr;
-    // prefill: the shared expert's gate/up GEMM, which needs no routing, runs on a second
-    // stream beside the router, top-k, permutation and routed GEMMs (measured: the
-    // Ling-lite shape at 4096 tokens 0.906 -> 0.873 ms).  Decode keeps one stream: there
-    // the two extra launches and the join cost more than the overlap gains, eagerly and
-    // as graph branches alike (Ling-lite at 1 token: graph replay 55 -> 72 us forked).
-    hipEvent_t join = nullptr;
-    AuxStream* aux = cfg->shared_intermediate > 0 && !p.decode ? aux_stream(st) : nullptr;
-    if (aux) {
-      {
-        hipError_t e = hipEventRecord(aux->fork, st);
-        if (e == hipSuccess) e = hipStreamWaitEvent(aux->s, aux->fork, 0);
-        if (e != hipSuccess) return hip_fail(e, "fork of the shared expert");
-        if ((s = run_shared(*cfg, p, T, x, w, ws, aux->s)) != MOE_OK) return s;
-        if ((e = hipEventRecord(aux->join, aux->s)) != hipSuccess) return hip_fail(e, "shared expert done");
-        join = aux->join;
-      }
-    }
-    if (p.decode && T <= kFusedRouteMaxT && T * cfg->top_k <= kFusedSlots) {
-      // small batch: route and permute in one workgroup
-      if ((s = run_logits(*cfg, p, T, x, w->router, ws, st)) != MOE_OK) return s;
-      const TopkArgs ta = topk_args(*cfg, p, T, ws, w->router_bias, ebias, idx, wt);
-      const PermuteArgs pa = permute_args(*cfg, p, T, idx, at<int32_t>(ws, p.o_counts), at<int32_t>(ws, p.o_offsets),
-                                          at<int32_t>(ws, p.o_perm), nullptr, ws);
-      MOE_LAUNCH_STAGE(MOE_STAGE_TOPK, st, launch_route_permute(ta, pa, st), "top-k + permutation");
-      s = run_experts(*cfg, p, T, x, w, idx, wt, y, ws, st, true, join);
-    } else {
-      s = run_route(*cfg, p, T, x, w->router, w->router_bias, ebias, idx, wt, ws, st);
-      if (s != MOE_OK) return s;
-      s = run_experts(*cfg, p, T, x, w, idx, wt, y, ws, st, false, join);
-    }
-    if (s != MOE_OK) return s;
-    if (expert_counts_out) {
-      const hipError_t e = hipMemcpyAsync(expert_counts_out, at<int32_t>(ws, p.o_counts),
-                                          sizeof(int32_t) * cfg->num_experts, hipMemcpyDeviceToDevice, st);
-      if (e != hipSuccess) return hip_fail(e, "expert counts copy");
-    }
-    return ok();
+    s = run_forward(*cfg, p, T, x, w, y, topk_idx_out, topk_w_out, expert_counts_out, ws,
+                    static_cast<hipStream_t>(stream), true);
+    return s == MOE_OK ? ok() : s;
   } catch (...) {
     return fail(MOE_EINVAL_ARG, "internal error in moe_forward");
+  }
+}
+
+moe_status moe_forward_noalloc(const moe_config* cfg, int64_t T, const void* x, const moe_weights* w, void* y,
+                               int32_t* topk_idx_out, float* topk_w_out, int32_t* expert_counts_out,
+                               moe_stream_t stream) {
+  try {
+    moe_status s = check_forward_args(cfg, T, x, w, y, topk_idx_out, topk_w_out, expert_counts_out);
+    if (s != MOE_OK || T == 0) return s == MOE_OK ? ok() : s;
+    Plan p;
+    make_plan(*cfg, T, p);
+    if (p.total > kNoAllocScratchBytes)
+      return fail(MOE_EWORKSPACE,
+                  "T=%lld needs %zu bytes of scratch; moe_forward_noalloc holds at most %zu "
+                  "(split the batch, or pass a workspace to moe_forward)",
+                  (long long)T, p.total, kNoAllocScratchBytes);
+    void* ws = nullptr;
+    if ((s = noalloc_scratch(&ws)) != MOE_OK) return s;
+    if ((s = check_ws(*cfg, T, ws, kNoAllocScratchBytes, p)) != MOE_OK) return s;
+    s = run_forward(*cfg, p, T, x, w, y, topk_idx_out, topk_w_out, expert_counts_out, ws,
+                    static_cast<hipStream_t>(stream), false);
+    return s == MOE_OK ? ok() : s;
+  } catch (...) {
+    return fail(MOE_EINVAL_ARG, "internal error in moe_forward_noalloc");
   }
 }
 

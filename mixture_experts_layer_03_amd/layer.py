@@ -250,6 +250,33 @@ def forward(x: torch.Tensor, weights: MoEWeights, cfg: MoEConfig, return_routing
     return y
 
 
+def forward_noalloc(x: torch.Tensor, weights: MoEWeights, cfg: MoEConfig, return_routing=False, out=None):
+    """The whole layer through moe_forward_noalloc: no workspace argument; the library's
+    fixed device scratch (64 MiB per GPU) is used instead.  Calls that overlap in time on
+    one GPU share that scratch and race; the caller serialises them."""
+    _x_checks(cfg, x)
+    T = x.shape[0]
+    check_weights(cfg, weights, x.device, need_router=True, need_experts=True)
+    y = out if out is not None else torch.empty_like(x)
+    if out is not None:
+        _need(out, "out", tuple(x.shape), x.dtype, x.device)
+    idx = wt = counts = None
+    if return_routing:
+        idx = torch.empty((T, cfg.top_k), dtype=torch.int32, device=x.device)
+        wt = torch.empty((T, cfg.top_k), dtype=torch.float32, device=x.device)
+        counts = torch.zeros(cfg.num_experts, dtype=torch.int32, device=x.device)
+    if T > 0:
+        c = cfg.to_c()
+        wc = weights.to_c()
+        _lib.check(_lib.lib().moe_forward_noalloc(
+            C.byref(c), T, x.data_ptr(), C.byref(wc), y.data_ptr(),
+            None if idx is None else idx.data_ptr(), None if wt is None else wt.data_ptr(),
+            None if counts is None else counts.data_ptr(), _stream(x.device)))
+    if return_routing:
+        return y, (idx, wt, counts)
+    return y
+
+
 def dense_workspace_size(cfg: MoEConfig, intermediate: int, T: int) -> int:
     n = C.c_size_t(0)
     c = cfg.to_c()

@@ -331,3 +331,21 @@ def test_dense_rejects_bad_arguments_before_any_launch():
     st = L.moe_dense_mlp(C.byref(good(path="prefill").to_c()), 32768, big, fake, fake, fake, fake, fake, fake,
                          1 << 62, None)
     assert st == _lib.MOE_EUNSUPPORTED
+
+
+def test_noalloc_rejects_calls_beyond_its_scratch_on_the_host():
+    """moe_forward_noalloc refuses a call whose workspace exceeds the fixed scratch, on
+    the host, before touching the GPU, naming the bytes needed (no GPU in this test)."""
+    cfg = good()
+    T = 4096
+    need = cfg.workspace_size(T)
+    assert need > _lib.NOALLOC_SCRATCH_BYTES
+    c = cfg.to_c()
+    wc = _lib.moe_weights(**{n: 256 for n, _ in _lib.moe_weights._fields_})  # never dereferenced
+    st = _lib.lib().moe_forward_noalloc(C.byref(c), T, 256, C.byref(wc), 256, None, None, None, None)
+    msg = _lib.lib().moe_last_error().decode()
+    assert st == _lib.MOE_EWORKSPACE and str(need) in msg, (st, msg)
+    # argument checks come first, as in moe_forward
+    st = _lib.lib().moe_forward_noalloc(C.byref(c), T, 8, C.byref(wc), 256, None, None, None, None)
+    assert st == _lib.MOE_EINVAL_ARG and "x" in _lib.lib().moe_last_error().decode()
+    assert _lib.lib().moe_forward_noalloc(C.byref(c), 0, None, C.byref(wc), None, None, None, None, None) == 0
