@@ -64,7 +64,14 @@ __device__ __forceinline__ uint4 ldg16(const void* p) { return *reinterpret_cast
 // XCD (hardware deals blocks round-robin over the 8 XCDs); within a group of G
 // consecutive M-tiles the N-tile index varies slowest, so the G blocks that read the
 // same weight panel run together and share it through L2, and the group's G
-// activation panels stay hot.  Returns false for a block past the last M-tile.
+// activation panels stay hot.  Routed products with few tokens per expert
+// (a.plain_order) keep the launch order instead and put an expert's N-tiles side by
+// side: measured on the MI355X, with one or two M-tiles per expert there is little
+// panel reuse to gain, and the tiles of one XCD crowding onto the same lines cost more
+// (gate/up at 4096 tokens of the Ling-2.6-flash shape 1200 -> 1095 us, at 8192 of the
+// Ling-3.0-flash shape 2146 -> 1930 us; Ling-lite, with 3-4 M-tiles per expert, is
+// faster the XCD way, 384 against 422-435 us).  Returns false for a block past the
+// last M-tile.
 struct TilePos {
   int nt, kp, e, m_begin, m_rows, kt0, kt1;
 };
@@ -75,7 +82,7 @@ __device__ __forceinline__ bool tile_pos(const TileArgs& a, TilePos& p, int nblo
   if (NT <= 0) NT = (a.N + NCOL - 1) / NCOL;
   const int per = nblocks / 8;
   const int KS = a.ksplit > 1 ? a.ksplit : 1;
-  const int Lx = (blockIdx.x % 8) * per + blockIdx.x / 8;
+  const int Lx = a.plain_order ? static_cast<int>(blockIdx.x) : (blockIdx.x % 8) * per + blockIdx.x / 8;
   p.kp = Lx % KS;
   const int L = Lx / KS;
   int mt;
@@ -90,8 +97,13 @@ __device__ __forceinline__ bool tile_pos(const TileArgs& a, TilePos& p, int nblo
     const int first = q - (a.tiles[2 * q + 1] - a.offsets[e]) / TBM;
     const int me = (a.offsets[e + 1] - a.offsets[e] + TBM - 1) / TBM;
     const int local = L - first * NT;
-    p.nt = local / me;
-    mt = first + local % me;
+    if (a.plain_order) {
+      p.nt = local % NT;
+      mt = first + local / NT;
+    } else {
+      p.nt = local / me;
+      mt = first + local % me;
+    }
   } else {
     const int G = a.group_m > 1 ? a.group_m : 1;
     const int grp = L / (G * NT), rem = L % (G * NT);

@@ -154,6 +154,9 @@ struct TileArgs {
   int ksplit;               // F32 epilogue only: K split into this many partial outputs
   int64_t part_stride;      // elements between partial outputs
   int group_m;              // M-tiles per block-order group (weight-panel reuse in L2)
+  int plain_order;          // routed: 1 = blocks in launch order, an expert's N-tiles
+                            // side by side; 0 = consecutive tiles on one XCD, an N-tile's
+                            // M-tiles side by side (see tile_pos)
   int ncu;                  // compute units of the device (tile-shape choice)
   // routed SwiGLU products whose last 256-column N-tile is at most half full: that
   // tile's columns are computed over chunks of 256 positions (tiles2, count meta[3])

@@ -59,6 +59,9 @@ constexpr int64_t kDecodeTokensTimesHidden = 40960, kDecodeHiddenFloor = 2048;
 constexpr int kDenseDecodeMaxT = 192;
 constexpr int kFusedRouteMaxT = 16;  // one workgroup routes and permutes up to this many tokens
 constexpr int kGroupM = 4;           // M-tiles per block-order group of the tiled GEMMs
+// Routed GEMMs keep the launch order of their blocks (TileArgs::plain_order) when the
+// experts average at most this many routed tokens (1.5 M-tiles of 128).
+constexpr int64_t kPlainOrderMaxSlotsPerExpert = 192;
 
 bool is_flag(int32_t v) { return v == 0 || v == 1; }
 
@@ -523,6 +526,7 @@ moe_status run_experts(const moe_config& c, const Plan& p, int64_t T, const void
   g.tiles2 = p.mtiles2_bound > 0 ? at<int32_t>(ws, p.o_tiles2) : nullptr;
   g.mtiles2_bound = p.mtiles2_bound;
   g.group_m = 0;  // blocks grouped by expert
+  g.plain_order = T * c.top_k <= kPlainOrderMaxSlotsPerExpert * c.num_experts;
   g.ncu = device_cus();
   MOE_LAUNCH_STAGE(MOE_STAGE_UP, s, launch_tile_gemm(g, AMode::GATHER, wf, Epi::SWIGLU, s), "expert gate/up (tiled)");
   TileArgs d{};
@@ -544,6 +548,7 @@ moe_status run_experts(const moe_config& c, const Plan& p, int64_t T, const void
   d.topk_w = topk_w;
   d.mtiles_bound = p.mtiles_bound;
   d.group_m = 0;
+  d.plain_order = g.plain_order;
   d.ncu = g.ncu;
   MOE_LAUNCH_STAGE(MOE_STAGE_DOWN, s, launch_tile_gemm(d, AMode::DENSE, wf, Epi::SCALED_SLOT, s), "expert down (tiled)");
   (void)dmax;
