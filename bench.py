@@ -6,9 +6,14 @@ SwiGLU experts, shared expert, combine) on one batch of seeded synthetic tokens,
 inputs and weights already resident in HBM.  The headline workload is the
 Ling-lite-shaped layer (hidden 2048, 64 experts top-6, moe_intermediate 1408,
 shared width 2816, bf16) at T=4096 tokens; decode batches T=1 and T=64 of the
-same layer are reported alongside (eager calls and HIP-graph replays).  Layer
-copies are rotated between steps so that weight reads come from HBM, not from
-the 256 MB Infinity Cache.
+same layer are reported alongside (eager calls and HIP-graph replays), and
+per_config repeats the protocol for other workloads (by default the
+Ling-2.6-flash-style layer at T=1/64/4096 and the u8 Ling-3.0-flash-style layer
+at T=1/64).  Layer copies are rotated between steps so that weight reads come
+from HBM, not from the 256 MB Infinity Cache.  Every batch also carries its
+comparison with the fp64 oracle (routing-set mismatches, near-ties, max relative
+error) and its p10/p50/p90 step times; the line carries the measured bandwidth of
+a 1 GiB device copy.
 
 Prints one JSON line (field meanings are in the repository's design notes).
 """
@@ -53,7 +58,14 @@ def parse():
     ap.add_argument("--cpu-sample-tokens", type=int, default=4096)
     ap.add_argument("--no-graph", action="store_true", help="skip the HIP-graph replay timing")
     ap.add_argument("--calib-copy", action="store_true",
-                    help="also run a 1 GiB device copy (reference kernel for counter scaling)")
+                    help="also run a 1 GiB device copy under the profiler (reference kernel for counter scaling); "
+                         "the copy's bandwidth is measured and reported in every run")
+    ap.add_argument("--per-config", default="3:1,64,4096;5:1,64",
+                    help="extra workloads reported in per_config, 'cfg:T,T;cfg:T' ('' = none)")
+    ap.add_argument("--parity-tokens", type=int, default=256,
+                    help="tokens of a batch above 64 tokens compared with the oracle (seeded sample; "
+                         "batches up to 64 tokens are compared on every token)")
+    ap.add_argument("--no-parity", action="store_true", help="skip the oracle comparison of each batch")
     return ap.parse_args()
 
 
@@ -156,6 +168,15 @@ def run_eager(moe, cfg, copies, x, steps, warmup, stage_mask, spinup_ms=0.0):
         moe.forward(x, copies[i % L], cfg, ws=ws, out=y)
     torch.cuda.synchronize()
     t1 = time.perf_counter()
+    # per-step durations for the percentiles: one event after each step on the launch
+    # stream (a pass of its own; the loop above records none)
+    ev = [torch.cuda.Event(enable_timing=True) for _ in range(steps + 1)]
+    ev[0].record()
+    for i in range(steps):
+        moe.forward(x, copies[i % L], cfg, ws=ws, out=y)
+        ev[i + 1].record()
+    torch.cuda.synchronize()
+    per_step = sorted(ev[i].elapsed_time(ev[i + 1]) for i in range(steps))
     _lib.check(moe.lib().moe_profile_enable(stage_mask, max(8, 16 * steps)))
     torch.cuda.synchronize()
     for i in range(steps):
@@ -163,7 +184,17 @@ def run_eager(moe, cfg, copies, x, steps, warmup, stage_mask, spinup_ms=0.0):
     torch.cuda.synchronize()
     st = stage_times(moe, stage_mask)
     _lib.check(moe.lib().moe_profile_disable())
-    return t1 - t0, st
+    return t1 - t0, st, per_step
+
+
+def percentile(sorted_vals, q):
+    """q-th percentile (0..100) of an ascending list, by linear interpolation."""
+    if not sorted_vals:
+        return None
+    pos = (len(sorted_vals) - 1) * q / 100.0
+    lo = int(np.floor(pos))
+    hi = min(lo + 1, len(sorted_vals) - 1)
+    return sorted_vals[lo] + (sorted_vals[hi] - sorted_vals[lo]) * (pos - lo)
 
 
 def run_graph(moe, cfg, copies, x, steps, warmup):
@@ -201,6 +232,8 @@ def run_graph(moe, cfg, copies, x, steps, warmup):
 
 
 def cpu_baseline(spec, L_host, x_host, n_tok):
+    """The fp64 oracle timed on the host on the first n_tok tokens of the batch; also
+    returns its first pass's outputs and diagnostics (for the parity fields)."""
     from dataclasses import fields
     import oracle.moe_oracle as om
     try:
@@ -213,15 +246,76 @@ def cpu_baseline(spec, L_host, x_host, n_tok):
     # repeat the token sample until about min_seconds of oracle work (bounded by max_passes)
     min_seconds, max_passes = 10.0, 20
     passes, t0 = 0, time.perf_counter()
+    first = None
     while True:
-        om.forward(x_host, L_host, ocfg, tokens=tok)
+        out = om.forward(x_host, L_host, ocfg, tokens=tok)
+        if first is None:
+            first = out
         passes += 1
         dt = time.perf_counter() - t0
         if dt >= min_seconds or passes >= max_passes:
             break
-    return dict(value=passes * len(tok) / dt, unit="tokens/s", cores=int(cores), kind="oracle",
-                sample=f"fp64 oracle (NumPy/BLAS) on {len(tok)} tokens of the T={x_host.shape[0]} batch "
-                       f"(same layer and routing), {passes} passes, {dt:.1f} s on {cores} threads")
+    rec = dict(value=passes * len(tok) / dt, unit="tokens/s", cores=int(cores), kind="oracle",
+               sample=f"fp64 oracle (NumPy/BLAS) on {len(tok)} tokens of the T={x_host.shape[0]} batch "
+                      f"(same layer and routing), {passes} passes, {dt:.1f} s on {cores} threads")
+    return rec, tok, first
+
+
+MARGIN = 1e-5      # routing decisions closer than this to a tie may flip under rounding
+Y_TOL = {"bf16": 2e-2, "f32": 1e-4}
+
+
+def parity_fields(spec, L_host, x_host, y_gpu, idx_gpu, tok, oracle_out=None):
+    """The GPU batch against the fp64 oracle on tokens `tok`: routing-set mismatches on
+    tokens whose decision margin exceeds 1e-5, the near-tie count, masked picks, and the
+    largest per-token relative error of the outputs (near-tie tokens compared with the
+    oracle re-run on the GPU's own expert sets)."""
+    from dataclasses import fields
+    import oracle.moe_oracle as om
+    ocfg = om.OracleConfig(**{f.name: getattr(spec, f.name) for f in fields(om.OracleConfig)})
+    y_o, d = oracle_out if oracle_out is not None else om.forward(x_host, L_host, ocfg, tokens=tok)
+    y_o = y_o.copy()
+    ig = idx_gpu[tok]
+    near = d["margin"] <= MARGIN
+    mism = sum(int(set(ig[t].tolist()) != set(d["idx"][t].tolist())) for t in np.nonzero(~near)[0])
+    if near.any():
+        nz = np.nonzero(near)[0]
+        y_f, _ = om.forward(x_host, L_host, ocfg, tokens=tok[nz], forced_idx=ig[nz])
+        y_o[nz] = y_f
+    yg = y_gpu[tok]
+    rel = np.abs(yg - y_o).max(axis=1) / np.maximum(np.abs(y_o).max(axis=1), 1e-30)
+    return dict(tokens=int(len(tok)), set_mismatches=int(mism), near_ties=int(near.sum()),
+                masked_picks=int(d["masked_pick"].sum()), max_rel_err=float(rel.max()),
+                tolerance=Y_TOL[spec.act_dtype], ok=bool(mism == 0 and rel.max() <= Y_TOL[spec.act_dtype]))
+
+
+def parity_sample(T, n, seed=0):
+    """Every token up to 64 (or n); beyond, the first, the last and a seeded random set."""
+    if T <= max(64, n):
+        return np.arange(T)
+    rng = np.random.default_rng(seed + T)
+    mid = rng.choice(np.arange(1, T - 1), size=n - 2, replace=False)
+    return np.sort(np.concatenate([[0, T - 1], mid]))
+
+
+def copy_bandwidth(dev, nbytes=1 << 30, reps=10):
+    """Device-to-device copy of nbytes (read + write bytes per second): the reference
+    kernel the HBM counters are scaled with, and a measured bandwidth ceiling."""
+    import torch
+    a = torch.empty(nbytes, dtype=torch.uint8, device=dev)
+    b = torch.empty_like(a)
+    b.copy_(a)
+    torch.cuda.synchronize()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record()
+    for _ in range(reps):
+        b.copy_(a)
+    e1.record()
+    torch.cuda.synchronize()
+    sec = e0.elapsed_time(e1) / 1e3 / reps
+    del a, b
+    torch.cuda.empty_cache()
+    return 2.0 * nbytes / sec / 1e9
 
 
 def recorded_traffic(kernel_key, digest, launch_div=1.0):
@@ -385,6 +479,89 @@ def bench_dense(args):
     print(json.dumps(line), flush=True)
 
 
+def measure_workload(args, spec, Ts, dev, headline_T=None, cpu=False):
+    """Every batch size of one workload: eager and graph-replay times (with per-step
+    percentiles), the routed gate/up kernel's event-timed average, the parity fields, and
+    (cpu) the oracle's host rate.  Returns (results by T, cpu_baseline record or None)."""
+    import torch
+    import synth
+    import mixture_experts_layer_03_amd as moe
+    from mixture_experts_layer_03_amd import _lib
+    t_gen = time.perf_counter()
+    L_host = synth.make_layer(spec)
+    W0 = moe.weights_from_host(L_host, dev)
+    gen_s = time.perf_counter() - t_gen
+    all_copies = [W0]
+
+    def get_copies(n):
+        while len(all_copies) < n:
+            all_copies.append(gpu_copy(spec, len(all_copies), W0, dev))
+        return all_copies[:n]
+
+    cfg = moe.MoEConfig.from_object(spec)
+    results, cpu_rec = {}, None
+    for T in Ts:
+        x_host = synth.make_x(spec, T)
+        x = moe.host_tensor_to_device(x_host, dev)
+        y0, (idx, wt, counts) = moe.forward(x, W0, cfg, return_routing=True)
+        torch.cuda.synchronize()
+        alg = algorithmic(spec, T, counts.cpu().numpy())
+        ncp = max(1, min(args.max_copies, int(np.ceil(args.min_rotation_bytes / max(alg["bytes"], 1.0)))))
+        cps = get_copies(ncp)
+        mask = _lib.STAGES["up"] | _lib.STAGES["down"]
+        steps = args.steps if T == headline_T else max(args.steps, 100)
+        secs, stages, per_step = run_eager(moe, cfg, cps, x, steps, args.warmup, mask, args.spinup_ms)
+        t_step = secs / steps
+        r = dict(T=T, copies=ncp, ms_per_step=t_step * 1e3, tokens_per_s=T / t_step,
+                 hbm_gbps=alg["bytes"] / t_step / 1e9, mfma_tflops=alg["flops"] / t_step / 1e12,
+                 distinct_experts=alg["D"], stage_ms=stages, alg=alg, path=cfg.kernel_path(T),
+                 step_ms_p10=percentile(per_step, 10), step_ms_p50=percentile(per_step, 50),
+                 step_ms_p90=percentile(per_step, 90))
+        r["hbm_frac"] = r["hbm_gbps"] / HBM_PEAK_GBPS
+        r["mfma_frac"] = r["mfma_tflops"] / BF16_PEAK_TFLOPS
+        r["roofline_frac"] = max(alg["bytes"] / (HBM_PEAK_GBPS * 1e9),
+                                 alg["flops"] / (BF16_PEAK_TFLOPS * 1e12)) / t_step
+        up_ms = stages.get("up")
+        if up_ms:
+            if r["path"] == "prefill":
+                r["up_tflops"] = alg["up_flops"] / (up_ms * 1e-3) / 1e12
+                r["up_mfma_frac"] = r["up_tflops"] / BF16_PEAK_TFLOPS
+            else:
+                r["up_gbps"] = alg["up_bytes_decode"] / (up_ms * 1e-3) / 1e9
+                r["up_hbm_frac"] = r["up_gbps"] / HBM_PEAK_GBPS
+        if not args.no_graph:
+            gsecs, ok = run_graph(moe, cfg, cps, x, steps, args.warmup)
+            gt = gsecs / steps
+            r.update(graph_ms_per_step=gt * 1e3, graph_tokens_per_s=T / gt,
+                     graph_hbm_gbps=alg["bytes"] / gt / 1e9,
+                     graph_hbm_frac=alg["bytes"] / gt / 1e9 / HBM_PEAK_GBPS,
+                     graph_roofline_frac=max(alg["bytes"] / (HBM_PEAK_GBPS * 1e9),
+                                             alg["flops"] / (BF16_PEAK_TFLOPS * 1e12)) / gt,
+                     graph_matches_eager=ok)
+        y_h = y0.float().cpu().numpy().astype(np.float64)
+        idx_h = idx.cpu().numpy()
+        if cpu and T == headline_T and not args.no_cpu_baseline:
+            cpu_rec, tok, first = cpu_baseline(spec, L_host, x_host, args.cpu_sample_tokens)
+            if not args.no_parity:
+                r["parity"] = parity_fields(spec, L_host, x_host, y_h, idx_h, tok, first)
+        elif not args.no_parity:
+            r["parity"] = parity_fields(spec, L_host, x_host, y_h, idx_h, parity_sample(T, args.parity_tokens))
+        results[T] = r
+    del all_copies, W0
+    torch.cuda.empty_cache()
+    return results, cpu_rec, gen_s
+
+
+def brief(r):
+    return {k: (round(v, 5) if isinstance(v, float) else v) for k, v in r.items() if k != "alg"}
+
+
+def workload_name(spec):
+    return (f"{spec.name} MoE layer: hidden {spec.hidden}, {spec.num_experts} experts top-{spec.top_k}, "
+            f"moe_intermediate {spec.moe_intermediate}, shared {spec.shared_intermediate}, {spec.score_function}, "
+            f"n_group {spec.n_group}, experts {spec.expert_dtype}")
+
+
 def main():
     args = parse()
     world = int(os.environ.get("WORLD_SIZE", "1"))
@@ -398,68 +575,25 @@ def main():
         return
     import torch
     import synth
-    import mixture_experts_layer_03_amd as moe
-    from mixture_experts_layer_03_amd import _lib
 
     spec = synth.SPECS[args.config]
     dev = torch.device("cuda:0")
-    t_gen = time.perf_counter()
-    L_host = synth.make_layer(spec)
-    W0 = moe.weights_from_host(L_host, dev)
-    gen_s = time.perf_counter() - t_gen
     lb = synth.layer_bytes(spec)
     layer_bytes = spec.num_experts * lb["expert"] + lb["shared"] + lb["router"]
     digest = source_digest()
-
-    all_copies = [W0]
-
-    def get_copies(n):
-        while len(all_copies) < n:
-            all_copies.append(gpu_copy(spec, len(all_copies), W0, dev))
-        return all_copies[:n]
-
-    cfg = moe.MoEConfig.from_object(spec)
-    results = {}
     Ts = [args.tokens] + [int(t) for t in args.decode_tokens.split(",") if t.strip()]
-    head_x_host = None
-    for T in Ts:
-        x_host = synth.make_x(spec, T)
-        x = moe.host_tensor_to_device(x_host, dev)
-        _, (idx, wt, counts) = moe.forward(x, W0, cfg, return_routing=True)
-        torch.cuda.synchronize()
-        alg = algorithmic(spec, T, counts.cpu().numpy())
-        ncp = max(1, min(args.max_copies, int(np.ceil(args.min_rotation_bytes / max(alg["bytes"], 1.0)))))
-        cps = get_copies(ncp)
-        mask = _lib.STAGES["up"] | _lib.STAGES["down"]
-        steps = args.steps if T == args.tokens else max(args.steps, 100)
-        secs, stages = run_eager(moe, cfg, cps, x, steps, args.warmup, mask, args.spinup_ms)
-        t_step = secs / steps
-        r = dict(T=T, copies=ncp, ms_per_step=t_step * 1e3, tokens_per_s=T / t_step,
-                 hbm_gbps=alg["bytes"] / t_step / 1e9, mfma_tflops=alg["flops"] / t_step / 1e12,
-                 distinct_experts=alg["D"], stage_ms=stages, alg=alg,
-                 path=cfg.kernel_path(T))
-        r["hbm_frac"] = r["hbm_gbps"] / HBM_PEAK_GBPS
-        r["mfma_frac"] = r["mfma_tflops"] / BF16_PEAK_TFLOPS
-        r["roofline_frac"] = max(alg["bytes"] / (HBM_PEAK_GBPS * 1e9),
-                                 alg["flops"] / (BF16_PEAK_TFLOPS * 1e12)) / t_step
-        if not args.no_graph:
-            gsecs, ok = run_graph(moe, cfg, cps, x, steps, args.warmup)
-            gt = gsecs / steps
-            r.update(graph_ms_per_step=gt * 1e3, graph_tokens_per_s=T / gt,
-                     graph_hbm_gbps=alg["bytes"] / gt / 1e9,
-                     graph_hbm_frac=alg["bytes"] / gt / 1e9 / HBM_PEAK_GBPS,
-                     graph_roofline_frac=max(alg["bytes"] / (HBM_PEAK_GBPS * 1e9),
-                                             alg["flops"] / (BF16_PEAK_TFLOPS * 1e12)) / gt,
-                     graph_matches_eager=ok)
-        results[T] = r
-        if T == args.tokens:
-            head_x_host = x_host
+    results, cpu, gen_s = measure_workload(args, spec, Ts, dev, headline_T=args.tokens, cpu=True)
 
-    if args.calib_copy:
-        a = torch.empty(1 << 30, dtype=torch.uint8, device=dev)
-        b = torch.empty_like(a)
-        b.copy_(a)
-        torch.cuda.synchronize()
+    per_config = []
+    for item in [q for q in args.per_config.split(";") if q.strip()]:
+        cid, ts = item.split(":")
+        pspec = synth.SPECS[int(cid)]
+        pT = [int(t) for t in ts.split(",") if t.strip()]
+        pres, _, _ = measure_workload(args, pspec, pT, dev, headline_T=max(pT))
+        per_config.append({"config": int(cid), "workload": workload_name(pspec),
+                           "per_T": [brief(pres[t]) for t in pT]})
+
+    copy_gbps = copy_bandwidth(dev)
 
     head = results[args.tokens]
     alg = head["alg"]
@@ -485,13 +619,6 @@ def main():
                             "f32": "k_skinny_up"}[spec.expert_dtype] + ")",
                         avg_ms=up_ms, algorithmic_bytes=alg["up_bytes_decode"])
 
-    cpu = None
-    if not args.no_cpu_baseline:
-        cpu = cpu_baseline(spec, L_host, head_x_host, args.cpu_sample_tokens)
-
-    def brief(r):
-        return {k: (round(v, 5) if isinstance(v, float) else v) for k, v in r.items() if k != "alg"}
-
     line = {
         "metric": METRIC,
         "value": head["tokens_per_s"],
@@ -506,17 +633,19 @@ def main():
         "vs_baseline": None,
         "dtype": "bf16" if spec.act_dtype == "bf16" else "f32",
         "data": "synthetic",
-        "config": {"workload": f"{spec.name} MoE layer: hidden {spec.hidden}, {spec.num_experts} experts "
-                               f"top-{spec.top_k}, moe_intermediate {spec.moe_intermediate}, shared "
-                               f"{spec.shared_intermediate}, {spec.score_function}, n_group {spec.n_group}, "
-                               f"experts {spec.expert_dtype}; T={args.tokens}",
+        "config": {"workload": workload_name(spec) + f"; T={args.tokens}",
                    "tokens": args.tokens, "layer_gb": round(layer_bytes / 1e9, 4)},
         "roofline": roof,
         "cpu_baseline": cpu,
         "hbm_gbps": head["hbm_gbps"],
         "mfma_frac": head["mfma_frac"],
         "roofline_frac": head["roofline_frac"],
+        "step_ms_p10": head["step_ms_p10"],
+        "step_ms_p90": head["step_ms_p90"],
+        "parity": head.get("parity"),
+        "copy_gbps": copy_gbps,
         "per_T": [brief(results[T]) for T in Ts],
+        "per_config": per_config,
         "source_digest": digest,
         "gen_seconds": round(gen_s, 2),
     }
