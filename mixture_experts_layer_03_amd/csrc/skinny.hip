@@ -565,25 +565,33 @@ __global__ __launch_bounds__(256) void k_skinny_down(SkinnyDownArgs a) {
 // the NMAT matrices), and every line of a weight row is requested once.
 //
 // Ring layout per step: rows [0, 16 NMAT) weights (matrix m: rows 16m ..), rows
-// [16 NMAT, 16 NMAT + 16) tokens; 128-byte rows with 16-byte chunks XOR-swizzled by
+// [16 NMAT, 16 NMAT + TR) tokens; 128-byte rows with 16-byte chunks XOR-swizzled by
 // row % 8.  Lane l of a copy instruction covering rows [8h, 8h + 8) takes row 8h + l/8
-// and logical chunk (l % 8) ^ (l / 8).
-template <int NMAT>
+// and logical chunk (l % 8) ^ (l / 8).  TR = 8 or 16 token rows: a chunk of at most 8
+// live tokens copies 8 (MFMA rows 8..15 reread rows 0..7; their results are dropped),
+// and the LDS it leaves holds more K-steps in flight within the same per-wavefront
+// ring budget, so the same number of blocks fits on a CU.
+template <int NMAT, int TR = 16>
 struct RingGeom {
-  static constexpr int ROWS = 16 * NMAT + 16;
-  static constexpr int SLOT = ROWS * 64;      // bf16 elements per K-step
-  static constexpr int CPS = 2 * NMAT + 2;    // copy instructions per K-step
+  static constexpr int ROWS = 16 * NMAT + TR;
+  static constexpr int SLOT = ROWS * 64;         // bf16 elements per K-step
+  static constexpr int CPS = 2 * NMAT + TR / 8;  // copy instructions per K-step
 };
+// K-steps in a ring of RB bytes with slots of SLOT_BYTES (at most 8)
+constexpr int ring_depth(int rb, int slot_bytes) { return rb / slot_bytes < 8 ? rb / slot_bytes : 8; }
 
-// acc[m] += tokens x W_m^T over [k0, k1) (multiples of 64) with a U-step ring at `ring`.
+// acc[m] += tokens x W_m^T over [k0, k1) (multiples of 64) with a ring of RB bytes at
+// `ring` (as many K-steps as fit, at most 8) and TR token rows.
 // wbase[m]: wave-uniform byte address of weight row 0 of matrix m (rows H_row bytes
 // apart, the stride folded into woff); woff[h]: this lane's byte offset of its row in
 // copy h (row 8h + l/8) plus its chunk; abase / aoff[h]: the same for the token rows.
-template <int NMAT, int U>
+template <int NMAT, int RB, int TR>
 __device__ __forceinline__ void ring_stream(const char* const (&wbase)[NMAT], const uint32_t (&woff)[2],
                                             const char* abase, const uint32_t (&aoff)[2], int k0, int k1,
                                             uint16_t* ring, f32x4 (&acc)[NMAT]) {
-  using G = RingGeom<NMAT>;
+  using G = RingGeom<NMAT, TR>;
+  constexpr int U = ring_depth(RB, G::SLOT * 2);
+  static_assert(U >= 2 && G::CPS * (U - 1) < 64, "ring depth");
   const int lane = lane_id();
   const int n = (k1 - k0) >> 6;
   auto issue = [&](int slot, int step) {
@@ -594,7 +602,7 @@ __device__ __forceinline__ void ring_stream(const char* const (&wbase)[NMAT], co
 #pragma unroll
       for (int h = 0; h < 2; ++h) copy_to_lds(uniform_ptr(wbase[m] + kb), woff[h], sl + (16 * m + 8 * h) * 64);
 #pragma unroll
-    for (int h = 0; h < 2; ++h) copy_to_lds(uniform_ptr(abase + kb), aoff[h], sl + (16 * NMAT + 8 * h) * 64);
+    for (int h = 0; h < TR / 8; ++h) copy_to_lds(uniform_ptr(abase + kb), aoff[h], sl + (16 * NMAT + 8 * h) * 64);
   };
   const int r = lane & 15, q = lane >> 4;
   auto compute = [&](int slot) {
@@ -602,7 +610,7 @@ __device__ __forceinline__ void ring_stream(const char* const (&wbase)[NMAT], co
 #pragma unroll
     for (int ks = 0; ks < 2; ++ks) {
       const int cc = ((ks * 4 + q) ^ (r & 7)) << 3;
-      const uint4 a = *reinterpret_cast<const uint4*>(sl + (16 * NMAT + r) * 64 + cc);
+      const uint4 a = *reinterpret_cast<const uint4*>(sl + (16 * NMAT + (r & (TR - 1))) * 64 + cc);
 #pragma unroll
       for (int m = 0; m < NMAT; ++m) {
         const uint4 w = *reinterpret_cast<const uint4*>(sl + (16 * m + r) * 64 + cc);
@@ -633,14 +641,13 @@ __device__ __forceinline__ void ring_lane(int& row_in_copy, int& chunk) {
   chunk = (lane & 7) ^ (lane >> 3);
 }
 
-template <int U, int NWK>
+template <int RB, int NWK>
 __global__ __launch_bounds__(256) void k_stream_up(SkinnyUpArgs a) {
-  using G = RingGeom<2>;
   constexpr int IPB = 4 / NWK;
-  __shared__ __attribute__((aligned(16))) uint16_t rings[4 * U * G::SLOT];
+  __shared__ __attribute__((aligned(16))) uint16_t rings[4 * RB / 2];
   const int lane = lane_id(), w = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   const int n = lane & 15;
-  uint16_t* ring = rings + w * U * G::SLOT;
+  uint16_t* ring = rings + w * (RB / 2);
   const int NQ = a.part == 2 ? 0 : a.meta[1];  // chunks; shared-only launches read no routing
   const int CH = a.I / 16, CHs = a.Is / 16;
   const int TC = (a.T + 15) / 16;
@@ -704,7 +711,12 @@ __global__ __launch_bounds__(256) void k_stream_up(SkinnyUpArgs a) {
         aoff[h] = static_cast<uint32_t>(tok) * a.H * 2 + ch * 16;
       }
       f32x4 acc[2] = {f32x4{0.f, 0.f, 0.f, 0.f}, f32x4{0.f, 0.f, 0.f, 0.f}};
-      if (live) ring_stream<2, U>(wb, woff, xb, aoff, k0, k1, ring, acc);
+      if (live) {
+        if (ntok <= 8)
+          ring_stream<2, RB, 8>(wb, woff, xb, aoff, k0, k1, ring, acc);
+        else
+          ring_stream<2, RB, 16>(wb, woff, xb, aoff, k0, k1, ring, acc);
+      }
       if constexpr (NWK > 1) {
         // K-split: partial sums through the (now idle) rings; wavefront 0 adds them
         float* red = reinterpret_cast<float*>(rings);
@@ -740,14 +752,13 @@ __global__ __launch_bounds__(256) void k_stream_up(SkinnyUpArgs a) {
   }
 }
 
-template <int U, int NWK>
+template <int RB, int NWK>
 __global__ __launch_bounds__(256) void k_stream_down(SkinnyDownArgs a) {
-  using G = RingGeom<1>;
   constexpr int IPB = 4 / NWK;
-  __shared__ __attribute__((aligned(16))) uint16_t rings[4 * U * G::SLOT];
+  __shared__ __attribute__((aligned(16))) uint16_t rings[4 * RB / 2];
   const int lane = lane_id(), w = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   const int n = lane & 15;
-  uint16_t* ring = rings + w * U * G::SLOT;
+  uint16_t* ring = rings + w * (RB / 2);
   const int NQ = a.part == 2 ? 0 : a.meta[1];  // chunks; shared-only launches read no routing
   const int CH = a.H / 16;
   const int TC = (a.T + 15) / 16;
@@ -808,7 +819,12 @@ __global__ __launch_bounds__(256) void k_stream_down(SkinnyDownArgs a) {
         aoff[h] = static_cast<uint32_t>(row) * K * 2 + ch * 16;
       }
       f32x4 acc[1] = {f32x4{0.f, 0.f, 0.f, 0.f}};
-      if (live) ring_stream<1, U>(wb, woff, ab, aoff, k0, k1, ring, acc);
+      if (live) {
+        if (ntok <= 8)
+          ring_stream<1, RB, 8>(wb, woff, ab, aoff, k0, k1, ring, acc);
+        else
+          ring_stream<1, RB, 16>(wb, woff, ab, aoff, k0, k1, ring, acc);
+      }
       if constexpr (NWK > 1) {
         float* red = reinterpret_cast<float*>(rings);
         __syncthreads();
@@ -853,12 +869,12 @@ __global__ __launch_bounds__(256) void k_stream_down(SkinnyDownArgs a) {
 // two fp16 values (groups 2t, 2t + 1) of matrix l / 32, kind (l / 16) % 2 (scale,
 // zero), row l % 16.  Products per group are exact: codes minus the zero point are
 // integers in [-255, 255], exact in bf16; the group scale multiplies the fp32 result.
-template <int NMAT>
+template <int NMAT, int TR = 16>
 struct RingGeomU8 {
   static constexpr int W_BYTES = NMAT * 16 * 128;
-  static constexpr int A_BYTES = 2 * 16 * 128;
+  static constexpr int A_BYTES = 2 * TR * 128;  // two token images of TR rows (8 or 16)
   static constexpr int SLOT_BYTES = W_BYTES + A_BYTES + 256;
-  static constexpr int CPS = 2 * NMAT + 4 + 1;  // copy instructions per step
+  static constexpr int CPS = 2 * NMAT + 2 * (TR / 8) + 1;  // copy instructions per step
 };
 
 // codes: 8 u8 in (lo, hi) minus zero point -> 8 bf16
@@ -877,11 +893,13 @@ __device__ __forceinline__ uint4 codes_minus_zero(uint2 c, float z) {
 // wbase[m]: wave-uniform byte address of code row 0 of matrix m; woff[h]: lane offset of
 // its code row in copy h (row 8h + l/8, rows K bytes apart) plus its chunk.  sz_src: this
 // lane's group-parameter address for group 0 of the range (4 bytes, 2 groups).
-template <int NMAT, int U>
+template <int NMAT, int RB, int TR>
 __device__ __forceinline__ void ring_stream_u8(const char* const (&wbase)[NMAT], const uint32_t (&woff)[2],
                                                const char* abase, const uint32_t (&aoff)[2], const uint16_t* sz_src,
                                                int k0, int k1, char* ring, f32x4 (&acc)[NMAT]) {
-  using G = RingGeomU8<NMAT>;
+  using G = RingGeomU8<NMAT, TR>;
+  constexpr int U = ring_depth(RB, G::SLOT_BYTES);
+  static_assert(U >= 2 && G::CPS * (U - 1) < 64, "ring depth");
   const int lane = lane_id();
   const int n = (k1 - k0) >> 7;
   auto issue = [&](int slot, int step) {
@@ -895,9 +913,9 @@ __device__ __forceinline__ void ring_stream_u8(const char* const (&wbase)[NMAT],
 #pragma unroll
     for (int half = 0; half < 2; ++half)
 #pragma unroll
-      for (int h = 0; h < 2; ++h)
+      for (int h = 0; h < TR / 8; ++h)
         copy_to_lds(uniform_ptr(abase + (kc + 64 * half) * 2), aoff[h],
-                    reinterpret_cast<uint16_t*>(sl + G::W_BYTES + half * 2048 + 8 * h * 128));
+                    reinterpret_cast<uint16_t*>(sl + G::W_BYTES + half * TR * 128 + 8 * h * 128));
     copy4_to_lds(sz_src + (kc >> 6), sl + G::W_BYTES + G::A_BYTES);
   };
   const int r = lane & 15, q = lane >> 4;
@@ -918,7 +936,8 @@ __device__ __forceinline__ void ring_stream_u8(const char* const (&wbase)[NMAT],
 #pragma unroll
       for (int ks = 0; ks < 2; ++ks) {
         const int c = ks * 4 + q;  // logical 16-byte chunk of the 64-element token image
-        const uint4 av = *reinterpret_cast<const uint4*>(sl + G::W_BYTES + g * 2048 + r * 128 + ((c ^ (r & 7)) << 4));
+        const uint4 av =
+            *reinterpret_cast<const uint4*>(sl + G::W_BYTES + g * TR * 128 + (r & (TR - 1)) * 128 + ((c ^ (r & 7)) << 4));
         const int cw = 4 * g + (c >> 1);  // 16-byte chunk of the code row holding codes 8c .. of group g
 #pragma unroll
         for (int m = 0; m < NMAT; ++m) {
@@ -1115,16 +1134,14 @@ __device__ __forceinline__ const uint16_t* u8_param_row(const uint16_t* const (&
 }
 
 // quantised routed experts (BITS = 8: u8 ring, 4: u4 ring); shared items stream bf16
-template <int BITS, int U, int NWK>
+// RB: ring bytes per wavefront
+template <int BITS, int RB, int NWK>
 __global__ __launch_bounds__(256) void k_stream_up_q(SkinnyUpArgs a) {
-  constexpr int QSLOT = BITS == 8 ? RingGeomU8<2>::SLOT_BYTES : kU4MaxSlot;
-  using GB = RingGeom<2>;
-  constexpr int SLOTB = QSLOT > GB::SLOT * 2 ? QSLOT : GB::SLOT * 2;
   constexpr int IPB = 4 / NWK;
-  __shared__ __attribute__((aligned(16))) char rings[4 * U * SLOTB];
+  __shared__ __attribute__((aligned(16))) char rings[4 * RB];
   const int lane = lane_id(), w = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   const int n = lane & 15;
-  char* ring = rings + w * U * SLOTB;
+  char* ring = rings + w * RB;
   const int NQ = a.part == 2 ? 0 : a.meta[1];  // chunks; shared-only launches read no routing
   const int CH = a.I / 16, CHs = a.Is / 16;
   const int TC = (a.T + 15) / 16;
@@ -1193,7 +1210,10 @@ __global__ __launch_bounds__(256) void k_stream_up_q(SkinnyUpArgs a) {
                                  uniform_ptr(static_cast<const uint8_t*>(a.up) + ro * a.H)};
             const uint32_t woff[2] = {static_cast<uint32_t>(rr * a.H + ch * 16),
                                       static_cast<uint32_t>((8 + rr) * a.H + ch * 16)};
-            ring_stream_u8<2, U>(wb, woff, xb, aoff, szs, k0, k1, ring, acc);
+            if (ntok <= 8)
+              ring_stream_u8<2, RB, 8>(wb, woff, xb, aoff, szs, k0, k1, ring, acc);
+            else
+              ring_stream_u8<2, RB, 16>(wb, woff, xb, aoff, szs, k0, k1, ring, acc);
           } else {
             const char* wb[2] = {uniform_ptr(static_cast<const uint8_t*>(a.gate) + ro * (a.H / 2)),
                                  uniform_ptr(static_cast<const uint8_t*>(a.up) + ro * (a.H / 2))};
@@ -1203,7 +1223,7 @@ __global__ __launch_bounds__(256) void k_stream_up_q(SkinnyUpArgs a) {
               constexpr int TR = decltype(trc)::value;
               uint32_t ao[TR / 4];
               u4_token_offsets<TR>(ntok, [&](int j) { return static_cast<uint32_t>(prow[j] / a.k) * a.H * 2; }, ao);
-              ring_stream_u4<2, U * SLOTB, TR>(wb, woff, xb, ao, szs, k0, k1, ring, acc);
+              ring_stream_u4<2, RB, TR>(wb, woff, xb, ao, szs, k0, k1, ring, acc);
             });
           }
         } else {
@@ -1211,7 +1231,10 @@ __global__ __launch_bounds__(256) void k_stream_up_q(SkinnyUpArgs a) {
                                uniform_ptr(static_cast<const uint16_t*>(a.sup) + static_cast<int64_t>(row0) * a.H)};
           const uint32_t woff[2] = {static_cast<uint32_t>((rr * a.H + ch * 8) * 2),
                                     static_cast<uint32_t>(((8 + rr) * a.H + ch * 8) * 2)};
-          ring_stream<2, U>(wb, woff, xb, aoff, k0, k1, reinterpret_cast<uint16_t*>(ring), acc);
+          if (ntok <= 8)
+            ring_stream<2, RB, 8>(wb, woff, xb, aoff, k0, k1, reinterpret_cast<uint16_t*>(ring), acc);
+          else
+            ring_stream<2, RB, 16>(wb, woff, xb, aoff, k0, k1, reinterpret_cast<uint16_t*>(ring), acc);
         }
       }
       if constexpr (NWK > 1) {
@@ -1248,16 +1271,14 @@ __global__ __launch_bounds__(256) void k_stream_up_q(SkinnyUpArgs a) {
   }
 }
 
-template <int BITS, int U, int NWK>
+// RB: ring bytes per wavefront
+template <int BITS, int RB, int NWK>
 __global__ __launch_bounds__(256) void k_stream_down_q(SkinnyDownArgs a) {
-  constexpr int QSLOT = BITS == 8 ? RingGeomU8<1>::SLOT_BYTES : RingGeomU4<1, 16>::SLOT_BYTES;
-  using GB = RingGeom<1>;
-  constexpr int SLOTB = QSLOT > GB::SLOT * 2 ? QSLOT : GB::SLOT * 2;
   constexpr int IPB = 4 / NWK;
-  __shared__ __attribute__((aligned(16))) char rings[4 * U * SLOTB];
+  __shared__ __attribute__((aligned(16))) char rings[4 * RB];
   const int lane = lane_id(), w = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   const int n = lane & 15;
-  char* ring = rings + w * U * SLOTB;
+  char* ring = rings + w * RB;
   const int NQ = a.part == 2 ? 0 : a.meta[1];  // chunks; shared-only launches read no routing
   const int CH = a.H / 16;
   const int TC = (a.T + 15) / 16;
@@ -1326,7 +1347,10 @@ __global__ __launch_bounds__(256) void k_stream_down_q(SkinnyDownArgs a) {
             const char* wb[1] = {uniform_ptr(static_cast<const uint8_t*>(a.down) + ro * a.I)};
             const uint32_t woff[2] = {static_cast<uint32_t>(rr * a.I + ch * 16),
                                       static_cast<uint32_t>((8 + rr) * a.I + ch * 16)};
-            ring_stream_u8<1, U>(wb, woff, ab, aoff, szs, k0, k1, ring, acc);
+            if (ntok <= 8)
+              ring_stream_u8<1, RB, 8>(wb, woff, ab, aoff, szs, k0, k1, ring, acc);
+            else
+              ring_stream_u8<1, RB, 16>(wb, woff, ab, aoff, szs, k0, k1, ring, acc);
           } else {
             const char* wb[1] = {uniform_ptr(static_cast<const uint8_t*>(a.down) + ro * (a.I / 2))};
             const uint32_t woff = u4_code_off(a.I / 2);
@@ -1335,14 +1359,17 @@ __global__ __launch_bounds__(256) void k_stream_down_q(SkinnyDownArgs a) {
               constexpr int TR = decltype(trc)::value;
               uint32_t ao[TR / 4];
               u4_token_offsets<TR>(ntok, [&](int j) { return static_cast<uint32_t>(row0t + j) * a.I * 2; }, ao);
-              ring_stream_u4<1, U * SLOTB, TR>(wb, woff, ab, ao, szs, k0, k1, ring, acc);
+              ring_stream_u4<1, RB, TR>(wb, woff, ab, ao, szs, k0, k1, ring, acc);
             });
           }
         } else {
           const char* wb[1] = {uniform_ptr(static_cast<const uint16_t*>(a.sdown) + static_cast<int64_t>(row0) * a.Is)};
           const uint32_t woff[2] = {static_cast<uint32_t>((rr * K + ch * 8) * 2),
                                     static_cast<uint32_t>(((8 + rr) * K + ch * 8) * 2)};
-          ring_stream<1, U>(wb, woff, ab, aoff, k0, k1, reinterpret_cast<uint16_t*>(ring), acc);
+          if (ntok <= 8)
+            ring_stream<1, RB, 8>(wb, woff, ab, aoff, k0, k1, reinterpret_cast<uint16_t*>(ring), acc);
+          else
+            ring_stream<1, RB, 16>(wb, woff, ab, aoff, k0, k1, reinterpret_cast<uint16_t*>(ring), acc);
         }
       }
       if constexpr (NWK > 1) {
@@ -1448,18 +1475,22 @@ int grid_for(int64_t items, int ipb, int ncu) {
   return static_cast<int>(blocks);
 }
 
-// K-steps per LDS ring (per wavefront) of the bf16 streaming kernels
-constexpr int kUpRing = 3, kDownRing = 4;
-// u8 gate/up: a two-step ring (two blocks per CU) split over the four wavefronts
-// measured 3-6% faster than three steps unsplit on the Ling-3.0-flash shape at 1 to 64
-// tokens (graph replay at 64 tokens 338.5 -> 317 us)
-constexpr int kUpRingU8 = 2, kDownRingU8 = 3;
-// u4 down: two steps (measured 3-5% faster than three on the Ling-3.0-flash u4 shape
-// at 1 to 64 tokens, graph replay at 64 tokens 260.8 -> 248.4 us)
-constexpr int kUpRingU4 = 3, kDownRingU4 = 2;
-// the split u4 gate/up kernel: a two-slot budget (still 3-5 steps in flight with 4-8
-// token rows) lets three blocks share a CU (measured 5-7% faster at 8-64 tokens)
-constexpr int kUpRingSplitU4 = 2;
+// LDS ring bytes per wavefront of the streaming kernels (the K-steps a ring holds follow
+// from its slot size, which depends on the token rows a chunk copies: 8 or 16).
+// bf16 gate/up: 20 KB (three steps of 16 token rows, four of 8; 80 KB per block, two
+// blocks per CU); bf16 down: 16 KB (four steps of 16 token rows, five of 8).
+constexpr int kUpRingB = 20480, kDownRingB = 16384;
+// u8 gate/up: two blocks per CU split over the four wavefronts (measured 3-6% faster
+// than three steps unsplit on the Ling-3.0-flash shape at 1 to 64 tokens); 20 KB: two
+// steps of 16 token rows, three of 8.  u8 down: three steps of 16 token rows, four of 8.
+constexpr int kUpRingU8B = 20480, kDownRingU8B = 3 * RingGeomU8<1>::SLOT_BYTES;
+// u4 (ring depth per the token rows inside ring_stream_u4): gate/up three slots of the
+// largest u4 step, the split gate/up two (still 3-5 steps in flight with 4-8 token rows;
+// three blocks share a CU, measured 5-7% faster at 8-64 tokens), down two slots
+// (measured 3-5% faster than three at 1 to 64 tokens, graph replay at 64 tokens
+// 260.8 -> 248.4 us)
+constexpr int kUpRingU4B = 3 * kU4MaxSlot, kUpRingSplitU4B = 2 * kU4MaxSlot,
+              kDownRingU4B = 2 * RingGeomU4<1, 16>::SLOT_BYTES;
 
 // work items of a launch covering `part` (see SkinnyUpArgs::part)
 int64_t part_items(int part, int64_t routed, int64_t shared) {
@@ -1548,19 +1579,19 @@ hipError_t launch_skinny_up(const SkinnyUpArgs& a, Act act, WFmt wf, int ncu, hi
     // the only u4 kernel: the configuration checks guarantee its conditions
     if (act != Act::BF16 || a.H % 128 || !stream_ok(a.T, a.H, a.T, a.Is) || !aligned4({a.gate_s, a.gate_z, a.up_s, a.up_z}))
       return hipErrorInvalidValue;
-    return launch_ring<kUpRingU4>(k_stream_up_q<4, kUpRingU4, 1>, k_stream_up_q<4, kUpRingSplitU4, 4>, ring,
-                                  split_ring, ncu, s, a);
+    return launch_ring<0>(k_stream_up_q<4, kUpRingU4B, 1>, k_stream_up_q<4, kUpRingSplitU4B, 4>, ring, split_ring,
+                          ncu, s, a);
   }
   if (act == Act::F32)
     MOE_DISPATCH_MT_NWK(k_skinny_up, a, items, a.T, split_skinny, Act::F32, WFmt::F32);
   else if (wf == WFmt::U8 && a.H % 128 == 0 && stream_ok(a.T, a.H, 0, 0) &&
            aligned4({a.gate_s, a.gate_z, a.up_s, a.up_z}))
-    return launch_ring<kUpRingU8>(k_stream_up_q<8, kUpRingU8, 1>, k_stream_up_q<8, kUpRingU8, 4>, ring, split_ring,
-                                  ncu, s, a);
+    return launch_ring<0>(k_stream_up_q<8, kUpRingU8B, 1>, k_stream_up_q<8, kUpRingU8B, 4>, ring, split_ring, ncu,
+                          s, a);
   else if (wf == WFmt::U8)
     MOE_DISPATCH_MT_NWK(k_skinny_up, a, items, a.T, split_skinny, Act::BF16, WFmt::U8);
   else if (stream_ok(a.T, a.H, a.T * a.k, a.I))
-    return launch_ring<kUpRing>(k_stream_up<kUpRing, 1>, k_stream_up<kUpRing, 4>, ring, split_ring, ncu, s, a);
+    return launch_ring<0>(k_stream_up<kUpRingB, 1>, k_stream_up<kUpRingB, 4>, ring, split_ring, ncu, s, a);
   else
     MOE_DISPATCH_MT_NWK(k_skinny_up, a, items, a.T, split_skinny, Act::BF16, WFmt::BF16);
   return hipGetLastError();
@@ -1582,20 +1613,19 @@ hipError_t launch_skinny_down(const SkinnyDownArgs& a, Act act, WFmt wf, int ncu
   if (wf == WFmt::U4) {
     if (act != Act::BF16 || a.I % 128 || !stream_ok(a.T * a.k, a.I, a.T, a.Is) || !aligned4({a.down_s, a.down_z}))
       return hipErrorInvalidValue;
-    return launch_ring<kDownRingU4>(k_stream_down_q<4, kDownRingU4, 1>, k_stream_down_q<4, kDownRingU4, 4>, ring,
-                                    split_ring, ncu, s, a);
+    return launch_ring<0>(k_stream_down_q<4, kDownRingU4B, 1>, k_stream_down_q<4, kDownRingU4B, 4>, ring,
+                          split_ring, ncu, s, a);
   }
   if (act == Act::F32)
     MOE_DISPATCH_MT_NWK(k_skinny_down, a, items, a.T, split_skinny, Act::F32, WFmt::F32);
   else if (wf == WFmt::U8 && a.I % 128 == 0 && stream_ok(a.T * a.k, a.I, a.T, a.Is) &&
            aligned4({a.down_s, a.down_z}))
-    return launch_ring<kDownRingU8>(k_stream_down_q<8, kDownRingU8, 1>, k_stream_down_q<8, kDownRingU8, 4>, ring,
-                                    split_ring, ncu, s, a);
+    return launch_ring<0>(k_stream_down_q<8, kDownRingU8B, 1>, k_stream_down_q<8, kDownRingU8B, 4>, ring,
+                          split_ring, ncu, s, a);
   else if (wf == WFmt::U8)
     MOE_DISPATCH_MT_NWK(k_skinny_down, a, items, a.T, split_skinny, Act::BF16, WFmt::U8);
   else if (stream_ok(a.T * a.k, a.I, a.T, a.Is))
-    return launch_ring<kDownRing>(k_stream_down<kDownRing, 1>, k_stream_down<kDownRing, 4>, ring, split_ring, ncu, s,
-                                  a);
+    return launch_ring<0>(k_stream_down<kDownRingB, 1>, k_stream_down<kDownRingB, 4>, ring, split_ring, ncu, s, a);
   else
     MOE_DISPATCH_MT_NWK(k_skinny_down, a, items, a.T, split_skinny, Act::BF16, WFmt::BF16);
   return hipGetLastError();
