@@ -40,6 +40,11 @@ struct PermuteArgs {
   int32_t* meta;        // [4]: D, number of M-tiles, valid slots, number of BM2 chunks
   int32_t* counts_copy; // optional extra copy of counts (caller output) or null
   int32_t* hist;        // [ceil(nslots / kPermChunk)][E] per-block histograms (multi-block form)
+  int4* chunks;         // optional: per entry of `tiles` one record (expert, first position of
+                        // the entry, the expert's first position, the expert's count), so a
+                        // streaming work item finds all it needs in one 16-byte load
+  const float* w;       // [nslots] routing weights, with wpos: also store them by position
+  float* wpos;          // [nslots] or null: wpos[perm position] = w[slot]
 };
 constexpr int kPermChunk = 2048;   // slots per workgroup in the multi-block permutation
 constexpr int kPermSingleMax = 4096;  // up to this many slots one workgroup does everything
@@ -78,10 +83,12 @@ struct SkinnyUpArgs {
   const int32_t* active;
   const int32_t* meta;     // meta[0] active experts, meta[1] chunks in `tiles`
   const int32_t* tiles;    // chunks of kDecodeChunk positions: (expert, first position)
+  const int4* chunks;      // the same chunks as records (PermuteArgs::chunks; ring kernels)
   int mtiles;              // upper bound on the chunks (grid sizing)
   int T, H, I, Is, k, E;
   int part;                // items: 0 routed and shared, 1 routed only, 2 shared only (reads no routing)
   int dense;               // 1: the dense MLP (shared items only, its own split rule)
+  int shared_first;        // ring kernels: the shared expert's items before the routed ones
 };
 hipError_t launch_skinny_up(const SkinnyUpArgs& a, Act act, WFmt wf, int ncu, hipStream_t s);
 
@@ -102,9 +109,12 @@ struct SkinnyDownArgs {
   const int32_t* active;
   const int32_t* meta;
   const int32_t* tiles;    // as SkinnyUpArgs
+  const int4* chunks;      // as SkinnyUpArgs
+  const float* wpos;       // [T*k] routing weight by position (ring kernels)
   int mtiles;
   int T, H, I, Is, k, E;
   int part;                // as SkinnyUpArgs::part
+  int shared_first;        // as SkinnyUpArgs::shared_first
 };
 hipError_t launch_skinny_down(const SkinnyDownArgs& a, Act act, WFmt wf, int ncu, hipStream_t s);
 

@@ -24,9 +24,10 @@ constexpr float kNegInf = -__builtin_huge_valf();
 // Expert e lives in lane e / EPL, register e % EPL: each lane owns EPL consecutive
 // experts, so a row of logits is read with contiguous per-lane runs.
 // Routes token t with one wavefront (all 64 lanes active).
-// (lds_idx: optional copy of the token's k expert indices in LDS, at lds_idx[t * k + j])
+// (lds_idx, lds_w: optional copies of the token's k expert indices and weights in LDS,
+// at [t * k + j])
 template <int EPL>
-__device__ void route_token(const TopkArgs& a, int t, int* lds_idx = nullptr) {
+__device__ void route_token(const TopkArgs& a, int t, int* lds_idx = nullptr, float* lds_w = nullptr) {
   const int lane = lane_id();
   const int E = a.E;
 
@@ -221,6 +222,7 @@ __device__ void route_token(const TopkArgs& a, int t, int* lds_idx = nullptr) {
     a.idx[static_cast<int64_t>(t) * a.k + lane] = my_idx;
     a.w[static_cast<int64_t>(t) * a.k + lane] = my_w;
     if (lds_idx) lds_idx[t * a.k + lane] = my_idx;
+    if (lds_w) lds_w[t * a.k + lane] = my_w;
   }
 }
 
@@ -293,6 +295,7 @@ __device__ void scan_experts(const PermuteArgs& a, int c, bool write, int* off, 
       for (int q = 0; q < nt; ++q) {
         a.tiles[2 * (te + q)] = tid;
         a.tiles[2 * (te + q) + 1] = ce + q * a.BM;
+        if (a.chunks) a.chunks[te + q] = make_int4(tid, ce + q * a.BM, ce, c);
       }
       for (int q = 0; q < nt2; ++q) {
         a.tiles2[2 * (te2 + q)] = tid;
@@ -354,6 +357,7 @@ __device__ void scatter_slots(const PermuteArgs& a, int s0, int s1, const int* b
         const int pos = base[e[u]] + p[u];
         a.perm[pos] = s;
         a.slot_pos[s] = pos;
+        if (a.wpos) a.wpos[pos] = a.w[s];
       }
     }
   }
@@ -386,8 +390,9 @@ __global__ __launch_bounds__(kPermThreads) void k_route_permute(TopkArgs ta, Per
   __shared__ int wtot[4][16];
   __shared__ int total_s;
   __shared__ int s_idx[kFusedSlots];
+  __shared__ float s_w[kFusedSlots];
   const int tid = threadIdx.x;
-  for (int t = tid >> 6; t < ta.T; t += kPermThreads / 64) route_token<EPL>(ta, t, s_idx);
+  for (int t = tid >> 6; t < ta.T; t += kPermThreads / 64) route_token<EPL>(ta, t, s_idx, s_w);
   if (tid < a.E) cnt[tid] = 0;
   __syncthreads();
   int e = -1, rank = -1;
@@ -401,6 +406,7 @@ __global__ __launch_bounds__(kPermThreads) void k_route_permute(TopkArgs ta, Per
     const int pos = off[e] + rank;
     a.perm[pos] = tid;
     a.slot_pos[tid] = pos;
+    if (a.wpos) a.wpos[pos] = s_w[tid];
   } else if (tid < a.nslots) {
     a.slot_pos[tid] = -1;
   }

@@ -641,6 +641,106 @@ __device__ __forceinline__ void ring_lane(int& row_in_copy, int& chunk) {
   chunk = (lane & 7) ^ (lane >> 3);
 }
 
+// A work item of the ring kernels: CH routed items per chunk-list entry and n_shared
+// items of the shared expert (row block si / TC, token chunk si % TC: the chunks of one
+// row block are neighbours, they share its rows).  Expert e's entries are
+// q0 .. q0 + nc - 1 and its items CH * q0 .. CH * (q0 + nc) - 1, ordered by row block and
+// then chunk, so the items of one expert are contiguous (neighbouring row blocks stream
+// together) and a popular expert's chunks read the same rows side by side.  Any entry
+// of the expert names it and its q0, and the entry's 16-byte record carries the rest: a
+// routed item waits for one load (the record, beside the chunk count) before its weight
+// copies.
+// shared_first: the shared items come first; they read no routing and start streaming
+// at once (batches of one token chunk, where every item is short and the routing loads
+// are a visible part of it).  Otherwise the routed items come first and the uniform
+// shared items fill the last round (measured better once chunks are long).
+// `item` must be below n_shared + (chunk bound) * CH, which keeps the record load in
+// bounds; items past the live ones decode to an in-range routed item of offset 0 and
+// one token, with live = false.
+// slot[v] and routing weight wgt[v] of position p0 + m, m = 4 (lane / 16) + v (the
+// rows this lane stores), for m < ntok
+__device__ __forceinline__ void routed_slots(const int32_t* perm, const float* wpos, int p0, int ntok, int (&slot)[4],
+                                             float (&wgt)[4]) {
+  const int lane = lane_id();
+#pragma unroll
+  for (int v = 0; v < 4; ++v) {
+    const int m = 4 * (lane >> 4) + v;
+    slot[v] = m < ntok ? perm[p0 + m] : 0;
+    wgt[v] = m < ntok ? wpos[p0 + m] : 0.f;
+  }
+}
+
+// Byte offsets of the ring kernels' token-row copies (copy h: chunk row 8h + rr, padded
+// rows repeating the last live one) for rows [m0, m0 + ntok) of a shared chunk (tokens
+// themselves) or of routed positions off + m0 .. (their tokens through the
+// permutation; with one token, token 0).  Both permutation loads go out before either
+// is used.
+__device__ __forceinline__ void token_offsets(const SkinnyUpArgs& a, bool shared, int off, int m0, int ntok, int rr,
+                                              int ch, uint32_t (&aoff)[2]) {
+  int tok[2];
+  if (shared || a.T == 1) {
+#pragma unroll
+    for (int h = 0; h < 2; ++h) tok[h] = shared ? m0 + min(8 * h + rr, ntok - 1) : 0;
+  } else {
+    int pv[2];
+#pragma unroll
+    for (int h = 0; h < 2; ++h) pv[h] = a.perm[off + m0 + min(8 * h + rr, ntok - 1)];
+#pragma unroll
+    for (int h = 0; h < 2; ++h) tok[h] = pv[h] / a.k;
+  }
+#pragma unroll
+  for (int h = 0; h < 2; ++h) aoff[h] = static_cast<uint32_t>(tok[h]) * a.H * 2 + ch * 16;
+}
+
+struct RingItem {
+  bool live, shared;
+  int e, off, ntot, row0, tc;
+};
+
+__device__ __forceinline__ RingItem ring_item(int item, int n_shared, int TC, int CH, int T, const int32_t* meta,
+                                              const int4* chunks, bool shared_first) {
+  RingItem r{};
+  int it;  // routed item index
+  if (shared_first) {
+    if (item < n_shared) {
+      r.live = r.shared = true;
+      r.row0 = (item / TC) * 16;
+      r.tc = item % TC;
+      r.ntot = T;
+      return r;
+    }
+    it = item - n_shared;
+  } else {
+    const int nr = meta[1] * CH;
+    if (item >= nr) {
+      const int si = item - nr;
+      r.live = si < n_shared;
+      r.shared = true;
+      r.row0 = (min(si, n_shared - 1) / TC) * 16;
+      r.tc = min(si, n_shared - 1) % TC;
+      r.ntot = T;
+      if (r.live || n_shared > 0) return r;
+    }
+    it = min(item, nr > 0 ? nr - 1 : 0);
+  }
+  const int qa = it / CH;
+  int4 rec = chunks[qa];  // (expert, entry's first position, expert's first position, count)
+  int nq = meta[1];
+  // both loads are issued before this point, which needs them: one memory round trip
+  asm volatile("" : "+v"(rec.x), "+v"(rec.y), "+v"(rec.z), "+v"(rec.w), "+v"(nq));
+  r.live = qa < nq && (shared_first || item < nq * CH);
+  const int first = r.live ? rec.z : 0, count = r.live ? rec.w : 1;
+  const int q0 = r.live ? qa - (rec.y - rec.z) / kDecodeChunk : qa;
+  const int nc = (count + kDecodeChunk - 1) / kDecodeChunk;
+  const int local = it - q0 * CH;
+  const int c = local % nc;
+  r.e = r.live ? rec.x : 0;
+  r.row0 = (local / nc) * 16;
+  r.off = first + c * kDecodeChunk;
+  r.ntot = count - c * kDecodeChunk;
+  return r;
+}
+
 template <int RB, int NWK>
 __global__ __launch_bounds__(256) void k_stream_up(SkinnyUpArgs a) {
   constexpr int IPB = 4 / NWK;
@@ -648,48 +748,20 @@ __global__ __launch_bounds__(256) void k_stream_up(SkinnyUpArgs a) {
   const int lane = lane_id(), w = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   const int n = lane & 15;
   uint16_t* ring = rings + w * (RB / 2);
-  const int NQ = a.part == 2 ? 0 : a.meta[1];  // chunks; shared-only launches read no routing
   const int CH = a.I / 16, CHs = a.Is / 16;
   const int TC = (a.T + 15) / 16;
-  const int n_routed = NQ * CH;
-  const int nitems = n_routed + (a.part == 1 ? 0 : CHs * TC);
+  const int n_shared = a.part == 1 ? 0 : CHs * TC;
+  const int nbound = n_shared + (a.part == 2 ? 0 : a.mtiles * CH);  // routed: up to the chunk bound
   int rr, ch;
   ring_lane(rr, ch);
   const char* xb = uniform_ptr(a.x);
-  for (int base = blockIdx.x * IPB; base < nitems; base += gridDim.x * IPB) {
+  for (int base = blockIdx.x * IPB; base < nbound; base += gridDim.x * IPB) {
     const int item = base + w / NWK;
-    const bool live = item < nitems;
-    const int it = live ? item : 0;
-    const bool shared = it >= n_routed;
+    const RingItem itm = ring_item(min(item, nbound - 1), n_shared, TC, CH, a.T, a.meta, a.chunks, a.shared_first || a.part == 2);
+    const bool live = item < nbound && itm.live, shared = itm.shared;
+    const int e = itm.e, off = itm.off, ntot = itm.ntot, row0 = itm.row0, tc_begin = itm.tc, tc_end = itm.tc + 1;
     int k0 = 0, k1 = a.H;
     if (NWK > 1) unit_range(a.H, w % NWK, NWK, k0, k1);
-    int e = 0, off = 0, ntot, row0, tc_begin, tc_end;
-    if (!shared) {
-      // one chunk of at most 16 positions.  Expert e's chunks are chunk-list entries
-      // q0 .. q0 + nc - 1, and its items CH * q0 .. CH * (q0 + nc) - 1, ordered by row
-      // block and then chunk: the items of one expert are contiguous (neighbouring row
-      // blocks stream together) and a popular expert's chunks read the same rows side
-      // by side.  Any entry of the expert, such as it / CH, names it and its q0.
-      const int qa = it / CH;
-      e = a.tiles[2 * qa];
-      const int first = a.offsets[e];
-      const int q0 = qa - (a.tiles[2 * qa + 1] - first) / kDecodeChunk;
-      const int nc = (a.counts[e] + kDecodeChunk - 1) / kDecodeChunk;
-      const int local = it - q0 * CH;
-      const int c = local % nc;
-      row0 = (local / nc) * 16;
-      off = first + c * kDecodeChunk;
-      ntot = a.counts[e] - c * kDecodeChunk;
-      tc_begin = 0;
-      tc_end = 1;
-    } else {
-      // shared item: the chunks of one row block are neighbours (they share its rows)
-      const int si = it - n_routed;
-      row0 = (si / TC) * 16;
-      tc_begin = si % TC;
-      tc_end = tc_begin + 1;
-      ntot = a.T;
-    }
     const char* wb[2];
     if (!shared) {
       const int64_t ro = static_cast<int64_t>(e) * a.I + row0;
@@ -704,12 +776,7 @@ __global__ __launch_bounds__(256) void k_stream_up(SkinnyUpArgs a) {
     for (int tc = tc_begin; tc < tc_end; ++tc) {
       const int ntok = min(16, ntot - tc * 16);
       uint32_t aoff[2];
-#pragma unroll
-      for (int h = 0; h < 2; ++h) {
-        const int m = tc * 16 + min(8 * h + rr, ntok - 1);  // padded rows repeat the last token
-        const int tok = shared ? m : a.perm[off + m] / a.k;
-        aoff[h] = static_cast<uint32_t>(tok) * a.H * 2 + ch * 16;
-      }
+      token_offsets(a, shared, off, tc * 16, ntok, rr, ch, aoff);
       f32x4 acc[2] = {f32x4{0.f, 0.f, 0.f, 0.f}, f32x4{0.f, 0.f, 0.f, 0.f}};
       if (live) {
         if (ntok <= 8)
@@ -759,48 +826,20 @@ __global__ __launch_bounds__(256) void k_stream_down(SkinnyDownArgs a) {
   const int lane = lane_id(), w = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   const int n = lane & 15;
   uint16_t* ring = rings + w * (RB / 2);
-  const int NQ = a.part == 2 ? 0 : a.meta[1];  // chunks; shared-only launches read no routing
   const int CH = a.H / 16;
   const int TC = (a.T + 15) / 16;
-  const int n_routed = NQ * CH;
-  const int nitems = n_routed + (a.Is > 0 && a.part != 1 ? CH * TC : 0);
+  const int n_shared = a.Is > 0 && a.part != 1 ? CH * TC : 0;
+  const int nbound = n_shared + (a.part == 2 ? 0 : a.mtiles * CH);  // routed: up to the chunk bound
   int rr, ch;
   ring_lane(rr, ch);
-  for (int base = blockIdx.x * IPB; base < nitems; base += gridDim.x * IPB) {
+  for (int base = blockIdx.x * IPB; base < nbound; base += gridDim.x * IPB) {
     const int item = base + w / NWK;
-    const bool live = item < nitems;
-    const int it = live ? item : 0;
-    const bool shared = it >= n_routed;
+    const RingItem itm = ring_item(min(item, nbound - 1), n_shared, TC, CH, a.T, a.meta, a.chunks, a.shared_first || a.part == 2);
+    const bool live = item < nbound && itm.live, shared = itm.shared;
+    const int e = itm.e, off = itm.off, ntot = itm.ntot, row0 = itm.row0, tc_begin = itm.tc, tc_end = itm.tc + 1;
     const int K = shared ? a.Is : a.I;
     int k0 = 0, k1 = K;
     if (NWK > 1) unit_range(K, w % NWK, NWK, k0, k1);
-    int e = 0, off = 0, ntot, row0, tc_begin, tc_end;
-    if (!shared) {
-      // one chunk of at most 16 positions.  Expert e's chunks are chunk-list entries
-      // q0 .. q0 + nc - 1, and its items CH * q0 .. CH * (q0 + nc) - 1, ordered by row
-      // block and then chunk: the items of one expert are contiguous (neighbouring row
-      // blocks stream together) and a popular expert's chunks read the same rows side
-      // by side.  Any entry of the expert, such as it / CH, names it and its q0.
-      const int qa = it / CH;
-      e = a.tiles[2 * qa];
-      const int first = a.offsets[e];
-      const int q0 = qa - (a.tiles[2 * qa + 1] - first) / kDecodeChunk;
-      const int nc = (a.counts[e] + kDecodeChunk - 1) / kDecodeChunk;
-      const int local = it - q0 * CH;
-      const int c = local % nc;
-      row0 = (local / nc) * 16;
-      off = first + c * kDecodeChunk;
-      ntot = a.counts[e] - c * kDecodeChunk;
-      tc_begin = 0;
-      tc_end = 1;
-    } else {
-      // shared item: the chunks of one row block are neighbours (they share its rows)
-      const int si = it - n_routed;
-      row0 = (si / TC) * 16;
-      tc_begin = si % TC;
-      tc_end = tc_begin + 1;
-      ntot = a.T;
-    }
     const char* wb[1];
     if (!shared)
       wb[0] = uniform_ptr(static_cast<const uint16_t*>(a.down) + (static_cast<int64_t>(e) * a.H + row0) * a.I);
@@ -818,6 +857,11 @@ __global__ __launch_bounds__(256) void k_stream_down(SkinnyDownArgs a) {
         const int row = shared ? m : off + m;
         aoff[h] = static_cast<uint32_t>(row) * K * 2 + ch * 16;
       }
+      // the output slots and routing weights of this lane's rows, loaded before the
+      // stream so that the store at its end waits for nothing
+      int slot[4];
+      float wgt[4];
+      if (!shared) routed_slots(a.perm, a.wpos, off + tc * 16, ntok, slot, wgt);
       f32x4 acc[1] = {f32x4{0.f, 0.f, 0.f, 0.f}};
       if (live) {
         if (ntok <= 8)
@@ -844,9 +888,8 @@ __global__ __launch_bounds__(256) void k_stream_down(SkinnyDownArgs a) {
           const int m = 4 * (lane >> 4) + v;
           if (m < ntok) {
             if (!shared) {
-              const int slot = a.perm[off + tc * 16 + m];
-              const float val = a.topk_w[slot] * acc[0][v];
-              const int64_t o = static_cast<int64_t>(slot) * a.H + row0 + n;
+              const float val = wgt[v] * acc[0][v];
+              const int64_t o = static_cast<int64_t>(slot[v]) * a.H + row0 + n;
               if (a.r_bf16)
                 static_cast<uint16_t*>(a.r)[o] = f32_to_bf16(val);
               else
@@ -1142,19 +1185,18 @@ __global__ __launch_bounds__(256) void k_stream_up_q(SkinnyUpArgs a) {
   const int lane = lane_id(), w = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   const int n = lane & 15;
   char* ring = rings + w * RB;
-  const int NQ = a.part == 2 ? 0 : a.meta[1];  // chunks; shared-only launches read no routing
   const int CH = a.I / 16, CHs = a.Is / 16;
   const int TC = (a.T + 15) / 16;
-  const int n_routed = NQ * CH;
-  const int nitems = n_routed + (a.part == 1 ? 0 : CHs * TC);
+  const int n_shared = a.part == 1 ? 0 : CHs * TC;
+  const int nbound = n_shared + (a.part == 2 ? 0 : a.mtiles * CH);  // routed: up to the chunk bound
   int rr, ch;
   ring_lane(rr, ch);
   const char* xb = uniform_ptr(a.x);
-  for (int base = blockIdx.x * IPB; base < nitems; base += gridDim.x * IPB) {
+  for (int base = blockIdx.x * IPB; base < nbound; base += gridDim.x * IPB) {
     const int item = base + w / NWK;
-    const bool live = item < nitems;
-    const int it = live ? item : 0;
-    const bool shared = it >= n_routed;
+    const RingItem itm = ring_item(min(item, nbound - 1), n_shared, TC, CH, a.T, a.meta, a.chunks, a.shared_first || a.part == 2);
+    const bool live = item < nbound && itm.live, shared = itm.shared;
+    const int e = itm.e, off = itm.off, ntot = itm.ntot, row0 = itm.row0, tc_begin = itm.tc, tc_end = itm.tc + 1;
     int k0 = 0, k1 = a.H;
     if (NWK > 1) {
       if (shared)
@@ -1162,43 +1204,11 @@ __global__ __launch_bounds__(256) void k_stream_up_q(SkinnyUpArgs a) {
       else
         unit_range128(a.H, w % NWK, NWK, k0, k1);
     }
-    int e = 0, off = 0, ntot, row0, tc_begin, tc_end;
-    if (!shared) {
-      // one chunk of at most 16 positions.  Expert e's chunks are chunk-list entries
-      // q0 .. q0 + nc - 1, and its items CH * q0 .. CH * (q0 + nc) - 1, ordered by row
-      // block and then chunk: the items of one expert are contiguous (neighbouring row
-      // blocks stream together) and a popular expert's chunks read the same rows side
-      // by side.  Any entry of the expert, such as it / CH, names it and its q0.
-      const int qa = it / CH;
-      e = a.tiles[2 * qa];
-      const int first = a.offsets[e];
-      const int q0 = qa - (a.tiles[2 * qa + 1] - first) / kDecodeChunk;
-      const int nc = (a.counts[e] + kDecodeChunk - 1) / kDecodeChunk;
-      const int local = it - q0 * CH;
-      const int c = local % nc;
-      row0 = (local / nc) * 16;
-      off = first + c * kDecodeChunk;
-      ntot = a.counts[e] - c * kDecodeChunk;
-      tc_begin = 0;
-      tc_end = 1;
-    } else {
-      // shared item: the chunks of one row block are neighbours (they share its rows)
-      const int si = it - n_routed;
-      row0 = (si / TC) * 16;
-      tc_begin = si % TC;
-      tc_end = tc_begin + 1;
-      ntot = a.T;
-    }
     const int64_t ro = static_cast<int64_t>(e) * a.I + row0;
     for (int tc = tc_begin; tc < tc_end; ++tc) {
       const int ntok = min(16, ntot - tc * 16);
       uint32_t aoff[2];
-#pragma unroll
-      for (int h = 0; h < 2; ++h) {
-        const int m = tc * 16 + min(8 * h + rr, ntok - 1);
-        const int tok = shared ? m : a.perm[off + m] / a.k;
-        aoff[h] = static_cast<uint32_t>(tok) * a.H * 2 + ch * 16;
-      }
+      token_offsets(a, shared, off, tc * 16, ntok, rr, ch, aoff);
       f32x4 acc[2] = {f32x4{0.f, 0.f, 0.f, 0.f}, f32x4{0.f, 0.f, 0.f, 0.f}};
       if (live) {
         if (!shared) {
@@ -1222,7 +1232,7 @@ __global__ __launch_bounds__(256) void k_stream_up_q(SkinnyUpArgs a) {
             with_token_rows(ntok, [&](auto trc) {
               constexpr int TR = decltype(trc)::value;
               uint32_t ao[TR / 4];
-              u4_token_offsets<TR>(ntok, [&](int j) { return static_cast<uint32_t>(prow[j] / a.k) * a.H * 2; }, ao);
+              u4_token_offsets<TR>(ntok, [&](int j) { return a.T == 1 ? 0u : static_cast<uint32_t>(prow[j] / a.k) * a.H * 2; }, ao);
               ring_stream_u4<2, RB, TR>(wb, woff, xb, ao, szs, k0, k1, ring, acc);
             });
           }
@@ -1279,18 +1289,17 @@ __global__ __launch_bounds__(256) void k_stream_down_q(SkinnyDownArgs a) {
   const int lane = lane_id(), w = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   const int n = lane & 15;
   char* ring = rings + w * RB;
-  const int NQ = a.part == 2 ? 0 : a.meta[1];  // chunks; shared-only launches read no routing
   const int CH = a.H / 16;
   const int TC = (a.T + 15) / 16;
-  const int n_routed = NQ * CH;
-  const int nitems = n_routed + (a.Is > 0 && a.part != 1 ? CH * TC : 0);
+  const int n_shared = a.Is > 0 && a.part != 1 ? CH * TC : 0;
+  const int nbound = n_shared + (a.part == 2 ? 0 : a.mtiles * CH);  // routed: up to the chunk bound
   int rr, ch;
   ring_lane(rr, ch);
-  for (int base = blockIdx.x * IPB; base < nitems; base += gridDim.x * IPB) {
+  for (int base = blockIdx.x * IPB; base < nbound; base += gridDim.x * IPB) {
     const int item = base + w / NWK;
-    const bool live = item < nitems;
-    const int it = live ? item : 0;
-    const bool shared = it >= n_routed;
+    const RingItem itm = ring_item(min(item, nbound - 1), n_shared, TC, CH, a.T, a.meta, a.chunks, a.shared_first || a.part == 2);
+    const bool live = item < nbound && itm.live, shared = itm.shared;
+    const int e = itm.e, off = itm.off, ntot = itm.ntot, row0 = itm.row0, tc_begin = itm.tc, tc_end = itm.tc + 1;
     const int K = shared ? a.Is : a.I;
     int k0 = 0, k1 = K;
     if (NWK > 1) {
@@ -1298,33 +1307,6 @@ __global__ __launch_bounds__(256) void k_stream_down_q(SkinnyDownArgs a) {
         unit_range(K, w % NWK, NWK, k0, k1);
       else
         unit_range128(K, w % NWK, NWK, k0, k1);
-    }
-    int e = 0, off = 0, ntot, row0, tc_begin, tc_end;
-    if (!shared) {
-      // one chunk of at most 16 positions.  Expert e's chunks are chunk-list entries
-      // q0 .. q0 + nc - 1, and its items CH * q0 .. CH * (q0 + nc) - 1, ordered by row
-      // block and then chunk: the items of one expert are contiguous (neighbouring row
-      // blocks stream together) and a popular expert's chunks read the same rows side
-      // by side.  Any entry of the expert, such as it / CH, names it and its q0.
-      const int qa = it / CH;
-      e = a.tiles[2 * qa];
-      const int first = a.offsets[e];
-      const int q0 = qa - (a.tiles[2 * qa + 1] - first) / kDecodeChunk;
-      const int nc = (a.counts[e] + kDecodeChunk - 1) / kDecodeChunk;
-      const int local = it - q0 * CH;
-      const int c = local % nc;
-      row0 = (local / nc) * 16;
-      off = first + c * kDecodeChunk;
-      ntot = a.counts[e] - c * kDecodeChunk;
-      tc_begin = 0;
-      tc_end = 1;
-    } else {
-      // shared item: the chunks of one row block are neighbours (they share its rows)
-      const int si = it - n_routed;
-      row0 = (si / TC) * 16;
-      tc_begin = si % TC;
-      tc_end = tc_begin + 1;
-      ntot = a.T;
     }
     const char* ab = uniform_ptr(shared ? a.hs : a.hm);
     const int64_t ro = static_cast<int64_t>(e) * a.H + row0;
@@ -1337,6 +1319,9 @@ __global__ __launch_bounds__(256) void k_stream_down_q(SkinnyDownArgs a) {
         const int row = shared ? m : off + m;
         aoff[h] = static_cast<uint32_t>(row) * K * 2 + ch * 16;
       }
+      int slot[4];
+      float wgt[4];
+      if (!shared) routed_slots(a.perm, a.wpos, off + tc * 16, ntok, slot, wgt);
       f32x4 acc[1] = {f32x4{0.f, 0.f, 0.f, 0.f}};
       if (live) {
         if (!shared) {
@@ -1391,9 +1376,8 @@ __global__ __launch_bounds__(256) void k_stream_down_q(SkinnyDownArgs a) {
           const int m = 4 * (lane >> 4) + v;
           if (m < ntok) {
             if (!shared) {
-              const int slot = a.perm[off + tc * 16 + m];
-              const float val = a.topk_w[slot] * acc[0][v];
-              const int64_t o = static_cast<int64_t>(slot) * a.H + row0 + n;
+              const float val = wgt[v] * acc[0][v];
+              const int64_t o = static_cast<int64_t>(slot[v]) * a.H + row0 + n;
               if (a.r_bf16)
                 static_cast<uint16_t*>(a.r)[o] = f32_to_bf16(val);
               else
@@ -1558,6 +1542,8 @@ hipError_t launch_skinny_router(const SkinnyRouterArgs& a, Act act, int ncu, hip
 // expert runs as a separate launch (a graph branch) do the same arithmetic.
 hipError_t launch_skinny_up(const SkinnyUpArgs& a, Act act, WFmt wf, int ncu, hipStream_t s) {
   if (a.T <= 0) return hipSuccess;
+  // routed items read the chunk records, the chunk count and the permutation
+  if (a.part != 2 && (!a.chunks || !a.meta || !a.perm)) return hipErrorInvalidValue;
   const int64_t slots = static_cast<int64_t>(a.T) * a.k;
   const int64_t dmax = slots < a.E ? slots : a.E;
   const int tch = 16 * pick_mt(a.T);
@@ -1599,6 +1585,8 @@ hipError_t launch_skinny_up(const SkinnyUpArgs& a, Act act, WFmt wf, int ncu, hi
 
 hipError_t launch_skinny_down(const SkinnyDownArgs& a, Act act, WFmt wf, int ncu, hipStream_t s) {
   if (a.T <= 0) return hipSuccess;
+  // routed items also store through the permutation with the weights by position
+  if (a.part != 2 && (!a.chunks || !a.meta || !a.perm || !a.wpos)) return hipErrorInvalidValue;
   const int64_t slots = static_cast<int64_t>(a.T) * a.k;
   const int64_t dmax = slots < a.E ? slots : a.E;
   const int tch = 16 * pick_mt(a.T);
