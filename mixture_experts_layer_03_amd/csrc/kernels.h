@@ -89,8 +89,18 @@ struct SkinnyUpArgs {
   int part;                // items: 0 routed and shared, 1 routed only, 2 shared only (reads no routing)
   int dense;               // 1: the dense MLP (shared items only, its own split rule)
   int shared_first;        // ring kernels: the shared expert's items before the routed ones
+  // One token (T = 1), ring kernels, every item in the first round of blocks: each block
+  // routes the token itself from the router's partial logits (ta) instead of reading
+  // a permutation, and block 0 also stores the routing and permutation tables (ta.idx,
+  // ta.w and everything pa names) for the stages after it.
+  int fused_route;
+  TopkArgs ta;
+  PermuteArgs pa;
 };
 hipError_t launch_skinny_up(const SkinnyUpArgs& a, Act act, WFmt wf, int ncu, hipStream_t s);
+// whether a gate/up launch with these arguments (fused_route aside) can route its one
+// token itself: one token, the whole layer, a ring kernel, every item in one round
+bool skinny_up_can_route(const SkinnyUpArgs& a, Act act, WFmt wf, int ncu);
 
 struct SkinnyDownArgs {
   const void* hm;          // [T*k, I] position order

@@ -429,9 +429,13 @@ moe_status run_permute(const moe_config& c, const Plan& p, int64_t T, const int3
 // shared_join: the shared expert's first stages (decode: gate/up and down; prefill:
 // gate/up) were launched on another stream that records this event when done; the
 // routed stages here skip them and the stream waits for the event before using them.
+// route_ta / route_pa (decode, small batches): the routing and permutation are still to
+// be done, in one workgroup launch, or for one token inside the gate/up launch when
+// skinny_up_can_route allows it (no launch of its own).
 moe_status run_experts(const moe_config& c, const Plan& p, int64_t T, const void* x, const moe_weights* w,
                        const int32_t* idx, const float* topk_w, void* y, void* ws, hipStream_t s,
-                       bool permuted = false, hipEvent_t shared_join = nullptr) {
+                       bool permuted = false, hipEvent_t shared_join = nullptr, const TopkArgs* route_ta = nullptr,
+                       const PermuteArgs* route_pa = nullptr) {
   const Act act = c.act_dtype == MOE_DT_F32 ? Act::F32 : Act::BF16;
   const WFmt wf = expert_fmt(c, act);
   const int Ti = static_cast<int>(T), H = static_cast<int>(c.hidden), I = static_cast<int>(c.moe_intermediate),
@@ -451,6 +455,8 @@ moe_status run_experts(const moe_config& c, const Plan& p, int64_t T, const void
     if (st != MOE_OK) return st;
   }
   const int ncu = device_cus();
+  if (route_ta && !p.decode)
+    MOE_LAUNCH_STAGE(MOE_STAGE_TOPK, s, launch_route_permute(*route_ta, *route_pa, s), "top-k + permutation");
   if (p.decode) {
     SkinnyUpArgs u{};
     u.x = x;
@@ -480,6 +486,15 @@ moe_status run_experts(const moe_config& c, const Plan& p, int64_t T, const void
     u.E = E;
     u.part = shared_join ? 1 : 0;
     u.shared_first = T <= kSharedFirstMaxT;
+    if (route_ta) {
+      if (skinny_up_can_route(u, act, wf, ncu)) {
+        u.fused_route = 1;
+        u.ta = *route_ta;
+        u.pa = *route_pa;
+      } else {
+        MOE_LAUNCH_STAGE(MOE_STAGE_TOPK, s, launch_route_permute(*route_ta, *route_pa, s), "top-k + permutation");
+      }
+    }
     MOE_LAUNCH_STAGE(MOE_STAGE_UP, s, launch_skinny_up(u, act, wf, ncu, s), "expert gate/up (streaming)");
     SkinnyDownArgs d{};
     d.hm = hm;
@@ -880,8 +895,7 @@ moe_status run_forward(const moe_config& c, const Plan& p, int64_t T, const void
     const TopkArgs ta = topk_args(*cfg, p, T, ws, w->router_bias, ebias, idx, wt);
     const PermuteArgs pa = permute_args(*cfg, p, T, idx, wt, at<int32_t>(ws, p.o_counts), at<int32_t>(ws, p.o_offsets),
                                           at<int32_t>(ws, p.o_perm), nullptr, ws);
-    MOE_LAUNCH_STAGE(MOE_STAGE_TOPK, st, launch_route_permute(ta, pa, st), "top-k + permutation");
-    s = run_experts(*cfg, p, T, x, w, idx, wt, y, ws, st, true, join);
+    s = run_experts(*cfg, p, T, x, w, idx, wt, y, ws, st, true, join, &ta, &pa);
   } else {
     s = run_route(*cfg, p, T, x, w->router, w->router_bias, ebias, idx, wt, ws, st);
     if (s != MOE_OK) return s;

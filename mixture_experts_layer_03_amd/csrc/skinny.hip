@@ -16,6 +16,7 @@
 
 #include "common.h"
 #include "kernels.h"
+#include "route_token.h"
 
 namespace moe {
 
@@ -741,7 +742,93 @@ __device__ __forceinline__ RingItem ring_item(int item, int n_shared, int TC, in
   return r;
 }
 
-template <int RB, int NWK>
+// One-token routing inside a gate/up launch (SkinnyUpArgs::fused_route).  Wave 0 routes
+// the token (route_token) and ranks its k picks, which are distinct experts, by expert
+// index: position p holds the p-th smallest valid pick, one chunk each, which is what
+// the permutation kernels build for a single token.  Block 0 stores the routing (ta.idx,
+// ta.w) and every table pa names; every block reads back the expert of its own item.
+// Called by all threads of the block before any ring is in use (the scratch lies in
+// the rings' LDS); returns the item as ring_item would for the shared-first order.
+// EPL: experts per lane of route_token (a template argument of the one-token kernels
+// only, so the other launches keep their registers).
+template <int EPL>
+__device__ RingItem one_token_item(const SkinnyUpArgs& a, char* scratch, int item, int n_shared, int CH) {
+  int* s_slot_e = reinterpret_cast<int*>(scratch);           // [k] expert of slot j
+  float* s_w = reinterpret_cast<float*>(s_slot_e + kMaxTopK);  // [k] weight of slot j
+  int* s_pos_e = reinterpret_cast<int*>(s_w + kMaxTopK);       // [k] expert at position p
+  int* s_kv = s_pos_e + kMaxTopK;                              // valid picks
+  const bool publish = blockIdx.x == 0;
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int k = a.ta.k, E = a.ta.E;
+  const PermuteArgs& pa = a.pa;
+  if (tid < 64) {
+    route_token<EPL>(a.ta, 0, s_slot_e, s_w, publish);
+    const int e = lane < k ? s_slot_e[lane] : -1;
+    const bool valid = lane < k && e >= 0 && e < E;
+    int rank = 0;
+    for (int i = 0; i < k; ++i) {
+      const int ei = s_slot_e[i];
+      rank += (ei >= 0 && ei < E && ei < e) ? 1 : 0;
+    }
+    const int kv = __popcll(__ballot(valid));
+    if (valid) s_pos_e[rank] = e;
+    if (lane == 0) *s_kv = kv;
+    if (publish && lane < k) {
+      if (valid) {
+        pa.perm[rank] = lane;
+        pa.slot_pos[lane] = rank;
+        pa.wpos[rank] = s_w[lane];
+        pa.chunks[rank] = make_int4(e, rank, rank, 1);
+        pa.tiles[2 * rank] = e;
+        pa.tiles[2 * rank + 1] = rank;
+        pa.active[rank] = e;
+      } else {
+        pa.slot_pos[lane] = -1;
+      }
+      if (lane >= kv) pa.perm[lane] = -1;
+    }
+    if (publish && lane == 0) {
+      pa.meta[0] = kv;  // active experts
+      pa.meta[1] = kv;  // chunks
+      pa.meta[2] = kv;  // valid slots
+      pa.meta[3] = 0;
+      pa.offsets[E] = kv;
+    }
+  }
+  __syncthreads();
+  const int kv = *s_kv;
+  if (publish) {
+    for (int e = tid; e < E; e += blockDim.x) {
+      int c = 0, before = 0;
+      for (int p = 0; p < kv; ++p) {
+        const int pe = s_pos_e[p];
+        c += pe == e ? 1 : 0;
+        before += pe < e ? 1 : 0;
+      }
+      pa.counts[e] = c;
+      pa.offsets[e] = before;
+      if (pa.counts_copy) pa.counts_copy[e] = c;
+    }
+  }
+  RingItem r{};
+  if (item < n_shared) {
+    r.live = r.shared = true;
+    r.row0 = item * 16;  // one token: one chunk per row block
+    r.ntot = 1;
+  } else {
+    const int it = item - n_shared, qa = it / CH;
+    r.live = qa < kv;
+    r.e = r.live ? s_pos_e[qa] : 0;
+    r.row0 = (it - qa * CH) * 16;
+    r.off = r.live ? qa : 0;
+    r.ntot = 1;
+  }
+  __syncthreads();  // every wave has read the scratch before a ring overwrites it
+  return r;
+}
+
+// FEPL > 0: the one-token launch that routes its token itself (route_token<FEPL>)
+template <int RB, int NWK, int FEPL = 0>
 __global__ __launch_bounds__(256) void k_stream_up(SkinnyUpArgs a) {
   constexpr int IPB = 4 / NWK;
   __shared__ __attribute__((aligned(16))) uint16_t rings[4 * RB / 2];
@@ -755,9 +842,16 @@ __global__ __launch_bounds__(256) void k_stream_up(SkinnyUpArgs a) {
   int rr, ch;
   ring_lane(rr, ch);
   const char* xb = uniform_ptr(a.x);
+  // one token: this block routes it itself (the launch covers every item in one round)
+  RingItem pre{};
+  if constexpr (FEPL > 0)
+    pre = one_token_item<FEPL>(a, reinterpret_cast<char*>(rings),
+                               min(static_cast<int>(blockIdx.x) * IPB + w / NWK, nbound - 1), n_shared, CH);
   for (int base = blockIdx.x * IPB; base < nbound; base += gridDim.x * IPB) {
     const int item = base + w / NWK;
-    const RingItem itm = ring_item(min(item, nbound - 1), n_shared, TC, CH, a.T, a.meta, a.chunks, a.shared_first || a.part == 2);
+    const RingItem itm = FEPL > 0 ? pre
+                                  : ring_item(min(item, nbound - 1), n_shared, TC, CH, a.T, a.meta, a.chunks,
+                                              a.shared_first || a.part == 2);
     const bool live = item < nbound && itm.live, shared = itm.shared;
     const int e = itm.e, off = itm.off, ntot = itm.ntot, row0 = itm.row0, tc_begin = itm.tc, tc_end = itm.tc + 1;
     int k0 = 0, k1 = a.H;
@@ -1178,7 +1272,8 @@ __device__ __forceinline__ const uint16_t* u8_param_row(const uint16_t* const (&
 
 // quantised routed experts (BITS = 8: u8 ring, 4: u4 ring); shared items stream bf16
 // RB: ring bytes per wavefront
-template <int BITS, int RB, int NWK>
+// FEPL > 0: the one-token launch that routes its token itself (route_token<FEPL>)
+template <int BITS, int RB, int NWK, int FEPL = 0>
 __global__ __launch_bounds__(256) void k_stream_up_q(SkinnyUpArgs a) {
   constexpr int IPB = 4 / NWK;
   __shared__ __attribute__((aligned(16))) char rings[4 * RB];
@@ -1192,9 +1287,16 @@ __global__ __launch_bounds__(256) void k_stream_up_q(SkinnyUpArgs a) {
   int rr, ch;
   ring_lane(rr, ch);
   const char* xb = uniform_ptr(a.x);
+  // one token: this block routes it itself (the launch covers every item in one round)
+  RingItem pre{};
+  if constexpr (FEPL > 0)
+    pre = one_token_item<FEPL>(a, reinterpret_cast<char*>(rings),
+                               min(static_cast<int>(blockIdx.x) * IPB + w / NWK, nbound - 1), n_shared, CH);
   for (int base = blockIdx.x * IPB; base < nbound; base += gridDim.x * IPB) {
     const int item = base + w / NWK;
-    const RingItem itm = ring_item(min(item, nbound - 1), n_shared, TC, CH, a.T, a.meta, a.chunks, a.shared_first || a.part == 2);
+    const RingItem itm = FEPL > 0 ? pre
+                                  : ring_item(min(item, nbound - 1), n_shared, TC, CH, a.T, a.meta, a.chunks,
+                                              a.shared_first || a.part == 2);
     const bool live = item < nbound && itm.live, shared = itm.shared;
     const int e = itm.e, off = itm.off, ntot = itm.ntot, row0 = itm.row0, tc_begin = itm.tc, tc_end = itm.tc + 1;
     int k0 = 0, k1 = a.H;
@@ -1540,10 +1642,55 @@ hipError_t launch_skinny_router(const SkinnyRouterArgs& a, Act act, int ncu, hip
 // Split decisions are taken from the item count of the whole layer (routed and shared
 // items), never from `part`, so that a layer launched in one piece and one whose shared
 // expert runs as a separate launch (a graph branch) do the same arithmetic.
+// the gate/up launch takes a ring kernel (else a register-staged one)
+static bool up_uses_ring(const SkinnyUpArgs& a, Act act, WFmt wf) {
+  if (act != Act::BF16) return false;
+  if (wf == WFmt::U4) return true;
+  if (wf == WFmt::U8)
+    return a.H % 128 == 0 && stream_ok(a.T, a.H, 0, 0) && aligned4({a.gate_s, a.gate_z, a.up_s, a.up_z});
+  return stream_ok(a.T, a.H, a.T * a.k, a.I);
+}
+
+// Ring items of a gate/up launch (one item = 16 weight rows x one chunk of 16 tokens)
+// and whether its blocks split K (one item per block).  Gate/up ring kernels split K
+// over the four wavefronts of a block at every size (measured faster on the bf16, u8
+// and u4 layers from 1 to 64 tokens: finer work units even out the last round), except
+// for the dense MLP, whose token chunks of one row block share its rows best inside one
+// block: it splits only when its items cannot occupy the CUs otherwise.  Split decisions
+// are taken from the whole layer's items, never from `part`.
+static int64_t up_ring_items(const SkinnyUpArgs& a, int ncu, bool& split) {
+  const int64_t shared_ring = static_cast<int64_t>(a.Is / 16) * ((a.T + 15) / 16);
+  const int64_t routed = static_cast<int64_t>(a.mtiles) * (a.I / 16);
+  split = a.dense ? part_items(0, routed, shared_ring) < 4ll * ncu : true;
+  return part_items(a.part, routed, shared_ring);
+}
+
+// One-token routing inside the gate/up launch pays the routing chain (partial logits
+// loaded, k rounds of arg-max) in every block that streams a routed item, before its
+// first copy: it only gains where all blocks are resident at once, so that the chain
+// is paid once per CU instead of once per round.  Measured at one token: Ling-3.0-tiny
+// (216 blocks) 29.8 -> 26.0 us; Ling-lite (704 blocks on 512 slots) no gain, Ling-2.6-
+// and Ling-3.0-flash (576) 2.6 to 4.3 us slower.
+bool skinny_up_can_route(const SkinnyUpArgs& a, Act act, WFmt wf, int ncu) {
+  if (a.T != 1 || a.part != 0 || a.dense || a.k > kMaxTopK || a.E > 512 || !up_uses_ring(a, act, wf)) return false;
+  bool split;
+  const int64_t blocks = up_ring_items(a, ncu, split);
+  const int64_t ring_bytes = 4ll * (wf == WFmt::U4 ? kUpRingSplitU4B : wf == WFmt::U8 ? kUpRingU8B : kUpRingB);
+  const int64_t per_cu = (160 * 1024) / ring_bytes;  // blocks resident on a CU (LDS)
+  return split && blocks <= per_cu * ncu;
+}
+
 hipError_t launch_skinny_up(const SkinnyUpArgs& a, Act act, WFmt wf, int ncu, hipStream_t s) {
   if (a.T <= 0) return hipSuccess;
+  // one-token routing inside the launch: only where skinny_up_can_route allows it, with
+  // the shared-first order it assumes and every table it stores
+  if (a.fused_route &&
+      (!skinny_up_can_route(a, act, wf, ncu) || !a.shared_first || !a.ta.logits || !a.ta.idx || !a.ta.w ||
+       a.ta.E != a.E || a.ta.k != a.k || !a.pa.perm || !a.pa.slot_pos || !a.pa.wpos || !a.pa.chunks ||
+       !a.pa.tiles || !a.pa.active || !a.pa.meta || !a.pa.counts || !a.pa.offsets))
+    return hipErrorInvalidValue;
   // routed items read the chunk records, the chunk count and the permutation
-  if (a.part != 2 && (!a.chunks || !a.meta || !a.perm)) return hipErrorInvalidValue;
+  if (a.part != 2 && !a.fused_route && (!a.chunks || !a.meta || !a.perm)) return hipErrorInvalidValue;
   const int64_t slots = static_cast<int64_t>(a.T) * a.k;
   const int64_t dmax = slots < a.E ? slots : a.E;
   const int tch = 16 * pick_mt(a.T);
@@ -1551,16 +1698,26 @@ hipError_t launch_skinny_up(const SkinnyUpArgs& a, Act act, WFmt wf, int ncu, hi
   const int64_t items = part_items(a.part, dmax * (a.I / 16), shared_skinny);
   const int64_t small = 4ll * ncu;
   const bool split_skinny = part_items(0, dmax * (a.I / 16), shared_skinny) < small;
-  // ring kernels: one item = 16 weight rows x one chunk of 16 tokens
-  const int64_t shared_ring = static_cast<int64_t>(a.Is / 16) * ((a.T + 15) / 16);
-  const int64_t ring = part_items(a.part, static_cast<int64_t>(a.mtiles) * (a.I / 16), shared_ring);
-  const int64_t ring_all = part_items(0, static_cast<int64_t>(a.mtiles) * (a.I / 16), shared_ring);
-  // Gate/up ring kernels split K over the four wavefronts of a block at every size
-  // (measured faster on the bf16, u8 and u4 layers from 1 to 64 tokens: finer work units
-  // even out the last round), except for the dense MLP, whose token chunks of one row
-  // block share its rows best inside one block: it splits only when its items cannot
-  // occupy the CUs otherwise.
-  const bool split_ring = a.dense ? ring_all < small : true;
+  bool split_ring;
+  const int64_t ring = up_ring_items(a, ncu, split_ring);
+  if (a.fused_route) {
+    // one round of split blocks (skinny_up_can_route); the kernel that routes with
+    // route_token<ceil(E / 64)>
+    const int epl = (a.E + 63) / 64, grid = static_cast<int>(ring);
+    void (*k)(SkinnyUpArgs) = nullptr;
+    if (wf == WFmt::U4)
+      k = epl <= 1 ? k_stream_up_q<4, kUpRingSplitU4B, 4, 1> : epl <= 2 ? k_stream_up_q<4, kUpRingSplitU4B, 4, 2>
+        : epl <= 4 ? k_stream_up_q<4, kUpRingSplitU4B, 4, 4> : k_stream_up_q<4, kUpRingSplitU4B, 4, 8>;
+    else if (wf == WFmt::U8)
+      k = epl <= 1 ? k_stream_up_q<8, kUpRingU8B, 4, 1> : epl <= 2 ? k_stream_up_q<8, kUpRingU8B, 4, 2>
+        : epl <= 4 ? k_stream_up_q<8, kUpRingU8B, 4, 4> : k_stream_up_q<8, kUpRingU8B, 4, 8>;
+    else
+      k = epl <= 1 ? k_stream_up<kUpRingB, 4, 1> : epl <= 2 ? k_stream_up<kUpRingB, 4, 2>
+        : epl <= 4 ? k_stream_up<kUpRingB, 4, 4> : k_stream_up<kUpRingB, 4, 8>;
+    if (!split_ring) return hipErrorInvalidValue;
+    hipLaunchKernelGGL(k, dim3(grid), dim3(256), 0, s, a);
+    return hipGetLastError();
+  }
   if (wf == WFmt::U4) {
     // the only u4 kernel: the configuration checks guarantee its conditions
     if (act != Act::BF16 || a.H % 128 || !stream_ok(a.T, a.H, a.T, a.Is) || !aligned4({a.gate_s, a.gate_z, a.up_s, a.up_z}))
