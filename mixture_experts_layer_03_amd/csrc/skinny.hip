@@ -693,6 +693,14 @@ __device__ __forceinline__ void token_offsets(const SkinnyUpArgs& a, bool shared
   for (int h = 0; h < 2; ++h) aoff[h] = static_cast<uint32_t>(tok[h]) * a.H * 2 + ch * 16;
 }
 
+// live items of a ring launch: the shared ones and CH per routed chunk (the chunk count
+// is a device value; the grid covers the host's bound, and the loop stops at the live
+// count, so blocks past it do no work)
+template <typename Args>
+__device__ __forceinline__ int live_items(const Args& a, int n_shared, int CH) {
+  return n_shared + (a.part == 2 ? 0 : a.meta[1] * CH);
+}
+
 struct RingItem {
   bool live, shared;
   int e, off, ntot, row0, tc;
@@ -847,11 +855,16 @@ __global__ __launch_bounds__(256) void k_stream_up(SkinnyUpArgs a) {
   if constexpr (FEPL > 0)
     pre = one_token_item<FEPL>(a, reinterpret_cast<char*>(rings),
                                min(static_cast<int>(blockIdx.x) * IPB + w / NWK, nbound - 1), n_shared, CH);
-  for (int base = blockIdx.x * IPB; base < nbound; base += gridDim.x * IPB) {
+  const bool sf = a.shared_first || a.part == 2;
+  int nlive = FEPL == 0 && !sf ? live_items(a, n_shared, CH) : nbound;
+  for (int base = blockIdx.x * IPB; base < nlive; base += gridDim.x * IPB) {
+    if (FEPL == 0 && sf && base >= n_shared && nlive == nbound) {
+      nlive = live_items(a, n_shared, CH);  // shared-first: loaded once a block reaches the routed items
+      if (base >= nlive) break;
+    }
     const int item = base + w / NWK;
     const RingItem itm = FEPL > 0 ? pre
-                                  : ring_item(min(item, nbound - 1), n_shared, TC, CH, a.T, a.meta, a.chunks,
-                                              a.shared_first || a.part == 2);
+                                  : ring_item(min(item, nbound - 1), n_shared, TC, CH, a.T, a.meta, a.chunks, sf);
     const bool live = item < nbound && itm.live, shared = itm.shared;
     const int e = itm.e, off = itm.off, ntot = itm.ntot, row0 = itm.row0, tc_begin = itm.tc, tc_end = itm.tc + 1;
     int k0 = 0, k1 = a.H;
@@ -926,9 +939,15 @@ __global__ __launch_bounds__(256) void k_stream_down(SkinnyDownArgs a) {
   const int nbound = n_shared + (a.part == 2 ? 0 : a.mtiles * CH);  // routed: up to the chunk bound
   int rr, ch;
   ring_lane(rr, ch);
-  for (int base = blockIdx.x * IPB; base < nbound; base += gridDim.x * IPB) {
+  const bool sf = a.shared_first || a.part == 2;
+  int nlive = sf ? nbound : live_items(a, n_shared, CH);
+  for (int base = blockIdx.x * IPB; base < nlive; base += gridDim.x * IPB) {
+    if (sf && base >= n_shared && nlive == nbound) {
+      nlive = live_items(a, n_shared, CH);  // shared-first: loaded once a block reaches the routed items
+      if (base >= nlive) break;
+    }
     const int item = base + w / NWK;
-    const RingItem itm = ring_item(min(item, nbound - 1), n_shared, TC, CH, a.T, a.meta, a.chunks, a.shared_first || a.part == 2);
+    const RingItem itm = ring_item(min(item, nbound - 1), n_shared, TC, CH, a.T, a.meta, a.chunks, sf);
     const bool live = item < nbound && itm.live, shared = itm.shared;
     const int e = itm.e, off = itm.off, ntot = itm.ntot, row0 = itm.row0, tc_begin = itm.tc, tc_end = itm.tc + 1;
     const int K = shared ? a.Is : a.I;
@@ -1292,11 +1311,16 @@ __global__ __launch_bounds__(256) void k_stream_up_q(SkinnyUpArgs a) {
   if constexpr (FEPL > 0)
     pre = one_token_item<FEPL>(a, reinterpret_cast<char*>(rings),
                                min(static_cast<int>(blockIdx.x) * IPB + w / NWK, nbound - 1), n_shared, CH);
-  for (int base = blockIdx.x * IPB; base < nbound; base += gridDim.x * IPB) {
+  const bool sf = a.shared_first || a.part == 2;
+  int nlive = FEPL == 0 && !sf ? live_items(a, n_shared, CH) : nbound;
+  for (int base = blockIdx.x * IPB; base < nlive; base += gridDim.x * IPB) {
+    if (FEPL == 0 && sf && base >= n_shared && nlive == nbound) {
+      nlive = live_items(a, n_shared, CH);  // shared-first: loaded once a block reaches the routed items
+      if (base >= nlive) break;
+    }
     const int item = base + w / NWK;
     const RingItem itm = FEPL > 0 ? pre
-                                  : ring_item(min(item, nbound - 1), n_shared, TC, CH, a.T, a.meta, a.chunks,
-                                              a.shared_first || a.part == 2);
+                                  : ring_item(min(item, nbound - 1), n_shared, TC, CH, a.T, a.meta, a.chunks, sf);
     const bool live = item < nbound && itm.live, shared = itm.shared;
     const int e = itm.e, off = itm.off, ntot = itm.ntot, row0 = itm.row0, tc_begin = itm.tc, tc_end = itm.tc + 1;
     int k0 = 0, k1 = a.H;
@@ -1397,9 +1421,15 @@ __global__ __launch_bounds__(256) void k_stream_down_q(SkinnyDownArgs a) {
   const int nbound = n_shared + (a.part == 2 ? 0 : a.mtiles * CH);  // routed: up to the chunk bound
   int rr, ch;
   ring_lane(rr, ch);
-  for (int base = blockIdx.x * IPB; base < nbound; base += gridDim.x * IPB) {
+  const bool sf = a.shared_first || a.part == 2;
+  int nlive = sf ? nbound : live_items(a, n_shared, CH);
+  for (int base = blockIdx.x * IPB; base < nlive; base += gridDim.x * IPB) {
+    if (sf && base >= n_shared && nlive == nbound) {
+      nlive = live_items(a, n_shared, CH);  // shared-first: loaded once a block reaches the routed items
+      if (base >= nlive) break;
+    }
     const int item = base + w / NWK;
-    const RingItem itm = ring_item(min(item, nbound - 1), n_shared, TC, CH, a.T, a.meta, a.chunks, a.shared_first || a.part == 2);
+    const RingItem itm = ring_item(min(item, nbound - 1), n_shared, TC, CH, a.T, a.meta, a.chunks, sf);
     const bool live = item < nbound && itm.live, shared = itm.shared;
     const int e = itm.e, off = itm.off, ntot = itm.ntot, row0 = itm.row0, tc_begin = itm.tc, tc_end = itm.tc + 1;
     const int K = shared ? a.Is : a.I;
