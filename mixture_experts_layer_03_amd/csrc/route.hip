@@ -233,6 +233,18 @@ __global__ __launch_bounds__(kPermThreads) void k_perm_scatter(PermuteArgs a) {
   for (int q = max(s0, total_s) + tid; q < s1; q += kPermThreads) a.perm[q] = -1;
 }
 
+// One token: one wavefront routes it and stores every table of the permutation (the
+// same tables k_route_permute builds, without its histogram, scans and block barriers).
+template <int EPL>
+__global__ __launch_bounds__(64) void k_route_one(TopkArgs ta, PermuteArgs a) {
+  __shared__ int s_slot_e[kMaxTopK], s_pos_e[kMaxTopK], s_kv;
+  __shared__ float s_w[kMaxTopK];
+  route_token<EPL>(ta, 0, s_slot_e, s_w);
+  one_token_tables(a, ta.k, ta.E, s_slot_e, s_w, s_pos_e, &s_kv, true);
+  __syncthreads();  // one wavefront: orders the LDS writes above before the reads below
+  one_token_counts(a, ta.E, s_pos_e, s_kv, threadIdx.x, 64);
+}
+
 }  // namespace
 
 hipError_t launch_topk(const TopkArgs& a, hipStream_t s) {
@@ -255,6 +267,21 @@ hipError_t launch_topk(const TopkArgs& a, hipStream_t s) {
 hipError_t launch_route_permute(const TopkArgs& t, const PermuteArgs& a, hipStream_t s) {
   if (a.nslots > kFusedSlots || a.E > kPermThreads) return hipErrorInvalidValue;
   const int epl = (t.E + 63) / 64;
+  if (t.T == 1 && t.k <= kMaxTopK && a.wpos && a.chunks && !a.BM2) {
+    // one token (the decode tables: chunk records and weights by position)
+    const dim3 g1(1), b1(64);
+    if (epl <= 1)
+      hipLaunchKernelGGL(k_route_one<1>, g1, b1, 0, s, t, a);
+    else if (epl <= 2)
+      hipLaunchKernelGGL(k_route_one<2>, g1, b1, 0, s, t, a);
+    else if (epl <= 4)
+      hipLaunchKernelGGL(k_route_one<4>, g1, b1, 0, s, t, a);
+    else if (epl <= 8)
+      hipLaunchKernelGGL(k_route_one<8>, g1, b1, 0, s, t, a);
+    else
+      hipLaunchKernelGGL(k_route_one<16>, g1, b1, 0, s, t, a);
+    return hipGetLastError();
+  }
   const dim3 g(1), b(kPermThreads);
   if (epl <= 1)
     hipLaunchKernelGGL(k_route_permute<1>, g, b, 0, s, t, a);

@@ -37,8 +37,9 @@ __device__ void route_token(const TopkArgs& a, int t, int* lds_idx = nullptr, fl
     valid[i] = lane * EPL + i < E;
     s[i] = 0.f;
   }
-  // both biases and the P partial logits are loaded together (one memory round trip
-  // for P <= 8: a token's routing is a chain of dependent steps)
+  // both biases and the P partial logits are loaded together, PB partials per batch:
+  // one memory round trip (a token's routing is a chain of dependent steps; the router's
+  // split keeps P * EPL <= 64, so one batch of PB = 64 / EPL, at most 16, covers it)
   float rb[EPL], eb[EPL];
 #pragma unroll
   for (int i = 0; i < EPL; ++i) {
@@ -46,17 +47,18 @@ __device__ void route_token(const TopkArgs& a, int t, int* lds_idx = nullptr, fl
     eb[i] = (valid[i] && a.use_ebias) ? a.expert_bias[lane * EPL + i] : 0.f;
   }
   const float* row = a.logits + static_cast<int64_t>(t) * E + lane * EPL;
+  constexpr int PB = EPL >= 4 ? 64 / EPL : 16;
   if (EPL % 4 == 0 && (E % 4) == 0 && lane * EPL + EPL <= E) {
-    for (int q0 = 0; q0 < a.P; q0 += 8) {
-      float4 v[8][EPL / 4 > 0 ? EPL / 4 : 1];
+    for (int q0 = 0; q0 < a.P; q0 += PB) {
+      float4 v[PB][EPL / 4 > 0 ? EPL / 4 : 1];
 #pragma unroll
-      for (int u = 0; u < 8; ++u)
+      for (int u = 0; u < PB; ++u)
 #pragma unroll
         for (int c = 0; c < EPL / 4; ++c)
           v[u][c] = q0 + u < a.P ? *reinterpret_cast<const float4*>(row + (q0 + u) * a.part_stride + 4 * c)
                                  : make_float4(0.f, 0.f, 0.f, 0.f);
 #pragma unroll
-      for (int u = 0; u < 8; ++u)
+      for (int u = 0; u < PB; ++u)
 #pragma unroll
         for (int c = 0; c < EPL / 4; ++c) {
           s[4 * c] += v[u][c].x;
@@ -66,14 +68,14 @@ __device__ void route_token(const TopkArgs& a, int t, int* lds_idx = nullptr, fl
         }
     }
   } else {
-    for (int q0 = 0; q0 < a.P; q0 += 8) {
-      float v[8][EPL];
+    for (int q0 = 0; q0 < a.P; q0 += PB) {
+      float v[PB][EPL];
 #pragma unroll
-      for (int u = 0; u < 8; ++u)
+      for (int u = 0; u < PB; ++u)
 #pragma unroll
         for (int i = 0; i < EPL; ++i) v[u][i] = (valid[i] && q0 + u < a.P) ? row[(q0 + u) * a.part_stride + i] : 0.f;
 #pragma unroll
-      for (int u = 0; u < 8; ++u)
+      for (int u = 0; u < PB; ++u)
 #pragma unroll
         for (int i = 0; i < EPL; ++i) s[i] += v[u][i];
     }
@@ -224,6 +226,70 @@ __device__ void route_token(const TopkArgs& a, int t, int* lds_idx = nullptr, fl
     }
     if (lds_idx) lds_idx[t * a.k + lane] = my_idx;
     if (lds_w) lds_w[t * a.k + lane] = my_w;
+  }
+}
+
+// The tables of a single token's routing, by one wavefront (all 64 lanes).  Its k picks
+// (expert of slot j in s_slot_e[j], weight in s_w[j], as route_token leaves them) are
+// distinct experts; each valid one is ranked by expert index: position p holds the
+// p-th smallest, one chunk each, which is what the permutation kernels build for one
+// token.  Leaves the experts by position in s_pos_e and the valid count in *s_kv; with
+// `publish`, stores perm, slot_pos, wpos, chunks, tiles, active and meta (the per-expert
+// counts and offsets: one_token_counts).
+__device__ __forceinline__ void one_token_tables(const PermuteArgs& pa, int k, int E, const int* s_slot_e,
+                                                 const float* s_w, int* s_pos_e, int* s_kv, bool publish) {
+  // the picks were written to LDS by other lanes of this wavefront: keep the reads after
+  // those writes (LDS serves one wavefront's accesses in order)
+  __builtin_amdgcn_fence(__ATOMIC_SEQ_CST, "wavefront");
+  const int lane = lane_id();
+  const int e = lane < k ? s_slot_e[lane] : -1;
+  const bool valid = lane < k && e >= 0 && e < E;
+  int rank = 0;
+  for (int i = 0; i < k; ++i) {
+    const int ei = s_slot_e[i];
+    rank += (ei >= 0 && ei < E && ei < e) ? 1 : 0;
+  }
+  const int kv = __popcll(__ballot(valid));
+  if (valid) s_pos_e[rank] = e;
+  if (lane == 0) *s_kv = kv;
+  if (publish && lane < k) {
+    if (valid) {
+      pa.perm[rank] = lane;
+      pa.slot_pos[lane] = rank;
+      pa.wpos[rank] = s_w[lane];
+      pa.chunks[rank] = make_int4(e, rank, rank, 1);
+      pa.tiles[2 * rank] = e;
+      pa.tiles[2 * rank + 1] = rank;
+      pa.active[rank] = e;
+    } else {
+      pa.slot_pos[lane] = -1;
+    }
+    if (lane >= kv) pa.perm[lane] = -1;
+  }
+  if (publish && lane == 0) {
+    pa.meta[0] = kv;  // active experts
+    pa.meta[1] = kv;  // chunks
+    pa.meta[2] = kv;  // valid slots
+    pa.meta[3] = 0;
+    pa.offsets[E] = kv;
+  }
+}
+
+// counts[e] and offsets[e] (experts before e's first position) of a single token's
+// routing, over threads tid = t0, t0 + nthr, ... (the experts by position and their
+// count from one_token_tables, visible to these threads)
+__device__ __forceinline__ void one_token_counts(const PermuteArgs& pa, int E, const int* s_pos_e, int kv, int t0,
+                                                 int nthr) {
+  for (int e = t0; e < E; e += nthr) {
+    int c = 0, before = 0;
+    for (int p = 0; p < kv; ++p) {
+      const int pe = s_pos_e[p];
+      c += pe == e ? 1 : 0;
+      before += pe < e ? 1 : 0;
+    }
+    pa.counts[e] = c;
+    pa.offsets[e] = before;
+    if (pa.counts_copy) pa.counts_copy[e] = c;
   }
 }
 

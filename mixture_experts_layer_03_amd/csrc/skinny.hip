@@ -766,58 +766,16 @@ __device__ RingItem one_token_item(const SkinnyUpArgs& a, char* scratch, int ite
   int* s_pos_e = reinterpret_cast<int*>(s_w + kMaxTopK);       // [k] expert at position p
   int* s_kv = s_pos_e + kMaxTopK;                              // valid picks
   const bool publish = blockIdx.x == 0;
-  const int tid = threadIdx.x, lane = tid & 63;
+  const int tid = threadIdx.x;
   const int k = a.ta.k, E = a.ta.E;
   const PermuteArgs& pa = a.pa;
   if (tid < 64) {
     route_token<EPL>(a.ta, 0, s_slot_e, s_w, publish);
-    const int e = lane < k ? s_slot_e[lane] : -1;
-    const bool valid = lane < k && e >= 0 && e < E;
-    int rank = 0;
-    for (int i = 0; i < k; ++i) {
-      const int ei = s_slot_e[i];
-      rank += (ei >= 0 && ei < E && ei < e) ? 1 : 0;
-    }
-    const int kv = __popcll(__ballot(valid));
-    if (valid) s_pos_e[rank] = e;
-    if (lane == 0) *s_kv = kv;
-    if (publish && lane < k) {
-      if (valid) {
-        pa.perm[rank] = lane;
-        pa.slot_pos[lane] = rank;
-        pa.wpos[rank] = s_w[lane];
-        pa.chunks[rank] = make_int4(e, rank, rank, 1);
-        pa.tiles[2 * rank] = e;
-        pa.tiles[2 * rank + 1] = rank;
-        pa.active[rank] = e;
-      } else {
-        pa.slot_pos[lane] = -1;
-      }
-      if (lane >= kv) pa.perm[lane] = -1;
-    }
-    if (publish && lane == 0) {
-      pa.meta[0] = kv;  // active experts
-      pa.meta[1] = kv;  // chunks
-      pa.meta[2] = kv;  // valid slots
-      pa.meta[3] = 0;
-      pa.offsets[E] = kv;
-    }
+    one_token_tables(pa, k, E, s_slot_e, s_w, s_pos_e, s_kv, publish);
   }
   __syncthreads();
   const int kv = *s_kv;
-  if (publish) {
-    for (int e = tid; e < E; e += blockDim.x) {
-      int c = 0, before = 0;
-      for (int p = 0; p < kv; ++p) {
-        const int pe = s_pos_e[p];
-        c += pe == e ? 1 : 0;
-        before += pe < e ? 1 : 0;
-      }
-      pa.counts[e] = c;
-      pa.offsets[e] = before;
-      if (pa.counts_copy) pa.counts_copy[e] = c;
-    }
-  }
+  if (publish) one_token_counts(pa, E, s_pos_e, kv, tid, blockDim.x);
   RingItem r{};
   if (item < n_shared) {
     r.live = r.shared = true;
