@@ -856,18 +856,18 @@ __global__ __launch_bounds__(256) void k_stream_up(SkinnyUpArgs a) {
 #pragma unroll
         for (int m = 0; m < 2; ++m) *reinterpret_cast<f32x4*>(red + ((w * 2 + m) * 64 + lane) * 4) = acc[m];
         __syncthreads();
-        if (w == 0) {
+        if (w % NWK == 0) {  // the first wavefront of each item adds its item's partials
 #pragma unroll
           for (int m = 0; m < 2; ++m) {
             f32x4 sum = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-            for (int p = 0; p < 4; ++p) sum += *reinterpret_cast<const f32x4*>(red + ((p * 2 + m) * 64 + lane) * 4);
+            for (int p = 0; p < NWK; ++p) sum += *reinterpret_cast<const f32x4*>(red + (((w + p) * 2 + m) * 64 + lane) * 4);
             acc[m] = sum;
           }
         }
         __syncthreads();
       }
-      if (live && (NWK == 1 || w == 0)) {
+      if (live && (NWK == 1 || w % NWK == 0)) {
         uint16_t* out = static_cast<uint16_t*>(shared ? a.hs : a.hm);
         const int ld = shared ? a.Is : a.I;
         const int64_t rbase = shared ? 0 : off;
@@ -945,15 +945,15 @@ __global__ __launch_bounds__(256) void k_stream_down(SkinnyDownArgs a) {
         __syncthreads();
         *reinterpret_cast<f32x4*>(red + (w * 64 + lane) * 4) = acc[0];
         __syncthreads();
-        if (w == 0) {
+        if (w % NWK == 0) {  // the first wavefront of each item adds its item's partials
           f32x4 sum = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-          for (int p = 0; p < 4; ++p) sum += *reinterpret_cast<const f32x4*>(red + (p * 64 + lane) * 4);
+          for (int p = 0; p < NWK; ++p) sum += *reinterpret_cast<const f32x4*>(red + ((w + p) * 64 + lane) * 4);
           acc[0] = sum;
         }
         __syncthreads();
       }
-      if (live && (NWK == 1 || w == 0)) {
+      if (live && (NWK == 1 || w % NWK == 0)) {
 #pragma unroll
         for (int v = 0; v < 4; ++v) {
           const int m = 4 * (lane >> 4) + v;
@@ -1337,18 +1337,18 @@ __global__ __launch_bounds__(256) void k_stream_up_q(SkinnyUpArgs a) {
 #pragma unroll
         for (int m = 0; m < 2; ++m) *reinterpret_cast<f32x4*>(red + ((w * 2 + m) * 64 + lane) * 4) = acc[m];
         __syncthreads();
-        if (w == 0) {
+        if (w % NWK == 0) {  // the first wavefront of each item adds its item's partials
 #pragma unroll
           for (int m = 0; m < 2; ++m) {
             f32x4 sum = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-            for (int p = 0; p < 4; ++p) sum += *reinterpret_cast<const f32x4*>(red + ((p * 2 + m) * 64 + lane) * 4);
+            for (int p = 0; p < NWK; ++p) sum += *reinterpret_cast<const f32x4*>(red + (((w + p) * 2 + m) * 64 + lane) * 4);
             acc[m] = sum;
           }
         }
         __syncthreads();
       }
-      if (live && (NWK == 1 || w == 0)) {
+      if (live && (NWK == 1 || w % NWK == 0)) {
         uint16_t* out = static_cast<uint16_t*>(shared ? a.hs : a.hm);
         const int ld = shared ? a.Is : a.I;
         const int64_t rbase = shared ? 0 : off;
@@ -1452,15 +1452,15 @@ __global__ __launch_bounds__(256) void k_stream_down_q(SkinnyDownArgs a) {
         __syncthreads();
         *reinterpret_cast<f32x4*>(red + (w * 64 + lane) * 4) = acc[0];
         __syncthreads();
-        if (w == 0) {
+        if (w % NWK == 0) {  // the first wavefront of each item adds its item's partials
           f32x4 sum = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-          for (int p = 0; p < 4; ++p) sum += *reinterpret_cast<const f32x4*>(red + (p * 64 + lane) * 4);
+          for (int p = 0; p < NWK; ++p) sum += *reinterpret_cast<const f32x4*>(red + ((w + p) * 64 + lane) * 4);
           acc[0] = sum;
         }
         __syncthreads();
       }
-      if (live && (NWK == 1 || w == 0)) {
+      if (live && (NWK == 1 || w % NWK == 0)) {
 #pragma unroll
         for (int v = 0; v < 4; ++v) {
           const int m = 4 * (lane >> 4) + v;
@@ -1583,11 +1583,12 @@ bool stream_ok(int64_t rows, int64_t cols, int64_t rows2, int64_t cols2) {
   return rows * cols * 2 < (int64_t(1) << 31) && rows2 * cols2 * 2 < (int64_t(1) << 31);
 }
 
-// split: the four wavefronts of a block share one item's K; else one item each
-template <int U, typename Args>
+// split: the NWKS wavefronts of an item share its K (4 / NWKS items per block); else
+// one item per wavefront
+template <int U, int NWKS = 4, typename Args>
 hipError_t launch_ring(void (*k1)(Args), void (*k4)(Args), int64_t items, bool split, int ncu, hipStream_t s,
                        const Args& a) {
-  const int grid = grid_for(items, split ? 1 : 4, ncu);
+  const int grid = grid_for(items, split ? 4 / NWKS : 4, ncu);
   hipLaunchKernelGGL(split ? k4 : k1, dim3(grid), dim3(256), 0, s, a);
   return hipGetLastError();
 }
@@ -1758,7 +1759,10 @@ hipError_t launch_skinny_down(const SkinnyDownArgs& a, Act act, WFmt wf, int ncu
   else if (wf == WFmt::U8)
     MOE_DISPATCH_MT_NWK(k_skinny_down, a, items, a.T, split_skinny, Act::BF16, WFmt::U8);
   else if (stream_ok(a.T * a.k, a.I, a.T, a.Is))
-    return launch_ring<0>(k_stream_down<kDownRingB, 1>, k_stream_down<kDownRingB, 4>, ring, split_ring, ncu, s, a);
+    // split items share K between two wavefronts (two items per block): measured against
+    // four on Ling-lite at 1 token (down 14.4 -> 13.7 us), the only split bf16 down of
+    // the measured shapes
+    return launch_ring<0, 2>(k_stream_down<kDownRingB, 1>, k_stream_down<kDownRingB, 2>, ring, split_ring, ncu, s, a);
   else
     MOE_DISPATCH_MT_NWK(k_skinny_down, a, items, a.T, split_skinny, Act::BF16, WFmt::BF16);
   return hipGetLastError();
