@@ -1658,8 +1658,9 @@ static int64_t up_ring_items(const SkinnyUpArgs& a, int ncu, bool& split) {
 // loaded, k rounds of arg-max) in every block that streams a routed item, before its
 // first copy: it only gains where all blocks are resident at once, so that the chain
 // is paid once per CU instead of once per round.  Measured at one token: Ling-3.0-tiny
-// (216 blocks) 29.8 -> 26.0 us; Ling-lite (704 blocks on 512 slots) no gain, Ling-2.6-
-// and Ling-3.0-flash (576) 2.6 to 4.3 us slower.
+// (216 blocks) 28.6 -> 26.1 us, Ling-3.0-flash u4 (576 blocks, three per CU) 53.7 ->
+// 50.5 us; Ling-lite (704 blocks on 512 slots) no gain, Ling-2.6- and Ling-3.0-flash
+// bf16 / u8 (576 blocks, two per CU) 2.6 to 4.3 us slower.
 bool skinny_up_can_route(const SkinnyUpArgs& a, Act act, WFmt wf, int ncu) {
   if (a.T != 1 || a.part != 0 || a.dense || a.k > kMaxTopK || a.E > 512 || !up_uses_ring(a, act, wf)) return false;
   bool split;
