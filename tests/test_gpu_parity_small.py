@@ -413,3 +413,38 @@ def test_u8_copy_pipeline(H, I):
         idx_h = idx.cpu().numpy()
         check_route(spec, idx_h, w.cpu().numpy(), L, x)
         check_forward(spec, y_to_f64(y), idx_h, L, x)
+
+
+# a Ling-lite-like layer whose one-token gate/up launch has more blocks (704) than the
+# CUs hold at once, so the layer routes one token in its own one-wavefront launch
+# rather than inside gate/up
+WIDE_LITE = synth.SPECS[2].variant("ling-lite-wide", 112, hidden=256)
+
+
+@pytest.mark.parametrize("cid,T", [(2, 1), (3, 1), (4, 1), (5, 1), (6, 1), (7, 1), ("wide", 1),
+                                   (2, 8), (3, 8), (6, 8), ("wide", 8)])
+def test_small_batch_routing_tables_match_the_general_permutation(cid, T):
+    """Batches of up to 16 tokens are routed and permuted by one-token or one-workgroup
+    launches (or, for one token, inside the gate/up launch); the expert stage fed the
+    same routing builds its tables with the general permutation kernel.  Every token's
+    arithmetic after routing is the same, so the outputs must be bit-identical."""
+    import mixture_experts_layer_03_amd as moe
+    if cid == "wide":
+        if "wide" not in _CACHE:
+            L = synth.make_layer(WIDE_LITE)
+            _CACHE["wide"] = (WIDE_LITE, L, device_weights(L))
+        spec, L, W = _CACHE["wide"]
+    else:
+        spec, L, W = layer(cid)
+    x, xd = xs(spec, T)
+    cfg = moe_cfg(spec, "decode")
+    log(f"routing tables cfg{cid} {spec.name} T={T}: kernels {cfg.kernel_path(T)}")
+    y, (idx, w, counts) = moe.forward(xd, W, cfg, return_routing=True)
+    y2 = moe.experts(xd, W, idx, w, cfg)
+    torch.cuda.synchronize()
+    idx_h = idx.cpu().numpy()
+    assert np.array_equal(counts.cpu().numpy(), np.bincount(idx_h.reshape(-1), minlength=spec.num_experts))
+    assert torch.equal(y, y2), "forward and experts-given-its-routing differ"
+    check_route(spec, idx_h, w.cpu().numpy(), L, x)
+    st = check_forward(spec, y_to_f64(y), idx_h, L, x)
+    log(f"  ok: bit-identical, max rel err {st['max_rel']:.3e}")
