@@ -411,25 +411,28 @@ def bench_dense(args):
                 call(i, ys[i], wss[i])
             torch.cuda.synchronize()
             ref = [t.clone() for t in ys]
-            graphs, s = [], torch.cuda.Stream()
+            # the L copies' calls back to back in one graph, as run_graph does
+            s = torch.cuda.Stream()
             s.wait_stream(torch.cuda.current_stream())
+            gr = torch.cuda.CUDAGraph()
             with torch.cuda.stream(s):
-                for i in range(L):
-                    gr = torch.cuda.CUDAGraph()
-                    with torch.cuda.graph(gr, stream=s):
+                with torch.cuda.graph(gr, stream=s):
+                    for i in range(L):
                         call(i, ys[i], wss[i])
-                    graphs.append(gr)
             torch.cuda.current_stream().wait_stream(s)
             torch.cuda.synchronize()
-            for i in range(max(args.warmup, L)):
-                graphs[i % L].replay()
+            for y in ys:
+                y.zero_()
+            reps = max(1, -(-steps // L))
+            for _ in range(max(1, -(-args.warmup // L))):
+                gr.replay()
             torch.cuda.synchronize()
             ok = all(torch.equal(ys[i], ref[i]) for i in range(L))
             t0 = time.perf_counter()
-            for i in range(steps):
-                graphs[i % L].replay()
+            for _ in range(reps):
+                gr.replay()
             torch.cuda.synchronize()
-            gt = (time.perf_counter() - t0) / steps
+            gt = (time.perf_counter() - t0) / (reps * L)
             r.update(graph_ms_per_step=gt * 1e3, graph_tokens_per_s=T / gt,
                      graph_roofline_frac=max(byt / (HBM_PEAK_GBPS * 1e9), fl / (BF16_PEAK_TFLOPS * 1e12)) / gt,
                      graph_matches_eager=ok)
