@@ -528,9 +528,20 @@ __device__ __forceinline__ void tile_dma_body(const TileArgs& a, const TilePos& 
   const int wm = w / WN, wn = w % WN;
   const int fr = lane & 15, fq = lane >> 4;
   const int a_rd = (wm * 64 + fr) * BK, b_rd = (wn * WT + fr) * BK;
-  auto compute = [&](int stage) {
+  // Compute of `stage` with the copies of a later stage spread over its MFMA groups.  A
+  // wave's instructions issue in order, and the load unit takes a CU's copy instructions
+  // one at a time (about 30 cycles each, from TA_TA_BUSY), so copies issued all at once
+  // hold back the MFMAs behind them.  With three stages (two K-steps of slack) spreading
+  // them lets both proceed: the Ling-3.0-tiny gate/up (128 x 256 x 64) 183 -> 173.5 us,
+  // the Ling-lite shared down + combine 77 -> 74.5 us.  With two stages the copies must
+  // land within one step, and spread they landed late (Ling-lite gate/up 382 -> 411 us),
+  // so those kernels issue them all at the start of the step.
+  constexpr int NG = (BK / 32) * NH * 4;  // MFMA groups (one row i of one sub-tile per group)
+  auto compute_issue = [&](int stage, bool do_issue, int nstage, int kt) {
     const uint16_t* As = smem + stage * STAGE_ELEMS;
     const uint16_t* Bs = As + TBM * BK;
+    const uint16_t* st = smem + nstage * STAGE_ELEMS;
+    const int kb = kt * BK * 2;
 #pragma unroll
     for (int ks = 0; ks < BK / 32; ++ks) {
       const int cc = ((ks * 4 + fq) ^ swz<BK>(fr)) << 3;
@@ -542,11 +553,22 @@ __device__ __forceinline__ void tile_dma_body(const TileArgs& a, const TilePos& 
 #pragma unroll
       for (int hh = 0; hh < NH; ++hh)
 #pragma unroll
-        for (int i = 0; i < 4; ++i)
+        for (int i = 0; i < 4; ++i) {
+          const int g = (ks * NH + hh) * 4 + i;
+#pragma unroll
+          for (int jc = 0; jc < J; ++jc) {
+            if (jc * NG / J == g && do_issue && (jc < J - 1 || w < NHI)) {
+              __builtin_amdgcn_sched_barrier(0);
+              copy_to_lds(ibase[jc] + kb, off[jc], st + (w + jc * NW) * 512);
+              __builtin_amdgcn_sched_barrier(0);
+            }
+          }
 #pragma unroll
           for (int j = 0; j < 4; ++j) acc[hh][i][j] = mfma16_bf16(af[i], bf[hh * 4 + j], acc[hh][i][j]);
+        }
     }
   };
+  auto compute = [&](int stage) { compute_issue(stage, false, 0, 0); };
 
   // K-step t lives in stage t % S.  Steps up to t + S - 2 are issued before step t is
   // consumed, so before the barrier of step t a wave lets min(S - 2, n - 1 - t) stages
@@ -563,8 +585,12 @@ __device__ __forceinline__ void tile_dma_body(const TileArgs& a, const TilePos& 
     else
       copy_wait_ahead<J - 1, S - 2>(ahead);
     lds_barrier();
-    if (t + S - 1 < n) issue(nxt, kt0 + t + S - 1);
-    compute(cur);
+    if constexpr (S >= 3) {
+      compute_issue(cur, t + S - 1 < n, nxt, kt0 + t + S - 1);
+    } else {
+      if (t + S - 1 < n) issue(nxt, kt0 + t + S - 1);
+      compute(cur);
+    }
     cur = cur + 1 == S ? 0 : cur + 1;
     nxt = nxt + 1 == S ? 0 : nxt + 1;
   }
