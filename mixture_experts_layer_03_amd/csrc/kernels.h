@@ -125,8 +125,16 @@ struct SkinnyDownArgs {
   int T, H, I, Is, k, E;
   int part;                // as SkinnyUpArgs::part
   int shared_first;        // as SkinnyUpArgs::shared_first
+  // one token (launch_down_one): the layer output is written here, combined
+  const int32_t* idx;      // [k] routing of the token (entries outside [0,E) skipped)
+  void* y;                 // [1, H] act
 };
 hipError_t launch_skinny_down(const SkinnyDownArgs& a, Act act, WFmt wf, int ncu, hipStream_t s);
+// One token, bf16 weights and activations, the whole layer (part 0): down of the shared
+// and selected experts and their weighted sum in one launch, into y (no r, rs, combine).
+// down_one_fits says whether launch_down_one takes these arguments.
+bool down_one_fits(const SkinnyDownArgs& a, Act act, WFmt wf);
+hipError_t launch_down_one(const SkinnyDownArgs& a, Act act, WFmt wf, hipStream_t s);
 
 // largest top_k the library accepts (the combine kernel keeps a token's k terms in registers)
 constexpr int kMaxTopK = 16;

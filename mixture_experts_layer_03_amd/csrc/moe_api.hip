@@ -524,6 +524,13 @@ moe_status run_experts(const moe_config& c, const Plan& p, int64_t T, const void
     d.E = E;
     d.part = shared_join ? 1 : 0;
     d.shared_first = T <= kSharedFirstMaxT;
+    d.idx = idx;
+    d.y = y;
+    if (down_one_fits(d, act, wf)) {
+      // one token: the down launch also forms the weighted sum (no combine launch)
+      MOE_LAUNCH_STAGE(MOE_STAGE_DOWN, s, launch_down_one(d, act, wf, s), "expert down + combine (one token)");
+      return MOE_OK;
+    }
     MOE_LAUNCH_STAGE(MOE_STAGE_DOWN, s, launch_skinny_down(d, act, wf, ncu, s), "expert down (streaming)");
     if (shared_join) {
       const hipError_t e = hipStreamWaitEvent(s, shared_join, 0);

@@ -975,6 +975,102 @@ __global__ __launch_bounds__(256) void k_stream_down(SkinnyDownArgs a) {
   }
 }
 
+// ------------------------------------------ one token: down and combine in one launch
+// With one token, element h of the layer output is a single dot product: the shared
+// expert's down row h against its activation row, plus each selected expert's down row
+// h against its own, scaled by the expert's routing weight [Bailing MoE block: the
+// routed outputs are weighted, summed and added to the shared expert's output].  A
+// wavefront owns one output element and issues every 16-byte load of its rows at once
+// (2-23 KB per element, no ring needed): the routing first (an L2 round trip), the
+// shared rows next (they need no routing), the selected experts' rows once the routing
+// is in.  The block stages the activation rows (hs row 0, then hm positions 0..k-1) in
+// LDS once for its NW elements.  No partial sum leaves the wavefront, so the weighted
+// sum needs no second launch and no device-scope fence.
+// NLS / NLR: 16-byte loads per lane for a shared / routed row (Is / 512 and I / 512
+// rounded up); K: top-k (position p of the one-token permutation holds a pick; with
+// fewer valid picks than K the last valid row is loaded again and not added).
+__device__ __forceinline__ float dot8_bf16(const uint4& a, const uint4& b, float c) {
+  c = __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2, a.x), __builtin_bit_cast(bf16x2, b.x), c, false);
+  c = __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2, a.y), __builtin_bit_cast(bf16x2, b.y), c, false);
+  c = __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2, a.z), __builtin_bit_cast(bf16x2, b.z), c, false);
+  c = __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2, a.w), __builtin_bit_cast(bf16x2, b.w), c, false);
+  return c;
+}
+
+constexpr int kDownOneWaves = 8;
+
+template <int NLS, int NLR, int K>
+__global__ __launch_bounds__(64 * kDownOneWaves) void k_down_one(SkinnyDownArgs a) {
+  constexpr int NW = kDownOneWaves, NT = 64 * NW;
+  constexpr int NST = ((NLS + K * NLR) * 64 + NT - 1) / NT;  // staging loads per thread
+  __shared__ __attribute__((aligned(16))) uint16_t act[NST * NT * 8];
+  // Every load is unconditional (lanes past a row's end load its last vector again, in
+  // the same line, and add nothing), so no branch splits the loads and each use waits
+  // only for the loads issued before its own.
+  const int lane = lane_id(), w = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  const int h = static_cast<int>(blockIdx.x) * NW + w;
+  const int hrow = min(h, a.H - 1);
+  const int nvs = a.Is / 8, nvr = a.I / 8, nst = nvs + K * nvr;
+  // lane p: position p's slot (the pick j, one token) and weight; lane j: pick j's expert
+  const int jl = min(lane, K - 1);
+  const int pslot = a.perm[jl];
+  const int pidx = a.idx[jl];
+  const float pw = a.wpos[jl];
+  __builtin_amdgcn_sched_barrier(0);
+  const uint16_t* hs = static_cast<const uint16_t*>(a.hs);
+  const uint16_t* hm = static_cast<const uint16_t*>(a.hm);
+  uint4 st[NST];
+#pragma unroll
+  for (int i = 0; i < NST; ++i) {
+    const int u = min(static_cast<int>(threadIdx.x) + NT * i, nst - 1);
+    st[i] = ld16(u < nvs ? hs + 8 * u : hm + 8 * (u - nvs));
+  }
+  __builtin_amdgcn_sched_barrier(0);
+  uint4 ws[NLS];
+  const uint16_t* srow = static_cast<const uint16_t*>(a.sdown) + static_cast<int64_t>(hrow) * a.Is;
+#pragma unroll
+  for (int i = 0; i < NLS; ++i) ws[i] = ld16(srow + 8 * min(lane + 64 * i, nvs - 1));
+  __builtin_amdgcn_sched_barrier(0);
+  // valid picks fill positions 0 .. npos - 1 in expert order
+  const int npos = __popcll(__ballot(lane < K && pidx >= 0 && pidx < a.E));
+  const int pe = __shfl(pidx, min(max(pslot, 0), K - 1));
+  uint4 wr[K][NLR];
+#pragma unroll
+  for (int p = 0; p < K; ++p) {
+    const int e = min(max(__builtin_amdgcn_readlane(pe, min(p, max(npos - 1, 0))), 0), a.E - 1);
+    const uint16_t* row = static_cast<const uint16_t*>(a.down) + (static_cast<int64_t>(e) * a.H + hrow) * a.I;
+#pragma unroll
+    for (int i = 0; i < NLR; ++i) wr[p][i] = ld16(row + 8 * min(lane + 64 * i, nvr - 1));
+  }
+#pragma unroll
+  for (int i = 0; i < NST; ++i) {
+    const int u = static_cast<int>(threadIdx.x) + NT * i;
+    if (u < nst) *reinterpret_cast<uint4*>(act + 8 * u) = st[i];
+  }
+  __syncthreads();
+  float acc = 0.f;
+#pragma unroll
+  for (int i = 0; i < NLS; ++i) {
+    const int v = lane + 64 * i, vc = min(v, nvs - 1);
+    const float t = dot8_bf16(ws[i], *reinterpret_cast<const uint4*>(act + 8 * vc), 0.f);
+    acc += v < nvs ? t : 0.f;
+  }
+#pragma unroll
+  for (int p = 0; p < K; ++p) {
+    float sp = 0.f;
+#pragma unroll
+    for (int i = 0; i < NLR; ++i) {
+      const int v = lane + 64 * i, vc = min(v, nvr - 1);
+      const float t = dot8_bf16(wr[p][i], *reinterpret_cast<const uint4*>(act + 8 * (nvs + p * nvr + vc)), 0.f);
+      sp += v < nvr ? t : 0.f;
+    }
+    const float wgt = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(pw), p));
+    acc = p < npos ? fmaf(wgt, sp, acc) : acc;
+  }
+  acc = wave_sum(acc);
+  if (lane == 0 && h < a.H) static_cast<uint16_t*>(a.y)[h] = f32_to_bf16(acc);
+}
+
 // ----------------------------------------------------- u8 weights through LDS rings
 // One ring step covers 128 elements of K (two quantisation groups), so a weight row's
 // codes for the step are one whole 128-byte line.  Slot layout (bytes): NMAT x 16 code
@@ -1766,6 +1862,40 @@ hipError_t launch_skinny_down(const SkinnyDownArgs& a, Act act, WFmt wf, int ncu
     return launch_ring<0, 2>(k_stream_down<kDownRingB, 1>, k_stream_down<kDownRingB, 2>, ring, split_ring, ncu, s, a);
   else
     MOE_DISPATCH_MT_NWK(k_skinny_down, a, items, a.T, split_skinny, Act::BF16, WFmt::BF16);
+  return hipGetLastError();
+}
+
+// instances of k_down_one: (NLS, NLR, K), smallest first per K
+namespace {
+struct DownOneShape {
+  int nls, nlr, k;
+  void (*fn)(SkinnyDownArgs);
+};
+const DownOneShape kDownOne[] = {
+    {1, 1, 8, k_down_one<1, 1, 8>},
+    {2, 2, 8, k_down_one<2, 2, 8>},
+    {6, 3, 6, k_down_one<6, 3, 6>},
+};
+const DownOneShape* down_one_shape(const SkinnyDownArgs& a) {
+  const int nls = (a.Is / 8 + 63) / 64, nlr = (a.I / 8 + 63) / 64;
+  for (const DownOneShape& d : kDownOne)
+    if (d.k == a.k && nls <= d.nls && nlr <= d.nlr) return &d;
+  return nullptr;
+}
+}  // namespace
+
+bool down_one_fits(const SkinnyDownArgs& a, Act act, WFmt wf) {
+  auto al16 = [](const void* q) { return reinterpret_cast<uintptr_t>(q) % 16 == 0; };
+  return a.T == 1 && a.part == 0 && act == Act::BF16 && wf == WFmt::BF16 && a.I % 8 == 0 && a.Is % 8 == 0 &&
+         a.I > 0 && a.Is > 0 && a.H > 0 && al16(a.down) && al16(a.sdown) && al16(a.hm) && al16(a.hs) && down_one_shape(a) != nullptr;
+}
+
+hipError_t launch_down_one(const SkinnyDownArgs& a, Act act, WFmt wf, hipStream_t s) {
+  if (!down_one_fits(a, act, wf)) return hipErrorInvalidValue;
+  if (!a.perm || !a.idx || !a.wpos || !a.y || !a.hm || !a.down || (a.Is > 0 && (!a.hs || !a.sdown)))
+    return hipErrorInvalidValue;
+  const int grid = (a.H + kDownOneWaves - 1) / kDownOneWaves;
+  hipLaunchKernelGGL(down_one_shape(a)->fn, dim3(grid), dim3(64 * kDownOneWaves), 0, s, a);
   return hipGetLastError();
 }
 

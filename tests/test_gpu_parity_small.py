@@ -448,3 +448,46 @@ def test_small_batch_routing_tables_match_the_general_permutation(cid, T):
     check_route(spec, idx_h, w.cpu().numpy(), L, x)
     st = check_forward(spec, y_to_f64(y), idx_h, L, x)
     log(f"  ok: bit-identical, max rel err {st['max_rel']:.3e}")
+
+
+@pytest.mark.parametrize("cid", [2, 3, "wide"])
+@pytest.mark.parametrize("pattern", ["one-invalid", "out-of-range", "duplicate", "none-valid"])
+def test_one_token_down_with_irregular_picks(cid, pattern):
+    """One token through the expert stage with picks the router never makes: a slot
+    marked invalid (-1), an index past E, one expert in two slots, no valid slot at all.
+    With one token the down launch also forms the weighted sum, reading the expert of
+    each position through the permutation; every valid slot is one term."""
+    import mixture_experts_layer_03_amd as moe
+    if cid == "wide":
+        if "wide" not in _CACHE:
+            L = synth.make_layer(WIDE_LITE)
+            _CACHE["wide"] = (WIDE_LITE, L, device_weights(L))
+        spec, L, W = _CACHE["wide"]
+    else:
+        spec, L, W = layer(cid)
+    x, xd = xs(spec, 1)
+    _, d = om.forward(x, L, oracle_cfg(spec))
+    idx = d["idx"].astype(np.int32).copy()
+    wt = d["w"].astype(np.float32).copy()
+    if pattern == "one-invalid":
+        idx[0, 1] = -1
+    elif pattern == "out-of-range":
+        idx[0, 0] = spec.num_experts + 2
+    elif pattern == "duplicate":
+        idx[0, 2] = idx[0, 4]
+        wt[0, 2] = 0.375
+    else:
+        idx[0, :] = -1
+    log(f"one-token experts cfg{cid} {spec.name} picks {pattern}: {idx[0].tolist()}")
+    y = moe.experts(xd, W, torch.from_numpy(idx).cuda(), torch.from_numpy(wt).cuda(), moe_cfg(spec, "decode"))
+    torch.cuda.synchronize()
+    X = om.to_f64(x)
+    ref = om.swiglu_mlp(X, om.to_f64(L["shared_gate"]), om.to_f64(L["shared_up"]), om.to_f64(L["shared_down"]))
+    for j in range(spec.top_k):
+        e = idx[0, j]
+        if 0 <= e < spec.num_experts:
+            ref = ref + wt[0, j] * om.swiglu_mlp(X, om.to_f64(L["gate"][e]), om.to_f64(L["up"][e]),
+                                                 om.to_f64(L["down"][e]))
+    rel = np.abs(y_to_f64(y) - ref).max() / np.abs(ref).max()
+    log(f"  max rel err {rel:.3e}")
+    assert rel <= 2e-2, rel
