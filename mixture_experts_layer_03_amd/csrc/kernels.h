@@ -89,15 +89,22 @@ struct SkinnyUpArgs {
   int part;                // items: 0 routed and shared, 1 routed only, 2 shared only (reads no routing)
   int dense;               // 1: the dense MLP (shared items only, its own split rule)
   int shared_first;        // ring kernels: the shared expert's items before the routed ones
-  // One token (T = 1), ring kernels, every item in the first round of blocks: each block
-  // routes the token itself from the router's partial logits (ta) instead of reading
-  // a permutation, and block 0 also stores the routing and permutation tables (ta.idx,
-  // ta.w and everything pa names) for the stages after it.
+  // One token (T = 1): each block routes the token itself from the router's partial
+  // logits (ta) instead of reading a permutation, and block 0 also stores the routing
+  // and permutation tables (ta.idx, ta.w and everything pa names) for the stages after
+  // it.  Taken by the one-token kernel (bf16 weights, up_one_fits) and by the u8 / u4
+  // ring kernels where every item is in the first round of blocks (skinny_up_can_route).
   int fused_route;
   TopkArgs ta;
   PermuteArgs pa;
+  const int32_t* idx;      // [T, k] routing (one-token kernel without fused_route: the expert
+                           // of position p is idx[perm[p]])
 };
 hipError_t launch_skinny_up(const SkinnyUpArgs& a, Act act, WFmt wf, int ncu, hipStream_t s);
+// whether the one-token gate/up kernel takes these arguments (bf16 weights, the whole
+// layer); it routes the token itself when fused_route is set, for any expert count up
+// to 512 and any number of blocks, so skinny_up_can_route does not apply to it
+bool up_one_fits(const SkinnyUpArgs& a, Act act, WFmt wf);
 // whether a gate/up launch with these arguments (fused_route aside) can route its one
 // token itself: one token, the whole layer, a ring kernel, every item in one round
 bool skinny_up_can_route(const SkinnyUpArgs& a, Act act, WFmt wf, int ncu);

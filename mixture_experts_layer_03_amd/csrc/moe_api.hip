@@ -486,8 +486,9 @@ moe_status run_experts(const moe_config& c, const Plan& p, int64_t T, const void
     u.E = E;
     u.part = shared_join ? 1 : 0;
     u.shared_first = T <= kSharedFirstMaxT;
+    u.idx = idx;
     if (route_ta) {
-      if (skinny_up_can_route(u, act, wf, ncu)) {
+      if (up_one_fits(u, act, wf) || skinny_up_can_route(u, act, wf, ncu)) {
         u.fused_route = 1;
         u.ta = *route_ta;
         u.pa = *route_pa;

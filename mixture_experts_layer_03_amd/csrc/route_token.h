@@ -24,8 +24,9 @@ constexpr float kNegInf = -__builtin_huge_valf();
 // experts, so a row of logits is read with contiguous per-lane runs.
 // Routes token t with one wavefront (all 64 lanes active).
 // (lds_idx, lds_w: optional copies of the token's k expert indices and weights in LDS,
-// at [t * k + j]; store = false leaves a.idx and a.w alone)
-template <int EPL>
+// at [t * k + j]; store = false leaves a.idx and a.w alone; MAXF: partial logits a lane
+// loads per batch, fewer registers for more round trips)
+template <int EPL, int MAXF = 64>
 __device__ void route_token(const TopkArgs& a, int t, int* lds_idx = nullptr, float* lds_w = nullptr, bool store = true) {
   const int lane = lane_id();
   const int E = a.E;
@@ -39,7 +40,8 @@ __device__ void route_token(const TopkArgs& a, int t, int* lds_idx = nullptr, fl
   }
   // both biases and the P partial logits are loaded together, PB partials per batch:
   // one memory round trip (a token's routing is a chain of dependent steps; the router's
-  // split keeps P * EPL <= 64, so one batch of PB = 64 / EPL, at most 16, covers it)
+  // split keeps P * EPL <= 64, so with MAXF = 64 one batch of PB = 64 / EPL, at most 16,
+  // covers it)
   float rb[EPL], eb[EPL];
 #pragma unroll
   for (int i = 0; i < EPL; ++i) {
@@ -47,7 +49,7 @@ __device__ void route_token(const TopkArgs& a, int t, int* lds_idx = nullptr, fl
     eb[i] = (valid[i] && a.use_ebias) ? a.expert_bias[lane * EPL + i] : 0.f;
   }
   const float* row = a.logits + static_cast<int64_t>(t) * E + lane * EPL;
-  constexpr int PB = EPL >= 4 ? 64 / EPL : 16;
+  constexpr int PB = EPL >= 4 ? MAXF / EPL : 16;
   if (EPL % 4 == 0 && (E % 4) == 0 && lane * EPL + EPL <= E) {
     for (int q0 = 0; q0 < a.P; q0 += PB) {
       float4 v[PB][EPL / 4 > 0 ? EPL / 4 : 1];

@@ -975,6 +975,116 @@ __global__ __launch_bounds__(256) void k_stream_down(SkinnyDownArgs a) {
   }
 }
 
+// sum of eight bf16 products (two per step, fp32 accumulation) added to c
+__device__ __forceinline__ float dot8_bf16(const uint4& a, const uint4& b, float c) {
+  c = __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2, a.x), __builtin_bit_cast(bf16x2, b.x), c, false);
+  c = __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2, a.y), __builtin_bit_cast(bf16x2, b.y), c, false);
+  c = __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2, a.z), __builtin_bit_cast(bf16x2, b.z), c, false);
+  c = __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2, a.w), __builtin_bit_cast(bf16x2, b.w), c, false);
+  return c;
+}
+
+// ---------------------------------------- one token: gate/up, with or without routing
+// With one token, column n of an expert's gated unit is silu(g_n . x) * (u_n . x): two
+// dot products over H [Bailing MoE expert MLP: SwiGLU].  A wavefront takes one column at
+// a time: it issues every 16-byte load of both rows (H / 512 per lane each) before using
+// the first, and reduces the two sums across its lanes; each lane keeps its slice of x
+// in registers (the same positions of every row).  The grid is sized so that every
+// block is resident at once.  Waves 1 .. NW-1 of a block stream its share of the shared
+// expert's columns while wave 0 finds the expert of each position: with FEPL > 0 it
+// routes the token from the router's partial logits (route_token; block 0 also stores
+// the routing and every table the permutation would build), with FEPL == 0 it reads
+// them through the caller's permutation.  Then all waves stream the block's share of
+// the selected experts' columns.  Lanes past the end of a row load its last vector
+// again (same line) and add nothing, so no branch splits the loads.
+constexpr int kUpOneWaves = 8;
+
+template <int NLH, int FEPL>
+__global__ __launch_bounds__(64 * kUpOneWaves, 4) void k_up_one(SkinnyUpArgs a) {
+  constexpr int NW = kUpOneWaves;
+  __shared__ int s_slot_e[kMaxTopK], s_pos_e[kMaxTopK], s_kv;
+  __shared__ float s_w[kMaxTopK];
+  const int lane = lane_id(), w = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  const int nvh = a.H / 8, nb = static_cast<int>(gridDim.x), b = static_cast<int>(blockIdx.x);
+  // this lane's vectors of a row (byte offsets, clamped to the row); rows are addressed
+  // as a wave-uniform base (scalar registers) plus these offsets
+  uint32_t vo[NLH];
+#pragma unroll
+  for (int i = 0; i < NLH; ++i) vo[i] = 16u * static_cast<uint32_t>(min(lane + 64 * i, nvh - 1));
+  // x in registers, loaded at once; with H = 4096 wave 0 loads it after routing (not
+  // live across the routing, the launch keeps two blocks per CU)
+  uint4 xv[NLH];
+  auto load_x = [&]() {
+    const char* xb = uniform_ptr(a.x);
+#pragma unroll
+    for (int i = 0; i < NLH; ++i) xv[i] = ld16(xb + vo[i]);
+  };
+  auto column = [&](const uint16_t* grow, const uint16_t* urow) {
+    const char* gb = uniform_ptr(grow);
+    const char* ub = uniform_ptr(urow);
+    uint4 gv[NLH], uv[NLH];
+#pragma unroll
+    for (int i = 0; i < NLH; ++i) gv[i] = ld16(gb + vo[i]);
+#pragma unroll
+    for (int i = 0; i < NLH; ++i) uv[i] = ld16(ub + vo[i]);
+    float g = 0.f, u = 0.f;
+#pragma unroll
+    for (int i = 0; i < NLH; ++i) {
+      const bool in = lane + 64 * i < nvh;
+      const float tg = dot8_bf16(gv[i], xv[i], 0.f), tu = dot8_bf16(uv[i], xv[i], 0.f);
+      g += in ? tg : 0.f;
+      u += in ? tu : 0.f;
+    }
+    return silu(wave_sum(g)) * wave_sum(u);
+  };
+  if (NLH < 8 || w > 0) load_x();
+  if (w > 0 && a.Is > 0) {
+    const int s0 = static_cast<int>(static_cast<int64_t>(b) * a.Is / nb);
+    const int s1 = static_cast<int>(static_cast<int64_t>(b + 1) * a.Is / nb);
+    const uint16_t* sg = static_cast<const uint16_t*>(a.sgate);
+    const uint16_t* su = static_cast<const uint16_t*>(a.sup);
+    for (int n = s0 + w - 1; n < s1; n += NW - 1) {
+      const int64_t ro = static_cast<int64_t>(n) * a.H;
+      const float h = column(sg + ro, su + ro);
+      if (lane == 0) static_cast<uint16_t*>(a.hs)[n] = f32_to_bf16(h);
+    }
+  }
+  if (w == 0) {
+    if constexpr (FEPL > 0) {
+      const bool publish = b == 0;
+      // 512 experts: the partial logits in two batches (the registers of one batch would
+      // cost this launch half its blocks per CU)
+      route_token<FEPL, FEPL >= 8 ? 32 : 64>(a.ta, 0, s_slot_e, s_w, publish);
+      one_token_tables(a.pa, a.k, a.E, s_slot_e, s_w, s_pos_e, &s_kv, publish);
+    } else {
+      // position p holds slot perm[p] (the pick j, one token); valid picks fill 0 .. kv-1
+      const int jl = min(lane, a.k - 1);
+      const int pslot = a.perm[jl];
+      const int pidx = a.idx[jl];
+      const int kv = __popcll(__ballot(lane < a.k && pidx >= 0 && pidx < a.E));
+      const int pe = __shfl(pidx, min(max(pslot, 0), a.k - 1));
+      if (lane < kv) s_pos_e[lane] = pe;
+      if (lane == 0) s_kv = kv;
+    }
+  }
+  __syncthreads();
+  if (NLH >= 8 && w == 0) load_x();
+  const int kv = s_kv;
+  if constexpr (FEPL > 0)
+    if (b == 0) one_token_counts(a.pa, a.E, s_pos_e, kv, threadIdx.x, blockDim.x);
+  const int64_t nr = static_cast<int64_t>(kv) * a.I;
+  const int r0 = static_cast<int>(static_cast<int64_t>(b) * nr / nb);
+  const int r1 = static_cast<int>(static_cast<int64_t>(b + 1) * nr / nb);
+  const uint16_t* gt = static_cast<const uint16_t*>(a.gate);
+  const uint16_t* ut = static_cast<const uint16_t*>(a.up);
+  for (int c = r0 + w; c < r1; c += NW) {
+    const int p = c / a.I, n = c - p * a.I;
+    const int64_t ro = (static_cast<int64_t>(s_pos_e[p]) * a.I + n) * a.H;
+    const float h = column(gt + ro, ut + ro);
+    if (lane == 0) static_cast<uint16_t*>(a.hm)[static_cast<int64_t>(p) * a.I + n] = f32_to_bf16(h);
+  }
+}
+
 // ------------------------------------------ one token: down and combine in one launch
 // With one token, element h of the layer output is a single dot product: the shared
 // expert's down row h against its activation row, plus each selected expert's down row
@@ -989,14 +1099,6 @@ __global__ __launch_bounds__(256) void k_stream_down(SkinnyDownArgs a) {
 // NLS / NLR: 16-byte loads per lane for a shared / routed row (Is / 512 and I / 512
 // rounded up); K: top-k (position p of the one-token permutation holds a pick; with
 // fewer valid picks than K the last valid row is loaded again and not added).
-__device__ __forceinline__ float dot8_bf16(const uint4& a, const uint4& b, float c) {
-  c = __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2, a.x), __builtin_bit_cast(bf16x2, b.x), c, false);
-  c = __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2, a.y), __builtin_bit_cast(bf16x2, b.y), c, false);
-  c = __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2, a.z), __builtin_bit_cast(bf16x2, b.z), c, false);
-  c = __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2, a.w), __builtin_bit_cast(bf16x2, b.w), c, false);
-  return c;
-}
-
 constexpr int kDownOneWaves = 8;
 
 template <int NLS, int NLR, int K>
@@ -1756,7 +1858,8 @@ static int64_t up_ring_items(const SkinnyUpArgs& a, int ncu, bool& split) {
 // is paid once per CU instead of once per round.  Measured at one token: Ling-3.0-tiny
 // (216 blocks) 28.6 -> 26.1 us, Ling-3.0-flash u4 (576 blocks, three per CU) 53.7 ->
 // 50.5 us; Ling-lite (704 blocks on 512 slots) no gain, Ling-2.6- and Ling-3.0-flash
-// bf16 / u8 (576 blocks, two per CU) 2.6 to 4.3 us slower.
+// bf16 / u8 (576 blocks, two per CU) 2.6 to 4.3 us slower.  (One token with bf16
+// weights now takes the one-token kernel, up_one_fits, before this rule is asked.)
 bool skinny_up_can_route(const SkinnyUpArgs& a, Act act, WFmt wf, int ncu) {
   if (a.T != 1 || a.part != 0 || a.dense || a.k > kMaxTopK || a.E > 512 || !up_uses_ring(a, act, wf)) return false;
   bool split;
@@ -1766,8 +1869,69 @@ bool skinny_up_can_route(const SkinnyUpArgs& a, Act act, WFmt wf, int ncu) {
   return split && blocks <= per_cu * ncu;
 }
 
+// k_up_one instances by row loads per lane (H / 512 rounded up: 1, 2, 4, 8) and
+// experts per lane of the routing (0: read the permutation; 1, 2, 4, 8)
+namespace {
+template <int NLH>
+void (*up_one_kernel(int fepl))(SkinnyUpArgs) {
+  switch (fepl) {
+    case 0: return k_up_one<NLH, 0>;
+    case 1: return k_up_one<NLH, 1>;
+    case 2: return k_up_one<NLH, 2>;
+    case 4: return k_up_one<NLH, 4>;
+    default: return k_up_one<NLH, 8>;
+  }
+}
+int up_one_nlh(int H) {
+  const int n = (H / 8 + 63) / 64;
+  return n <= 1 ? 1 : n <= 2 ? 2 : n <= 4 ? 4 : n <= 8 ? 8 : 0;
+}
+}  // namespace
+
+bool up_one_fits(const SkinnyUpArgs& a, Act act, WFmt wf) {
+  auto al16 = [](const void* q) { return reinterpret_cast<uintptr_t>(q) % 16 == 0; };
+  return a.T == 1 && a.part == 0 && !a.dense && act == Act::BF16 && wf == WFmt::BF16 && a.H % 8 == 0 &&
+         a.H > 0 && a.I > 0 && up_one_nlh(a.H) > 0 && a.k <= kMaxTopK && a.E <= 512 && al16(a.x) &&
+         al16(a.gate) && al16(a.up) && (a.Is == 0 || (al16(a.sgate) && al16(a.sup)));
+}
+
+static hipError_t launch_up_one(const SkinnyUpArgs& a, int ncu, hipStream_t s) {
+  if (a.fused_route) {
+    if (!a.ta.logits || !a.ta.idx || !a.ta.w || a.ta.E != a.E || a.ta.k != a.k || a.ta.T != 1 || !a.pa.perm ||
+        !a.pa.slot_pos || !a.pa.wpos || !a.pa.chunks || !a.pa.tiles || !a.pa.active || !a.pa.meta ||
+        !a.pa.counts || !a.pa.offsets)
+      return hipErrorInvalidValue;
+  } else if (!a.perm || !a.idx) {
+    return hipErrorInvalidValue;
+  }
+  if (!a.hm || (a.Is > 0 && !a.hs)) return hipErrorInvalidValue;
+  const int epl = (a.E + 63) / 64;
+  const int fepl = !a.fused_route ? 0 : epl <= 1 ? 1 : epl <= 2 ? 2 : epl <= 4 ? 4 : 8;
+  void (*k)(SkinnyUpArgs) = nullptr;
+  switch (up_one_nlh(a.H)) {
+    case 1: k = up_one_kernel<1>(fepl); break;
+    case 2: k = up_one_kernel<2>(fepl); break;
+    case 4: k = up_one_kernel<4>(fepl); break;
+    default: k = up_one_kernel<8>(fepl); break;
+  }
+  // every block resident at once (each finds the routing once), at most two per CU
+  // (Ling-lite at one token: 20.3 us with two, 20.8 us with three); at least one block
+  int per_cu = 0;
+  if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, k, 64 * kUpOneWaves, 0) != hipSuccess || per_cu < 1)
+    per_cu = 1;
+  if (per_cu > 2) per_cu = 2;
+  const int64_t cols = static_cast<int64_t>(a.Is) + static_cast<int64_t>(a.k) * a.I;
+  int64_t grid = static_cast<int64_t>(per_cu) * ncu;
+  const int64_t need = (cols + kUpOneWaves - 1) / kUpOneWaves;
+  if (grid > need) grid = need;
+  if (grid < 1) grid = 1;
+  hipLaunchKernelGGL(k, dim3(static_cast<unsigned>(grid)), dim3(64 * kUpOneWaves), 0, s, a);
+  return hipGetLastError();
+}
+
 hipError_t launch_skinny_up(const SkinnyUpArgs& a, Act act, WFmt wf, int ncu, hipStream_t s) {
   if (a.T <= 0) return hipSuccess;
+  if (up_one_fits(a, act, wf)) return launch_up_one(a, ncu, s);
   // one-token routing inside the launch: only where skinny_up_can_route allows it, with
   // the shared-first order it assumes and every table it stores
   if (a.fused_route &&
