@@ -984,6 +984,22 @@ __device__ __forceinline__ float dot8_bf16(const uint4& a, const uint4& b, float
   return c;
 }
 
+// sum over 16 u8 codes c_j of (c_j - z) * a_j, a_j the bf16 values in a0 (j < 8) and a1
+// (each code minus the zero point is exact in fp32, and so is its product with a_j)
+__device__ __forceinline__ float dot16_u8(const uint4& c, const uint4& a0, const uint4& a1, float z) {
+  const uint32_t cw[4] = {c.x, c.y, c.z, c.w};
+  const uint32_t aw[8] = {a0.x, a0.y, a0.z, a0.w, a1.x, a1.y, a1.z, a1.w};
+  float acc = 0.f;
+#pragma unroll
+  for (int j = 0; j < 16; ++j) {
+    const float cj = static_cast<float>((cw[j >> 2] >> (8 * (j & 3))) & 0xffu);
+    const uint32_t w2 = aw[j >> 1];
+    const float aj = __uint_as_float((j & 1) ? (w2 & 0xffff0000u) : (w2 << 16));
+    acc = fmaf(cj - z, aj, acc);
+  }
+  return acc;
+}
+
 // ---------------------------------------- one token: gate/up, with or without routing
 // With one token, column n of an expert's gated unit is silu(g_n . x) * (u_n . x): two
 // dot products over H [Bailing MoE expert MLP: SwiGLU].  A wavefront takes one column at
@@ -998,6 +1014,32 @@ __device__ __forceinline__ float dot8_bf16(const uint4& a, const uint4& b, float
 // the selected experts' columns.  Lanes past the end of a row load its last vector
 // again (same line) and add nothing, so no branch splits the loads.
 constexpr int kUpOneWaves = 8;
+
+// The experts by position of a one-token launch, found by one wavefront into LDS
+// (s_pos_e[p], valid count *s_kv): FEPL > 0 routes the token from the router's partial
+// logits (route_token, with `publish` storing the routing and every table the
+// permutation would build); FEPL == 0 reads them through the caller's permutation
+// (position p holds slot perm[p], the pick j of the one token; valid picks fill
+// positions 0 .. kv - 1).
+template <int FEPL>
+__device__ __forceinline__ void up_one_picks(const SkinnyUpArgs& a, bool publish, int* s_slot_e, float* s_w,
+                                             int* s_pos_e, int* s_kv) {
+  if constexpr (FEPL > 0) {
+    // 512 experts: the partial logits in two batches (the registers of one batch would
+    // cost the launch half its blocks per CU)
+    route_token<FEPL, FEPL >= 8 ? 32 : 64>(a.ta, 0, s_slot_e, s_w, publish);
+    one_token_tables(a.pa, a.k, a.E, s_slot_e, s_w, s_pos_e, s_kv, publish);
+  } else {
+    const int lane = lane_id();
+    const int jl = min(lane, a.k - 1);
+    const int pslot = a.perm[jl];
+    const int pidx = a.idx[jl];
+    const int kv = __popcll(__ballot(lane < a.k && pidx >= 0 && pidx < a.E));
+    const int pe = __shfl(pidx, min(max(pslot, 0), a.k - 1));
+    if (lane < kv) s_pos_e[lane] = pe;
+    if (lane == 0) *s_kv = kv;
+  }
+}
 
 template <int NLH, int FEPL>
 __global__ __launch_bounds__(64 * kUpOneWaves, 4) void k_up_one(SkinnyUpArgs a) {
@@ -1049,24 +1091,7 @@ __global__ __launch_bounds__(64 * kUpOneWaves, 4) void k_up_one(SkinnyUpArgs a) 
       if (lane == 0) static_cast<uint16_t*>(a.hs)[n] = f32_to_bf16(h);
     }
   }
-  if (w == 0) {
-    if constexpr (FEPL > 0) {
-      const bool publish = b == 0;
-      // 512 experts: the partial logits in two batches (the registers of one batch would
-      // cost this launch half its blocks per CU)
-      route_token<FEPL, FEPL >= 8 ? 32 : 64>(a.ta, 0, s_slot_e, s_w, publish);
-      one_token_tables(a.pa, a.k, a.E, s_slot_e, s_w, s_pos_e, &s_kv, publish);
-    } else {
-      // position p holds slot perm[p] (the pick j, one token); valid picks fill 0 .. kv-1
-      const int jl = min(lane, a.k - 1);
-      const int pslot = a.perm[jl];
-      const int pidx = a.idx[jl];
-      const int kv = __popcll(__ballot(lane < a.k && pidx >= 0 && pidx < a.E));
-      const int pe = __shfl(pidx, min(max(pslot, 0), a.k - 1));
-      if (lane < kv) s_pos_e[lane] = pe;
-      if (lane == 0) s_kv = kv;
-    }
-  }
+  if (w == 0) up_one_picks<FEPL>(a, b == 0, s_slot_e, s_w, s_pos_e, &s_kv);
   __syncthreads();
   if (NLH >= 8 && w == 0) load_x();
   const int kv = s_kv;
@@ -1081,6 +1106,122 @@ __global__ __launch_bounds__(64 * kUpOneWaves, 4) void k_up_one(SkinnyUpArgs a) 
     const int p = c / a.I, n = c - p * a.I;
     const int64_t ro = (static_cast<int64_t>(s_pos_e[p]) * a.I + n) * a.H;
     const float h = column(gt + ro, ut + ro);
+    if (lane == 0) static_cast<uint16_t*>(a.hm)[static_cast<int64_t>(p) * a.I + n] = f32_to_bf16(h);
+  }
+}
+
+// The same with u8 routed experts (codes [E, I, H], fp16 scale and zero point per 64
+// codes; the shared expert stays bf16).  A lane takes units of 16 elements, u = lane +
+// 64 i (i < NU): one 16-byte load of codes, or two of bf16, per unit; the 64 groups of
+// a row (H <= 4096) come in with one scale and one zero-point load per lane and reach
+// the lanes that use them across the wavefront.  Per unit, sum_j (c_j - z) x_j is
+// formed as sum_j c_j x_j - z sum_j x_j, the unit's sum of x taken once per launch.
+template <int NU, int FEPL>
+__global__ __launch_bounds__(64 * kUpOneWaves, 4) void k_up_one_q8(SkinnyUpArgs a) {
+  constexpr int NW = kUpOneWaves;
+  __shared__ int s_slot_e[kMaxTopK], s_pos_e[kMaxTopK], s_kv;
+  __shared__ float s_w[kMaxTopK];
+  const int lane = lane_id(), w = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  const int nu = a.H / 16, ng = a.H / 64, nb = static_cast<int>(gridDim.x), b = static_cast<int>(blockIdx.x);
+  int uc[NU];  // this lane's units (clamped to the row)
+#pragma unroll
+  for (int i = 0; i < NU; ++i) uc[i] = min(lane + 64 * i, nu - 1);
+  uint4 xv[2 * NU];
+  float sx[NU];
+  auto load_x = [&]() {
+    const char* xb = uniform_ptr(a.x);
+#pragma unroll
+    for (int i = 0; i < NU; ++i) {
+      xv[2 * i] = ld16(xb + 32 * uc[i]);
+      xv[2 * i + 1] = ld16(xb + 32 * uc[i] + 16);
+    }
+#pragma unroll
+    for (int i = 0; i < NU; ++i) {
+      const uint32_t v[8] = {xv[2 * i].x, xv[2 * i].y, xv[2 * i].z, xv[2 * i].w,
+                             xv[2 * i + 1].x, xv[2 * i + 1].y, xv[2 * i + 1].z, xv[2 * i + 1].w};
+      float t = 0.f;
+#pragma unroll
+      for (int j = 0; j < 8; ++j) t += __uint_as_float(v[j] << 16) + __uint_as_float(v[j] & 0xffff0000u);
+      sx[i] = t;
+    }
+  };
+  // a bf16 column (the shared expert)
+  auto column16 = [&](const uint16_t* grow, const uint16_t* urow) {
+    const char* gb = uniform_ptr(grow);
+    const char* ub = uniform_ptr(urow);
+    uint4 gv[2 * NU], uv[2 * NU];
+#pragma unroll
+    for (int i = 0; i < NU; ++i) {
+      gv[2 * i] = ld16(gb + 32 * uc[i]);
+      gv[2 * i + 1] = ld16(gb + 32 * uc[i] + 16);
+    }
+#pragma unroll
+    for (int i = 0; i < NU; ++i) {
+      uv[2 * i] = ld16(ub + 32 * uc[i]);
+      uv[2 * i + 1] = ld16(ub + 32 * uc[i] + 16);
+    }
+    float g = 0.f, u = 0.f;
+#pragma unroll
+    for (int i = 0; i < NU; ++i) {
+      const bool in = lane + 64 * i < nu;
+      const float tg = dot8_bf16(gv[2 * i + 1], xv[2 * i + 1], dot8_bf16(gv[2 * i], xv[2 * i], 0.f));
+      const float tu = dot8_bf16(uv[2 * i + 1], xv[2 * i + 1], dot8_bf16(uv[2 * i], xv[2 * i], 0.f));
+      g += in ? tg : 0.f;
+      u += in ? tu : 0.f;
+    }
+    return silu(wave_sum(g)) * wave_sum(u);
+  };
+  // a u8 column: rows r of gate and up (codes, and their group parameters)
+  auto column8 = [&](int64_t r) {
+    const char* gb = uniform_ptr(static_cast<const uint8_t*>(a.gate) + r * a.H);
+    const char* ub = uniform_ptr(static_cast<const uint8_t*>(a.up) + r * a.H);
+    const int gl = min(lane, ng - 1);
+    const int64_t pr = r * ng + gl;
+    uint4 gv[NU], uv[NU];
+#pragma unroll
+    for (int i = 0; i < NU; ++i) gv[i] = ld16(gb + 16 * uc[i]);
+#pragma unroll
+    for (int i = 0; i < NU; ++i) uv[i] = ld16(ub + 16 * uc[i]);
+    const float gsc = f16_to_f32(a.gate_s[pr]), gzp = f16_to_f32(a.gate_z[pr]);
+    const float usc = f16_to_f32(a.up_s[pr]), uzp = f16_to_f32(a.up_z[pr]);
+    float g = 0.f, u = 0.f;
+#pragma unroll
+    for (int i = 0; i < NU; ++i) {
+      const bool in = lane + 64 * i < nu;
+      const int src = uc[i] >> 2;  // the lane holding this unit's group
+      const float gs_ = __shfl(gsc, src), gz_ = __shfl(gzp, src);
+      const float us_ = __shfl(usc, src), uz_ = __shfl(uzp, src);
+      const float tg = gs_ * (dot16_u8(gv[i], xv[2 * i], xv[2 * i + 1], 0.f) - gz_ * sx[i]);
+      const float tu = us_ * (dot16_u8(uv[i], xv[2 * i], xv[2 * i + 1], 0.f) - uz_ * sx[i]);
+      g += in ? tg : 0.f;
+      u += in ? tu : 0.f;
+    }
+    return silu(wave_sum(g)) * wave_sum(u);
+  };
+  if (NU < 4 || w > 0) load_x();
+  if (w > 0 && a.Is > 0) {
+    const int s0 = static_cast<int>(static_cast<int64_t>(b) * a.Is / nb);
+    const int s1 = static_cast<int>(static_cast<int64_t>(b + 1) * a.Is / nb);
+    const uint16_t* sg = static_cast<const uint16_t*>(a.sgate);
+    const uint16_t* su = static_cast<const uint16_t*>(a.sup);
+    for (int n = s0 + w - 1; n < s1; n += NW - 1) {
+      const int64_t ro = static_cast<int64_t>(n) * a.H;
+      const float h = column16(sg + ro, su + ro);
+      if (lane == 0) static_cast<uint16_t*>(a.hs)[n] = f32_to_bf16(h);
+    }
+  }
+  if (w == 0) up_one_picks<FEPL>(a, b == 0, s_slot_e, s_w, s_pos_e, &s_kv);
+  __syncthreads();
+  if (NU >= 4 && w == 0) load_x();
+  const int kv = s_kv;
+  if constexpr (FEPL > 0)
+    if (b == 0) one_token_counts(a.pa, a.E, s_pos_e, kv, threadIdx.x, blockDim.x);
+  const int64_t nr = static_cast<int64_t>(kv) * a.I;
+  const int r0 = static_cast<int>(static_cast<int64_t>(b) * nr / nb);
+  const int r1 = static_cast<int>(static_cast<int64_t>(b + 1) * nr / nb);
+  for (int c = r0 + w; c < r1; c += NW) {
+    const int p = c / a.I, n = c - p * a.I;
+    const float h = column8(static_cast<int64_t>(s_pos_e[p]) * a.I + n);
     if (lane == 0) static_cast<uint16_t*>(a.hm)[static_cast<int64_t>(p) * a.I + n] = f32_to_bf16(h);
   }
 }
@@ -1101,10 +1242,11 @@ __global__ __launch_bounds__(64 * kUpOneWaves, 4) void k_up_one(SkinnyUpArgs a) 
 // fewer valid picks than K the last valid row is loaded again and not added).
 constexpr int kDownOneWaves = 8;
 
-template <int NLS, int NLR, int K>
+template <int NLS, int NLR, int K, bool Q8>
 __global__ __launch_bounds__(64 * kDownOneWaves) void k_down_one(SkinnyDownArgs a) {
   constexpr int NW = kDownOneWaves, NT = 64 * NW;
-  constexpr int NST = ((NLS + K * NLR) * 64 + NT - 1) / NT;  // staging loads per thread
+  constexpr int EPV = Q8 ? 16 : 8;  // routed-row elements per 16-byte vector
+  constexpr int NST = ((NLS + K * NLR * EPV / 8) * 64 + NT - 1) / NT;  // staging loads per thread
   __shared__ __attribute__((aligned(16))) uint16_t act[NST * NT * 8];
   // Every load is unconditional (lanes past a row's end load its last vector again, in
   // the same line, and add nothing), so no branch splits the loads and each use waits
@@ -1112,7 +1254,7 @@ __global__ __launch_bounds__(64 * kDownOneWaves) void k_down_one(SkinnyDownArgs 
   const int lane = lane_id(), w = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   const int h = static_cast<int>(blockIdx.x) * NW + w;
   const int hrow = min(h, a.H - 1);
-  const int nvs = a.Is / 8, nvr = a.I / 8, nst = nvs + K * nvr;
+  const int nvs = a.Is / 8, nvr = a.I / EPV, nst = nvs + K * (a.I / 8);
   // lane p: position p's slot (the pick j, one token) and weight; lane j: pick j's expert
   const int jl = min(lane, K - 1);
   const int pslot = a.perm[jl];
@@ -1137,12 +1279,22 @@ __global__ __launch_bounds__(64 * kDownOneWaves) void k_down_one(SkinnyDownArgs 
   const int npos = __popcll(__ballot(lane < K && pidx >= 0 && pidx < a.E));
   const int pe = __shfl(pidx, min(max(pslot, 0), K - 1));
   uint4 wr[K][NLR];
+  uint16_t gs[Q8 ? K : 1][NLR], gz[Q8 ? K : 1][NLR];  // u8: the group's fp16 scale, zero point
 #pragma unroll
   for (int p = 0; p < K; ++p) {
     const int e = min(max(__builtin_amdgcn_readlane(pe, min(p, max(npos - 1, 0))), 0), a.E - 1);
-    const uint16_t* row = static_cast<const uint16_t*>(a.down) + (static_cast<int64_t>(e) * a.H + hrow) * a.I;
+    const int64_t r = static_cast<int64_t>(e) * a.H + hrow;
 #pragma unroll
-    for (int i = 0; i < NLR; ++i) wr[p][i] = ld16(row + 8 * min(lane + 64 * i, nvr - 1));
+    for (int i = 0; i < NLR; ++i) {
+      const int vc = min(lane + 64 * i, nvr - 1);
+      if constexpr (Q8) {
+        wr[p][i] = ld16(static_cast<const uint8_t*>(a.down) + r * a.I + 16 * vc);
+        gs[p][i] = a.down_s[r * (a.I / 64) + vc / 4];
+        gz[p][i] = a.down_z[r * (a.I / 64) + vc / 4];
+      } else {
+        wr[p][i] = ld16(static_cast<const uint16_t*>(a.down) + r * a.I + 8 * vc);
+      }
+    }
   }
 #pragma unroll
   for (int i = 0; i < NST; ++i) {
@@ -1160,10 +1312,18 @@ __global__ __launch_bounds__(64 * kDownOneWaves) void k_down_one(SkinnyDownArgs 
 #pragma unroll
   for (int p = 0; p < K; ++p) {
     float sp = 0.f;
+    const uint16_t* ap = act + 8 * nvs + p * a.I;  // position p's activation row
 #pragma unroll
     for (int i = 0; i < NLR; ++i) {
       const int v = lane + 64 * i, vc = min(v, nvr - 1);
-      const float t = dot8_bf16(wr[p][i], *reinterpret_cast<const uint4*>(act + 8 * (nvs + p * nvr + vc)), 0.f);
+      float t;
+      if constexpr (Q8) {
+        const uint4 a0 = *reinterpret_cast<const uint4*>(ap + 16 * vc);
+        const uint4 a1 = *reinterpret_cast<const uint4*>(ap + 16 * vc + 8);
+        t = f16_to_f32(gs[p][i]) * dot16_u8(wr[p][i], a0, a1, f16_to_f32(gz[p][i]));
+      } else {
+        t = dot8_bf16(wr[p][i], *reinterpret_cast<const uint4*>(ap + 8 * vc), 0.f);
+      }
       sp += v < nvr ? t : 0.f;
     }
     const float wgt = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(pw), p));
@@ -1888,14 +2048,29 @@ int up_one_nlh(int H) {
 }
 }  // namespace
 
-bool up_one_fits(const SkinnyUpArgs& a, Act act, WFmt wf) {
-  auto al16 = [](const void* q) { return reinterpret_cast<uintptr_t>(q) % 16 == 0; };
-  return a.T == 1 && a.part == 0 && !a.dense && act == Act::BF16 && wf == WFmt::BF16 && a.H % 8 == 0 &&
-         a.H > 0 && a.I > 0 && up_one_nlh(a.H) > 0 && a.k <= kMaxTopK && a.E <= 512 && al16(a.x) &&
-         al16(a.gate) && al16(a.up) && (a.Is == 0 || (al16(a.sgate) && al16(a.sup)));
+template <int NU>
+void (*up_one_q8_kernel(int fepl))(SkinnyUpArgs) {
+  switch (fepl) {
+    case 0: return k_up_one_q8<NU, 0>;
+    case 1: return k_up_one_q8<NU, 1>;
+    case 2: return k_up_one_q8<NU, 2>;
+    case 4: return k_up_one_q8<NU, 4>;
+    default: return k_up_one_q8<NU, 8>;
+  }
 }
 
-static hipError_t launch_up_one(const SkinnyUpArgs& a, int ncu, hipStream_t s) {
+bool up_one_fits(const SkinnyUpArgs& a, Act act, WFmt wf) {
+  auto al16 = [](const void* q) { return reinterpret_cast<uintptr_t>(q) % 16 == 0; };
+  const bool q8 = wf == WFmt::U8;
+  // u8: units of 16 elements, the row's groups one per lane (H <= 4096)
+  const bool shape = q8 ? a.H % 64 == 0 && a.H <= 4096 && a.gate_s && a.gate_z && a.up_s && a.up_z
+                        : a.H % 8 == 0 && up_one_nlh(a.H) > 0;
+  return a.T == 1 && a.part == 0 && !a.dense && act == Act::BF16 && (wf == WFmt::BF16 || q8) && shape &&
+         a.H > 0 && a.I > 0 && a.k <= kMaxTopK && a.E <= 512 && al16(a.x) && al16(a.gate) && al16(a.up) &&
+         (a.Is == 0 || (al16(a.sgate) && al16(a.sup)));
+}
+
+static hipError_t launch_up_one(const SkinnyUpArgs& a, WFmt wf, int ncu, hipStream_t s) {
   if (a.fused_route) {
     if (!a.ta.logits || !a.ta.idx || !a.ta.w || a.ta.E != a.E || a.ta.k != a.k || a.ta.T != 1 || !a.pa.perm ||
         !a.pa.slot_pos || !a.pa.wpos || !a.pa.chunks || !a.pa.tiles || !a.pa.active || !a.pa.meta ||
@@ -1908,11 +2083,16 @@ static hipError_t launch_up_one(const SkinnyUpArgs& a, int ncu, hipStream_t s) {
   const int epl = (a.E + 63) / 64;
   const int fepl = !a.fused_route ? 0 : epl <= 1 ? 1 : epl <= 2 ? 2 : epl <= 4 ? 4 : 8;
   void (*k)(SkinnyUpArgs) = nullptr;
-  switch (up_one_nlh(a.H)) {
-    case 1: k = up_one_kernel<1>(fepl); break;
-    case 2: k = up_one_kernel<2>(fepl); break;
-    case 4: k = up_one_kernel<4>(fepl); break;
-    default: k = up_one_kernel<8>(fepl); break;
+  if (wf == WFmt::U8) {
+    const int nu = (a.H / 16 + 63) / 64;
+    k = nu <= 1 ? up_one_q8_kernel<1>(fepl) : nu <= 2 ? up_one_q8_kernel<2>(fepl) : up_one_q8_kernel<4>(fepl);
+  } else {
+    switch (up_one_nlh(a.H)) {
+      case 1: k = up_one_kernel<1>(fepl); break;
+      case 2: k = up_one_kernel<2>(fepl); break;
+      case 4: k = up_one_kernel<4>(fepl); break;
+      default: k = up_one_kernel<8>(fepl); break;
+    }
   }
   // every block resident at once (each finds the routing once), at most two per CU
   // (Ling-lite at one token: 20.3 us with two, 20.8 us with three); at least one block
@@ -1931,7 +2111,7 @@ static hipError_t launch_up_one(const SkinnyUpArgs& a, int ncu, hipStream_t s) {
 
 hipError_t launch_skinny_up(const SkinnyUpArgs& a, Act act, WFmt wf, int ncu, hipStream_t s) {
   if (a.T <= 0) return hipSuccess;
-  if (up_one_fits(a, act, wf)) return launch_up_one(a, ncu, s);
+  if (up_one_fits(a, act, wf)) return launch_up_one(a, wf, ncu, s);
   // one-token routing inside the launch: only where skinny_up_can_route allows it, with
   // the shared-first order it assumes and every table it stores
   if (a.fused_route &&
@@ -2029,29 +2209,35 @@ hipError_t launch_skinny_down(const SkinnyDownArgs& a, Act act, WFmt wf, int ncu
   return hipGetLastError();
 }
 
-// instances of k_down_one: (NLS, NLR, K), smallest first per K
+// instances of k_down_one: (NLS, NLR, K, u8), smallest first per K and format
 namespace {
 struct DownOneShape {
   int nls, nlr, k;
+  bool q8;
   void (*fn)(SkinnyDownArgs);
 };
 const DownOneShape kDownOne[] = {
-    {1, 1, 8, k_down_one<1, 1, 8>},
-    {2, 2, 8, k_down_one<2, 2, 8>},
-    {6, 3, 6, k_down_one<6, 3, 6>},
+    {1, 1, 8, false, k_down_one<1, 1, 8, false>},
+    {2, 2, 8, false, k_down_one<2, 2, 8, false>},
+    {6, 3, 6, false, k_down_one<6, 3, 6, false>},
+    {1, 1, 8, true, k_down_one<1, 1, 8, true>},
+    {2, 1, 8, true, k_down_one<2, 1, 8, true>},
 };
-const DownOneShape* down_one_shape(const SkinnyDownArgs& a) {
-  const int nls = (a.Is / 8 + 63) / 64, nlr = (a.I / 8 + 63) / 64;
+const DownOneShape* down_one_shape(const SkinnyDownArgs& a, WFmt wf) {
+  const bool q8 = wf == WFmt::U8;
+  const int nls = (a.Is / 8 + 63) / 64, nlr = (a.I / (q8 ? 16 : 8) + 63) / 64;
   for (const DownOneShape& d : kDownOne)
-    if (d.k == a.k && nls <= d.nls && nlr <= d.nlr) return &d;
+    if (d.q8 == q8 && d.k == a.k && nls <= d.nls && nlr <= d.nlr) return &d;
   return nullptr;
 }
 }  // namespace
 
 bool down_one_fits(const SkinnyDownArgs& a, Act act, WFmt wf) {
   auto al16 = [](const void* q) { return reinterpret_cast<uintptr_t>(q) % 16 == 0; };
-  return a.T == 1 && a.part == 0 && act == Act::BF16 && wf == WFmt::BF16 && a.I % 8 == 0 && a.Is % 8 == 0 &&
-         a.I > 0 && a.Is > 0 && a.H > 0 && al16(a.down) && al16(a.sdown) && al16(a.hm) && al16(a.hs) && down_one_shape(a) != nullptr;
+  const bool q8 = wf == WFmt::U8;
+  return a.T == 1 && a.part == 0 && act == Act::BF16 && (wf == WFmt::BF16 || q8) && a.I % (q8 ? 64 : 8) == 0 &&
+         a.Is % 8 == 0 && a.I > 0 && a.Is > 0 && a.H > 0 && al16(a.down) && al16(a.sdown) && al16(a.hm) &&
+         al16(a.hs) && (!q8 || (a.down_s && a.down_z)) && down_one_shape(a, wf) != nullptr;
 }
 
 hipError_t launch_down_one(const SkinnyDownArgs& a, Act act, WFmt wf, hipStream_t s) {
@@ -2059,7 +2245,7 @@ hipError_t launch_down_one(const SkinnyDownArgs& a, Act act, WFmt wf, hipStream_
   if (!a.perm || !a.idx || !a.wpos || !a.y || !a.hm || !a.down || (a.Is > 0 && (!a.hs || !a.sdown)))
     return hipErrorInvalidValue;
   const int grid = (a.H + kDownOneWaves - 1) / kDownOneWaves;
-  hipLaunchKernelGGL(down_one_shape(a)->fn, dim3(grid), dim3(64 * kDownOneWaves), 0, s, a);
+  hipLaunchKernelGGL(down_one_shape(a, wf)->fn, dim3(grid), dim3(64 * kDownOneWaves), 0, s, a);
   return hipGetLastError();
 }
 

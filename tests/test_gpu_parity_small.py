@@ -450,13 +450,14 @@ def test_small_batch_routing_tables_match_the_general_permutation(cid, T):
     log(f"  ok: bit-identical, max rel err {st['max_rel']:.3e}")
 
 
-@pytest.mark.parametrize("cid", [2, 3, "wide"])
+@pytest.mark.parametrize("cid", [2, 3, 5, "wide"])
 @pytest.mark.parametrize("pattern", ["one-invalid", "out-of-range", "duplicate", "none-valid"])
 def test_one_token_down_with_irregular_picks(cid, pattern):
     """One token through the expert stage with picks the router never makes: a slot
     marked invalid (-1), an index past E, one expert in two slots, no valid slot at all.
     With one token the down launch also forms the weighted sum, reading the expert of
-    each position through the permutation; every valid slot is one term."""
+    each position through the permutation; every valid slot is one term (bf16 and u8
+    experts)."""
     import mixture_experts_layer_03_amd as moe
     if cid == "wide":
         if "wide" not in _CACHE:
@@ -486,8 +487,8 @@ def test_one_token_down_with_irregular_picks(cid, pattern):
     for j in range(spec.top_k):
         e = idx[0, j]
         if 0 <= e < spec.num_experts:
-            ref = ref + wt[0, j] * om.swiglu_mlp(X, om.to_f64(L["gate"][e]), om.to_f64(L["up"][e]),
-                                                 om.to_f64(L["down"][e]))
+            ref = ref + wt[0, j] * om.swiglu_mlp(X, om.expert_matrix(L, "gate", e, 64),
+                                                 om.expert_matrix(L, "up", e, 64), om.expert_matrix(L, "down", e, 64))
     rel = np.abs(y_to_f64(y) - ref).max() / np.abs(ref).max()
     log(f"  max rel err {rel:.3e}")
     assert rel <= 2e-2, rel
