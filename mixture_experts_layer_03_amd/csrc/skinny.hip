@@ -1000,6 +1000,20 @@ __device__ __forceinline__ float dot16_u8(const uint4& c, const uint4& a0, const
   return acc;
 }
 
+// the same for 16 u4 codes packed two per byte, element 2i in the low nibble of byte i
+__device__ __forceinline__ float dot16_u4(const uint2& c, const uint4& a0, const uint4& a1, float z) {
+  const uint32_t aw[8] = {a0.x, a0.y, a0.z, a0.w, a1.x, a1.y, a1.z, a1.w};
+  float acc = 0.f;
+#pragma unroll
+  for (int j = 0; j < 16; ++j) {
+    const float cj = static_cast<float>(((j < 8 ? c.x : c.y) >> (4 * (j & 7))) & 0xfu);
+    const uint32_t w2 = aw[j >> 1];
+    const float aj = __uint_as_float((j & 1) ? (w2 & 0xffff0000u) : (w2 << 16));
+    acc = fmaf(cj - z, aj, acc);
+  }
+  return acc;
+}
+
 // ---------------------------------------- one token: gate/up, with or without routing
 // With one token, column n of an expert's gated unit is silu(g_n . x) * (u_n . x): two
 // dot products over H [Bailing MoE expert MLP: SwiGLU].  A wavefront takes one column at
@@ -1237,15 +1251,19 @@ __global__ __launch_bounds__(64 * kUpOneWaves, 4) void k_up_one_q8(SkinnyUpArgs 
 // is in.  The block stages the activation rows (hs row 0, then hm positions 0..k-1) in
 // LDS once for its NW elements.  No partial sum leaves the wavefront, so the weighted
 // sum needs no second launch and no device-scope fence.
-// NLS / NLR: 16-byte loads per lane for a shared / routed row (Is / 512 and I / 512
-// rounded up); K: top-k (position p of the one-token permutation holds a pick; with
-// fewer valid picks than K the last valid row is loaded again and not added).
+// NLS / NLR: loads per lane for a shared / routed row (Is / 512 and I / 512 rounded up
+// for bf16; u8 and u4 routed rows take 16 codes per lane and load, I / 1024); K: top-k
+// (position p of the one-token permutation holds a pick; with fewer valid picks than K
+// the last valid row is loaded again and not added); QB: 0 for bf16 routed experts, 8
+// or 4 for u8 or u4 codes with an fp16 scale and zero point per 64 (one group per four
+// of a lane's 16-code vectors).
 constexpr int kDownOneWaves = 8;
 
-template <int NLS, int NLR, int K, bool Q8>
+template <int NLS, int NLR, int K, int QB>
 __global__ __launch_bounds__(64 * kDownOneWaves) void k_down_one(SkinnyDownArgs a) {
   constexpr int NW = kDownOneWaves, NT = 64 * NW;
-  constexpr int EPV = Q8 ? 16 : 8;  // routed-row elements per 16-byte vector
+  constexpr bool Q = QB != 0;  // u8 or u4 routed experts (16 codes per lane vector)
+  constexpr int EPV = Q ? 16 : 8;  // routed-row elements per lane vector
   constexpr int NST = ((NLS + K * NLR * EPV / 8) * 64 + NT - 1) / NT;  // staging loads per thread
   __shared__ __attribute__((aligned(16))) uint16_t act[NST * NT * 8];
   // Every load is unconditional (lanes past a row's end load its last vector again, in
@@ -1279,7 +1297,8 @@ __global__ __launch_bounds__(64 * kDownOneWaves) void k_down_one(SkinnyDownArgs 
   const int npos = __popcll(__ballot(lane < K && pidx >= 0 && pidx < a.E));
   const int pe = __shfl(pidx, min(max(pslot, 0), K - 1));
   uint4 wr[K][NLR];
-  uint16_t gs[Q8 ? K : 1][NLR], gz[Q8 ? K : 1][NLR];  // u8: the group's fp16 scale, zero point
+  uint2 wq[QB == 4 ? K : 1][NLR];
+  uint16_t gs[Q ? K : 1][NLR], gz[Q ? K : 1][NLR];  // u8 / u4: the group's fp16 scale, zero point
 #pragma unroll
   for (int p = 0; p < K; ++p) {
     const int e = min(max(__builtin_amdgcn_readlane(pe, min(p, max(npos - 1, 0))), 0), a.E - 1);
@@ -1287,8 +1306,10 @@ __global__ __launch_bounds__(64 * kDownOneWaves) void k_down_one(SkinnyDownArgs 
 #pragma unroll
     for (int i = 0; i < NLR; ++i) {
       const int vc = min(lane + 64 * i, nvr - 1);
-      if constexpr (Q8) {
-        wr[p][i] = ld16(static_cast<const uint8_t*>(a.down) + r * a.I + 16 * vc);
+      if constexpr (QB == 8) wr[p][i] = ld16(static_cast<const uint8_t*>(a.down) + r * a.I + 16 * vc);
+      if constexpr (QB == 4)
+        wq[p][i] = *reinterpret_cast<const uint2*>(static_cast<const uint8_t*>(a.down) + r * (a.I / 2) + 8 * vc);
+      if constexpr (Q) {
         gs[p][i] = a.down_s[r * (a.I / 64) + vc / 4];
         gz[p][i] = a.down_z[r * (a.I / 64) + vc / 4];
       } else {
@@ -1317,10 +1338,11 @@ __global__ __launch_bounds__(64 * kDownOneWaves) void k_down_one(SkinnyDownArgs 
     for (int i = 0; i < NLR; ++i) {
       const int v = lane + 64 * i, vc = min(v, nvr - 1);
       float t;
-      if constexpr (Q8) {
+      if constexpr (Q) {
         const uint4 a0 = *reinterpret_cast<const uint4*>(ap + 16 * vc);
         const uint4 a1 = *reinterpret_cast<const uint4*>(ap + 16 * vc + 8);
-        t = f16_to_f32(gs[p][i]) * dot16_u8(wr[p][i], a0, a1, f16_to_f32(gz[p][i]));
+        const float z = f16_to_f32(gz[p][i]);
+        t = f16_to_f32(gs[p][i]) * (QB == 8 ? dot16_u8(wr[p][i], a0, a1, z) : dot16_u4(wq[p][i], a0, a1, z));
       } else {
         t = dot8_bf16(wr[p][i], *reinterpret_cast<const uint4*>(ap + 8 * vc), 0.f);
       }
@@ -2209,35 +2231,38 @@ hipError_t launch_skinny_down(const SkinnyDownArgs& a, Act act, WFmt wf, int ncu
   return hipGetLastError();
 }
 
-// instances of k_down_one: (NLS, NLR, K, u8), smallest first per K and format
+// instances of k_down_one: (NLS, NLR, K, code bits: 0 for bf16), smallest first per K and
+// format
 namespace {
 struct DownOneShape {
-  int nls, nlr, k;
-  bool q8;
+  int nls, nlr, k, qb;
   void (*fn)(SkinnyDownArgs);
 };
 const DownOneShape kDownOne[] = {
-    {1, 1, 8, false, k_down_one<1, 1, 8, false>},
-    {2, 2, 8, false, k_down_one<2, 2, 8, false>},
-    {6, 3, 6, false, k_down_one<6, 3, 6, false>},
-    {1, 1, 8, true, k_down_one<1, 1, 8, true>},
-    {2, 1, 8, true, k_down_one<2, 1, 8, true>},
+    {1, 1, 8, 0, k_down_one<1, 1, 8, 0>},
+    {2, 2, 8, 0, k_down_one<2, 2, 8, 0>},
+    {6, 3, 6, 0, k_down_one<6, 3, 6, 0>},
+    {1, 1, 8, 8, k_down_one<1, 1, 8, 8>},
+    {2, 1, 8, 8, k_down_one<2, 1, 8, 8>},
+    {1, 1, 8, 4, k_down_one<1, 1, 8, 4>},
+    {2, 1, 8, 4, k_down_one<2, 1, 8, 4>},
 };
+int down_one_qb(WFmt wf) { return wf == WFmt::U8 ? 8 : wf == WFmt::U4 ? 4 : 0; }
 const DownOneShape* down_one_shape(const SkinnyDownArgs& a, WFmt wf) {
-  const bool q8 = wf == WFmt::U8;
-  const int nls = (a.Is / 8 + 63) / 64, nlr = (a.I / (q8 ? 16 : 8) + 63) / 64;
+  const int qb = down_one_qb(wf);
+  const int nls = (a.Is / 8 + 63) / 64, nlr = (a.I / (qb ? 16 : 8) + 63) / 64;
   for (const DownOneShape& d : kDownOne)
-    if (d.q8 == q8 && d.k == a.k && nls <= d.nls && nlr <= d.nlr) return &d;
+    if (d.qb == qb && d.k == a.k && nls <= d.nls && nlr <= d.nlr) return &d;
   return nullptr;
 }
 }  // namespace
 
 bool down_one_fits(const SkinnyDownArgs& a, Act act, WFmt wf) {
   auto al16 = [](const void* q) { return reinterpret_cast<uintptr_t>(q) % 16 == 0; };
-  const bool q8 = wf == WFmt::U8;
-  return a.T == 1 && a.part == 0 && act == Act::BF16 && (wf == WFmt::BF16 || q8) && a.I % (q8 ? 64 : 8) == 0 &&
+  const bool q = wf == WFmt::U8 || wf == WFmt::U4;
+  return a.T == 1 && a.part == 0 && act == Act::BF16 && (wf == WFmt::BF16 || q) && a.I % (q ? 64 : 8) == 0 &&
          a.Is % 8 == 0 && a.I > 0 && a.Is > 0 && a.H > 0 && al16(a.down) && al16(a.sdown) && al16(a.hm) &&
-         al16(a.hs) && (!q8 || (a.down_s && a.down_z)) && down_one_shape(a, wf) != nullptr;
+         al16(a.hs) && (!q || (a.down_s && a.down_z)) && down_one_shape(a, wf) != nullptr;
 }
 
 hipError_t launch_down_one(const SkinnyDownArgs& a, Act act, WFmt wf, hipStream_t s) {

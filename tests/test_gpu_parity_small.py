@@ -450,14 +450,14 @@ def test_small_batch_routing_tables_match_the_general_permutation(cid, T):
     log(f"  ok: bit-identical, max rel err {st['max_rel']:.3e}")
 
 
-@pytest.mark.parametrize("cid", [2, 3, 5, "wide"])
+@pytest.mark.parametrize("cid", [2, 3, 5, 6, "wide"])
 @pytest.mark.parametrize("pattern", ["one-invalid", "out-of-range", "duplicate", "none-valid"])
 def test_one_token_down_with_irregular_picks(cid, pattern):
     """One token through the expert stage with picks the router never makes: a slot
     marked invalid (-1), an index past E, one expert in two slots, no valid slot at all.
     With one token the down launch also forms the weighted sum, reading the expert of
-    each position through the permutation; every valid slot is one term (bf16 and u8
-    experts)."""
+    each position through the permutation; every valid slot is one term (bf16, u8 and
+    u4 experts)."""
     import mixture_experts_layer_03_amd as moe
     if cid == "wide":
         if "wide" not in _CACHE:
