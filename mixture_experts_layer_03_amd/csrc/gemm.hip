@@ -839,8 +839,38 @@ inline int64_t grid_blocks(const TileArgs& a, int ncol, int NT = 0) {
   return (blocks + 7) / 8 * 8;
 }
 
+// Dense products (group_m <= 0): the M-tiles per block-order group.  Each XCD takes a
+// contiguous eighth of the logical tile order (tile_pos), so with G M-tiles per group
+// it reads about min(G, P) activation panels of BM rows and ceil(P / G) weight panels
+// of `brows` rows (P tiles per XCD).  G is the power of two (padding the M-tiles by at
+// most an eighth) that minimises those rows: for the Ling-lite shared gate/up at 4096
+// tokens (32 M-tiles, 11 panels of 512 rows, 44 tiles per XCD) 16 instead of 4, which
+// takes each XCD from all 11 weight panels to 3.
+inline int dense_group_m(const TileArgs& a, int ncol, int brows) {
+  const int64_t mt = a.mtiles_bound, NT = (a.N + ncol - 1) / ncol, KS = a.ksplit > 1 ? a.ksplit : 1;
+  int best = 1;
+  int64_t best_rows = -1;
+  for (int G = 1; G <= 64 && G <= mt; G *= 2) {
+    const int64_t mt_pad = (mt + G - 1) / G * G;
+    if ((mt_pad - mt) * 8 > mt) continue;
+    const int64_t P = (mt_pad * NT * KS + 7) / 8;
+    const int64_t rows = std::min<int64_t>(G, P) * BM + (P + G - 1) / G * brows;
+    if (best_rows < 0 || rows < best_rows) {
+      best = G;
+      best_rows = rows;
+    }
+  }
+  return best;
+}
+inline TileArgs with_dense_group(const TileArgs& a, int ncol, int brows) {
+  TileArgs b = a;
+  if (!a.routed && a.group_m <= 0) b.group_m = dense_group_m(a, ncol, brows);
+  return b;
+}
+
 template <int BN, int BK, WFmt WF, bool DUAL, AMode AM, Epi EPI>
-hipError_t launch_one(const TileArgs& a, hipStream_t s) {
+hipError_t launch_one(const TileArgs& a0, hipStream_t s) {
+  const TileArgs a = with_dense_group(a0, DUAL ? BN / 2 : BN, BN);
   const int64_t blocks = grid_blocks(a, DUAL ? BN / 2 : BN);
   if (blocks <= 0) return hipSuccess;
   hipLaunchKernelGGL((k_tile<BN, BK, WF, DUAL, AM, EPI>), dim3(static_cast<unsigned>(blocks)), dim3(BN * 2), 0, s, a);
@@ -861,7 +891,8 @@ constexpr int wave_width() {
 }
 
 template <int BN, int BK, int S, bool DUAL, AMode AM, Epi EPI>
-hipError_t launch_dma(const TileArgs& a, hipStream_t s) {
+hipError_t launch_dma(const TileArgs& a0, hipStream_t s) {
+  const TileArgs a = with_dense_group(a0, DUAL ? BN / 2 : BN, BN);
   constexpr int WT = wave_width<BN, DUAL, AM>();
   const int64_t blocks = grid_blocks(a, DUAL ? BN / 2 : BN);
   if (blocks <= 0) return hipSuccess;

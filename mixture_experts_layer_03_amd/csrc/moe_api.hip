@@ -65,7 +65,7 @@ constexpr int kFusedRouteMaxT = 16;  // one workgroup routes and permutes up to 
 // at 1 token 47.2 -> 43.7 us with the single-load chunk records), 64 tokens faster
 // routed-first for gate/up.
 constexpr int64_t kSharedFirstMaxT = 16;
-constexpr int kGroupM = 4;           // M-tiles per block-order group of the tiled GEMMs
+constexpr int kGroupAuto = 0;  // dense tiled GEMMs: the launch picks the M-tiles per block-order group
 // Routed GEMMs keep the launch order of their blocks (TileArgs::plain_order) when the
 // experts average at most this many routed tokens (1.5 M-tiles of 128).
 constexpr int64_t kPlainOrderMaxSlotsPerExpert = 192;
@@ -342,7 +342,7 @@ moe_status run_logits(const moe_config& c, const Plan& p, int64_t T, const void*
     g.out = logits;
     g.ldo = static_cast<int>(c.num_experts);
     g.mtiles_bound = static_cast<int>((T + kTileM - 1) / kTileM);
-  g.group_m = kGroupM;
+  g.group_m = kGroupAuto;
     g.ncu = device_cus();
     g.ksplit = p.P;
     g.part_stride = T * c.num_experts;
@@ -609,7 +609,7 @@ moe_status run_experts(const moe_config& c, const Plan& p, int64_t T, const void
     su.out = hs;
     su.ldo = Is;
     su.mtiles_bound = static_cast<int>((T + kTileM - 1) / kTileM);
-  su.group_m = kGroupM;
+  su.group_m = kGroupAuto;
     su.ncu = device_cus();
     if (!shared_join)
       MOE_LAUNCH_STAGE(MOE_STAGE_SHARED_UP, s, launch_tile_gemm(su, AMode::DENSE, WFmt::BF16, Epi::SWIGLU, s), "shared gate/up (tiled)");
@@ -627,7 +627,7 @@ moe_status run_experts(const moe_config& c, const Plan& p, int64_t T, const void
     sd.k = k;
     sd.E = E;
     sd.mtiles_bound = su.mtiles_bound;
-  sd.group_m = kGroupM;
+  sd.group_m = kGroupAuto;
     sd.ncu = su.ncu;
     MOE_LAUNCH_STAGE(MOE_STAGE_SHARED_DOWN, s, launch_tile_gemm(sd, AMode::DENSE, WFmt::BF16, Epi::COMBINE, s), "shared down + combine (tiled)");
   } else {
@@ -688,7 +688,7 @@ moe_status run_shared(const moe_config& c, const Plan& p, int64_t T, const void*
   su.out = hs;
   su.ldo = Is;
   su.mtiles_bound = static_cast<int>((T + kTileM - 1) / kTileM);
-  su.group_m = kGroupM;
+  su.group_m = kGroupAuto;
   su.ncu = ncu;
   MOE_LAUNCH_STAGE(MOE_STAGE_SHARED_UP, s, launch_tile_gemm(su, AMode::DENSE, WFmt::BF16, Epi::SWIGLU, s), "shared gate/up (tiled)");
   return MOE_OK;
@@ -805,7 +805,7 @@ moe_status run_dense(const moe_config& c, const DensePlan& p, int64_t T, int64_t
   su.out = hs;
   su.ldo = Id;
   su.mtiles_bound = static_cast<int>((T + kTileM - 1) / kTileM);
-  su.group_m = kGroupM;
+  su.group_m = kGroupAuto;
   su.ncu = ncu;
   MOE_LAUNCH_STAGE(MOE_STAGE_SHARED_UP, s, launch_tile_gemm(su, AMode::DENSE, WFmt::BF16, Epi::SWIGLU, s), "dense gate/up (tiled)");
   TileArgs sd{};
@@ -819,7 +819,7 @@ moe_status run_dense(const moe_config& c, const DensePlan& p, int64_t T, int64_t
   sd.ldo = H;
   sd.k = 0;  // the combine epilogue with no routed terms: y = rounded output
   sd.mtiles_bound = su.mtiles_bound;
-  sd.group_m = kGroupM;
+  sd.group_m = kGroupAuto;
   sd.ncu = ncu;
   MOE_LAUNCH_STAGE(MOE_STAGE_SHARED_DOWN, s, launch_tile_gemm(sd, AMode::DENSE, WFmt::BF16, Epi::COMBINE, s), "dense down (tiled)");
   return MOE_OK;

@@ -208,7 +208,7 @@ __device__ void route_token(const TopkArgs& a, int t, int* lds_idx = nullptr, fl
       }
     }
     const int own = bi;
-    wave_argmax(bv, bi);
+    wave_argmax_lane_ordered(bv, bi);  // lane l holds experts l * EPL .. l * EPL + EPL - 1
     // the unbiased score of the winner, from the lane that holds it
     const float wo = bi != 0x7fffffff ? __int_as_float(__builtin_amdgcn_readlane(__float_as_int(bo), bi / EPL)) : 0.f;
     if (bi != 0x7fffffff && own == bi) taken |= 1u << (bi - lane * EPL);
