@@ -13,6 +13,7 @@
 // contiguous bytes of every one of its 16 rows (bf16: two instructions per step,
 // u8: one), i.e. whole cache-line halves.
 #include <initializer_list>
+#include <mutex>
 
 #include "common.h"
 #include "kernels.h"
@@ -2092,6 +2093,31 @@ bool up_one_fits(const SkinnyUpArgs& a, Act act, WFmt wf) {
          (a.Is == 0 || (al16(a.sgate) && al16(a.sup)));
 }
 
+// Resident blocks per CU of a one-token gate/up instance on the current device, asked
+// of the runtime once per (instance, device) and kept; 1 if the query fails.
+static int up_one_blocks_per_cu(void (*k)(SkinnyUpArgs)) {
+  struct Entry {
+    void (*k)(SkinnyUpArgs);
+    int dev, per_cu;
+  };
+  static std::mutex mu;
+  static Entry cache[128];
+  static int n = 0;
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess) dev = -1;
+  {
+    std::lock_guard<std::mutex> lock(mu);
+    for (int i = 0; i < n; ++i)
+      if (cache[i].k == k && cache[i].dev == dev) return cache[i].per_cu;
+  }
+  int per_cu = 0;
+  if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, k, 64 * kUpOneWaves, 0) != hipSuccess || per_cu < 1)
+    per_cu = 1;
+  std::lock_guard<std::mutex> lock(mu);
+  if (n < 128) cache[n++] = Entry{k, dev, per_cu};
+  return per_cu;
+}
+
 static hipError_t launch_up_one(const SkinnyUpArgs& a, WFmt wf, int ncu, hipStream_t s) {
   if (a.fused_route) {
     if (!a.ta.logits || !a.ta.idx || !a.ta.w || a.ta.E != a.E || a.ta.k != a.k || a.ta.T != 1 || !a.pa.perm ||
@@ -2118,9 +2144,7 @@ static hipError_t launch_up_one(const SkinnyUpArgs& a, WFmt wf, int ncu, hipStre
   }
   // every block resident at once (each finds the routing once), at most two per CU
   // (Ling-lite at one token: 20.3 us with two, 20.8 us with three); at least one block
-  int per_cu = 0;
-  if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, k, 64 * kUpOneWaves, 0) != hipSuccess || per_cu < 1)
-    per_cu = 1;
+  int per_cu = up_one_blocks_per_cu(k);
   if (per_cu > 2) per_cu = 2;
   const int64_t cols = static_cast<int64_t>(a.Is) + static_cast<int64_t>(a.k) * a.I;
   int64_t grid = static_cast<int64_t>(per_cu) * ncu;
