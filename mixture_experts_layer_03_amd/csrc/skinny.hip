@@ -1364,13 +1364,19 @@ __global__ __launch_bounds__(64 * kDownOneWaves) void k_down_one(SkinnyDownArgs 
 // two fp16 values (groups 2t, 2t + 1) of matrix l / 32, kind (l / 16) % 2 (scale,
 // zero), row l % 16.  Products per group are exact: codes minus the zero point are
 // integers in [-255, 255], exact in bf16; the group scale multiplies the fp32 result.
-template <int NMAT, int TR = 16>
+// PRE: the group parameters of the whole range are copied to their own area before the
+// stream (ring_stream_u8), so a slot carries codes and token rows only.
+template <int NMAT, int TR = 16, bool PRE = false>
 struct RingGeomU8 {
   static constexpr int W_BYTES = NMAT * 16 * 128;
   static constexpr int A_BYTES = 2 * TR * 128;  // two token images of TR rows (8 or 16)
-  static constexpr int SLOT_BYTES = W_BYTES + A_BYTES + 256;
-  static constexpr int CPS = 2 * NMAT + 2 * (TR / 8) + 1;  // copy instructions per step
+  static constexpr int SLOT_BYTES = W_BYTES + A_BYTES + (PRE ? 0 : 256);
+  static constexpr int CPS = 2 * NMAT + 2 * (TR / 8) + (PRE ? 0 : 1);  // copy instructions per step
 };
+// LDS bytes of the preloaded group parameters: 32 * NMAT rows of scales or zero points,
+// at most 16 groups (two 16-byte chunks) each
+template <int NMAT>
+constexpr int kU8ParamBytes = NMAT * 32 * 2 * 16;
 
 // codes: 8 u8 in (lo, hi) minus zero point -> 8 bf16
 __device__ __forceinline__ uint4 codes_minus_zero(uint2 c, float z) {
@@ -1387,16 +1393,36 @@ __device__ __forceinline__ uint4 codes_minus_zero(uint2 c, float z) {
 // acc[m] += tokens x dequant(W_m)^T over [k0, k1) (multiples of 128).
 // wbase[m]: wave-uniform byte address of code row 0 of matrix m; woff[h]: lane offset of
 // its code row in copy h (row 8h + l/8, rows K bytes apart) plus its chunk.  sz_src: this
-// lane's group-parameter address for group 0 of the range (4 bytes, 2 groups).
-template <int NMAT, int RB, int TR>
+// lane's group-parameter row (u8_param_row: scales or zero points of one row, group 0).
+// Without PRE every step copies the step's two groups, 4 bytes per lane: one cache line
+// per parameter row, so 32 NMAT line requests per step, as many as the codes and the
+// token rows of a 16-token chunk together.  PRE (k1 - k0 a multiple of 512, at most
+// 1024, parameter rows 16-byte aligned): before the stream the range's groups are copied
+// once into kU8ParamBytes<NMAT> at `pa`, 16 bytes (8 groups) per lane and row, stored as
+// chunk c = 16-byte piece j of parameter row rk at pa + 16 (j * 32 NMAT + rk); the whole
+// range then costs 32 NMAT lines per 8 groups instead of per group pair.
+template <int NMAT, int RB, int TR, bool PRE = false>
 __device__ __forceinline__ void ring_stream_u8(const char* const (&wbase)[NMAT], const uint32_t (&woff)[2],
                                                const char* abase, const uint32_t (&aoff)[2], const uint16_t* sz_src,
-                                               int k0, int k1, char* ring, f32x4 (&acc)[NMAT]) {
-  using G = RingGeomU8<NMAT, TR>;
+                                               int k0, int k1, char* ring, f32x4 (&acc)[NMAT],
+                                               char* pa = nullptr) {
+  using G = RingGeomU8<NMAT, TR, PRE>;
   constexpr int U = ring_depth(RB, G::SLOT_BYTES);
+  constexpr int NRK = 32 * NMAT;  // parameter rows: NMAT matrices x (scales, zero points) x 16 rows
   static_assert(U >= 2 && G::CPS * (U - 1) < 64, "ring depth");
   const int lane = lane_id();
   const int n = (k1 - k0) >> 7;
+  if constexpr (PRE) {
+    // lane l of copy i brings chunk c = 64 i + l: row c % NRK (that row is this lane's
+    // sz_src row, since NRK divides 64), piece min(c / NRK, pieces - 1)
+    const int pieces = (k1 - k0) >> 9;
+#pragma unroll
+    for (int i = 0; i < (2 * NRK + 63) / 64; ++i) {
+      const int c = 64 * i + lane;
+      if (i * 64 < pieces * NRK) copy_to_lds(sz_src + (k0 >> 6) + 8 * min(c / NRK, pieces - 1),
+                                             reinterpret_cast<uint16_t*>(pa + 1024 * i));
+    }
+  }
   auto issue = [&](int slot, int step) {
     char* sl = ring + slot * G::SLOT_BYTES;
     const int kc = k0 + 128 * step;  // element index = code byte offset
@@ -1411,10 +1437,10 @@ __device__ __forceinline__ void ring_stream_u8(const char* const (&wbase)[NMAT],
       for (int h = 0; h < TR / 8; ++h)
         copy_to_lds(uniform_ptr(abase + (kc + 64 * half) * 2), aoff[h],
                     reinterpret_cast<uint16_t*>(sl + G::W_BYTES + half * TR * 128 + 8 * h * 128));
-    copy4_to_lds(sz_src + (kc >> 6), sl + G::W_BYTES + G::A_BYTES);
+    if constexpr (!PRE) copy4_to_lds(sz_src + (kc >> 6), sl + G::W_BYTES + G::A_BYTES);
   };
   const int r = lane & 15, q = lane >> 4;
-  auto compute = [&](int slot) {
+  auto compute = [&](int slot, int step) {
     const char* sl = ring + slot * G::SLOT_BYTES;
     const uint32_t* szp = reinterpret_cast<const uint32_t*>(sl + G::W_BYTES + G::A_BYTES);
 #pragma unroll
@@ -1424,9 +1450,16 @@ __device__ __forceinline__ void ring_stream_u8(const char* const (&wbase)[NMAT],
 #pragma unroll
       for (int m = 0; m < NMAT; ++m) {
         part[m] = f32x4{0.f, 0.f, 0.f, 0.f};
-        const uint32_t sv = szp[m * 32 + r], zv = szp[m * 32 + 16 + r];
-        sf[m] = f16_to_f32(static_cast<uint16_t>(g ? sv >> 16 : sv & 0xffffu));
-        zf[m] = f16_to_f32(static_cast<uint16_t>(g ? zv >> 16 : zv & 0xffffu));
+        if constexpr (PRE) {
+          const int gg = 2 * step + g;  // group within the range
+          const uint16_t* pp = reinterpret_cast<const uint16_t*>(pa + 16 * ((gg >> 3) * NRK + m * 32 + r)) + (gg & 7);
+          sf[m] = f16_to_f32(pp[0]);
+          zf[m] = f16_to_f32(pp[128]);  // zero-point row m * 32 + 16 + r: 16 rows x 16 bytes further
+        } else {
+          const uint32_t sv = szp[m * 32 + r], zv = szp[m * 32 + 16 + r];
+          sf[m] = f16_to_f32(static_cast<uint16_t>(g ? sv >> 16 : sv & 0xffffu));
+          zf[m] = f16_to_f32(static_cast<uint16_t>(g ? zv >> 16 : zv & 0xffffu));
+        }
       }
 #pragma unroll
       for (int ks = 0; ks < 2; ++ks) {
@@ -1452,7 +1485,7 @@ __device__ __forceinline__ void ring_stream_u8(const char* const (&wbase)[NMAT],
   for (int t = 0; t < n; ++t) {
     copy_wait_ahead<G::CPS, U - 2>(n - 1 - t);
     if (t + U - 1 < n) issue(nxt, t + U - 1);
-    compute(cur);
+    compute(cur, t);
     cur = cur + 1 == U ? 0 : cur + 1;
     nxt = nxt + 1 == U ? 0 : nxt + 1;
   }
@@ -1475,12 +1508,12 @@ __device__ __forceinline__ void ring_stream_u8(const char* const (&wbase)[NMAT],
 // as 0 4 1 5 2 6 3 7; the token fragment is permuted the same way, which leaves the dot
 // product unchanged.  Per group, sum_k a_k (q_k - z) = sum_k a_k (128 + q_k)
 // - (128 + z) sum_k a_k, with sum_k a_k from one more MFMA against ones.
-template <int NMAT, int TR>
+template <int NMAT, int TR, bool PRE = false>
 struct RingGeomU4 {
   static constexpr int W_BYTES = NMAT * 16 * 64;
   static constexpr int A_BYTES = TR * 256;
-  static constexpr int SLOT_BYTES = W_BYTES + A_BYTES + 256;
-  static constexpr int CPS = NMAT + TR / 4 + 1;  // copy instructions per step
+  static constexpr int SLOT_BYTES = W_BYTES + A_BYTES + (PRE ? 0 : 256);
+  static constexpr int CPS = NMAT + TR / 4 + (PRE ? 0 : 1);  // copy instructions per step
 };
 constexpr int kU4MaxSlot = RingGeomU4<2, 16>::SLOT_BYTES;
 
@@ -1509,16 +1542,27 @@ __device__ __forceinline__ uint32_t u4_code_off(int row_bytes) {
 // many steps (at most 8) as RB bytes hold: fewer token rows leave room for more steps in
 // flight.  wbase[m]: wave-uniform byte address of code row 0 of matrix m; woff: this
 // lane's offset (u4_code_off).  abase / aoff[i]: token rows of copy i (rows 4i + l/16;
-// row byte offset plus 16 x logical chunk (l % 16) ^ row).  sz_src: as for the u8 ring.
-template <int NMAT, int RB, int TR>
+// row byte offset plus 16 x logical chunk (l % 16) ^ row).  sz_src, PRE and pa: as for
+// the u8 ring.
+template <int NMAT, int RB, int TR, bool PRE = false>
 __device__ __forceinline__ void ring_stream_u4(const char* const (&wbase)[NMAT], uint32_t woff, const char* abase,
                                                const uint32_t (&aoff)[TR / 4], const uint16_t* sz_src, int k0,
-                                               int k1, char* ring, f32x4 (&acc)[NMAT]) {
-  using G = RingGeomU4<NMAT, TR>;
+                                               int k1, char* ring, f32x4 (&acc)[NMAT], char* pa = nullptr) {
+  using G = RingGeomU4<NMAT, TR, PRE>;
   constexpr int U = RB / G::SLOT_BYTES < 8 ? RB / G::SLOT_BYTES : 8;
+  constexpr int NRK = 32 * NMAT;
   static_assert(U >= 2, "ring too small");
   const int lane = lane_id();
   const int n = (k1 - k0) >> 7;
+  if constexpr (PRE) {
+    const int pieces = (k1 - k0) >> 9;
+#pragma unroll
+    for (int i = 0; i < (2 * NRK + 63) / 64; ++i) {
+      const int c = 64 * i + lane;
+      if (i * 64 < pieces * NRK) copy_to_lds(sz_src + (k0 >> 6) + 8 * min(c / NRK, pieces - 1),
+                                             reinterpret_cast<uint16_t*>(pa + 1024 * i));
+    }
+  }
   auto issue = [&](int slot, int step) {
     char* sl = ring + slot * G::SLOT_BYTES;
     const int kc = k0 + 128 * step;
@@ -1528,12 +1572,12 @@ __device__ __forceinline__ void ring_stream_u4(const char* const (&wbase)[NMAT],
 #pragma unroll
     for (int i = 0; i < TR / 4; ++i)
       copy_to_lds(uniform_ptr(abase + kc * 2), aoff[i], reinterpret_cast<uint16_t*>(sl + G::W_BYTES + i * 1024));
-    copy4_to_lds(sz_src + (kc >> 6), sl + G::W_BYTES + G::A_BYTES);
+    if constexpr (!PRE) copy4_to_lds(sz_src + (kc >> 6), sl + G::W_BYTES + G::A_BYTES);
   };
   const int r = lane & 15, q = lane >> 4;
   const int tr = r & (TR - 1);
   const uint4 ones = make_uint4(0x3f803f80u, 0x3f803f80u, 0x3f803f80u, 0x3f803f80u);
-  auto compute = [&](int slot) {
+  auto compute = [&](int slot, int step) {
     const char* sl = ring + slot * G::SLOT_BYTES;
     const uint32_t* szp = reinterpret_cast<const uint32_t*>(sl + G::W_BYTES + G::A_BYTES);
 #pragma unroll
@@ -1544,9 +1588,16 @@ __device__ __forceinline__ void ring_stream_u4(const char* const (&wbase)[NMAT],
 #pragma unroll
       for (int m = 0; m < NMAT; ++m) {
         part[m] = f32x4{0.f, 0.f, 0.f, 0.f};
-        const uint32_t sv = szp[m * 32 + r], zv = szp[m * 32 + 16 + r];
-        sf[m] = f16_to_f32(static_cast<uint16_t>(g ? sv >> 16 : sv & 0xffffu));
-        zf[m] = 128.f + f16_to_f32(static_cast<uint16_t>(g ? zv >> 16 : zv & 0xffffu));
+        if constexpr (PRE) {
+          const int gg = 2 * step + g;
+          const uint16_t* pp = reinterpret_cast<const uint16_t*>(pa + 16 * ((gg >> 3) * NRK + m * 32 + r)) + (gg & 7);
+          sf[m] = f16_to_f32(pp[0]);
+          zf[m] = 128.f + f16_to_f32(pp[128]);
+        } else {
+          const uint32_t sv = szp[m * 32 + r], zv = szp[m * 32 + 16 + r];
+          sf[m] = f16_to_f32(static_cast<uint16_t>(g ? sv >> 16 : sv & 0xffffu));
+          zf[m] = 128.f + f16_to_f32(static_cast<uint16_t>(g ? zv >> 16 : zv & 0xffffu));
+        }
       }
 #pragma unroll
       for (int ks = 0; ks < 2; ++ks) {
@@ -1573,7 +1624,7 @@ __device__ __forceinline__ void ring_stream_u4(const char* const (&wbase)[NMAT],
   for (int t = 0; t < n; ++t) {
     copy_wait_ahead<G::CPS, U - 2>(n - 1 - t);
     if (t + U - 1 < n) issue(nxt, t + U - 1);
-    compute(cur);
+    compute(cur, t);
     cur = cur + 1 == U ? 0 : cur + 1;
     nxt = nxt + 1 == U ? 0 : nxt + 1;
   }
@@ -1626,6 +1677,15 @@ __device__ __forceinline__ const uint16_t* u8_param_row(const uint16_t* const (&
   const int kind = (lane >> 4) & 1;
   const uint16_t* base = kind ? z[m] : s[m];
   return base + (row0 + (lane & 15)) * (K / 64);
+}
+
+// Whether a u8 ring range [k0, k1) of rows K elements long takes the preloaded group
+// parameters (ring_stream_u8 PRE): 8-group pieces that start on 16-byte boundaries
+// (K, k0 and k1 multiples of 512, parameter arrays 16-byte aligned), at most 16 groups.
+__device__ __forceinline__ bool u8_pre(int k0, int k1, int K, std::initializer_list<const uint16_t*> ps) {
+  uintptr_t al = 0;
+  for (const uint16_t* p : ps) al |= reinterpret_cast<uintptr_t>(p);
+  return ((al & 15) | (K & 511) | (k0 & 511) | (k1 & 511)) == 0 && k1 - k0 <= 1024 && k1 > k0;
 }
 
 // quantised routed experts (BITS = 8: u8 ring, 4: u4 ring); shared items stream bf16
@@ -1685,10 +1745,17 @@ __global__ __launch_bounds__(256) void k_stream_up_q(SkinnyUpArgs a) {
                                  uniform_ptr(static_cast<const uint8_t*>(a.up) + ro * a.H)};
             const uint32_t woff[2] = {static_cast<uint32_t>(rr * a.H + ch * 16),
                                       static_cast<uint32_t>((8 + rr) * a.H + ch * 16)};
-            if (ntok <= 8)
+            if (u8_pre(k0, k1, a.H, {a.gate_s, a.gate_z, a.up_s, a.up_z})) {
+              constexpr int PB = kU8ParamBytes<2>;
+              if (ntok <= 8)
+                ring_stream_u8<2, RB - PB, 8, true>(wb, woff, xb, aoff, szs, k0, k1, ring, acc, ring + RB - PB);
+              else
+                ring_stream_u8<2, RB - PB, 16, true>(wb, woff, xb, aoff, szs, k0, k1, ring, acc, ring + RB - PB);
+            } else if (ntok <= 8) {
               ring_stream_u8<2, RB, 8>(wb, woff, xb, aoff, szs, k0, k1, ring, acc);
-            else
+            } else {
               ring_stream_u8<2, RB, 16>(wb, woff, xb, aoff, szs, k0, k1, ring, acc);
+            }
           } else {
             const char* wb[2] = {uniform_ptr(static_cast<const uint8_t*>(a.gate) + ro * (a.H / 2)),
                                  uniform_ptr(static_cast<const uint8_t*>(a.up) + ro * (a.H / 2))};
@@ -1698,7 +1765,17 @@ __global__ __launch_bounds__(256) void k_stream_up_q(SkinnyUpArgs a) {
               constexpr int TR = decltype(trc)::value;
               uint32_t ao[TR / 4];
               u4_token_offsets<TR>(ntok, [&](int j) { return a.T == 1 ? 0u : static_cast<uint32_t>(prow[j] / a.k) * a.H * 2; }, ao);
-              ring_stream_u4<2, RB, TR>(wb, woff, xb, ao, szs, k0, k1, ring, acc);
+              // preloaded parameters where their area leaves at least two slots (at most
+              // 8 token rows)
+              constexpr int PB = kU8ParamBytes<2>;
+              bool done = false;
+              if constexpr (TR <= 8) {
+                if (u8_pre(k0, k1, a.H, {a.gate_s, a.gate_z, a.up_s, a.up_z})) {
+                  ring_stream_u4<2, RB - PB, TR, true>(wb, woff, xb, ao, szs, k0, k1, ring, acc, ring + RB - PB);
+                  done = true;
+                }
+              }
+              if (!done) ring_stream_u4<2, RB, TR>(wb, woff, xb, ao, szs, k0, k1, ring, acc);
             });
           }
         } else {
@@ -1803,10 +1880,17 @@ __global__ __launch_bounds__(256) void k_stream_down_q(SkinnyDownArgs a) {
             const char* wb[1] = {uniform_ptr(static_cast<const uint8_t*>(a.down) + ro * a.I)};
             const uint32_t woff[2] = {static_cast<uint32_t>(rr * a.I + ch * 16),
                                       static_cast<uint32_t>((8 + rr) * a.I + ch * 16)};
-            if (ntok <= 8)
+            if (u8_pre(k0, k1, a.I, {a.down_s, a.down_z})) {
+              constexpr int PB = kU8ParamBytes<1>;
+              if (ntok <= 8)
+                ring_stream_u8<1, RB - PB, 8, true>(wb, woff, ab, aoff, szs, k0, k1, ring, acc, ring + RB - PB);
+              else
+                ring_stream_u8<1, RB - PB, 16, true>(wb, woff, ab, aoff, szs, k0, k1, ring, acc, ring + RB - PB);
+            } else if (ntok <= 8) {
               ring_stream_u8<1, RB, 8>(wb, woff, ab, aoff, szs, k0, k1, ring, acc);
-            else
+            } else {
               ring_stream_u8<1, RB, 16>(wb, woff, ab, aoff, szs, k0, k1, ring, acc);
+            }
           } else {
             const char* wb[1] = {uniform_ptr(static_cast<const uint8_t*>(a.down) + ro * (a.I / 2))};
             const uint32_t woff = u4_code_off(a.I / 2);
@@ -1815,7 +1899,17 @@ __global__ __launch_bounds__(256) void k_stream_down_q(SkinnyDownArgs a) {
               constexpr int TR = decltype(trc)::value;
               uint32_t ao[TR / 4];
               u4_token_offsets<TR>(ntok, [&](int j) { return static_cast<uint32_t>(row0t + j) * a.I * 2; }, ao);
-              ring_stream_u4<1, RB, TR>(wb, woff, ab, ao, szs, k0, k1, ring, acc);
+              // preloaded parameters where their area leaves at least two slots (at most
+              // 8 token rows)
+              constexpr int PB = kU8ParamBytes<1>;
+              bool done = false;
+              if constexpr (TR <= 8) {
+                if (u8_pre(k0, k1, a.I, {a.down_s, a.down_z})) {
+                  ring_stream_u4<1, RB - PB, TR, true>(wb, woff, ab, ao, szs, k0, k1, ring, acc, ring + RB - PB);
+                  done = true;
+                }
+              }
+              if (!done) ring_stream_u4<1, RB, TR>(wb, woff, ab, ao, szs, k0, k1, ring, acc);
             });
           }
         } else {
@@ -1938,7 +2032,7 @@ constexpr int kUpRingB = 20480, kDownRingB = 16384;
 // u8 gate/up: two blocks per CU split over the four wavefronts (measured 3-6% faster
 // than three steps unsplit on the Ling-3.0-flash shape at 1 to 64 tokens); 20 KB: two
 // steps of 16 token rows, three of 8.  u8 down: three steps of 16 token rows, four of 8.
-constexpr int kUpRingU8B = 20480, kDownRingU8B = 3 * RingGeomU8<1>::SLOT_BYTES;
+constexpr int kUpRingU8B = 20480, kDownRingU8B = 3 * RingGeomU8<1, 16, true>::SLOT_BYTES + kU8ParamBytes<1>;
 // u4 (ring depth per the token rows inside ring_stream_u4): gate/up three slots of the
 // largest u4 step, the split gate/up two (still 3-5 steps in flight with 4-8 token rows;
 // three blocks share a CU, measured 5-7% faster at 8-64 tokens), down two slots
