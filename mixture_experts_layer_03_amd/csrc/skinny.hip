@@ -707,8 +707,15 @@ struct RingItem {
   int e, off, ntot, row0, tc;
 };
 
+// S: row blocks per placement group (8 x items per block).  Blocks are dealt to the
+// eight XCDs in turn, so block b runs on XCD b % 8.  Within an expert, items are placed
+// by groups of S row blocks: item g S nc + c S + j is chunk c of row block g S + j, so
+// all chunks of a row block land S items apart, on blocks 8 apart, on one XCD, and run
+// in the same window of S nc items: that XCD's L2 fetches the block's rows once for all
+// its chunks (items one after another put them on different XCDs, each fetching the
+// same rows).  With S = 1 the order is row block by row block, chunk innermost.
 __device__ __forceinline__ RingItem ring_item(int item, int n_shared, int TC, int CH, int T, const int32_t* meta,
-                                              const int4* chunks, bool shared_first) {
+                                              const int4* chunks, bool shared_first, int S = 1) {
   RingItem r{};
   int it;  // routed item index
   if (shared_first) {
@@ -743,9 +750,11 @@ __device__ __forceinline__ RingItem ring_item(int item, int n_shared, int TC, in
   const int q0 = r.live ? qa - (rec.y - rec.z) / kDecodeChunk : qa;
   const int nc = (count + kDecodeChunk - 1) / kDecodeChunk;
   const int local = it - q0 * CH;
-  const int c = local % nc;
+  const int gs = S * nc, g = local / gs, rem = local - g * gs;
+  const int R = min(S, CH - g * S);  // row blocks of this group (fewer in the last one)
+  const int c = rem / R;
   r.e = r.live ? rec.x : 0;
-  r.row0 = (local / nc) * 16;
+  r.row0 = (g * S + rem % R) * 16;
   r.off = first + c * kDecodeChunk;
   r.ntot = count - c * kDecodeChunk;
   return r;
@@ -823,7 +832,7 @@ __global__ __launch_bounds__(256) void k_stream_up(SkinnyUpArgs a) {
     }
     const int item = base + w / NWK;
     const RingItem itm = FEPL > 0 ? pre
-                                  : ring_item(min(item, nbound - 1), n_shared, TC, CH, a.T, a.meta, a.chunks, sf);
+                                  : ring_item(min(item, nbound - 1), n_shared, TC, CH, a.T, a.meta, a.chunks, sf, 8 * IPB);
     const bool live = item < nbound && itm.live, shared = itm.shared;
     const int e = itm.e, off = itm.off, ntot = itm.ntot, row0 = itm.row0, tc_begin = itm.tc, tc_end = itm.tc + 1;
     int k0 = 0, k1 = a.H;
@@ -906,7 +915,7 @@ __global__ __launch_bounds__(256) void k_stream_down(SkinnyDownArgs a) {
       if (base >= nlive) break;
     }
     const int item = base + w / NWK;
-    const RingItem itm = ring_item(min(item, nbound - 1), n_shared, TC, CH, a.T, a.meta, a.chunks, sf);
+    const RingItem itm = ring_item(min(item, nbound - 1), n_shared, TC, CH, a.T, a.meta, a.chunks, sf, 8 * IPB);
     const bool live = item < nbound && itm.live, shared = itm.shared;
     const int e = itm.e, off = itm.off, ntot = itm.ntot, row0 = itm.row0, tc_begin = itm.tc, tc_end = itm.tc + 1;
     const int K = shared ? a.Is : a.I;
@@ -1719,7 +1728,7 @@ __global__ __launch_bounds__(256) void k_stream_up_q(SkinnyUpArgs a) {
     }
     const int item = base + w / NWK;
     const RingItem itm = FEPL > 0 ? pre
-                                  : ring_item(min(item, nbound - 1), n_shared, TC, CH, a.T, a.meta, a.chunks, sf);
+                                  : ring_item(min(item, nbound - 1), n_shared, TC, CH, a.T, a.meta, a.chunks, sf, 8 * IPB);
     const bool live = item < nbound && itm.live, shared = itm.shared;
     const int e = itm.e, off = itm.off, ntot = itm.ntot, row0 = itm.row0, tc_begin = itm.tc, tc_end = itm.tc + 1;
     int k0 = 0, k1 = a.H;
@@ -1845,7 +1854,7 @@ __global__ __launch_bounds__(256) void k_stream_down_q(SkinnyDownArgs a) {
       if (base >= nlive) break;
     }
     const int item = base + w / NWK;
-    const RingItem itm = ring_item(min(item, nbound - 1), n_shared, TC, CH, a.T, a.meta, a.chunks, sf);
+    const RingItem itm = ring_item(min(item, nbound - 1), n_shared, TC, CH, a.T, a.meta, a.chunks, sf, 8 * IPB);
     const bool live = item < nbound && itm.live, shared = itm.shared;
     const int e = itm.e, off = itm.off, ntot = itm.ntot, row0 = itm.row0, tc_begin = itm.tc, tc_end = itm.tc + 1;
     const int K = shared ? a.Is : a.I;
