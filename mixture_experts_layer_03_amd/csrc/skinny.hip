@@ -707,22 +707,34 @@ struct RingItem {
   int e, off, ntot, row0, tc;
 };
 
-// S: row blocks per placement group (8 x items per block).  Blocks are dealt to the
-// eight XCDs in turn, so block b runs on XCD b % 8.  Within an expert, items are placed
-// by groups of S row blocks: item g S nc + c S + j is chunk c of row block g S + j, so
-// all chunks of a row block land S items apart, on blocks 8 apart, on one XCD, and run
-// in the same window of S nc items: that XCD's L2 fetches the block's rows once for all
-// its chunks (items one after another put them on different XCDs, each fetching the
-// same rows).  With S = 1 the order is row block by row block, chunk innermost.
+// Row block rb and chunk c of item `local` among CH row blocks x nc chunks, placed by
+// groups of S row blocks: item g S nc + c S + j is chunk c of row block g S + j.
+// With one item per block, blocks are dealt to the eight XCDs in turn (block b runs on
+// XCD b % 8), so with S = 8 all chunks of a row block run on one XCD, 8 blocks apart,
+// in the same window of 8 nc items, and that XCD's L2 fetches the rows once for all of
+// them; items one after another would put them on different XCDs, each fetching the
+// same rows.  With S = 1 the order is row block by row block, chunk innermost (with
+// four items per block, a row block's chunks then share one block).
+__device__ __forceinline__ void place_item(int local, int CH, int nc, int S, int& rb, int& c) {
+  const int gs = S * nc, g = local / gs, rem = local - g * gs;
+  const int R = min(S, CH - g * S);  // row blocks of this group (fewer in the last one)
+  c = rem / R;
+  rb = g * S + rem % R;
+}
+
+// S: as for place_item, applied to the routed items of each expert and to the shared
+// items.
 __device__ __forceinline__ RingItem ring_item(int item, int n_shared, int TC, int CH, int T, const int32_t* meta,
                                               const int4* chunks, bool shared_first, int S = 1) {
   RingItem r{};
   int it;  // routed item index
+  const int CHs = n_shared / (TC > 0 ? TC : 1);
   if (shared_first) {
     if (item < n_shared) {
       r.live = r.shared = true;
-      r.row0 = (item / TC) * 16;
-      r.tc = item % TC;
+      int rb;
+      place_item(item, CHs, TC, S, rb, r.tc);
+      r.row0 = rb * 16;
       r.ntot = T;
       return r;
     }
@@ -733,10 +745,13 @@ __device__ __forceinline__ RingItem ring_item(int item, int n_shared, int TC, in
       const int si = item - nr;
       r.live = si < n_shared;
       r.shared = true;
-      r.row0 = (min(si, n_shared - 1) / TC) * 16;
-      r.tc = min(si, n_shared - 1) % TC;
       r.ntot = T;
-      if (r.live || n_shared > 0) return r;
+      if (n_shared > 0) {
+        int rb;
+        place_item(min(si, n_shared - 1), CHs, TC, S, rb, r.tc);
+        r.row0 = rb * 16;
+        return r;
+      }
     }
     it = min(item, nr > 0 ? nr - 1 : 0);
   }
@@ -749,12 +764,10 @@ __device__ __forceinline__ RingItem ring_item(int item, int n_shared, int TC, in
   const int first = r.live ? rec.z : 0, count = r.live ? rec.w : 1;
   const int q0 = r.live ? qa - (rec.y - rec.z) / kDecodeChunk : qa;
   const int nc = (count + kDecodeChunk - 1) / kDecodeChunk;
-  const int local = it - q0 * CH;
-  const int gs = S * nc, g = local / gs, rem = local - g * gs;
-  const int R = min(S, CH - g * S);  // row blocks of this group (fewer in the last one)
-  const int c = rem / R;
+  int rb, c;
+  place_item(it - q0 * CH, CH, nc, S, rb, c);
   r.e = r.live ? rec.x : 0;
-  r.row0 = (g * S + rem % R) * 16;
+  r.row0 = rb * 16;
   r.off = first + c * kDecodeChunk;
   r.ntot = count - c * kDecodeChunk;
   return r;
@@ -832,7 +845,7 @@ __global__ __launch_bounds__(256) void k_stream_up(SkinnyUpArgs a) {
     }
     const int item = base + w / NWK;
     const RingItem itm = FEPL > 0 ? pre
-                                  : ring_item(min(item, nbound - 1), n_shared, TC, CH, a.T, a.meta, a.chunks, sf, 8 * IPB);
+                                  : ring_item(min(item, nbound - 1), n_shared, TC, CH, a.T, a.meta, a.chunks, sf, IPB == 1 ? 8 : 1);
     const bool live = item < nbound && itm.live, shared = itm.shared;
     const int e = itm.e, off = itm.off, ntot = itm.ntot, row0 = itm.row0, tc_begin = itm.tc, tc_end = itm.tc + 1;
     int k0 = 0, k1 = a.H;
@@ -915,7 +928,7 @@ __global__ __launch_bounds__(256) void k_stream_down(SkinnyDownArgs a) {
       if (base >= nlive) break;
     }
     const int item = base + w / NWK;
-    const RingItem itm = ring_item(min(item, nbound - 1), n_shared, TC, CH, a.T, a.meta, a.chunks, sf, 8 * IPB);
+    const RingItem itm = ring_item(min(item, nbound - 1), n_shared, TC, CH, a.T, a.meta, a.chunks, sf, IPB == 1 ? 8 : 1);
     const bool live = item < nbound && itm.live, shared = itm.shared;
     const int e = itm.e, off = itm.off, ntot = itm.ntot, row0 = itm.row0, tc_begin = itm.tc, tc_end = itm.tc + 1;
     const int K = shared ? a.Is : a.I;
@@ -1728,7 +1741,7 @@ __global__ __launch_bounds__(256) void k_stream_up_q(SkinnyUpArgs a) {
     }
     const int item = base + w / NWK;
     const RingItem itm = FEPL > 0 ? pre
-                                  : ring_item(min(item, nbound - 1), n_shared, TC, CH, a.T, a.meta, a.chunks, sf, 8 * IPB);
+                                  : ring_item(min(item, nbound - 1), n_shared, TC, CH, a.T, a.meta, a.chunks, sf, IPB == 1 ? 8 : 1);
     const bool live = item < nbound && itm.live, shared = itm.shared;
     const int e = itm.e, off = itm.off, ntot = itm.ntot, row0 = itm.row0, tc_begin = itm.tc, tc_end = itm.tc + 1;
     int k0 = 0, k1 = a.H;
@@ -1854,7 +1867,7 @@ __global__ __launch_bounds__(256) void k_stream_down_q(SkinnyDownArgs a) {
       if (base >= nlive) break;
     }
     const int item = base + w / NWK;
-    const RingItem itm = ring_item(min(item, nbound - 1), n_shared, TC, CH, a.T, a.meta, a.chunks, sf, 8 * IPB);
+    const RingItem itm = ring_item(min(item, nbound - 1), n_shared, TC, CH, a.T, a.meta, a.chunks, sf, IPB == 1 ? 8 : 1);
     const bool live = item < nbound && itm.live, shared = itm.shared;
     const int e = itm.e, off = itm.off, ntot = itm.ntot, row0 = itm.row0, tc_begin = itm.tc, tc_end = itm.tc + 1;
     const int K = shared ? a.Is : a.I;
