@@ -2141,13 +2141,26 @@ static bool up_uses_ring(const SkinnyUpArgs& a, Act act, WFmt wf) {
 // and whether its blocks split K (one item per block).  Gate/up ring kernels split K
 // over the four wavefronts of a block at every size (measured faster on the bf16, u8
 // and u4 layers from 1 to 64 tokens: finer work units even out the last round), except
-// for the dense MLP, whose token chunks of one row block share its rows best inside one
-// block: it splits only when its items cannot occupy the CUs otherwise.  Split decisions
-// are taken from the whole layer's items, never from `part`.
+// for the dense MLP, whose token chunks of one row block share its rows inside one
+// block unsplit: it splits when its items cannot occupy the CUs otherwise, or, with at
+// most 4 chunks per row block, when split blocks fill the rounds of resident blocks (two
+// per CU) better (unsplit, 64 tokens at intermediate 9216 are 576 blocks, a second round
+// of 64; split, 2304 blocks in 4.5 rounds, a row block's chunks on one XCD: place_item).
+// Measured on the Ling-2.6 layer-0 shape: 32 tokens 78.3 -> 64.9 us, 64 tokens 100.0 ->
+// 95.7 us; split at 128 and 192 tokens (8 and 12 chunks) was slower, 160.8 -> 172.3 us
+// and 218.4 -> 229.2 us.  Split decisions are taken from the whole layer's items, never
+// from `part`.
 static int64_t up_ring_items(const SkinnyUpArgs& a, int ncu, bool& split) {
   const int64_t shared_ring = static_cast<int64_t>(a.Is / 16) * ((a.T + 15) / 16);
   const int64_t routed = static_cast<int64_t>(a.mtiles) * (a.I / 16);
-  split = a.dense ? part_items(0, routed, shared_ring) < 4ll * ncu : true;
+  if (a.dense) {
+    const int64_t items = part_items(0, routed, shared_ring), slots = 2ll * ncu;
+    // share of the block slots of its rounds that `blocks` blocks fill
+    auto fill = [&](int64_t blocks) { return static_cast<double>(blocks) / (((blocks + slots - 1) / slots) * slots); };
+    split = items < 4ll * ncu || ((a.T + 15) / 16 <= 4 && fill(items) > fill((items + 3) / 4));
+  } else {
+    split = true;
+  }
   return part_items(a.part, routed, shared_ring);
 }
 
