@@ -197,12 +197,14 @@ def percentile(sorted_vals, q):
     return sorted_vals[lo] + (sorted_vals[hi] - sorted_vals[lo]) * (pos - lo)
 
 
-def run_graph(moe, cfg, copies, x, steps, warmup):
+def run_graph(moe, cfg, copies, x, steps, warmup, spinup_ms=0.0):
     """HIP-graph replay: the L layer copies' calls captured back to back in one graph (as
     a model's decode step captures its layers), replayed until `steps` layer calls have
     run; returns the seconds for `steps` layer calls and whether every layer's output
     equals its eager result.  (One graph per layer call would add the runtime's per-graph
-    launch cost, about 8 us on this stack, to every call.)"""
+    launch cost, about 8 us on this stack, to every call.)  Like the eager loop, the
+    replays first run untimed for `spinup_ms`: the capture leaves the GPU idle, and the
+    clocks take tens of milliseconds of load to come back up."""
     import torch
     T = x.shape[0]
     L = len(copies)
@@ -228,6 +230,8 @@ def run_graph(moe, cfg, copies, x, steps, warmup):
         g.replay()
     torch.cuda.synchronize()
     ok = all(torch.equal(ys[i], ref[i]) for i in range(L))
+    if spinup_ms > 0:
+        spin_up(lambda i: g.replay(), spinup_ms)
     t0 = time.perf_counter()
     for _ in range(reps):
         g.replay()
@@ -428,6 +432,8 @@ def bench_dense(args):
                 gr.replay()
             torch.cuda.synchronize()
             ok = all(torch.equal(ys[i], ref[i]) for i in range(L))
+            if args.spinup_ms > 0:
+                spin_up(lambda i: gr.replay(), args.spinup_ms)
             t0 = time.perf_counter()
             for _ in range(reps):
                 gr.replay()
@@ -538,7 +544,7 @@ def measure_workload(args, spec, Ts, dev, headline_T=None, cpu=False):
                 r["up_gbps"] = alg["up_bytes_decode"] / (up_ms * 1e-3) / 1e9
                 r["up_hbm_frac"] = r["up_gbps"] / HBM_PEAK_GBPS
         if not args.no_graph:
-            gsecs, ok = run_graph(moe, cfg, cps, x, steps, args.warmup)
+            gsecs, ok = run_graph(moe, cfg, cps, x, steps, args.warmup, args.spinup_ms)
             gt = gsecs / steps
             r.update(graph_ms_per_step=gt * 1e3, graph_tokens_per_s=T / gt,
                      graph_hbm_gbps=alg["bytes"] / gt / 1e9,
